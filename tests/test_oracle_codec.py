@@ -1,0 +1,209 @@
+"""Pins for oracle/codec.py: hand-worked groups, brute force, error bounds, byte layout."""
+import os
+
+import numpy as np
+import pytest
+
+from oracle import codec, numerics as nx, rotation as rot
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(name):
+    with open(os.path.join(GOLD, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                yield line.split()
+
+
+def test_int4_pack_golden():
+    for a, b, byte in _rows("int4_pack.txt"):
+        got = codec.pack_elems(np.array([[int(a), int(b)]]), "int4")[0, 0]
+        assert got == int(byte, 16)
+        back = codec.unpack_elems(np.array([[got]]), "int4", signed=True)[0]
+        assert list(back) == [int(a), int(b)]
+
+
+@pytest.mark.parametrize("fmt,signed,lo,hi", [("int4", True, -8, 7), ("int8", True, -128, 127),
+                                             ("int2", False, 0, 3), ("fp4", False, 0, 15)])
+def test_pack_roundtrip(fmt, signed, lo, hi):
+    rng = np.random.default_rng(0)
+    c = rng.integers(lo, hi + 1, (17, 128))
+    assert np.array_equal(codec.unpack_elems(codec.pack_elems(c, fmt), fmt, signed), c)
+
+
+def test_int2_pack_bit_positions():
+    # element e at bits 2*(e % 4) of byte e // 4
+    c = np.array([[1, 2, 3, 0, 0, 0, 0, 3]])
+    assert list(codec.pack_elems(c, "int2")[0]) == [1 | 2 << 2 | 3 << 4, 3 << 6]
+
+
+def test_int_groups_golden():
+    for kind, vals, codes, scale, off in _rows("int_codes.txt"):
+        y = np.zeros(128, np.float32)
+        v = np.array([float(t) for t in vals.split(",")], np.float32)
+        y[:8] = v
+        want = [int(t) for t in codes.split(",")]
+        if kind == "int4":
+            c, s = codec.quantize_sym(y, "int4", 32)
+            assert float(s[0]) == float(scale)
+            assert list(c[:8]) == want and not c[8:32].any()
+        else:
+            c, s, z = codec.quantize_asym2(y)
+            assert float(s[0]) == float(scale) and float(z[0]) == float(off)
+            assert list(c[:8]) == want and np.all(c[8:32] == 1)
+
+
+def _brute_sym(y, sf, qmax):
+    cand = np.arange(-qmax, qmax + 1)
+    d = np.abs(y.astype(np.float64)[..., None] - cand * np.asarray(sf)[..., None])
+    out = np.empty(y.shape, np.int64)
+    for idx in np.ndindex(y.shape):
+        di = d[idx]
+        best = cand[di == di.min()]
+        out[idx] = best[0] if len(best) == 1 else best[best % 2 == 0][0]
+    return out
+
+
+@pytest.mark.parametrize("fmt,group", [("int4", 32), ("int4", 128), ("int8", 128), ("int8", 32)])
+def test_sym_quant_brute_force_and_bound(fmt, group):
+    rng = np.random.default_rng(11)
+    y = (rng.standard_normal((40, 128)) * rng.uniform(0.01, 5, (40, 1))).astype(np.float32)
+    y[3, :] = 0  # zero vector -> zero scale, zero codes
+    c, s = codec.quantize_sym(y, fmt, group)
+    qmax = codec.qmax_of(fmt)
+    g = group
+    yg = y.reshape(40, 128 // g, g)
+    a = np.abs(yg).max(-1)
+    # scale: nearest fp16 to fl32(a / qmax)
+    t = (a / np.float32(qmax)).astype(np.float32)
+    assert np.array_equal(s, t.astype(np.float16))
+    sf = s.astype(np.float64)[..., None]
+    cg = c.reshape(40, 128 // g, g)
+    assert np.all(np.abs(cg) <= qmax)
+    nz = (sf[..., 0] != 0)
+    assert np.array_equal(cg[nz], _brute_sym(yg, sf, qmax)[nz])
+    # |y - c s| <= s/2 (the clamp can only bite by qmax * |fl32 - fp16| << s/2)
+    err = np.abs(yg - cg * sf)
+    assert np.all(err <= sf / 2 * (1 + 2.0 ** -9))
+    assert not c[3].any() and not s[3].any()
+
+
+def test_asym2_brute_force_and_bound():
+    rng = np.random.default_rng(12)
+    y = (rng.standard_normal((50, 128)) * 0.7).astype(np.float32)
+    t = np.full(128, 1.5, np.float32)
+    c, s, z = codec.quantize_asym2(y, t)
+    yc = np.clip(y, -1.5, 1.5).reshape(50, 4, 32)
+    assert np.array_equal(s, ((yc.max(-1) - yc.min(-1)).astype(np.float32) / np.float32(3)).astype(np.float16))
+    assert np.array_equal(z, yc.min(-1).astype(np.float16))
+    sf = s.astype(np.float64)[..., None]
+    zf = z.astype(np.float32)[..., None]
+    r = (yc - zf).astype(np.float32).astype(np.float64)
+    cand = np.arange(4)
+    cg = c.reshape(50, 4, 32)
+    for idx in np.ndindex(r.shape):
+        d = np.abs(r[idx] - cand * sf[idx[:2]][0])
+        best = cand[d == d.min()]
+        assert cg[idx] == (best[0] if len(best) == 1 else best[best % 2 == 0][0])
+    deq = codec.dequant_asym2(c, s, z).reshape(50, 4, 32)
+    lo = yc.min(-1)[..., None].astype(np.float64)
+    slack = np.abs(lo - zf) + 3 * np.abs(((yc.max(-1) - yc.min(-1)) / 3)[..., None] - sf)
+    assert np.all(np.abs(yc - deq) <= sf / 2 + slack + 1e-12)
+
+
+def test_fp4_golden_blocks():
+    for name, mode, sc, codes, vals in _rows("fp4_search_block.txt"):
+        y = np.zeros(128, np.float32)
+        y[:16] = [float(t) for t in vals.split(",")]
+        c, scodes = codec.quantize_fp4(y, mode)
+        assert scodes[0] == int(sc, 16), name
+        assert "".join("%X" % v for v in c[:16]) == codes, name
+
+
+def test_fp4_search_never_worse_than_absmax():
+    rng = np.random.default_rng(13)
+    y = rng.standard_t(4, (300, 128)).astype(np.float32)
+    cs, ss = codec.quantize_fp4(y, "search9")
+    ca, sa = codec.quantize_fp4(y, "absmax")
+    es = ((codec.dequant_fp4(cs, ss) - y) ** 2).reshape(300, 8, 16).sum(-1)
+    ea = ((codec.dequant_fp4(ca, sa) - y) ** 2).reshape(300, 8, 16).sum(-1)
+    assert np.all(es <= ea * (1 + 1e-6))
+    assert es.sum() < ea.sum()  # the search actually finds better scales on t(4) data
+    # chosen scale is among the 9 candidates, and no candidate is better in fp64 beyond rounding
+    t = (np.abs(y.reshape(300, 8, 16)).max(-1) / np.float32(6)).astype(np.float32)
+    for m in codec.SEARCH_M:
+        S = nx.e4m3_value(nx.e4m3_encode_nonneg((t * m).astype(np.float32)))
+        q = nx.e2m1_quantize(y.reshape(300, 8, 16), np.where(S == 0, 1, S)[..., None])
+        e = ((nx.e2m1_value(q) * S[..., None] - y.reshape(300, 8, 16)) ** 2).sum(-1)
+        assert np.all(es <= e * (1 + 1e-5) + 1e-30)
+
+
+def test_fp4_element_bound():
+    rng = np.random.default_rng(14)
+    y = rng.standard_normal((100, 128)).astype(np.float32)
+    c, sc = codec.quantize_fp4(y, "absmax")
+    S = nx.e4m3_value(sc)[..., None]
+    err = np.abs(codec.dequant_fp4(c, sc).reshape(100, 8, 16) - y.reshape(100, 8, 16))
+    # inside the grid the error is at most half the local spacing (<= 1 * S); above 6S it saturates
+    inside = np.abs(y.reshape(100, 8, 16)) <= 6 * S
+    assert np.all(err[inside] <= S.repeat(16, -1)[inside] * 1.0 + 1e-12)
+
+
+def _layout_cache(fmt_k, fmt_v, T=192):
+    return codec.Cache(2, 3, T, fmt_k, fmt_v, 32, 32, keep_fp16_copy=False)
+
+
+def test_v_tile_layout_by_hand():
+    cache = _layout_cache("int4", "int4")
+    codes = np.zeros((64, 128), np.int16)
+    codes[:, 5] = (np.arange(64) % 15) - 7  # channel 5 holds -7..7 along tokens
+    meta = np.ones((64, 4), np.float16)
+    cache._v_store(0, 0, 0, codes, meta)
+    row = cache.v_codes[0, 0, 0, 5]  # 32 bytes: tokens 2j (low), 2j+1 (high)
+    for j in range(32):
+        lo, hi = codes[2 * j, 5] & 0xF, codes[2 * j + 1, 5] & 0xF
+        assert row[j] == lo | hi << 4
+    assert not cache.v_codes[0, 0, 0, 4].any()
+
+
+def test_append_split_equals_single_call():
+    rng = np.random.default_rng(15)
+    s = np.where(rng.integers(0, 2, 128) == 1, 1, -1)
+    for kf, vf in [("int4", "int4"), ("int8", "int2"), ("fp4", "fp4")]:
+        k = (rng.standard_normal((2, 3, 150, 128)) * 2).astype(np.float16).view(np.uint16)
+        v = (rng.standard_normal((2, 3, 150, 128)) * 2).astype(np.float16).view(np.uint16)
+        a = _layout_cache(kf, vf)
+        b = _layout_cache(kf, vf)
+        codec.append(a, k, v, np.array([3, 10]), "f16", "sign_fwht", s)
+        codec.append(b, k[:, :, :37], v[:, :, :37], np.array([3, 10]), "f16", "sign_fwht", s)
+        codec.append(b, k[:, :, 37:], v[:, :, 37:], np.array([40, 47]), "f16", "sign_fwht", s)
+        for name in ("k_codes", "k_meta", "v_codes", "v_meta"):
+            assert np.array_equal(getattr(a, name), getattr(b, name)), (kf, vf, name)
+
+
+def test_decode_matches_quantize():
+    rng = np.random.default_rng(16)
+    s = np.where(rng.integers(0, 2, 128) == 1, 1, -1)
+    k = rng.standard_normal((2, 3, 100, 128)).astype(np.float16).view(np.uint16)
+    v = rng.standard_normal((2, 3, 100, 128)).astype(np.float16).view(np.uint16)
+    cache = _layout_cache("int4", "fp4")
+    yk, yv = codec.append(cache, k, v, np.array([0, 64]), "f16", "sign_fwht", s)
+    for b, t0 in ((0, 0), (1, 64)):
+        for h in range(3):
+            ck, mk = codec.quantize(yk[b, h], "int4", 32)
+            cv, mv = codec.quantize(yv[b, h], "fp4")
+            assert np.array_equal(codec.decode_k(cache, b, h, t0, t0 + 100), codec.dequantize(ck, mk, "int4", 32))
+            assert np.array_equal(codec.decode_v(cache, b, h, t0, t0 + 100), codec.dequantize(cv, mv, "fp4"))
+
+
+def test_calibrate_clip_definition():
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal((2, 300, 128)).astype(np.float16).view(np.uint16)
+    q, rr = np.linalg.qr(rng.standard_normal((128, 128)))
+    r16 = q.astype(np.float16)
+    t = codec.calibrate_clip(x, "f16", "dense", r16=r16)
+    y = x.view(np.float16).astype(np.float64) @ r16.astype(np.float64).T
+    ref = 0.9 * np.abs(y).max(axis=1)
+    assert np.allclose(t, ref, rtol=1e-5)

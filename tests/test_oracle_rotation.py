@@ -1,0 +1,105 @@
+"""Pins for oracle/rotation.py: closed forms, library routines and hand-derived orders."""
+import os
+from fractions import Fraction
+
+import numpy as np
+import scipy.linalg
+
+from oracle import rotation as rot
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(name):
+    with open(os.path.join(GOLD, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                yield line.split()
+
+
+def test_hadamard_matches_scipy():
+    assert np.array_equal(rot.hadamard_sylvester(128), scipy.linalg.hadamard(128).astype(np.float64))
+
+
+def test_hadamard_involution():
+    h = rot.hadamard_sylvester(128)
+    assert np.array_equal(h @ h, 128 * np.eye(128))
+
+
+def test_inv_sqrt_constant_is_nearest_fp32():
+    c = rot.INV_SQRT_D_F32
+    assert int(c.view(np.uint32)) == 0x3DB504F3
+    # |c^2 * 128 - 1| is smallest among c and its neighbours (exact rationals)
+    cands = [np.nextafter(c, np.float32(0)), c, np.nextafter(c, np.float32(1))]
+    err = [abs(Fraction(float(x)) ** 2 * 128 - 1) for x in cands]
+    assert err[1] == min(err)
+
+
+def test_sign_fwht_close_to_closed_form():
+    rng = np.random.default_rng(1)
+    s = np.where(rng.integers(0, 2, 128) == 1, 1, -1)
+    x = rng.standard_normal((500, 128)).astype(np.float16).astype(np.float32)
+    x[:, 5] *= 30
+    y = rot.sign_fwht_f32(x, s)
+    R = rot.rotation_matrix_f64("sign_fwht", s)
+    ref = x.astype(np.float64) @ R.T
+    # 7 rounded stages + 1 multiply: error well under 16 ulp of the vector norm
+    tol = 16 * 2.0 ** -24 * np.linalg.norm(x, axis=1, keepdims=True)
+    assert np.all(np.abs(y - ref) <= tol)
+    # norm preserved up to fp32 rounding; orthogonality of the fp64 operator
+    assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-5)
+    assert np.allclose(R @ R.T, np.eye(128), atol=1e-12)
+
+
+def test_sign_fwht_unit_vector_is_scaled_first_column():
+    s = np.ones(128)
+    s[0] = -1
+    x = np.zeros((1, 128), np.float32)
+    x[0, 0] = 1
+    y = rot.sign_fwht_f32(x, s)
+    assert np.all(y == -rot.INV_SQRT_D_F32)
+
+
+def test_sign_fwht_integer_inputs_exact():
+    # small integers: every butterfly is exact, so y = fl32((H diag(s) x) * c) exactly
+    rng = np.random.default_rng(2)
+    s = np.where(rng.integers(0, 2, 128) == 1, 1, -1)
+    x = rng.integers(-50, 50, (64, 128)).astype(np.float32)
+    hx = (x.astype(np.int64) * s) @ scipy.linalg.hadamard(128).T
+    want = hx.astype(np.float32) * rot.INV_SQRT_D_F32
+    assert np.array_equal(rot.sign_fwht_f32(x, s), want)
+
+
+def test_fwht_stage_order_golden():
+    x = np.zeros(128, np.float32)
+    x[0], x[1], x[2] = 2.0, 3 * 2.0 ** -24, 2.0 ** -23
+    assert np.float16(x[1]) == x[1] and np.float16(x[2]) == x[2]  # valid fp16 inputs
+    u = rot.fwht_f32(x)
+    for idx, bits in _rows("fwht_stage_order.txt"):
+        assert int(u[int(idx)].view(np.uint32)) == int(bits, 16)
+
+
+def test_dense_chain_order_golden():
+    x = np.full(128, 2.0 ** -24, np.float32)
+    x[0] = 1.0
+    r = np.zeros((128, 128), np.float16)
+    r[0, :] = 1
+    r[1, 1:] = 1
+    y = rot.dense_rotate_f32(x[None, :], r)[0]
+    for row, bits in _rows("dense_chain_order.txt"):
+        assert int(y[int(row)].view(np.uint32)) == int(bits, 16)
+
+
+def test_dense_rotation_close_to_matvec():
+    rng = np.random.default_rng(3)
+    q, rr = np.linalg.qr(rng.standard_normal((128, 128)))
+    r16 = (q * np.sign(np.diag(rr))).astype(np.float16)
+    x = rng.standard_normal((200, 128)).astype(np.float16).astype(np.float32)
+    y = rot.dense_rotate_f32(x, r16)
+    ref = x.astype(np.float64) @ r16.astype(np.float64).T
+    bound = 128 * 2.0 ** -24 * (np.abs(x).astype(np.float64) @ np.abs(r16.astype(np.float64)).T)
+    assert np.all(np.abs(y - ref) <= bound)
+    # fp16 rounding of an orthogonal matrix keeps it orthogonal to ~1e-3
+    R = rot.rotation_matrix_f64("dense", r16=r16)
+    assert np.abs(R @ R.T - np.eye(128)).max() < 2e-3
