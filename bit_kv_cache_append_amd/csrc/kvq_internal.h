@@ -1,0 +1,119 @@
+// Internal declarations shared by the kvq HIP translation units (not installed).
+// gfx950 only: wave64, MFMA, 160 KiB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+constexpr int D = 128;         // head dim
+constexpr int TILE = 64;       // tokens per V tile / descriptor block / decode chunk
+constexpr int MAX_BATCH = 256;
+
+// ----------------------------------------------------------------- format facts
+__host__ __device__ constexpr int fmt_bits(int f) { return f == KVQ_INT8 ? 8 : (f == KVQ_INT2 ? 2 : 4); }
+__host__ __device__ constexpr int row_bytes(int f) { return D * fmt_bits(f) / 8; }  // KB
+__host__ __device__ constexpr int chan_bytes(int f) { return TILE * fmt_bits(f) / 8; }  // CB
+// group size of a format: INT4/INT8 take the configured group, INT2 32, FP4 16
+__host__ __device__ constexpr int fmt_group(int f, int g) { return f == KVQ_INT2 ? 32 : (f == KVQ_FP4 ? 16 : g); }
+// metadata elements per vector and bytes per element
+__host__ __device__ constexpr int meta_elems(int f, int g) {
+  return f == KVQ_INT2 ? 8 : (f == KVQ_FP4 ? 8 : D / g);
+}
+__host__ __device__ constexpr int meta_esize(int f) { return f == KVQ_FP4 ? 1 : 2; }
+__host__ __device__ constexpr int meta_bytes(int f, int g) { return meta_elems(f, g) * meta_esize(f); }  // KM
+
+// ----------------------------------------------------------------- kernel args
+struct SeqArray {
+  int32_t v[MAX_BATCH];
+};
+
+struct AppendArgs {
+  const uint16_t* k_new;  // [B][H][n][128]
+  const uint16_t* v_new;
+  uint8_t* k_codes;
+  uint8_t* k_meta;
+  uint8_t* v_codes;
+  uint8_t* v_meta;
+  float* desc;  // may be null
+  uint16_t* k_orig;  // may be null
+  uint16_t* v_orig;
+  const int8_t* signs;
+  const uint16_t* rot;  // fp16 bits [128][128]
+  const float* clip_k;
+  const float* clip_v;
+  int32_t B, H, Tmax, n_new;
+  int32_t in_bf16;
+  int32_t k_fmt, v_fmt, k_group, v_group, scale_mode, rotation;
+  SeqArray start;
+};
+
+struct CalibArgs {
+  const uint16_t* x;  // [H][n][128]
+  float* out;         // [H][128]
+  const int8_t* signs;
+  const uint16_t* rot;
+  int32_t H, n, in_bf16, rotation;
+  float ratio;
+};
+
+struct BoundArgs {
+  const uint16_t* q;  // [B][Hq][128]
+  const float* desc;  // [B][H][nt][3]
+  float* bound;       // [B][H][nt]
+  uint8_t* flags;
+  int32_t B, Hq, H, nt, in_bf16;
+  float scale, tau;
+  SeqArray seq;
+};
+
+// Decode partial results, one record per (b, hq, split) in the workspace.
+// m: running max (log2 domain), l: sum of exp2, eta: sum of p * ev (certified),
+// ekmax/vnmax: maxima over this split's blocks, o: rotated-basis accumulator,
+// oo: original-basis accumulator for exactly recomputed blocks.
+constexpr int PART_FLOATS = 8 + 2 * D;
+constexpr int MAX_SPLITS = 128;
+
+struct DecodeArgs {
+  const uint16_t* q;  // [B][Hq][128]
+  const uint8_t* k_codes;
+  const uint8_t* k_meta;
+  const uint8_t* v_codes;
+  const uint8_t* v_meta;
+  const float* desc;
+  const uint16_t* k_orig;
+  const uint16_t* v_orig;
+  const uint8_t* flags;  // [B][H][nt] or null
+  const int8_t* signs;
+  const uint16_t* rot;
+  float* part;  // [B][Hq][n_splits][PART_FLOATS]
+  int32_t B, Hq, H, G, Tmax, nt;
+  int32_t in_bf16, rotation, k_group, v_group;
+  int32_t n_splits, chunks_per_split;
+  float scale;  // softmax scale
+  SeqArray seq;
+};
+
+struct CombineArgs {
+  const float* part;
+  float* out;   // [B][Hq][128]
+  float* cert;  // [B][Hq] or null
+  const int8_t* signs;
+  const uint16_t* rot;
+  const uint16_t* q;  // for ||q|| in the certificate
+  int32_t B, Hq, n_splits, rotation, in_bf16;
+  float scale;
+  SeqArray seq;
+};
+
+// host-side launchers (defined in the .hip files)
+hipError_t launch_append(const AppendArgs& a, int tensor, int grid_x, hipStream_t s);
+hipError_t launch_calibrate(const CalibArgs& a, hipStream_t s);
+hipError_t launch_bound(const BoundArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int k_fmt, int v_fmt, bool dense, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace kvq

@@ -1,0 +1,233 @@
+/*
+ * kvq.h -- rotate-then-quantize KV cache with fused single-token decode attention
+ * for AMD Instinct MI355X (gfx950).  C ABI; all compute runs in HIP kernels that
+ * are enqueued on the caller's stream.
+ *
+ * What the calls compute (the pages, by title and section):
+ *  - kvq_append: each new K/V head vector is widened to fp32, sign-flipped and
+ *    rotated by a fast orthogonal transform, scaled per group and rounded to
+ *    signed int4/int8 with two int4 codes per byte ("When Quantization Is Free:
+ *    An int4 KV Cache That Outruns fp16 on Apple Silicon", Methodology sections
+ *    1-3); or rotated by a fixed dense matrix, clipped per channel and coded in
+ *    2 bits ("OSCAR: Offline Spectral Covariance-Aware Rotation for 2-bit KV
+ *    Cache Quantization", section 2.2); or coded as FP4 E2M1 with one E4M3 scale
+ *    per 16 elements whose value is searched around the absmax scale ("Search
+ *    Your Block Floating Point Scales!", Methodology, ScaleSearch).  With
+ *    keep_fp16_copy it also stores the original vectors and per-block error
+ *    descriptors ("Runtime-Certified Bounded-Error Quantized Attention",
+ *    Methodology section 1).
+ *  - kvq_error_bound: per 64-token block, a certified bound on the logit and
+ *    value errors from the query norm and the descriptors, and the blocks it
+ *    flags for exact recompute ("Runtime-Certified ...", Methodology section 2).
+ *  - kvq_decode_attn: rotates the query once, streams the packed cache,
+ *    dequantizes in registers and computes softmax(q k^T * scale) v for the
+ *    newest token with grouped-query heads; flagged blocks are recomputed from
+ *    the stored originals; the output is rotated back to the original basis
+ *    ("OSCAR", section 2.2B: unpack, dequantize, inverse rotation, attention).
+ *  - kvq_decode_attn_dense: the same decode over uncompressed fp16/bf16 K/V
+ *    (the baseline the compressed cache is compared against, and the full
+ *    dense rung of the fallback).
+ *  - kvq_calibrate_clip: per-channel clipping thresholds from rotated
+ *    calibration vectors ("OSCAR", section 2.2A, clipping thresholds).
+ *
+ * Conventions for every call:
+ *  - Ownership: the caller allocates and frees every buffer; the library never
+ *    allocates device or host memory and keeps no state between calls.
+ *    Pointers named *_host are host memory, all others device memory.
+ *  - Asynchrony: work is enqueued on `stream` (0 = the null stream); results are
+ *    valid once the stream has synchronised.  Calls that share buffers must be
+ *    ordered by the caller (same stream or events).
+ *  - Errors: arguments are validated on the host before anything is enqueued; a
+ *    failure returns a negative kvq_status, enqueues nothing, and leaves a
+ *    message for kvq_last_error() (thread-local).  A failed kernel launch
+ *    returns KVQ_ERR_HIP.  No C++ exception crosses this interface.
+ *  - Sizes: head_dim must be 128; max_ctx a positive multiple of 64; batch at
+ *    most 256; n_q_heads a multiple of n_kv_heads (the group size G =
+ *    n_q_heads / n_kv_heads; query head hq reads kv head hq / G).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_ABI_VERSION 1
+
+typedef int32_t kvq_status;
+#define KVQ_OK 0
+#define KVQ_ERR_INVALID_ARG (-1)  /* bad shape, enum, pointer, alignment or range */
+#define KVQ_ERR_UNSUPPORTED (-2)  /* valid but not implemented combination */
+#define KVQ_ERR_WORKSPACE (-3)    /* workspace missing or too small */
+#define KVQ_ERR_HIP (-4)          /* a HIP runtime call or launch failed */
+
+/* input dtype of K/V/q vectors */
+#define KVQ_F16 0
+#define KVQ_BF16 1
+
+/* code formats (K and V independently) */
+#define KVQ_INT4 0 /* symmetric, codes -7..7, fp16 scale per group (32 or 128) */
+#define KVQ_INT8 1 /* symmetric, codes -127..127, fp16 scale per group (32 or 128) */
+#define KVQ_INT2 2 /* asymmetric, codes 0..3, fp16 scale + fp16 offset per 32 */
+#define KVQ_FP4 3  /* E2M1 codes, one E4M3 scale per 16 */
+
+/* rotation applied before quantization (and to the query / output) */
+#define KVQ_ROT_NONE 0
+#define KVQ_ROT_SIGN_FWHT 1 /* y = fl32(FWHT(s * x) * fl32(1/sqrt(128))) */
+#define KVQ_ROT_DENSE 2     /* y_j = sum_k R16[j][k] x_k, fp32 chain in k order */
+
+/* FP4 scale selection */
+#define KVQ_SCALE_ABSMAX 0  /* S = E4M3(absmax / 6) */
+#define KVQ_SCALE_SEARCH9 1 /* best of E4M3(absmax/6 * m), m = 0.900, 0.925, ..., 1.100 */
+
+/* indices into the array filled by kvq_buffer_bytes */
+#define KVQ_BUF_K_CODES 0
+#define KVQ_BUF_K_META 1
+#define KVQ_BUF_V_CODES 2
+#define KVQ_BUF_V_META 3
+#define KVQ_BUF_BLK_DESC 4
+#define KVQ_BUF_K_ORIG 5
+#define KVQ_BUF_V_ORIG 6
+#define KVQ_NUM_BUFS 7
+
+/* Shapes and formats of one cache (one layer).  Plain values, passed by pointer. */
+typedef struct kvq_params {
+  int32_t batch;          /* B, 1..256 */
+  int32_t n_q_heads;      /* Hq */
+  int32_t n_kv_heads;     /* Hkv; Hq % Hkv == 0 */
+  int32_t head_dim;       /* must be 128 */
+  int32_t max_ctx;        /* Tmax positions per sequence, multiple of 64 */
+  int32_t in_dtype;       /* KVQ_F16 | KVQ_BF16 */
+  int32_t k_fmt, v_fmt;   /* KVQ_INT4 | KVQ_INT8 | KVQ_INT2 | KVQ_FP4 (V: not INT8) */
+  int32_t k_group;        /* INT4/INT8: 32 or 128; ignored otherwise */
+  int32_t v_group;        /* INT4: 32 or 128; ignored otherwise */
+  int32_t scale_mode;     /* KVQ_SCALE_*: FP4 only */
+  int32_t rotation;       /* KVQ_ROT_* */
+  int32_t keep_fp16_copy; /* nonzero: store originals + per-block descriptors */
+  float softmax_scale;    /* 0 => 1/sqrt(head_dim) */
+} kvq_params;
+
+/*
+ * Device buffers of one cache.  Byte layouts (little-endian; b batch, h kv head,
+ * t position, c channel, nt = max_ctx / 64):
+ *   k_codes [B][Hkv][Tmax][KB]      KB = 64 (INT4, FP4), 128 (INT8), 32 (INT2):
+ *                                   element c at nibble c%2 of byte c/2 (INT4/FP4,
+ *                                   even element low), bits 2*(c%4) of byte c/4
+ *                                   (INT2), byte c (INT8); INT4/INT8 two's complement
+ *   k_meta  [B][Hkv][Tmax][KM]      fp16 scales per group (INT4/INT8: 128/group of
+ *                                   them), INT2: 4 fp16 scales then 4 fp16 offsets,
+ *                                   FP4: 8 E4M3 bytes
+ *   v_codes [B][Hkv][nt][128][CB]   per 64-token tile, channel-major: channel c's 64
+ *                                   codes packed along tokens with the rules above
+ *                                   (CB = 32 for INT4/FP4, 16 for INT2)
+ *   v_meta  [B][Hkv][nt][NM][64]    per tile, metadata element m of token tau
+ *                                   (fp16, or E4M3 bytes for FP4)
+ *   blk_desc[B][Hkv][nt][3]         fp32 (ek, ev, vn) per 64-token block: max key /
+ *                                   value reconstruction error norm and max value
+ *                                   norm; combined by max, so zero it when a cache
+ *                                   is (re)started.  Needed iff keep_fp16_copy.
+ *   k_orig, v_orig [B][Hkv][Tmax][128]  in_dtype originals; needed iff keep_fp16_copy
+ *   signs   [128] int8 of +1/-1                 needed for KVQ_ROT_SIGN_FWHT
+ *   rot_f16 [128][128] fp16 bits, row-major     needed for KVQ_ROT_DENSE
+ *   clip_k, clip_v [Hkv][128] fp32 thresholds   optional, INT2 only (NULL = none)
+ * Code and metadata buffers must be 16-byte aligned.
+ */
+typedef struct kvq_cache {
+  void* k_codes;
+  void* k_meta;
+  void* v_codes;
+  void* v_meta;
+  float* blk_desc;
+  void* k_orig;
+  void* v_orig;
+  const int8_t* signs;
+  const uint16_t* rot_f16;
+  const float* clip_k;
+  const float* clip_v;
+} kvq_cache;
+
+/* Returns KVQ_ABI_VERSION. */
+int32_t kvq_abi_version(void);
+
+/* Human-readable name of a status code (static string). */
+const char* kvq_status_str(kvq_status s);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* kvq_last_error(void);
+
+/* Bytes of each cache buffer for these params, written to out_bytes[KVQ_NUM_BUFS]
+ * (0 for buffers the configuration does not use).  Host only. */
+kvq_status kvq_buffer_bytes(const kvq_params* p, size_t* out_bytes);
+
+/* Workspace bytes kvq_decode_attn / kvq_decode_attn_dense need for these params
+ * (depends on batch, heads and max_ctx only).  Host only; 0 on invalid params. */
+size_t kvq_decode_workspace_bytes(const kvq_params* p);
+
+/*
+ * Append n_new tokens to every sequence: positions [start_pos_host[b],
+ * start_pos_host[b] + n_new) of sequence b are (over)written.
+ *   k_new, v_new: device [B][Hkv][n_new][128] in_dtype, contiguous.
+ *   start_pos_host: host [B]; 0 <= start < start + n_new <= max_ctx.
+ * Codes and scales are bit-exact functions of the inputs (fp32 arithmetic in a
+ * fixed order, round-half-to-even of exact quotients).  Other positions of the
+ * cache are left unchanged.  n_new == 0 is a no-op.
+ */
+kvq_status kvq_append(const kvq_params* p, const kvq_cache* cache, const void* k_new, const void* v_new,
+                      const int32_t* start_pos_host, int32_t n_new, void* stream);
+
+/*
+ * Per-block error bound (needs keep_fp16_copy and descriptors).  For block j of
+ * kv head h of sequence b (tokens [64j, 64j+64) below seq_len_host[b]):
+ *   bound = max_{hq in group h} ||q_hq|| * scale * ek_j + ev_j,  flag = bound > tau;
+ * blocks at or beyond seq_len get bound 0 and flag 0.
+ *   q: device [B][Hq][128] in_dtype; seq_len_host: host [B], 0..max_ctx.
+ *   block_bound: device fp32 [B][Hkv][max_ctx/64]; block_flags: device uint8, same shape.
+ */
+kvq_status kvq_error_bound(const kvq_params* p, const kvq_cache* cache, const void* q,
+                           const int32_t* seq_len_host, float tau, float* block_bound,
+                           uint8_t* block_flags, void* stream);
+
+/*
+ * Decode attention of one query token per (b, hq) over positions [0, seq_len_host[b]).
+ *   q: device [B][Hq][128] in_dtype.
+ *   block_flags: device uint8 [B][Hkv][max_ctx/64] or NULL; a nonzero flag makes
+ *     the block use k_orig/v_orig exactly (needs keep_fp16_copy).
+ *   out: device fp32 [B][Hq][128], original (unrotated) basis.  Rows with
+ *     seq_len 0 are written as zeros.
+ *   certificate: device fp32 [B][Hq] or NULL (needs keep_fp16_copy): an upper bound
+ *     on ||out - dense attention over the originals||_2 for that row.
+ *   workspace: device, >= kvq_decode_workspace_bytes(p) bytes, 256-byte aligned.
+ * Attention output differs from exact fp64 attention over the decoded cache by
+ * fp16 rounding of the query/probabilities and fp32 accumulation only.
+ */
+kvq_status kvq_decode_attn(const kvq_params* p, const kvq_cache* cache, const void* q,
+                           const int32_t* seq_len_host, const uint8_t* block_flags, float* out,
+                           float* certificate, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode attention over uncompressed K/V in the layout of k_orig/v_orig
+ * ([B][Hkv][Tmax][128] in_dtype); no rotation.  Same q/out/workspace contract as
+ * kvq_decode_attn.  Only the shape fields and in_dtype of p are used.
+ */
+kvq_status kvq_decode_attn_dense(const kvq_params* p, const void* k, const void* v, const void* q,
+                                 const int32_t* seq_len_host, float* out, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
+ * Clipping thresholds for KVQ_INT2: t[h][c] = fl32(ratio * max_t |y_t,c|), with y
+ * the same fp32 rotation kvq_append applies.
+ *   calib_k, calib_v: device [Hkv][n_tokens][128] in_dtype; n_tokens >= 1.
+ *   clip_k_out, clip_v_out: device fp32 [Hkv][128].
+ */
+kvq_status kvq_calibrate_clip(const kvq_params* p, const kvq_cache* cache, const void* calib_k,
+                              const void* calib_v, int32_t n_tokens, float ratio, float* clip_k_out,
+                              float* clip_v_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,70 @@
+"""CPU checks of the C-ABI library: it loads, exports every declared entry point,
+reports sizes, and rejects bad arguments before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_kv_cache_append_amd as kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = kvq.lib()
+    names = _declared()
+    assert "kvq_append" in names and "kvq_decode_attn" in names and "kvq_error_bound" in names
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+    assert L.kvq_abi_version() == 1
+
+
+def test_buffer_sizes():
+    p = kvq.make_params(16, 32, 8, 8192, "int4", "int4", 32, 32)
+    sz = kvq.buffer_bytes(p)
+    streams = 16 * 8
+    assert sz["k_codes"] == streams * 8192 * 64
+    assert sz["k_meta"] == streams * 8192 * 8
+    assert sz["v_codes"] == streams * 8192 * 64
+    assert sz["v_meta"] == streams * 8192 * 8
+    assert sz["blk_desc"] == 0 and sz["k_orig"] == 0
+    p3 = kvq.make_params(32, 32, 8, 32768, "int8", "int4", 128, 128, keep_fp16_copy=True)
+    s3 = kvq.buffer_bytes(p3)
+    assert s3["k_codes"] == 256 * 32768 * 128 and s3["k_meta"] == 256 * 32768 * 2
+    assert s3["v_meta"] == 256 * 32768 * 2 and s3["blk_desc"] == 256 * 512 * 12
+    p4 = kvq.make_params(64, 32, 8, 32768, "int2", "int2", rotation="dense")
+    s4 = kvq.buffer_bytes(p4)
+    assert s4["k_codes"] == 512 * 32768 * 32 and s4["k_meta"] == 512 * 32768 * 16
+    p5 = kvq.make_params(8, 32, 8, 131072, "fp4", "fp4", dtype="bf16", scale_mode="search9")
+    s5 = kvq.buffer_bytes(p5)
+    assert s5["k_codes"] == 64 * 131072 * 64 and s5["v_meta"] == 64 * 131072 * 8
+    assert kvq.decode_workspace_bytes(p) > 0
+
+
+@pytest.mark.parametrize("field,value", [("head_dim", 64), ("max_ctx", 100), ("batch", 0), ("n_q_heads", 7),
+                                         ("k_group", 16), ("v_fmt", 1), ("rotation", 9)])
+def test_invalid_params_rejected(field, value):
+    p = kvq.make_params(2, 8, 2, 256)
+    setattr(p, field, value)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.buffer_bytes(p)
+    assert e.value.status in (-1, -2)
+
+
+def test_null_pointers_rejected_without_gpu():
+    L = kvq.lib()
+    p = kvq.make_params(2, 8, 2, 256)
+    cs = kvq.CacheStruct()
+    starts = (ctypes.c_int32 * 2)(0, 0)
+    st = L.kvq_append(ctypes.byref(p), ctypes.byref(cs), None, None, starts, 4, None)
+    assert st == -1 and b"NULL" in L.kvq_last_error()
+    seq = (ctypes.c_int32 * 2)(10, 10)
+    st = L.kvq_decode_attn(ctypes.byref(p), ctypes.byref(cs), None, seq, None, None, None, None, 0, None)
+    assert st == -1
+    assert L.kvq_status_str(-3) == b"KVQ_ERR_WORKSPACE"
