@@ -106,6 +106,13 @@ int choose_splits(const kvq_params* p, int max_chunks) {
 
 int max_splits_for(const kvq_params* p) { return choose_splits(p, p->max_ctx / TILE); }
 
+// workspace: arrival counters (one per (b, kv head, head group)), 256-byte aligned, then records
+size_t counter_bytes(const kvq_params* p) {
+  const int G = p->n_q_heads / p->n_kv_heads;
+  const size_t n = (size_t)p->batch * p->n_kv_heads * ((G + 3) / 4);
+  return (n * sizeof(unsigned int) + 255) & ~(size_t)255;
+}
+
 }  // namespace
 
 extern "C" {
@@ -145,7 +152,7 @@ kvq_status kvq_buffer_bytes(const kvq_params* p, size_t* out) {
 
 size_t kvq_decode_workspace_bytes(const kvq_params* p) {
   if (check_params(p)) return 0;
-  return (size_t)p->batch * p->n_q_heads * max_splits_for(p) * PART_FLOATS * sizeof(float);
+  return counter_bytes(p) + (size_t)p->batch * p->n_q_heads * max_splits_for(p) * PART_FLOATS * sizeof(float);
 }
 
 kvq_status kvq_append(const kvq_params* p, const kvq_cache* c, const void* k_new, const void* v_new,
@@ -196,11 +203,8 @@ kvq_status kvq_append(const kvq_params* p, const kvq_cache* c, const void* k_new
   a.v_group = eff_group(p->v_fmt, p->v_group);
   a.scale_mode = p->scale_mode;
   a.rotation = p->rotation;
-  hipStream_t s = (hipStream_t)stream;
-  for (int tensor = 0; tensor < 2; ++tensor) {
-    hipError_t e = launch_append(a, tensor, max_tiles, s);
-    if (e != hipSuccess) return hip_fail(e, "append launch");
-  }
+  hipError_t e = launch_append(a, max_tiles, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
   return KVQ_OK;
 }
 
@@ -299,7 +303,10 @@ static kvq_status decode_common(const kvq_params* p, const kvq_cache* c, const v
     a.signs = c->signs;
     a.rot = c->rot_f16;
   }
-  a.part = (float*)ws;
+  a.counters = (unsigned int*)ws;
+  a.part = (float*)((char*)ws + counter_bytes(p));
+  a.out = out;
+  a.cert = dense ? nullptr : cert;
   a.B = p->batch;
   a.Hq = p->n_q_heads;
   a.H = p->n_kv_heads;
@@ -318,23 +325,6 @@ static kvq_status decode_common(const kvq_params* p, const kvq_cache* c, const v
   hipError_t e = launch_decode(a, p->k_fmt, p->v_fmt, dense, s);
   if (e == hipErrorNotSupported) return fail(KVQ_ERR_UNSUPPORTED, "format combination not supported by decode");
   if (e != hipSuccess) return hip_fail(e, "decode launch");
-  CombineArgs cb;
-  memset(&cb, 0, sizeof(cb));
-  cb.part = a.part;
-  cb.out = out;
-  cb.cert = dense ? nullptr : cert;
-  cb.signs = a.signs;
-  cb.rot = a.rot;
-  cb.q = a.q;
-  cb.B = a.B;
-  cb.Hq = a.Hq;
-  cb.n_splits = n_splits;
-  cb.rotation = a.rotation;
-  cb.in_bf16 = a.in_bf16;
-  cb.scale = a.scale;
-  cb.seq = a.seq;
-  e = launch_combine(cb, s);
-  if (e != hipSuccess) return hip_fail(e, "combine launch");
   return KVQ_OK;
 }
 

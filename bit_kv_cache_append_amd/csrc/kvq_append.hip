@@ -319,9 +319,10 @@ struct __align__(16) DenseSmem {
 }  // namespace
 
 template <bool DENSE>
-__global__ __launch_bounds__(NT) void append_kernel(AppendArgs a, int tensor) {
+__global__ __launch_bounds__(NT) void append_kernel(AppendArgs a) {
   __shared__ StageSmem sm;
-  const int b = blockIdx.z, h = blockIdx.y;
+  const int b = blockIdx.z >> 1, h = blockIdx.y;
+  const int tensor = blockIdx.z & 1;  // 0 = K, 1 = V
   const int start = a.start.v[b];
   const int tile = start / TILE + (int)blockIdx.x;
   const int lo = max(start, tile * TILE), hi = min(start + a.n_new, tile * TILE + TILE);
@@ -535,12 +536,12 @@ __global__ __launch_bounds__(NT) void append_kernel(AppendArgs a, int tensor) {
   }
 }
 
-hipError_t launch_append(const AppendArgs& a, int tensor, int grid_x, hipStream_t s) {
-  dim3 grid(grid_x, a.H, a.B);
+hipError_t launch_append(const AppendArgs& a, int grid_x, hipStream_t s) {
+  dim3 grid(grid_x, a.H, 2 * a.B);  // K and V of every sequence in one launch
   if (a.rotation == KVQ_ROT_DENSE)
-    hipLaunchKernelGGL(append_kernel<true>, grid, dim3(NT), 0, s, a, tensor);
+    hipLaunchKernelGGL(append_kernel<true>, grid, dim3(NT), 0, s, a);
   else
-    hipLaunchKernelGGL(append_kernel<false>, grid, dim3(NT), 0, s, a, tensor);
+    hipLaunchKernelGGL(append_kernel<false>, grid, dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 

@@ -191,6 +191,7 @@ struct __align__(16) DecodeSmem {
   float mrg_ek[4], mrg_vn[4];
   float mrg_o[4][4][D];    // per wave, head, channel
   float mrg_oo[4][4][D];
+  int is_last;
 };
 
 // ------------------------------------------------------------------ prologue
@@ -268,6 +269,147 @@ __device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, int b, int h
   if ((l & 15) == 0) sm.qsum[j][l >> 4] = gs;
   if (l == 0) sm.qs[j] = qs;
   __syncthreads();
+}
+
+// ------------------------------------------------------------------ split merge
+// Writes this workgroup's record (per head: running max, sum, value-error mass,
+// descriptor maxima, unnormalised accumulators); the last workgroup to arrive for
+// its (sequence, kv head, head group) merges every split with log-sum-exp weights,
+// rotates the result back to the original basis ("OSCAR", section 2.2B: inverse
+// rotation) and writes the output and the certificate.  The arrival counters live
+// in the caller's workspace and are reset to zero by that last workgroup.
+template <bool CERT>
+__device__ void finish(const DecodeArgs& a, DecodeSmem& sm, int b, int hq0, int nh, int split) {
+  const int t = threadIdx.x, hh = t >> 6, l = t & 63, c = 2 * l;
+  if (hh < nh) {
+    float M = NEG_INF;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm.mrg_m[w][hh]);
+    float wgt[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) wgt[w] = (M == NEG_INF) ? 0.0f : exp2f(sm.mrg_m[w][hh] - M);
+    float* rec = a.part + (((size_t)b * a.Hq + hq0 + hh) * a.n_splits + split) * PART_FLOATS;
+    float o0 = 0.0f, o1 = 0.0f, p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      o0 += wgt[w] * sm.mrg_o[w][hh][c];
+      o1 += wgt[w] * sm.mrg_o[w][hh][c + 1];
+      if constexpr (CERT) {
+        p0 += wgt[w] * sm.mrg_oo[w][hh][c];
+        p1 += wgt[w] * sm.mrg_oo[w][hh][c + 1];
+      }
+    }
+    rec[8 + c] = o0;
+    rec[8 + c + 1] = o1;
+    if constexpr (CERT) {
+      rec[8 + D + c] = p0;
+      rec[8 + D + c + 1] = p1;
+    }
+    if (l == 0) {
+      float L = 0.0f, E = 0.0f, ek = 0.0f, vn = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        L += wgt[w] * sm.mrg_l[w][hh];
+        E += wgt[w] * sm.mrg_e[w][hh];
+        ek = fmaxf(ek, sm.mrg_ek[w]);
+        vn = fmaxf(vn, sm.mrg_vn[w]);
+      }
+      rec[0] = M;
+      rec[1] = L;
+      rec[2] = E;
+      rec[3] = ek;
+      rec[4] = vn;
+    }
+  }
+  __threadfence();
+  __syncthreads();
+  if (t == 0) {
+    unsigned int* ctr = a.counters + ((size_t)b * gridDim.y + blockIdx.y);
+    const unsigned int old = atomicAdd(ctr, 1u);
+    const bool last = old == (unsigned int)(a.n_splits - 1);
+    if (last) *ctr = 0u;
+    sm.is_last = last ? 1 : 0;
+  }
+  __syncthreads();
+  if (!sm.is_last) return;
+  __threadfence();
+  if (hh >= nh) return;  // whole waves: no barrier below
+  const int hq = hq0 + hh;
+  const size_t row = (size_t)b * a.Hq + hq;
+  float* out = a.out + row * D;
+  if (a.seq.v[b] == 0) {
+    out[c] = 0.0f;
+    out[c + 1] = 0.0f;
+    if (a.cert && l == 0) a.cert[row] = 0.0f;
+    return;
+  }
+  const float* rec0 = a.part + row * a.n_splits * PART_FLOATS;
+  float M = NEG_INF;
+  for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, rec0[s * PART_FLOATS]);
+  float L = 0.0f, E = 0.0f, ek = 0.0f, vn = 0.0f, o0 = 0.0f, o1 = 0.0f, p0 = 0.0f, p1 = 0.0f;
+  for (int s = 0; s < a.n_splits; ++s) {
+    const float* rec = rec0 + s * PART_FLOATS;
+    const float w = (rec[0] == NEG_INF) ? 0.0f : exp2f(rec[0] - M);
+    L += w * rec[1];
+    E += w * rec[2];
+    ek = fmaxf(ek, rec[3]);
+    vn = fmaxf(vn, rec[4]);
+    const float2 ov = *reinterpret_cast<const float2*>(rec + 8 + c);
+    o0 += w * ov.x;
+    o1 += w * ov.y;
+    if constexpr (CERT) {
+      const float2 pv = *reinterpret_cast<const float2*>(rec + 8 + D + c);
+      p0 += w * pv.x;
+      p1 += w * pv.y;
+    }
+  }
+  const float inv = 1.0f / L;
+  o0 *= inv;
+  o1 *= inv;
+  float r0 = o0, r1 = o1;
+  if (a.rotation == KVQ_ROT_SIGN_FWHT) {
+    // R^T o = diag(s) H o / sqrt(128): the butterflies over this head's 64 lanes
+    r0 = o0 + o1;
+    r1 = o0 - o1;
+    for (int msk = 1; msk < 64; msk <<= 1) {
+      const float q0 = __shfl_xor(r0, msk), q1 = __shfl_xor(r1, msk);
+      const bool up = (l & msk) != 0;
+      r0 = up ? q0 - r0 : r0 + q0;
+      r1 = up ? q1 - r1 : r1 + q1;
+    }
+    const float cn = bits_to_f32(KVQ_INV_SQRT_D_BITS);
+    r0 *= a.signs[c] < 0 ? -cn : cn;
+    r1 *= a.signs[c + 1] < 0 ? -cn : cn;
+  } else if (a.rotation == KVQ_ROT_DENSE) {
+    sm.qr[hh][c] = o0;
+    sm.qr[hh][c + 1] = o1;
+    lds_wait();
+    float acc0 = 0.0f, acc1 = 0.0f;
+    for (int k = 0; k < D; ++k) {
+      const float z = sm.qr[hh][k];
+      const uint32_t rr = *reinterpret_cast<const uint32_t*>(a.rot + (size_t)k * D + c);
+      acc0 = fmaf(f16_bits_to_f32((uint16_t)(rr & 0xFFFF)), z, acc0);
+      acc1 = fmaf(f16_bits_to_f32((uint16_t)(rr >> 16)), z, acc1);
+    }
+    r0 = acc0;
+    r1 = acc1;
+  }
+  if constexpr (CERT) {
+    r0 += p0 * inv;
+    r1 += p1 * inv;
+  }
+  *reinterpret_cast<float2*>(out + c) = make_float2(r0, r1);
+  if (CERT && a.cert) {
+    // ||q||: the prologue kept q * scale * log2(e) in LDS
+    const float q0 = sm.qo[hh][c], q1 = sm.qo[hh][c + 1];
+    float sq = q0 * q0 + q1 * q1;
+    for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
+    if (l == 0) {
+      const float qn = sqrtf(sq) / LOG2E;  // = ||q|| * scale
+      const float dstar = qn * ek;
+      a.cert[row] = 2.0f * (1.0f - expf(-2.0f * dstar)) * vn + E * inv;
+    }
+  }
 }
 
 // ------------------------------------------------------------------ split kernel
@@ -577,47 +719,7 @@ __global__ __launch_bounds__(NT, 2) void decode_split(DecodeArgs a) {
     }
   }
   __syncthreads();
-  {
-    const int hh = t >> 6, c = (t & 63) * 2;
-    if (hh < nh) {
-      float M = NEG_INF;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, sm.mrg_m[w][hh]);
-      float wgt[4];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) wgt[w] = (M == NEG_INF) ? 0.0f : exp2f(sm.mrg_m[w][hh] - M);
-      float* rec = a.part + (((size_t)b * a.Hq + hq0 + hh) * a.n_splits + split) * PART_FLOATS;
-      float o0 = 0.0f, o1 = 0.0f, p0 = 0.0f, p1 = 0.0f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        o0 += wgt[w] * sm.mrg_o[w][hh][c];
-        o1 += wgt[w] * sm.mrg_o[w][hh][c + 1];
-        if constexpr (CERT) {
-          p0 += wgt[w] * sm.mrg_oo[w][hh][c];
-          p1 += wgt[w] * sm.mrg_oo[w][hh][c + 1];
-        }
-      }
-      rec[8 + c] = o0;
-      rec[8 + c + 1] = o1;
-      rec[8 + D + c] = p0;
-      rec[8 + D + c + 1] = p1;
-      if ((t & 63) == 0) {
-        float L = 0.0f, E = 0.0f, ek = 0.0f, vn = 0.0f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          L += wgt[w] * sm.mrg_l[w][hh];
-          E += wgt[w] * sm.mrg_e[w][hh];
-          ek = fmaxf(ek, sm.mrg_ek[w]);
-          vn = fmaxf(vn, sm.mrg_vn[w]);
-        }
-        rec[0] = M;
-        rec[1] = L;
-        rec[2] = E;
-        rec[3] = ek;
-        rec[4] = vn;
-      }
-    }
-  }
+  finish<CERT>(a, sm, b, hq0, nh, split);
 }
 
 // ------------------------------------------------------------------ dense fp16 baseline
@@ -720,6 +822,11 @@ __global__ __launch_bounds__(NT, 2) void decode_dense_split(DecodeArgs a) {
   if (lane < 4) {
     sm.mrg_m[wv][lane] = m;
     sm.mrg_l[wv][lane] = lt;
+    sm.mrg_e[wv][lane] = 0.0f;
+  }
+  if (lane == 0) {
+    sm.mrg_ek[wv] = 0.0f;
+    sm.mrg_vn[wv] = 0.0f;
   }
 #pragma unroll
   for (int hh = 0; hh < 4; ++hh) {
@@ -727,107 +834,7 @@ __global__ __launch_bounds__(NT, 2) void decode_dense_split(DecodeArgs a) {
     sm.mrg_o[wv][hh][2 * lane + 1] = o[1][hh];
   }
   __syncthreads();
-  const int hh = t >> 6, c = (t & 63) * 2;
-  if (hh < nh) {
-    float M = NEG_INF;
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm.mrg_m[w][hh]);
-    float wgt[4];
-    for (int w = 0; w < 4; ++w) wgt[w] = (M == NEG_INF) ? 0.0f : exp2f(sm.mrg_m[w][hh] - M);
-    float* rec = a.part + (((size_t)b * a.Hq + hq0 + hh) * a.n_splits + split) * PART_FLOATS;
-    float o0 = 0.0f, o1 = 0.0f;
-    for (int w = 0; w < 4; ++w) {
-      o0 += wgt[w] * sm.mrg_o[w][hh][c];
-      o1 += wgt[w] * sm.mrg_o[w][hh][c + 1];
-    }
-    rec[8 + c] = o0;
-    rec[8 + c + 1] = o1;
-    rec[8 + D + c] = 0.0f;
-    rec[8 + D + c + 1] = 0.0f;
-    if ((t & 63) == 0) {
-      float L = 0.0f;
-      for (int w = 0; w < 4; ++w) L += wgt[w] * sm.mrg_l[w][hh];
-      rec[0] = M;
-      rec[1] = L;
-      rec[2] = 0.0f;
-      rec[3] = 0.0f;
-      rec[4] = 0.0f;
-    }
-  }
-}
-
-// ------------------------------------------------------------------ combine
-__global__ __launch_bounds__(D) void combine_kernel(CombineArgs a) {
-  const int row = blockIdx.x;  // b * Hq + hq
-  const int b = row / a.Hq;
-  const int c = threadIdx.x;
-  __shared__ float z[D];
-  __shared__ float red[2];
-  const float* rec0 = a.part + (size_t)row * a.n_splits * PART_FLOATS;
-  float* out = a.out + (size_t)row * D;
-  if (a.seq.v[b] == 0) {
-    out[c] = 0.0f;
-    if (a.cert && c == 0) a.cert[row] = 0.0f;
-    return;
-  }
-  float M = NEG_INF;
-  for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, rec0[s * PART_FLOATS]);
-  float L = 0.0f, E = 0.0f, ek = 0.0f, vn = 0.0f, o = 0.0f, oo = 0.0f;
-  for (int s = 0; s < a.n_splits; ++s) {
-    const float* rec = rec0 + s * PART_FLOATS;
-    const float w = (rec[0] == NEG_INF) ? 0.0f : exp2f(rec[0] - M);
-    L += w * rec[1];
-    E += w * rec[2];
-    ek = fmaxf(ek, rec[3]);
-    vn = fmaxf(vn, rec[4]);
-    o += w * rec[8 + c];
-    oo += w * rec[8 + D + c];
-  }
-  const float inv = 1.0f / L;
-  o *= inv;
-  oo *= inv;
-  float res;
-  if (a.rotation == KVQ_ROT_SIGN_FWHT) {
-    z[c] = o;
-    __syncthreads();
-    for (int h = 1; h < D; h <<= 1) {
-      float u = 0.0f, v = 0.0f;
-      const int i = (c / h) * 2 * h + (c % h);
-      if (c < 64) {
-        u = z[i];
-        v = z[i + h];
-      }
-      __syncthreads();
-      if (c < 64) {
-        z[i] = u + v;
-        z[i + h] = u - v;
-      }
-      __syncthreads();
-    }
-    const float r = z[c] * bits_to_f32(KVQ_INV_SQRT_D_BITS);
-    res = a.signs[c] < 0 ? -r : r;
-  } else if (a.rotation == KVQ_ROT_DENSE) {
-    z[c] = o;
-    __syncthreads();
-    float acc = 0.0f;
-    for (int k = 0; k < D; ++k) acc = fmaf(f16_bits_to_f32(a.rot[(size_t)k * D + c]), z[k], acc);
-    res = acc;
-  } else {
-    res = o;
-  }
-  out[c] = res + oo;
-  if (a.cert) {
-    const uint16_t* qp = a.q + (size_t)row * D;
-    const float qv = widen(qp[c], a.in_bf16 != 0);
-    float sq = qv * qv;
-    for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
-    if ((c & 63) == 0) red[c >> 6] = sq;
-    __syncthreads();
-    if (c == 0) {
-      const float qn = sqrtf(red[0] + red[1]);
-      const float dstar = qn * a.scale * ek;
-      a.cert[row] = 2.0f * (1.0f - expf(-2.0f * dstar)) * vn + E * inv;
-    }
-  }
+  finish<false>(a, sm, b, hq0, nh, split);
 }
 
 }  // namespace
@@ -857,9 +864,5 @@ hipError_t launch_decode(const DecodeArgs& a, int k_fmt, int v_fmt, bool dense, 
   return hipErrorNotSupported;
 }
 
-hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3(a.B * a.Hq), dim3(D), 0, s, a);
-  return hipGetLastError();
-}
 
 }  // namespace kvq

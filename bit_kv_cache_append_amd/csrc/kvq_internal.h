@@ -70,7 +70,8 @@ struct BoundArgs {
   SeqArray seq;
 };
 
-// Decode partial results, one record per (b, hq, split) in the workspace.
+// Workspace of a decode call: arrival counters (zero before the first call, left
+// zero by every call), then one partial-result record per (b, hq, split).
 // m: running max (log2 domain), l: sum of exp2, eta: sum of p * ev (certified),
 // ekmax/vnmax: maxima over this split's blocks, o: rotated-basis accumulator,
 // oo: original-basis accumulator for exactly recomputed blocks.
@@ -89,7 +90,10 @@ struct DecodeArgs {
   const uint8_t* flags;  // [B][H][nt] or null
   const int8_t* signs;
   const uint16_t* rot;
-  float* part;  // [B][Hq][n_splits][PART_FLOATS]
+  float* part;              // [B][Hq][n_splits][PART_FLOATS]
+  unsigned int* counters;   // [B][gridDim.y] arrival counters, zero between calls
+  float* out;               // [B][Hq][128]
+  float* cert;              // [B][Hq] or null
   int32_t B, Hq, H, G, Tmax, nt;
   int32_t in_bf16, rotation, k_group, v_group;
   int32_t n_splits, chunks_per_split;
@@ -97,23 +101,11 @@ struct DecodeArgs {
   SeqArray seq;
 };
 
-struct CombineArgs {
-  const float* part;
-  float* out;   // [B][Hq][128]
-  float* cert;  // [B][Hq] or null
-  const int8_t* signs;
-  const uint16_t* rot;
-  const uint16_t* q;  // for ||q|| in the certificate
-  int32_t B, Hq, n_splits, rotation, in_bf16;
-  float scale;
-  SeqArray seq;
-};
 
 // host-side launchers (defined in the .hip files)
-hipError_t launch_append(const AppendArgs& a, int tensor, int grid_x, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, int grid_x, hipStream_t s);
 hipError_t launch_calibrate(const CalibArgs& a, hipStream_t s);
 hipError_t launch_bound(const BoundArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int k_fmt, int v_fmt, bool dense, hipStream_t s);
-hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
 }  // namespace kvq
