@@ -106,13 +106,6 @@ int choose_splits(const kvq_params* p, int max_chunks) {
 
 int max_splits_for(const kvq_params* p) { return choose_splits(p, p->max_ctx / TILE); }
 
-// workspace: arrival counters (one per (b, kv head, head group)), 256-byte aligned, then records
-size_t counter_bytes(const kvq_params* p) {
-  const int G = p->n_q_heads / p->n_kv_heads;
-  const size_t n = (size_t)p->batch * p->n_kv_heads * ((G + 3) / 4);
-  return (n * sizeof(unsigned int) + 255) & ~(size_t)255;
-}
-
 }  // namespace
 
 extern "C" {
@@ -152,7 +145,7 @@ kvq_status kvq_buffer_bytes(const kvq_params* p, size_t* out) {
 
 size_t kvq_decode_workspace_bytes(const kvq_params* p) {
   if (check_params(p)) return 0;
-  return counter_bytes(p) + (size_t)p->batch * p->n_q_heads * max_splits_for(p) * PART_FLOATS * sizeof(float);
+  return (size_t)p->batch * p->n_q_heads * max_splits_for(p) * PART_FLOATS * sizeof(float);
 }
 
 kvq_status kvq_append(const kvq_params* p, const kvq_cache* c, const void* k_new, const void* v_new,
@@ -303,8 +296,7 @@ static kvq_status decode_common(const kvq_params* p, const kvq_cache* c, const v
     a.signs = c->signs;
     a.rot = c->rot_f16;
   }
-  a.counters = (unsigned int*)ws;
-  a.part = (float*)((char*)ws + counter_bytes(p));
+  a.part = (float*)ws;
   a.out = out;
   a.cert = dense ? nullptr : cert;
   a.B = p->batch;

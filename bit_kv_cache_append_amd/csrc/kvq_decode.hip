@@ -191,41 +191,58 @@ struct __align__(16) DecodeSmem {
   float mrg_ek[4], mrg_vn[4];
   float mrg_o[4][4][D];    // per wave, head, channel
   float mrg_oo[4][4][D];
-  int is_last;
 };
 
 // ------------------------------------------------------------------ prologue
-// rotate the 4 query heads of this workgroup, prescale, quantize to 16 bits
+// Rotate the 4 query heads of this workgroup (wave j holds head j, lane l its
+// channels 2l and 2l+1), prescale, quantize to 16 bits, and publish the int8
+// halves in MFMA operand order.  The Walsh-Hadamard butterflies run in the
+// order h = 1, 2, ..., 64 with the in-lane pair first and lane exchanges after.
+// The loads of the query and sign bits, issued before the first chunk's loads
+// (unconditionally, from valid addresses, so the count in flight is static).
+struct QueryIn {
+  uint16_t q0, q1;  // channels 2l, 2l+1 of head j (the wave index)
+  uint16_t sg;      // sign bytes of those channels
+};
+__device__ __forceinline__ QueryIn query_loads(const DecodeArgs& a, int b, int hq0, int nh) {
+  const int t = threadIdx.x, j = t >> 6, l = t & 63;
+  const uint16_t* qp = a.q + ((size_t)b * a.Hq + hq0 + (j < nh ? j : 0)) * D;
+  const int8_t* sp = a.rotation == KVQ_ROT_SIGN_FWHT ? a.signs : reinterpret_cast<const int8_t*>(a.q);
+  QueryIn r;
+  r.q0 = qp[2 * l];
+  r.q1 = qp[2 * l + 1];
+  r.sg = *reinterpret_cast<const uint16_t*>(sp + 2 * l);
+  return r;
+}
+
 template <int KF>
-__device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, int b, int hq0, int nh, int kgroup) {
+__device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryIn& qin, int nh, int kgroup) {
   const int t = threadIdx.x, j = t >> 6, l = t & 63;
   const bool bf16 = a.in_bf16 != 0;
   float x0 = 0.0f, x1 = 0.0f;
   if (j < nh) {
-    const uint16_t* qp = a.q + ((size_t)b * a.Hq + hq0 + j) * D;
-    x0 = widen(qp[2 * l], bf16);
-    x1 = widen(qp[2 * l + 1], bf16);
+    x0 = widen(qin.q0, bf16);
+    x1 = widen(qin.q1, bf16);
   }
   const float pre = a.scale * LOG2E;
   sm.qo[j][2 * l] = x0 * pre;
   sm.qo[j][2 * l + 1] = x1 * pre;
+  float y0 = x0, y1 = x1;
   if (a.rotation == KVQ_ROT_SIGN_FWHT) {
-    x0 = a.signs[2 * l] < 0 ? -x0 : x0;
-    x1 = a.signs[2 * l + 1] < 0 ? -x1 : x1;
-  }
-  sm.qf[j][2 * l] = x0;
-  sm.qf[j][2 * l + 1] = x1;
-  __syncthreads();
-  if (a.rotation == KVQ_ROT_SIGN_FWHT) {
-    for (int h = 1; h < D; h <<= 1) {
-      const int i = (l / h) * 2 * h + (l % h);
-      float u = sm.qf[j][i], v = sm.qf[j][i + h];
-      __syncthreads();
-      sm.qf[j][i] = u + v;
-      sm.qf[j][i + h] = u - v;
-      __syncthreads();
+    x0 = (qin.sg & 0x80u) ? -x0 : x0;
+    x1 = (qin.sg & 0x8000u) ? -x1 : x1;
+    y0 = x0 + x1;
+    y1 = x0 - x1;
+    for (int msk = 1; msk < 64; msk <<= 1) {
+      const float p0 = __shfl_xor(y0, msk), p1 = __shfl_xor(y1, msk);
+      const bool up = (l & msk) != 0;
+      y0 = up ? p0 - y0 : y0 + p0;
+      y1 = up ? p1 - y1 : y1 + p1;
     }
   } else if (a.rotation == KVQ_ROT_DENSE) {
+    sm.qf[j][2 * l] = x0;
+    sm.qf[j][2 * l + 1] = x1;
+    __syncthreads();
     for (int rr = 0; rr < 2; ++rr) {
       const int row = l + 64 * rr;
       const uint16_t* rp = a.rot + (size_t)row * D;
@@ -234,12 +251,12 @@ __device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, int b, int h
       sm.qr[j][row] = acc;
     }
     __syncthreads();
-    sm.qf[j][2 * l] = sm.qr[j][2 * l];
-    sm.qf[j][2 * l + 1] = sm.qr[j][2 * l + 1];
-    __syncthreads();
+    y0 = sm.qr[j][2 * l];
+    y1 = sm.qr[j][2 * l + 1];
   }
   const float norm = a.rotation == KVQ_ROT_SIGN_FWHT ? bits_to_f32(KVQ_INV_SQRT_D_BITS) : 1.0f;
-  float y0 = sm.qf[j][2 * l] * norm * pre, y1 = sm.qf[j][2 * l + 1] * norm * pre;
+  y0 = y0 * norm * pre;
+  y1 = y1 * norm * pre;
   float mx = wave_max(fmaxf(fabsf(y0), fabsf(y1)));
   const float qs = mx > 0.0f ? mx / 32000.0f : 1.0f;
   const int q0 = (int)rintf(y0 / qs), q1 = (int)rintf(y1 / qs);
@@ -271,96 +288,90 @@ __device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, int b, int h
   __syncthreads();
 }
 
-// ------------------------------------------------------------------ split merge
-// Writes this workgroup's record (per head: running max, sum, value-error mass,
-// descriptor maxima, unnormalised accumulators); the last workgroup to arrive for
-// its (sequence, kv head, head group) merges every split with log-sum-exp weights,
-// rotates the result back to the original basis ("OSCAR", section 2.2B: inverse
-// rotation) and writes the output and the certificate.  The arrival counters live
-// in the caller's workspace and are reset to zero by that last workgroup.
+// ------------------------------------------------------------------ split record
+// Merges the 4 waves of this workgroup (in LDS, log-sum-exp weights) and writes
+// the record of (sequence, query head, split) for the combine kernel.
 template <bool CERT>
-__device__ void finish(const DecodeArgs& a, DecodeSmem& sm, int b, int hq0, int nh, int split) {
+__device__ void write_record(const DecodeArgs& a, DecodeSmem& sm, int b, int hq0, int nh, int split) {
   const int t = threadIdx.x, hh = t >> 6, l = t & 63, c = 2 * l;
-  if (hh < nh) {
-    float M = NEG_INF;
+  if (hh >= nh) return;
+  float M = NEG_INF;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm.mrg_m[w][hh]);
-    float wgt[4];
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, sm.mrg_m[w][hh]);
+  float wgt[4];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) wgt[w] = (M == NEG_INF) ? 0.0f : exp2f(sm.mrg_m[w][hh] - M);
-    float* rec = a.part + (((size_t)b * a.Hq + hq0 + hh) * a.n_splits + split) * PART_FLOATS;
-    float o0 = 0.0f, o1 = 0.0f, p0 = 0.0f, p1 = 0.0f;
+  for (int w = 0; w < 4; ++w) wgt[w] = (M == NEG_INF) ? 0.0f : exp2f(sm.mrg_m[w][hh] - M);
+  float* rec = a.part + (((size_t)b * a.Hq + hq0 + hh) * a.n_splits + split) * PART_FLOATS;
+  float o0 = 0.0f, o1 = 0.0f, p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    o0 += wgt[w] * sm.mrg_o[w][hh][c];
+    o1 += wgt[w] * sm.mrg_o[w][hh][c + 1];
+    if constexpr (CERT) {
+      p0 += wgt[w] * sm.mrg_oo[w][hh][c];
+      p1 += wgt[w] * sm.mrg_oo[w][hh][c + 1];
+    }
+  }
+  *reinterpret_cast<float2*>(rec + 8 + c) = make_float2(o0, o1);
+  if constexpr (CERT) *reinterpret_cast<float2*>(rec + 8 + D + c) = make_float2(p0, p1);
+  float qn = 0.0f;
+  if constexpr (CERT) {
+    // ||q|| * scale from the prologue's q * scale * log2(e)
+    const float q0 = sm.qo[hh][c], q1 = sm.qo[hh][c + 1];
+    float sq = q0 * q0 + q1 * q1;
+    for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
+    qn = sqrtf(sq) / LOG2E;
+  }
+  if (l == 0) {
+    float L = 0.0f, E = 0.0f, ek = 0.0f, vn = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      o0 += wgt[w] * sm.mrg_o[w][hh][c];
-      o1 += wgt[w] * sm.mrg_o[w][hh][c + 1];
-      if constexpr (CERT) {
-        p0 += wgt[w] * sm.mrg_oo[w][hh][c];
-        p1 += wgt[w] * sm.mrg_oo[w][hh][c + 1];
-      }
+      L += wgt[w] * sm.mrg_l[w][hh];
+      E += wgt[w] * sm.mrg_e[w][hh];
+      ek = fmaxf(ek, sm.mrg_ek[w]);
+      vn = fmaxf(vn, sm.mrg_vn[w]);
     }
-    rec[8 + c] = o0;
-    rec[8 + c + 1] = o1;
-    if constexpr (CERT) {
-      rec[8 + D + c] = p0;
-      rec[8 + D + c + 1] = p1;
-    }
-    if (l == 0) {
-      float L = 0.0f, E = 0.0f, ek = 0.0f, vn = 0.0f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        L += wgt[w] * sm.mrg_l[w][hh];
-        E += wgt[w] * sm.mrg_e[w][hh];
-        ek = fmaxf(ek, sm.mrg_ek[w]);
-        vn = fmaxf(vn, sm.mrg_vn[w]);
-      }
-      rec[0] = M;
-      rec[1] = L;
-      rec[2] = E;
-      rec[3] = ek;
-      rec[4] = vn;
-    }
+    *reinterpret_cast<float4*>(rec) = make_float4(M, L, E, ek);
+    *reinterpret_cast<float4*>(rec + 4) = make_float4(vn, qn, 0.0f, 0.0f);
   }
-  __threadfence();
-  __syncthreads();
-  if (t == 0) {
-    unsigned int* ctr = a.counters + ((size_t)b * gridDim.y + blockIdx.y);
-    const unsigned int old = atomicAdd(ctr, 1u);
-    const bool last = old == (unsigned int)(a.n_splits - 1);
-    if (last) *ctr = 0u;
-    sm.is_last = last ? 1 : 0;
-  }
-  __syncthreads();
-  if (!sm.is_last) return;
-  __threadfence();
-  if (hh >= nh) return;  // whole waves: no barrier below
-  const int hq = hq0 + hh;
-  const size_t row = (size_t)b * a.Hq + hq;
-  float* out = a.out + row * D;
+}
+
+// ------------------------------------------------------------------ combine kernel
+// One wave per (sequence, query head): log-sum-exp merge of the split records,
+// inverse rotation back to the original basis ("OSCAR", section 2.2B), and the
+// certificate.  A separate launch on the same stream orders it after every split.
+template <bool CERT>
+__global__ __launch_bounds__(NT) void combine_kernel(DecodeArgs a) {
+  __shared__ float zs[4][D];
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, c = 2 * l;
+  const int row = blockIdx.x * 4 + w;
+  if (row >= a.B * a.Hq) return;  // whole waves; no barrier below
+  const int b = row / a.Hq;
+  float* out = a.out + (size_t)row * D;
   if (a.seq.v[b] == 0) {
-    out[c] = 0.0f;
-    out[c + 1] = 0.0f;
-    if (a.cert && l == 0) a.cert[row] = 0.0f;
+    *reinterpret_cast<float2*>(out + c) = make_float2(0.0f, 0.0f);
+    if (CERT && a.cert && l == 0) a.cert[row] = 0.0f;
     return;
   }
-  const float* rec0 = a.part + row * a.n_splits * PART_FLOATS;
+  const float* rec0 = a.part + (size_t)row * a.n_splits * PART_FLOATS;
   float M = NEG_INF;
   for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, rec0[s * PART_FLOATS]);
   float L = 0.0f, E = 0.0f, ek = 0.0f, vn = 0.0f, o0 = 0.0f, o1 = 0.0f, p0 = 0.0f, p1 = 0.0f;
   for (int s = 0; s < a.n_splits; ++s) {
     const float* rec = rec0 + s * PART_FLOATS;
-    const float w = (rec[0] == NEG_INF) ? 0.0f : exp2f(rec[0] - M);
-    L += w * rec[1];
-    E += w * rec[2];
-    ek = fmaxf(ek, rec[3]);
+    const float4 h0 = *reinterpret_cast<const float4*>(rec);
+    const float wt = (h0.x == NEG_INF) ? 0.0f : exp2f(h0.x - M);
+    L += wt * h0.y;
+    E += wt * h0.z;
+    ek = fmaxf(ek, h0.w);
     vn = fmaxf(vn, rec[4]);
     const float2 ov = *reinterpret_cast<const float2*>(rec + 8 + c);
-    o0 += w * ov.x;
-    o1 += w * ov.y;
+    o0 += wt * ov.x;
+    o1 += wt * ov.y;
     if constexpr (CERT) {
       const float2 pv = *reinterpret_cast<const float2*>(rec + 8 + D + c);
-      p0 += w * pv.x;
-      p1 += w * pv.y;
+      p0 += wt * pv.x;
+      p1 += wt * pv.y;
     }
   }
   const float inv = 1.0f / L;
@@ -381,12 +392,13 @@ __device__ void finish(const DecodeArgs& a, DecodeSmem& sm, int b, int hq0, int 
     r0 *= a.signs[c] < 0 ? -cn : cn;
     r1 *= a.signs[c + 1] < 0 ? -cn : cn;
   } else if (a.rotation == KVQ_ROT_DENSE) {
-    sm.qr[hh][c] = o0;
-    sm.qr[hh][c + 1] = o1;
+    zs[w][c] = o0;
+    zs[w][c + 1] = o1;
+    __builtin_amdgcn_wave_barrier();
     lds_wait();
     float acc0 = 0.0f, acc1 = 0.0f;
     for (int k = 0; k < D; ++k) {
-      const float z = sm.qr[hh][k];
+      const float z = zs[w][k];
       const uint32_t rr = *reinterpret_cast<const uint32_t*>(a.rot + (size_t)k * D + c);
       acc0 = fmaf(f16_bits_to_f32((uint16_t)(rr & 0xFFFF)), z, acc0);
       acc1 = fmaf(f16_bits_to_f32((uint16_t)(rr >> 16)), z, acc1);
@@ -399,21 +411,99 @@ __device__ void finish(const DecodeArgs& a, DecodeSmem& sm, int b, int hq0, int 
     r1 += p1 * inv;
   }
   *reinterpret_cast<float2*>(out + c) = make_float2(r0, r1);
-  if (CERT && a.cert) {
-    // ||q||: the prologue kept q * scale * log2(e) in LDS
-    const float q0 = sm.qo[hh][c], q1 = sm.qo[hh][c + 1];
-    float sq = q0 * q0 + q1 * q1;
-    for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
-    if (l == 0) {
-      const float qn = sqrtf(sq) / LOG2E;  // = ||q|| * scale
-      const float dstar = qn * ek;
-      a.cert[row] = 2.0f * (1.0f - expf(-2.0f * dstar)) * vn + E * inv;
-    }
+  if (CERT && a.cert && l == 0) {
+    const float dstar = rec0[5] * ek;
+    a.cert[row] = 2.0f * (1.0f - expf(-2.0f * dstar)) * vn + E * inv;
   }
 }
 
 // ------------------------------------------------------------------ split kernel
-template <int KF, int KG, int VF, bool CERT>
+// Registers holding one chunk of packed data for one lane.
+template <int KF, int VF>
+struct ChunkRegs {
+  uint32_t krow[KFmt<KF>::DW];            // K row of token pi(s_a, r_a)
+  uint32_t kmeta[4];                      // its metadata (scales [, offsets])
+  uint32_t vw[2 * VFmt<VF>::CDW];         // V codes of channels 2*lane, 2*lane+1
+  uint32_t vmeta[VF == KVQ_INT2 ? 4 : 2]; // this lane's share of the V metadata tile
+};
+
+// Issue the loads of chunk ch (no waits: the caller consumes them one chunk later).
+template <int KF, int KG, int VF, int VG>
+__device__ __forceinline__ void load_chunk(const DecodeArgs& a, size_t stream, int ch, int lane, int tok_a,
+                                           ChunkRegs<KF, VF>& R) {
+  constexpr int KDW = KFmt<KF>::DW;
+  constexpr int KM = meta_bytes(KF, KG);
+  constexpr int CDW = VFmt<VF>::CDW;
+  const int tok0 = ch * TILE;
+  const uint4* rp = reinterpret_cast<const uint4*>(a.k_codes + (stream * a.Tmax + tok0 + tok_a) * (KDW * 4));
+#pragma unroll
+  for (int i = 0; i < KDW / 4; ++i) {
+    const uint4 u = rp[i];
+    R.krow[4 * i] = u.x; R.krow[4 * i + 1] = u.y; R.krow[4 * i + 2] = u.z; R.krow[4 * i + 3] = u.w;
+  }
+  const uint8_t* mp = a.k_meta + (stream * a.Tmax + tok0 + tok_a) * KM;
+  if constexpr (KM == 16) {
+    const uint4 u = *reinterpret_cast<const uint4*>(mp);
+    R.kmeta[0] = u.x; R.kmeta[1] = u.y; R.kmeta[2] = u.z; R.kmeta[3] = u.w;
+  } else if constexpr (KM == 8) {
+    const uint2 u = *reinterpret_cast<const uint2*>(mp);
+    R.kmeta[0] = u.x; R.kmeta[1] = u.y;
+  } else {
+    R.kmeta[0] = *reinterpret_cast<const uint16_t*>(mp);
+  }
+  const uint4* vp = reinterpret_cast<const uint4*>(a.v_codes + (stream * a.nt + ch) * (size_t)(D * CDW * 4) +
+                                                   (size_t)(2 * lane) * CDW * 4);
+#pragma unroll
+  for (int i = 0; i < CDW / 2; ++i) {
+    const uint4 u = vp[i];
+    R.vw[4 * i] = u.x; R.vw[4 * i + 1] = u.y; R.vw[4 * i + 2] = u.z; R.vw[4 * i + 3] = u.w;
+  }
+  constexpr int NM = meta_elems(VF, VG);
+  const uint8_t* vm = a.v_meta + (stream * a.nt + ch) * (size_t)(NM * TILE * 2);
+  if constexpr (VF == KVQ_INT2) {  // 8 elements x 64 tokens: 16 bytes per lane
+    const uint4 u = reinterpret_cast<const uint4*>(vm)[lane];
+    R.vmeta[0] = u.x; R.vmeta[1] = u.y; R.vmeta[2] = u.z; R.vmeta[3] = u.w;
+  } else if constexpr (NM == 4) {  // 4 groups x 64 tokens: 8 bytes per lane
+    const uint2 u = reinterpret_cast<const uint2*>(vm)[lane];
+    R.vmeta[0] = u.x; R.vmeta[1] = u.y;
+  } else {  // one scale per token
+    R.vmeta[0] = reinterpret_cast<const uint16_t*>(vm)[lane];
+  }
+}
+
+// V metadata of a chunk -> this wave's LDS area, laid out [element][slice][pair][half]
+// so that slice s of element m is two dwords: (pi(s,0), pi(s,1)) and (pi(s,2), pi(s,3)).
+template <int VF, int VG>
+__device__ __forceinline__ void stage_vmeta(uint16_t* L, int lane, const uint32_t* vmeta) {
+  constexpr int NM = meta_elems(VF, VG);
+  if constexpr (VF == KVQ_INT2) {
+    const int mm = lane >> 3, u = lane & 7;  // tokens 8u..8u+7 of element mm
+    const int base = (mm * 16 + 4 * (u >> 1)) * 4 + (u & 1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) L[base + 2 * e] = (uint16_t)(vmeta[e >> 1] >> (16 * (e & 1)));
+  } else if constexpr (NM == 4) {
+    const int mm = lane >> 4, t0 = 4 * (lane & 15);  // tokens t0..t0+3 of group mm
+    const int base = (mm * 16 + 2 * (t0 >> 3)) * 4 + ((t0 >> 2) & 1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) L[base + 2 * e] = (uint16_t)(vmeta[e >> 1] >> (16 * (e & 1)));
+  } else {
+    const int tau = lane, e = tau & 7;
+    L[(2 * (tau >> 3)) * 4 + ((e >> 2) & 1) + 2 * (e & 3)] = (uint16_t)vmeta[0];
+  }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max over the 16 lanes sharing (lane & 3): rotate within rows of 16, then across rows
+__device__ __forceinline__ float max_same_head_fast(float v) {
+  v = fmaxf(v, dpp_f<0x124>(v));  // row_ror:4
+  v = fmaxf(v, dpp_f<0x128>(v));  // row_ror:8
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+template <int KF, int KG, int VF, int VG, bool CERT>
 __global__ __launch_bounds__(NT, 2) void decode_split(DecodeArgs a) {
   __shared__ DecodeSmem sm;
   const int b = blockIdx.z;
@@ -426,17 +516,28 @@ __global__ __launch_bounds__(NT, 2) void decode_split(DecodeArgs a) {
   const int nchunks = (T + TILE - 1) / TILE;
   const int c0 = split * a.chunks_per_split;
   const int c1 = min(nchunks, c0 + a.chunks_per_split);
-  const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
-  const int j = lane & 3;       // head of this lane (QK output / softmax role)
-  const int s_a = lane >> 2;    // QK slice of this lane (A role)
+  const int t = threadIdx.x, lane = t & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: the chunk walk is scalar
+  const int j = lane & 3;     // head of this lane (QK output / softmax role)
+  const int s_a = lane >> 2;  // QK slice of this lane (A role)
   const int r_a = lane & 3;
+  const int tok_a = tok_of<VF>(s_a, r_a);
   const size_t stream = (size_t)b * a.H + hkv;
-  constexpr int KDW = KFmt<KF>::DW;
-  constexpr int KM = meta_bytes(KF, KG);
-  const int vg = a.v_group;
-  const int vgrp = (vg == 128) ? 0 : (lane >> 4);  // V group of channels 2*lane, 2*lane+1
+  constexpr int CDW = VFmt<VF>::CDW;
+  const int vgrp = (VG == 128) ? 0 : (lane >> 4);  // V group of channels 2*lane, 2*lane+1
+  uint16_t* vml = &sm.vmeta[wv][0][0][0];
 
-  query_prologue<KF>(a, sm, b, hq0, nh, KG);
+  // The first chunk's loads are in flight during the query prologue.  Every
+  // prefetch is unconditional (a wave past its last chunk reloads a chunk index
+  // that is always inside the cache), so the number of loads in flight is the
+  // same on every path.
+  const QueryIn qin = query_loads(a, b, hq0, nh);
+  __builtin_amdgcn_sched_barrier(0);
+  ChunkRegs<KF, VF> RA, RB;
+  int ch = c0 + wv;
+  load_chunk<KF, KG, VF, VG>(a, stream, ch < c1 ? ch : 0, lane, tok_a, RA);
+  __builtin_amdgcn_sched_barrier(0);
+  query_prologue<KF>(a, sm, qin, nh, KG);
 
   uint32_t qh[32], ql[32];
 #pragma unroll
@@ -458,242 +559,228 @@ __global__ __launch_bounds__(NT, 2) void decode_split(DecodeArgs a) {
   }
   oz = f4{0, 0, 0, 0};
 
-  for (int ch = c0 + wv; ch < c1; ch += 4) {
+  // ---------------------------------------------------------------- one quantized chunk
+  auto quant_chunk = [&](const ChunkRegs<KF, VF>& R, int ch, float ev_c) {
     const int tok0 = ch * TILE;
-    bool flagged = false;
+    stage_vmeta<VF, VG>(vml, lane, R.vmeta);
+    // ---- QK^T: exact integer dot products, the NG group chains interleaved
+    constexpr int NG = (KG == 128) ? 1 : 4;
+    constexpr int PER = 32 / NG;
+    i4 acc[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) acc[g] = i4{0, 0, 0, 0};
+#pragma unroll
+    for (int n = 0; n < PER; ++n)
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+        acc[g] = __builtin_amdgcn_mfma_i32_4x4x4i8(KFmt<KF>::a_op(R.krow, g * PER + n), (int)qh[g * PER + n],
+                                                   acc[g], 0, 0, 0);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      int corr = 0;
+      if constexpr (KF == KVQ_INT4) corr = -8 * (int)qsum[g];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[g][r] = acc[g][r] * 256 + corr;
+    }
+#pragma unroll
+    for (int n = 0; n < PER; ++n)
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+        acc[g] = __builtin_amdgcn_mfma_i32_4x4x4i8(KFmt<KF>::a_op(R.krow, g * PER + n), (int)ql[g * PER + n],
+                                                   acc[g], 0, 0, 0);
+    // ---- group scales of tokens pi(s, r), held by lanes 4s + r (A role): quad broadcast
+    float l[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      uint32_t sw[2], zw[2] = {0u, 0u};
+#pragma unroll
+      for (int w = 0; w < (NG == 1 ? 1 : 2); ++w) {
+        sw[w] = r == 0 ? quad_bcast_u<0>(R.kmeta[w]) : r == 1 ? quad_bcast_u<1>(R.kmeta[w])
+              : r == 2 ? quad_bcast_u<2>(R.kmeta[w]) : quad_bcast_u<3>(R.kmeta[w]);
+        if constexpr (KF == KVQ_INT2)
+          zw[w] = r == 0 ? quad_bcast_u<0>(R.kmeta[2 + w]) : r == 1 ? quad_bcast_u<1>(R.kmeta[2 + w])
+                : r == 2 ? quad_bcast_u<2>(R.kmeta[2 + w]) : quad_bcast_u<3>(R.kmeta[2 + w]);
+      }
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const uint16_t sb = (uint16_t)(sw[g >> 1] >> (16 * (g & 1)));
+        float v = (float)acc[g][r] * f16_bits_to_f32(sb);
+        if constexpr (KF == KVQ_INT2) {
+          const uint16_t zb = (uint16_t)(zw[g >> 1] >> (16 * (g & 1)));
+          v = fmaf(f16_bits_to_f32(zb), qsum[g], v);
+        }
+        l[r] += v;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      l[r] *= qs;
+      if (tok0 + tok_of<VF>(s_a, r) >= T) l[r] = NEG_INF;
+    }
+    // ---- online softmax (exp2 domain)
+    const float cmax = max_same_head_fast(fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3])));
+    const float m_new = fmaxf(m, cmax);
+    const bool none = m_new == NEG_INF;
+    const float alpha = none ? 1.0f : fast_exp2(m - m_new);
+    float p[4], ps = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = none ? 0.0f : fast_exp2(l[r] - m_new);
+      ps += p[r];
+    }
+    lsum = lsum * alpha + ps;
+    if constexpr (CERT) eta = eta * alpha + ps * ev_c;
+    m = m_new;
+    const f4 av = {quad_bcast<0>(alpha), quad_bcast<1>(alpha), quad_bcast<2>(alpha), quad_bcast<3>(alpha)};
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      o[hf] *= av;
+      if constexpr (CERT) oo[hf] *= av;
+    }
+    if constexpr (VF == KVQ_INT2) oz *= av;
+    // ---- PV
+    lds_wait();
+    const uint32_t P0 = as_u(h2{(_Float16)p[0], (_Float16)p[1]});
+    const uint32_t P1 = as_u(h2{(_Float16)p[2], (_Float16)p[3]});
+    const uint2* sc2 = reinterpret_cast<const uint2*>(vml) + vgrp * 16;
+    if constexpr (VF == KVQ_INT4) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        h2 c0[4], c1[4];
+        v_int4_pairs(R.vw[d], c0);
+        v_int4_pairs(R.vw[CDW + d], c1);
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int s = 2 * d + x;
+          const int src = (4 * s + j) << 2;
+          const uint32_t A0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)P0);
+          const uint32_t A1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)P1);
+          const uint2 sc = sc2[s];
+          const h4 A = cat(as_h2(A0) * as_h2(sc.x), as_h2(A1) * as_h2(sc.y));
+          o[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, cat(c0[2 * x], c0[2 * x + 1]), o[0], 0, 0, 0);
+          o[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, cat(c1[2 * x], c1[2 * x + 1]), o[1], 0, 0, 0);
+        }
+      }
+    } else {  // INT2 values: codes 0..3, value = c * s + z
+      const h4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
+      const uint2* zc2 = reinterpret_cast<const uint2*>(vml) + (4 + vgrp) * 16;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        h2 c0[8], c1[8];
+        v_int2_pairs(R.vw[w], c0);
+        v_int2_pairs(R.vw[CDW + w], c1);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int s = 4 * w + kk;
+          const int src = (4 * s + j) << 2;
+          const uint32_t A0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)P0);
+          const uint32_t A1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)P1);
+          const uint2 sc = sc2[s];
+          const uint2 zc = zc2[s];
+          const h4 A = cat(as_h2(A0) * as_h2(sc.x), as_h2(A1) * as_h2(sc.y));
+          const h4 Az = cat(as_h2(A0) * as_h2(zc.x), as_h2(A1) * as_h2(zc.y));
+          o[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, cat(c0[2 * kk], c0[2 * kk + 1]), o[0], 0, 0, 0);
+          o[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, cat(c1[2 * kk], c1[2 * kk + 1]), o[1], 0, 0, 0);
+          oz = __builtin_amdgcn_mfma_f32_4x4x4f16(Az, ones, oz, 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // ---------------------------------------------------------------- one exactly recomputed chunk
+  auto exact_chunk = [&](int ch) {
+    const int tok0 = ch * TILE;
+    const bool bf16 = a.in_bf16 != 0;
+    const int tau = lane;
+    const bool live = tok0 + tau < T;
+    float lh[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint4* kp = reinterpret_cast<const uint4*>(a.k_orig + (stream * a.Tmax + tok0 + tau) * D);
+    for (int i = 0; i < 16; ++i) {
+      const uint4 u = kp[i];
+      const uint32_t ws[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int c = 8 * i + 2 * jj;
+        const float k0 = widen((uint16_t)(ws[jj] & 0xFFFF), bf16), k1 = widen((uint16_t)(ws[jj] >> 16), bf16);
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh) lh[hh] = fmaf(sm.qo[hh][c + 1], k1, fmaf(sm.qo[hh][c], k0, lh[hh]));
+      }
+    }
+    float cm[4];
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      if (!live) lh[hh] = NEG_INF;
+      cm[hh] = wave_max(lh[hh]);
+    }
+    const float mine = (j == 0) ? cm[0] : (j == 1) ? cm[1] : (j == 2) ? cm[2] : cm[3];
+    const float m_new = fmaxf(m, mine);
+    const float alpha = (m_new == NEG_INF) ? 1.0f : fast_exp2(m - m_new);
+    m = m_new;
+    const float mh[4] = {quad_bcast<0>(m), quad_bcast<1>(m), quad_bcast<2>(m), quad_bcast<3>(m)};
+    float sums[4];
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      const float ph = (mh[hh] == NEG_INF || !live) ? 0.0f : fast_exp2(lh[hh] - mh[hh]);
+      sums[hh] = wave_sum(ph);
+      sm.pb[wv][tau][hh] = ph;
+    }
+    const float mysum = (j == 0) ? sums[0] : (j == 1) ? sums[1] : (j == 2) ? sums[2] : sums[3];
+    lsum = lsum * alpha + (lane < 4 ? mysum : 0.0f);
+    eta = eta * alpha;
+    const f4 av = {quad_bcast<0>(alpha), quad_bcast<1>(alpha), quad_bcast<2>(alpha), quad_bcast<3>(alpha)};
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      o[hf] *= av;
+      oo[hf] *= av;
+    }
+    if constexpr (VF == KVQ_INT2) oz *= av;
+    lds_wait();
+    const uint32_t* vp = reinterpret_cast<const uint32_t*>(a.v_orig + (stream * a.Tmax + tok0) * D) + lane;
+    for (int tt = 0; tt < TILE; ++tt) {
+      const uint32_t vv = vp[(size_t)tt * (D / 2)];
+      const float v0 = widen((uint16_t)(vv & 0xFFFF), bf16), v1 = widen((uint16_t)(vv >> 16), bf16);
+      const float4 pp = *reinterpret_cast<const float4*>(&sm.pb[wv][tt][0]);
+      oo[0] += f4{pp.x, pp.y, pp.z, pp.w} * v0;
+      oo[1] += f4{pp.x, pp.y, pp.z, pp.w} * v1;
+    }
+    lds_wait();
+  };
+
+  // ---------------------------------------------------------------- software-pipelined walk
+  // Chunks c0+wv, c0+wv+4, ...: the loads of the next chunk are in flight while
+  // the current one is computed (two register sets used alternately).
+  auto is_flagged = [&](int ch) -> bool {
+    if constexpr (CERT) return a.flags != nullptr && a.flags[stream * a.nt + ch] != 0;
+    return false;
+  };
+  auto visit = [&](const ChunkRegs<KF, VF>& R, int ch, bool fl) {
     float ev_c = 0.0f;
     if constexpr (CERT) {
       const float* dsc = a.desc + (stream * a.nt + ch) * 3;
-      const float ek_c = dsc[0];
       ev_c = dsc[1];
       vnmax = fmaxf(vnmax, dsc[2]);
-      flagged = a.flags != nullptr && a.flags[stream * a.nt + ch] != 0;
-      if (!flagged) ekmax = fmaxf(ekmax, ek_c);
+      if (!fl) ekmax = fmaxf(ekmax, dsc[0]);
     }
-    float p[4];
-    float alpha;
-    if (!flagged) {
-      // ---------------- K: row of token pi(s_a, r_a) and its metadata
-      const int tok_a = tok_of<VF>(s_a, r_a);
-      uint32_t row[KDW];
-      {
-        const uint4* rp = reinterpret_cast<const uint4*>(a.k_codes + (stream * a.Tmax + tok0 + tok_a) * (KDW * 4));
-#pragma unroll
-        for (int i = 0; i < KDW / 4; ++i) {
-          uint4 u = rp[i];
-          row[4 * i] = u.x; row[4 * i + 1] = u.y; row[4 * i + 2] = u.z; row[4 * i + 3] = u.w;
-        }
-      }
-      uint32_t mt[4] = {0, 0, 0, 0};
-      {
-        const uint8_t* mp = a.k_meta + (stream * a.Tmax + tok0 + tok_a) * KM;
-        if constexpr (KM == 16) {
-          uint4 u = *reinterpret_cast<const uint4*>(mp);
-          mt[0] = u.x; mt[1] = u.y; mt[2] = u.z; mt[3] = u.w;
-        } else if constexpr (KM == 8) {
-          uint2 u = *reinterpret_cast<const uint2*>(mp);
-          mt[0] = u.x; mt[1] = u.y;
-        } else {
-          mt[0] = *reinterpret_cast<const uint16_t*>(mp);
-        }
-      }
-      // ---------------- V: channels 2*lane, 2*lane+1 of this tile
-      constexpr int CDW = VFmt<VF>::CDW;
-      uint32_t vw[2 * CDW];
-      {
-        const uint4* vp = reinterpret_cast<const uint4*>(a.v_codes + (stream * a.nt + ch) * (size_t)(D * CDW * 4) +
-                                                         (size_t)(2 * lane) * CDW * 4);
-#pragma unroll
-        for (int i = 0; i < CDW / 2; ++i) {
-          uint4 u = vp[i];
-          vw[4 * i] = u.x; vw[4 * i + 1] = u.y; vw[4 * i + 2] = u.z; vw[4 * i + 3] = u.w;
-        }
-      }
-      // V metadata tile -> LDS, ordered by (element, slice, r)
-      {
-        const int NM = meta_elems(VF, vg);
-        const uint16_t* vm = reinterpret_cast<const uint16_t*>(a.v_meta + (stream * a.nt + ch) * (size_t)(NM * TILE * 2));
-        for (int e = lane; e < NM * TILE; e += 64) {
-          const int mm = e >> 6, tau = e & 63;
-          const int ps = pos_of<VF>(tau);
-          sm.vmeta[wv][mm][ps >> 2][ps & 3] = vm[e];
-        }
-      }
-      // ---------------- QK^T: exact integer group dot products
-      float l[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      constexpr int NG = (KG == 128) ? 1 : 4;
-      constexpr int PER = 32 / NG;
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        i4 acc = {0, 0, 0, 0};
-#pragma unroll
-        for (int n = g * PER; n < (g + 1) * PER; ++n)
-          acc = __builtin_amdgcn_mfma_i32_4x4x4i8(KFmt<KF>::a_op(row, n), (int)qh[n], acc, 0, 0, 0);
-        int corr = 0;
-        if constexpr (KF == KVQ_INT4) corr = -8 * (int)qsum[g];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = acc[r] * 256 + corr;
-#pragma unroll
-        for (int n = g * PER; n < (g + 1) * PER; ++n)
-          acc = __builtin_amdgcn_mfma_i32_4x4x4i8(KFmt<KF>::a_op(row, n), (int)ql[n], acc, 0, 0, 0);
-        // scales of tokens pi(s, r): held by lanes 4s + r (A role); gather within the quad
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          uint32_t sw, zw = 0;
-          const int widx = (KF == KVQ_INT2) ? (g >> 1) : (g >> 1);
-          uint32_t src = mt[widx];
-          uint32_t srcz = (KF == KVQ_INT2) ? mt[2 + (g >> 1)] : 0u;
-          if (r == 0) { sw = quad_bcast_u<0>(src); if (KF == KVQ_INT2) zw = quad_bcast_u<0>(srcz); }
-          else if (r == 1) { sw = quad_bcast_u<1>(src); if (KF == KVQ_INT2) zw = quad_bcast_u<1>(srcz); }
-          else if (r == 2) { sw = quad_bcast_u<2>(src); if (KF == KVQ_INT2) zw = quad_bcast_u<2>(srcz); }
-          else { sw = quad_bcast_u<3>(src); if (KF == KVQ_INT2) zw = quad_bcast_u<3>(srcz); }
-          const uint16_t sb = (g & 1) ? (uint16_t)(sw >> 16) : (uint16_t)(sw & 0xFFFF);
-          float v = (float)acc[r] * f16_bits_to_f32(sb);
-          if constexpr (KF == KVQ_INT2) {
-            const uint16_t zb = (g & 1) ? (uint16_t)(zw >> 16) : (uint16_t)(zw & 0xFFFF);
-            v = fmaf(f16_bits_to_f32(zb), qsum[g], v);
-          }
-          l[r] += v;
-        }
-      }
-      // mask tokens past the sequence end
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        l[r] *= qs;
-        if (tok0 + tok_of<VF>(s_a, r) >= T) l[r] = NEG_INF;
-      }
-      // ---------------- online softmax
-      float cmax = fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3]));
-      cmax = max_same_head(cmax);
-      const float m_new = fmaxf(m, cmax);
-      alpha = (m_new == NEG_INF) ? 1.0f : exp2f(m - m_new);
-      float ps = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[r] = (m_new == NEG_INF) ? 0.0f : exp2f(l[r] - m_new);
-        ps += p[r];
-      }
-      lsum = lsum * alpha + ps;
-      if constexpr (CERT) eta = eta * alpha + ps * ev_c;
-      m = m_new;
-      // rescale accumulators (row h of the PV output needs head h's alpha)
-      const float a0 = quad_bcast<0>(alpha), a1 = quad_bcast<1>(alpha), a2 = quad_bcast<2>(alpha),
-                  a3 = quad_bcast<3>(alpha);
-      const f4 av = {a0, a1, a2, a3};
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        o[hf] *= av;
-        if constexpr (CERT) oo[hf] *= av;
-      }
-      if constexpr (VF == KVQ_INT2) oz *= av;
-      // ---------------- PV
-      lds_wait();
-      const uint32_t P0 = as_u(h2{(_Float16)p[0], (_Float16)p[1]});
-      const uint32_t P1 = as_u(h2{(_Float16)p[2], (_Float16)p[3]});
-      if constexpr (VF == KVQ_INT4) {
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-          h2 c0[4], c1[4];
-          v_int4_pairs(vw[d], c0);
-          v_int4_pairs(vw[CDW + d], c1);
-#pragma unroll
-          for (int x = 0; x < 2; ++x) {
-            const int s = 2 * d + x;
-            const int src = (4 * s + j) << 2;
-            const uint32_t A0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)P0);
-            const uint32_t A1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)P1);
-            const uint2 sc = *reinterpret_cast<const uint2*>(&sm.vmeta[wv][vgrp][s][0]);
-            const h4 A = cat(as_h2(A0) * as_h2(sc.x), as_h2(A1) * as_h2(sc.y));
-            o[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, cat(c0[2 * x], c0[2 * x + 1]), o[0], 0, 0, 0);
-            o[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, cat(c1[2 * x], c1[2 * x + 1]), o[1], 0, 0, 0);
-          }
-        }
-      } else {  // INT2 values: codes 0..3, value = c * s + z
-        const h4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          h2 c0[8], c1[8];
-          v_int2_pairs(vw[w], c0);
-          v_int2_pairs(vw[CDW + w], c1);
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            const int s = 4 * w + kk;
-            const int src = (4 * s + j) << 2;
-            const uint32_t A0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)P0);
-            const uint32_t A1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)P1);
-            const uint2 sc = *reinterpret_cast<const uint2*>(&sm.vmeta[wv][vgrp][s][0]);
-            const uint2 zc = *reinterpret_cast<const uint2*>(&sm.vmeta[wv][4 + vgrp][s][0]);
-            const h4 A = cat(as_h2(A0) * as_h2(sc.x), as_h2(A1) * as_h2(sc.y));
-            const h4 Az = cat(as_h2(A0) * as_h2(zc.x), as_h2(A1) * as_h2(zc.y));
-            o[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, cat(c0[2 * kk], c0[2 * kk + 1]), o[0], 0, 0, 0);
-            o[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, cat(c1[2 * kk], c1[2 * kk + 1]), o[1], 0, 0, 0);
-            oz = __builtin_amdgcn_mfma_f32_4x4x4f16(Az, ones, oz, 0, 0, 0);
-          }
-        }
-      }
-    } else if constexpr (CERT) {
-      // ---------------- exact recompute from the fp16 originals (original basis)
-      const bool bf16 = a.in_bf16 != 0;
-      const int tau = lane;
-      const bool live = tok0 + tau < T;
-      float lh[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      {
-        const uint4* kp = reinterpret_cast<const uint4*>(a.k_orig + (stream * a.Tmax + tok0 + tau) * D);
-        for (int i = 0; i < 16; ++i) {
-          uint4 u = kp[i];
-          uint32_t ws[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int c = 8 * i + 2 * jj;
-            const float k0 = widen((uint16_t)(ws[jj] & 0xFFFF), bf16), k1 = widen((uint16_t)(ws[jj] >> 16), bf16);
-#pragma unroll
-            for (int hh = 0; hh < 4; ++hh) lh[hh] = fmaf(sm.qo[hh][c + 1], k1, fmaf(sm.qo[hh][c], k0, lh[hh]));
-          }
-        }
-      }
-      float cm[4];
-#pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        if (!live) lh[hh] = NEG_INF;
-        cm[hh] = wave_max(lh[hh]);
-      }
-      const float mine = (j == 0) ? cm[0] : (j == 1) ? cm[1] : (j == 2) ? cm[2] : cm[3];
-      const float m_new = fmaxf(m, mine);
-      alpha = (m_new == NEG_INF) ? 1.0f : exp2f(m - m_new);
-      m = m_new;
-      const float mh[4] = {quad_bcast<0>(m), quad_bcast<1>(m), quad_bcast<2>(m), quad_bcast<3>(m)};
-      float ph[4], sums[4];
-#pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        ph[hh] = (mh[hh] == NEG_INF || !live) ? 0.0f : exp2f(lh[hh] - mh[hh]);
-        sums[hh] = wave_sum(ph[hh]);
-        sm.pb[wv][tau][hh] = ph[hh];
-      }
-      const float mysum = (j == 0) ? sums[0] : (j == 1) ? sums[1] : (j == 2) ? sums[2] : sums[3];
-      lsum = lsum * alpha + (lane < 4 ? mysum : 0.0f);
-      eta = eta * alpha;
-      const float a0 = quad_bcast<0>(alpha), a1 = quad_bcast<1>(alpha), a2 = quad_bcast<2>(alpha),
-                  a3 = quad_bcast<3>(alpha);
-      const f4 av = {a0, a1, a2, a3};
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        o[hf] *= av;
-        oo[hf] *= av;
-      }
-      if constexpr (VF == KVQ_INT2) oz *= av;
-      lds_wait();
-      const uint32_t* vp = reinterpret_cast<const uint32_t*>(a.v_orig + (stream * a.Tmax + tok0) * D) + lane;
-      for (int tt = 0; tt < TILE; ++tt) {
-        const uint32_t vv = vp[(size_t)tt * (D / 2)];
-        const float v0 = widen((uint16_t)(vv & 0xFFFF), bf16), v1 = widen((uint16_t)(vv >> 16), bf16);
-        const float4 pp = *reinterpret_cast<const float4*>(&sm.pb[wv][tt][0]);
-        oo[0] += f4{pp.x, pp.y, pp.z, pp.w} * v0;
-        oo[1] += f4{pp.x, pp.y, pp.z, pp.w} * v1;
-      }
-      lds_wait();
-      (void)p;
+    if (fl) {
+      if constexpr (CERT) exact_chunk(ch);
+    } else {
+      quant_chunk(R, ch, ev_c);
     }
+  };
+  // Pairs of chunks, then an odd last one: the loop has a single exit, so the
+  // loads in flight at its head are the same on entry and on every iteration.
+  const int n_my = c1 > ch ? (c1 - ch + 3) / 4 : 0;
+  for (int k = 0; k + 1 < n_my; k += 2) {
+    load_chunk<KF, KG, VF, VG>(a, stream, ch + 4, lane, tok_a, RB);
+    __builtin_amdgcn_sched_barrier(0);
+    visit(RA, ch, is_flagged(ch));
+    const int nx2 = ch + 8;
+    load_chunk<KF, KG, VF, VG>(a, stream, nx2 < c1 ? nx2 : ch, lane, tok_a, RA);
+    __builtin_amdgcn_sched_barrier(0);
+    visit(RB, ch + 4, is_flagged(ch + 4));
+    ch = nx2;
   }
+  if (n_my & 1) visit(RA, ch, is_flagged(ch));
 
   // ---------------- per-wave totals, then merge the 4 waves in LDS
   const float lt = sum_same_head(lsum);
@@ -719,7 +806,7 @@ __global__ __launch_bounds__(NT, 2) void decode_split(DecodeArgs a) {
     }
   }
   __syncthreads();
-  finish<CERT>(a, sm, b, hq0, nh, split);
+  write_record<CERT>(a, sm, b, hq0, nh, split);
 }
 
 // ------------------------------------------------------------------ dense fp16 baseline
@@ -834,7 +921,7 @@ __global__ __launch_bounds__(NT, 2) void decode_dense_split(DecodeArgs a) {
     sm.mrg_o[wv][hh][2 * lane + 1] = o[1][hh];
   }
   __syncthreads();
-  finish<false>(a, sm, b, hq0, nh, split);
+  write_record<false>(a, sm, b, hq0, nh, split);
 }
 
 }  // namespace
@@ -842,24 +929,33 @@ __global__ __launch_bounds__(NT, 2) void decode_dense_split(DecodeArgs a) {
 hipError_t launch_decode(const DecodeArgs& a, int k_fmt, int v_fmt, bool dense, hipStream_t s) {
   const int HG = (a.G + 3) / 4;
   dim3 grid(a.n_splits, a.H * HG, a.B);
+  const dim3 cgrid((a.B * a.Hq + 3) / 4);
   if (dense) {
     hipLaunchKernelGGL(decode_dense_split, grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL(combine_kernel<false>, cgrid, dim3(NT), 0, s, a);
     return hipGetLastError();
   }
   const bool cert = a.desc != nullptr;
-#define KVQ_LAUNCH(KF, KG, VF)                                                        \
-  if (k_fmt == KF && a.k_group == KG && v_fmt == VF) {                                \
-    if (cert)                                                                         \
-      hipLaunchKernelGGL((decode_split<KF, KG, VF, true>), grid, dim3(NT), 0, s, a);  \
-    else                                                                              \
-      hipLaunchKernelGGL((decode_split<KF, KG, VF, false>), grid, dim3(NT), 0, s, a); \
-    return hipGetLastError();                                                         \
+#define KVQ_LAUNCH(KF, KG, VF, VG)                                                            \
+  if (k_fmt == KF && a.k_group == KG && v_fmt == VF && a.v_group == VG) {                     \
+    if (cert) {                                                                               \
+      hipLaunchKernelGGL((decode_split<KF, KG, VF, VG, true>), grid, dim3(NT), 0, s, a);      \
+      hipLaunchKernelGGL(combine_kernel<true>, cgrid, dim3(NT), 0, s, a);                     \
+    } else {                                                                                  \
+      hipLaunchKernelGGL((decode_split<KF, KG, VF, VG, false>), grid, dim3(NT), 0, s, a);     \
+      hipLaunchKernelGGL(combine_kernel<false>, cgrid, dim3(NT), 0, s, a);                    \
+    }                                                                                         \
+    return hipGetLastError();                                                                 \
   }
-  KVQ_LAUNCH(KVQ_INT4, 32, KVQ_INT4)
-  KVQ_LAUNCH(KVQ_INT4, 128, KVQ_INT4)
-  KVQ_LAUNCH(KVQ_INT8, 128, KVQ_INT4)
-  KVQ_LAUNCH(KVQ_INT8, 32, KVQ_INT4)
-  KVQ_LAUNCH(KVQ_INT2, 32, KVQ_INT2)
+  KVQ_LAUNCH(KVQ_INT4, 32, KVQ_INT4, 32)
+  KVQ_LAUNCH(KVQ_INT4, 128, KVQ_INT4, 128)
+  KVQ_LAUNCH(KVQ_INT4, 32, KVQ_INT4, 128)
+  KVQ_LAUNCH(KVQ_INT4, 128, KVQ_INT4, 32)
+  KVQ_LAUNCH(KVQ_INT8, 128, KVQ_INT4, 128)
+  KVQ_LAUNCH(KVQ_INT8, 128, KVQ_INT4, 32)
+  KVQ_LAUNCH(KVQ_INT8, 32, KVQ_INT4, 32)
+  KVQ_LAUNCH(KVQ_INT8, 32, KVQ_INT4, 128)
+  KVQ_LAUNCH(KVQ_INT2, 32, KVQ_INT2, 32)
 #undef KVQ_LAUNCH
   return hipErrorNotSupported;
 }

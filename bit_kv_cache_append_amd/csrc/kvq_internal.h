@@ -70,11 +70,12 @@ struct BoundArgs {
   SeqArray seq;
 };
 
-// Workspace of a decode call: arrival counters (zero before the first call, left
-// zero by every call), then one partial-result record per (b, hq, split).
-// m: running max (log2 domain), l: sum of exp2, eta: sum of p * ev (certified),
-// ekmax/vnmax: maxima over this split's blocks, o: rotated-basis accumulator,
-// oo: original-basis accumulator for exactly recomputed blocks.
+// Workspace of a decode call: one partial-result record per (b, hq, split),
+// written by the split kernel and read by the combine kernel:
+// [0] m: running max (log2 domain), [1] l: sum of exp2, [2] eta: sum of p * ev
+// (certified), [3] ekmax, [4] vnmax: maxima over this split's blocks,
+// [5] ||q|| * softmax_scale, [8..8+D) o: rotated-basis accumulator,
+// [8+D..8+2D) oo: original-basis accumulator of exactly recomputed blocks.
 constexpr int PART_FLOATS = 8 + 2 * D;
 constexpr int MAX_SPLITS = 128;
 
@@ -91,7 +92,6 @@ struct DecodeArgs {
   const int8_t* signs;
   const uint16_t* rot;
   float* part;              // [B][Hq][n_splits][PART_FLOATS]
-  unsigned int* counters;   // [B][gridDim.y] arrival counters, zero between calls
   float* out;               // [B][Hq][128]
   float* cert;              // [B][Hq] or null
   int32_t B, Hq, H, G, Tmax, nt;

@@ -164,9 +164,10 @@ kvq_status kvq_buffer_bytes(const kvq_params* p, size_t* out_bytes);
 
 /* Workspace bytes kvq_decode_attn / kvq_decode_attn_dense need for these params
  * (depends on batch, heads and max_ctx only).  Host only; 0 on invalid params.
- * The workspace starts with arrival counters: zero-fill it once before its first
- * use; every call that completes leaves them zero again.  Calls that share one
- * workspace must not overlap (order them on one stream). */
+ * The workspace holds one partial-result record per (sequence, query head,
+ * context split); every call writes all records it reads, so its initial
+ * contents do not matter.  Calls that share one workspace must not overlap
+ * (order them on one stream). */
 size_t kvq_decode_workspace_bytes(const kvq_params* p);
 
 /*
@@ -202,8 +203,8 @@ kvq_status kvq_error_bound(const kvq_params* p, const kvq_cache* cache, const vo
  *     seq_len 0 are written as zeros.
  *   certificate: device fp32 [B][Hq] or NULL (needs keep_fp16_copy): an upper bound
  *     on ||out - dense attention over the originals||_2 for that row.
- *   workspace: device, >= kvq_decode_workspace_bytes(p) bytes, 256-byte aligned,
- *     zero-filled before its first use (see kvq_decode_workspace_bytes).
+ *   workspace: device, >= kvq_decode_workspace_bytes(p) bytes, 256-byte aligned
+ *     (scratch for the split records; any contents).
  * Attention output differs from exact fp64 attention over the decoded cache by
  * fp16 rounding of the query/probabilities and fp32 accumulation only.
  */
