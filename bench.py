@@ -6,21 +6,25 @@ kv heads, head_dim 128, context 8192; fp16 K/V N(0,1) with 10 seeded (head,
 channel) pairs x8; sign + Walsh-Hadamard rotation; symmetric int4 with one fp16
 scale per 32 channels for K and V.
 
-One step = the whole hot path over one batch:
-  1. kvq_append of a 4096-token prefill into every sequence (positions
-     4096..8191; 16 x 8 x 4096 K and V vectors), then
+One step = the whole hot path:
+  1. kvq_append of a 4096-token prefill (positions 4096..8191 of all 16
+     sequences, 16 x 8 x 4096 K and V vectors) into one cache, then
   2. kvq_decode_attn of one query token per (sequence, query head) over all 8192
-     positions.
-Before each timed kernel the L2 and the 256 MB Infinity Cache are flushed by
-reading a 1 GiB buffer (a reduction; reading leaves only clean lines behind, so
-no write-back lands inside the timed kernel), so the packed cache (144 MiB) is
-read from HBM.  Each
-kernel is bracketed by HIP events on the stream it runs on.
+     positions of another cache.
+Four caches (and four copies of the prefill input) are used in rotation: the
+decode of step i reads the cache appended in step i-2, so between two uses of a
+cache at least 3 x 144 MiB of other data streams through the 256 MB Infinity
+Cache and every timed call reads its inputs from HBM.  Each kernel sequence is
+also timed on its own (back-to-back calls over the rotating buffers, HIP events
+around the batch on the stream the calls are launched on), and once more with a
+1 GiB read flush and events around every single call (that figure includes the
+event and launch overhead of one isolated call).
 
 value = decode effective KV GB/s = packed K/V bytes (codes + scales) / mean
-decode time.  The same-shape fp16 decode (kvq_decode_attn_dense) is timed the
-same way for the int4-vs-fp16 comparison; append throughput is reported in
-Mvec/s.  The CPU oracle is timed on a bounded sample as a reported baseline.
+decode call time (split kernel + combine kernel).  The same-shape fp16 decode
+(kvq_decode_attn_dense) is timed the same way for the int4-vs-fp16 comparison;
+append throughput is reported in Mvec/s.  The CPU oracle is timed on a bounded
+sample as a reported baseline.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
 """
@@ -35,6 +39,7 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "decode-attn effective KV GB/s & % HBM peak (int4 vs fp16); append Mvec/s"
+NROT = 4
 
 
 def parse():
@@ -73,11 +78,11 @@ def cpu_baseline(c, sample_b):
     kv_bytes = sample_b * H * T * 144
     vecs = sample_b * H * P * 2
     return {
-        "value": kv_bytes / t_dec / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "value": round(kv_bytes / t_dec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
         "sample": (f"{sample_b} of {c['B']} sequences: decode over {T} tokens (all {c['Hq']} q heads) took "
                    f"{t_dec:.2f} s; the {P}-token prefill append of those sequences ({vecs} vectors) took "
                    f"{t_app:.2f} s"),
-        "append_mvec_s": vecs / t_app / 1e6,
+        "append_mvec_s": round(vecs / t_app / 1e6, 4),
     }
 
 
@@ -104,73 +109,100 @@ def main():
     v_dev = kvq.to_device_bits(v_all)
     del k_all, v_all
     q = kvq.to_device_bits(q_np)
-    k_pre = k_dev[:, :, T - P:].contiguous()
-    v_pre = v_dev[:, :, T - P:].contiguous()
     s_dev = torch.from_numpy(synth.signs(c).copy()).to(dev)
     p = kvq.params_from_config(c)
-    cache = kvq.Cache(p, signs=s_dev)
+    seq = [T] * B
+    # NROT caches with the context [0, T - P) appended once (untimed), NROT copies of the prefill input
+    caches = [kvq.Cache(p, signs=s_dev) for _ in range(NROT)]
+    k_ctx = k_dev[:, :, :T - P].contiguous()
+    v_ctx = v_dev[:, :, :T - P].contiguous()
+    for cc in caches:
+        kvq.append(p, cc, k_ctx, v_ctx, [0] * B)
+    del k_ctx, v_ctx
+    k_pre = [k_dev[:, :, T - P:].contiguous() for _ in range(NROT)]
+    v_pre = [v_dev[:, :, T - P:].contiguous() for _ in range(NROT)]
+    for cc in caches:  # every cache holds the full context before any decode
+        kvq.append(p, cc, k_pre[0], v_pre[0], [T - P] * B)
     ws = kvq.workspace(p)
     out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
-    seq = [T] * B
-    # context [0, T - P) once, untimed
-    kvq.append(p, cache, k_dev[:, :, :T - P].contiguous(), v_dev[:, :, :T - P].contiguous(), [0] * B)
-    flush_buf = torch.ones(1 << 27, dtype=torch.int64, device=dev)  # 1 GiB
-    sink = torch.zeros((), dtype=torch.int64, device=dev)
-
-    def flush():
-        torch.sum(flush_buf, dim=0, out=sink)
-
-    torch.cuda.synchronize()
-
-    def step(i, ev):
-        flush()
-        ev[0].record()
-        kvq.append(p, cache, k_pre, v_pre, [T - P] * B)
-        ev[1].record()
-        flush()
-        ev[2].record()
-        kvq.decode_attn(p, cache, q, seq, ws=ws, out=out)
-        ev[3].record()
-
-    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    for i in range(args.warmup):
-        step(i, mk())
-    torch.cuda.synchronize()
-    events = [mk() for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    app_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
-    dec_ms = np.array([e[2].elapsed_time(e[3]) for e in events])
-
-    # same-shape fp16 decode (dense K/V already resident: the inputs themselves)
+    # fp16 baseline: two copies of the dense K/V (2 x 512 MiB) in rotation
+    kd = [k_dev, k_dev.clone()]
+    vd = [v_dev, v_dev.clone()]
     dws = kvq.workspace(p)
     dout = torch.empty_like(out)
-    fev = []
-    for i in range(args.warmup + args.steps):
-        flush()
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        e[0].record()
-        kvq.decode_attn_dense(p, k_dev, v_dev, q, seq, ws=dws, out=dout)
-        e[1].record()
-        if i >= args.warmup:
-            fev.append(e)
+    flush_buf = torch.ones(1 << 27, dtype=torch.int64, device=dev)  # 1 GiB
+    sink = torch.zeros((), dtype=torch.int64, device=dev)
     torch.cuda.synchronize()
-    f16_ms = np.array([e[0].elapsed_time(e[1]) for e in fev])
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def batch_time(fn, n):
+        """Mean ms per call of fn(i) for n back-to-back calls (events around the batch)."""
+        e0, e1 = ev(), ev()
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    def do_append(i):
+        kvq.append(p, caches[i % NROT], k_pre[i % NROT], v_pre[i % NROT], [T - P] * B)
+
+    def do_decode(i):
+        kvq.decode_attn(p, caches[i % NROT], q, seq, ws=ws, out=out)
+
+    def do_dense(i):
+        kvq.decode_attn_dense(p, kd[i % 2], vd[i % 2], q, seq, ws=dws, out=dout)
+
+    def step(i):
+        do_append(i)
+        do_decode(i + 2)
+
+    # warm-up, then the timed steps (whole hot path)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step_ms = batch_time(lambda i: step(args.warmup + i), args.steps)
+    wall = time.perf_counter() - t0
+    # each kernel sequence on its own over the rotating buffers
+    n_each = max(args.steps, 4 * NROT)
+    batch_time(do_decode, NROT)
+    dec_ms = batch_time(do_decode, n_each)
+    batch_time(do_append, NROT)
+    app_ms = batch_time(do_append, n_each)
+    batch_time(do_dense, 2)
+    f16_ms = batch_time(do_dense, n_each)
+    # isolated calls: 1 GiB read flush, events around each call
+    iso = []
+    for i in range(args.warmup + args.steps):
+        torch.sum(flush_buf, dim=0, out=sink)
+        e0, e1 = ev(), ev()
+        e0.record()
+        do_decode(i)
+        e1.record()
+        if i >= args.warmup:
+            iso.append((e0, e1))
+    torch.cuda.synchronize()
+    iso_ms = float(np.mean([a.elapsed_time(b) for a, b in iso]))
+    # int4 vs fp16 outputs on the same query (quantization effect, informational)
+    do_decode(0)
+    do_dense(0)
+    torch.cuda.synchronize()
     rel = (out - dout).abs().amax(dim=-1) / dout.abs().amax(dim=-1)
     int4_vs_fp16_maxrel = float(rel.max().item())
 
-    kv_bytes = B * H * T * (64 + 8) * 2           # packed K and V: codes + fp16 group scales
+    kv_bytes = B * H * T * (64 + 8) * 2            # packed K and V: codes + fp16 group scales
     io_bytes = B * Hq * 128 * 2 + B * Hq * 128 * 4  # query in, fp32 output out
     f16_bytes = B * H * T * 128 * 2 * 2
     vecs = B * H * P * 2
     app_bytes = vecs * (256 + 72)
-    dec_s = dec_ms.mean() / 1e3
-    f16_s = f16_ms.mean() / 1e3
-    app_s = app_ms.mean() / 1e3
+    dec_s, f16_s, app_s = dec_ms / 1e3, f16_ms / 1e3, app_ms / 1e3
     dec_gbs = kv_bytes / dec_s / 1e9
+    achieved = (kv_bytes + io_bytes) / dec_s / 1e9
+    n_splits = kvq.decode_splits(p, seq)
     result = {
         "metric": METRIC,
         "value": round(dec_gbs, 1),
@@ -178,7 +210,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "ms_per_step": round(step_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -187,12 +219,14 @@ def main():
         "config": {"workload": "llama3-8b-shaped GQA int4 decode + prefill append", "B": B, "Hq": Hq, "Hkv": H,
                    "head_dim": 128, "context": T, "prefill_tokens": P, "k_fmt": "int4 g32", "v_fmt": "int4 g32",
                    "rotation": "sign+fwht"},
-        "roofline": {"bound": "hbm", "achieved": round((kv_bytes + io_bytes) / dec_s / 1e9, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round((kv_bytes + io_bytes) / dec_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_split<int4,g32,int4> (one launch per kvq_decode_attn)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_split<int4 g32, int4 g32> + combine_kernel (one kvq_decode_attn call)",
+                     "bytes_per_call": kv_bytes + io_bytes},
         "decode_us": round(dec_s * 1e6, 2),
         "decode_pct_hbm_peak": round(100 * dec_gbs / HBM_PEAK_GBS, 2),
+        "decode_isolated_call_us": round(iso_ms * 1e3, 2),
+        "decode_grid": [n_splits, H * ((Hq // H + 3) // 4), B],
         "fp16_decode_us": round(f16_s * 1e6, 2),
         "fp16_decode_gbs": round(f16_bytes / f16_s / 1e9, 1),
         "fp16_decode_pct_hbm_peak": round(100 * f16_bytes / f16_s / 1e9 / HBM_PEAK_GBS, 2),
@@ -203,6 +237,7 @@ def main():
         "append_mvec_s": round(vecs / app_s / 1e6, 1),
         "append_gbs": round(app_bytes / app_s / 1e9, 1),
         "append_pct_hbm_peak": round(100 * app_bytes / app_s / 1e9 / HBM_PEAK_GBS, 2),
+        "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "input_gen_s": round(t_gen, 2),
     }
     if not args.no_cpu_baseline:

@@ -4,7 +4,7 @@ Every computation runs in the HIP kernels of libkvq.so; this module turns torch
 tensors into device pointers and the current HIP stream, calls the C entry
 points of the same names (kvq_append, kvq_error_bound, kvq_decode_attn,
 kvq_decode_attn_dense, kvq_calibrate_clip, kvq_buffer_bytes,
-kvq_decode_workspace_bytes) and raises KvqError on a non-zero status.  There is
+kvq_decode_workspace_bytes, kvq_decode_splits) and raises KvqError on a non-zero status.  There is
 no fallback: if the library is not built, importing the functions raises.
 """
 
@@ -68,6 +68,8 @@ def lib():
         L.kvq_buffer_bytes.argtypes = [P(Params), P(ctypes.c_size_t)]
         L.kvq_decode_workspace_bytes.restype = ctypes.c_size_t
         L.kvq_decode_workspace_bytes.argtypes = [P(Params)]
+        L.kvq_decode_splits.restype = i32
+        L.kvq_decode_splits.argtypes = [P(Params), P(i32)]
         L.kvq_append.restype = i32
         L.kvq_append.argtypes = [P(Params), P(CacheStruct), vp, vp, P(i32), i32, vp]
         L.kvq_error_bound.restype = i32
@@ -115,6 +117,11 @@ def buffer_bytes(p):
 
 def decode_workspace_bytes(p):
     return int(lib().kvq_decode_workspace_bytes(ctypes.byref(p)))
+
+
+def decode_splits(p, seq_len):
+    """kvq_decode_splits: context splits of a decode call with these sequence lengths."""
+    return int(lib().kvq_decode_splits(ctypes.byref(p), _i32(seq_len)))
 
 
 def _ptr(t):
@@ -183,10 +190,10 @@ def error_bound(p, cache, q, seq_len, tau, bound=None, flags=None, stream=None):
 
 
 def workspace(p, device="cuda"):
-    """A zero-filled decode workspace (its counters must start at zero; calls keep them zero)."""
+    """A decode workspace (split records; its contents on entry do not matter)."""
     import torch
     n = decode_workspace_bytes(p)
-    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def decode_attn(p, cache, q, seq_len, flags=None, certificate=False, ws=None, out=None, cert=None, stream=None):

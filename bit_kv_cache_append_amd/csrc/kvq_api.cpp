@@ -143,6 +143,18 @@ kvq_status kvq_buffer_bytes(const kvq_params* p, size_t* out) {
   return KVQ_OK;
 }
 
+int32_t kvq_decode_splits(const kvq_params* p, const int32_t* seq_len_host) {
+  if (check_params(p) || !seq_len_host) return 0;
+  int max_chunks = 0;
+  for (int b = 0; b < p->batch; ++b) {
+    const int32_t t = seq_len_host[b];
+    if (t < 0 || t > p->max_ctx) return 0;
+    const int ch = (t + TILE - 1) / TILE;
+    if (ch > max_chunks) max_chunks = ch;
+  }
+  return choose_splits(p, max_chunks > 0 ? max_chunks : 1);
+}
+
 size_t kvq_decode_workspace_bytes(const kvq_params* p) {
   if (check_params(p)) return 0;
   return (size_t)p->batch * p->n_q_heads * max_splits_for(p) * PART_FLOATS * sizeof(float);

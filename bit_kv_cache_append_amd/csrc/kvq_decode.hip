@@ -77,9 +77,10 @@ template <>
 struct KFmt<KVQ_INT4> {
   static constexpr int DW = 16;  // dwords per row
   static constexpr int MDW = 2;  // metadata dwords per token (g32: 4 fp16); g128 uses 1 fp16
+  // offset-binary nibbles (code + 8) as bytes: the low or the high nibble of each byte
   __device__ static __forceinline__ int a_op(const uint32_t* row, int n) {
-    uint32_t t = row[n >> 1] ^ 0x88888888u;
-    return (int)((n & 1) ? ((t >> 4) & 0x0F0F0F0Fu) : (t & 0x0F0F0F0Fu));
+    const uint32_t t = (n & 1) ? (row[n >> 1] >> 4) : row[n >> 1];
+    return (int)((t & 0x0F0F0F0Fu) ^ 0x08080808u);
   }
   __device__ static __forceinline__ int chan(int n, int m) { return 8 * (n >> 1) + 2 * m + (n & 1); }
   __device__ static __forceinline__ int slot(int c) { return 4 * (2 * (c >> 3) + (c & 1)) + ((c & 7) >> 1); }
@@ -105,16 +106,17 @@ struct KFmt<KVQ_INT2> {
 
 // ------------------------------------------------------------------ V formats
 // exact fp16 codes of one dword of a channel's token run, as fp16 pairs
+// (the nibble n of a two's complement code c is placed in an fp16 mantissa as
+// n ^ 8 = c + 8 under exponent 2^10: one and-xor per pair, then one packed op)
 __device__ __forceinline__ void v_int4_pairs(uint32_t w, h2 out[4]) {
-  const uint32_t t = w ^ 0x88888888u;
-  const uint32_t t8 = t >> 8;
+  const uint32_t w8 = w >> 8;
   const h2 k1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
   const h2 k16 = {(_Float16)0.0625f, (_Float16)0.0625f};
   const h2 k72 = {(_Float16)-72.0f, (_Float16)-72.0f};
-  out[0] = as_h2((t & 0x000F000Fu) | 0x64006400u) + k1032;                     // tokens 0, 4
-  out[1] = as_h2((t & 0x00F000F0u) | 0x64006400u) * k16 + k72;                 // tokens 1, 5
-  out[2] = as_h2((t8 & 0x000F000Fu) | 0x64006400u) + k1032;                    // tokens 2, 6
-  out[3] = as_h2((t8 & 0x00F000F0u) | 0x64006400u) * k16 + k72;                // tokens 3, 7
+  out[0] = as_h2((w & 0x000F000Fu) ^ 0x64086408u) + k1032;                     // tokens 0, 4
+  out[1] = as_h2((w & 0x00F000F0u) ^ 0x64806480u) * k16 + k72;                 // tokens 1, 5
+  out[2] = as_h2((w8 & 0x000F000Fu) ^ 0x64086408u) + k1032;                    // tokens 2, 6
+  out[3] = as_h2((w8 & 0x00F000F0u) ^ 0x64806480u) * k16 + k72;                // tokens 3, 7
 }
 // int2: element k and k+8 of a 16-token dword, codes 0..3
 __device__ __forceinline__ void v_int2_pairs(uint32_t w, h2 out[8]) {
@@ -353,26 +355,53 @@ __global__ __launch_bounds__(NT) void combine_kernel(DecodeArgs a) {
     if (CERT && a.cert && l == 0) a.cert[row] = 0.0f;
     return;
   }
+  // Records in batches of 8 splits: all loads of a batch are issued together
+  // (indices past the last split reload it and get weight 0), then merged with
+  // a running maximum.
   const float* rec0 = a.part + (size_t)row * a.n_splits * PART_FLOATS;
-  float M = NEG_INF;
-  for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, rec0[s * PART_FLOATS]);
-  float L = 0.0f, E = 0.0f, ek = 0.0f, vn = 0.0f, o0 = 0.0f, o1 = 0.0f, p0 = 0.0f, p1 = 0.0f;
-  for (int s = 0; s < a.n_splits; ++s) {
-    const float* rec = rec0 + s * PART_FLOATS;
-    const float4 h0 = *reinterpret_cast<const float4*>(rec);
-    const float wt = (h0.x == NEG_INF) ? 0.0f : exp2f(h0.x - M);
-    L += wt * h0.y;
-    E += wt * h0.z;
-    ek = fmaxf(ek, h0.w);
-    vn = fmaxf(vn, rec[4]);
-    const float2 ov = *reinterpret_cast<const float2*>(rec + 8 + c);
-    o0 += wt * ov.x;
-    o1 += wt * ov.y;
-    if constexpr (CERT) {
-      const float2 pv = *reinterpret_cast<const float2*>(rec + 8 + D + c);
-      p0 += wt * pv.x;
-      p1 += wt * pv.y;
+  constexpr int SB = 8;
+  float M = NEG_INF, L = 0.0f, E = 0.0f, ek = 0.0f, vn = 0.0f, o0 = 0.0f, o1 = 0.0f, p0 = 0.0f, p1 = 0.0f;
+  for (int s0 = 0; s0 < a.n_splits; s0 += SB) {
+    float4 hd[SB];
+    float vs[SB];
+    float2 ov[SB], pv[SB];
+#pragma unroll
+    for (int i = 0; i < SB; ++i) {
+      const float* rec = rec0 + (size_t)min(s0 + i, a.n_splits - 1) * PART_FLOATS;
+      hd[i] = *reinterpret_cast<const float4*>(rec);
+      vs[i] = rec[4];
+      ov[i] = *reinterpret_cast<const float2*>(rec + 8 + c);
+      if constexpr (CERT) pv[i] = *reinterpret_cast<const float2*>(rec + 8 + D + c);
     }
+    float Mb = M;
+#pragma unroll
+    for (int i = 0; i < SB; ++i)
+      if (s0 + i < a.n_splits) Mb = fmaxf(Mb, hd[i].x);
+    const float sc = (M == NEG_INF) ? 0.0f : exp2f(M - Mb);
+    L *= sc;
+    E *= sc;
+    o0 *= sc;
+    o1 *= sc;
+    if constexpr (CERT) {
+      p0 *= sc;
+      p1 *= sc;
+    }
+#pragma unroll
+    for (int i = 0; i < SB; ++i) {
+      if (s0 + i >= a.n_splits) continue;
+      const float wt = (hd[i].x == NEG_INF) ? 0.0f : exp2f(hd[i].x - Mb);
+      L += wt * hd[i].y;
+      E += wt * hd[i].z;
+      ek = fmaxf(ek, hd[i].w);
+      vn = fmaxf(vn, vs[i]);
+      o0 += wt * ov[i].x;
+      o1 += wt * ov[i].y;
+      if constexpr (CERT) {
+        p0 += wt * pv[i].x;
+        p1 += wt * pv[i].y;
+      }
+    }
+    M = Mb;
   }
   const float inv = 1.0f / L;
   o0 *= inv;
@@ -563,31 +592,41 @@ __global__ __launch_bounds__(NT, 2) void decode_split(DecodeArgs a) {
   auto quant_chunk = [&](const ChunkRegs<KF, VF>& R, int ch, float ev_c) {
     const int tok0 = ch * TILE;
     stage_vmeta<VF, VG>(vml, lane, R.vmeta);
-    // ---- QK^T: exact integer dot products, the NG group chains interleaved
+    // ---- QK^T: exact integer dot products.  Four independent accumulator
+    // chains per query half (chain c covers channels 32c..32c+31, i.e. one
+    // 32-channel group); each K operand is unpacked once and feeds both halves.
     constexpr int NG = (KG == 128) ? 1 : 4;
-    constexpr int PER = 32 / NG;
-    i4 acc[NG];
+    constexpr int NC = 4, PER = 32 / NC;
+    i4 ah[NC], al[NC];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) acc[g] = i4{0, 0, 0, 0};
-#pragma unroll
-    for (int n = 0; n < PER; ++n)
-#pragma unroll
-      for (int g = 0; g < NG; ++g)
-        acc[g] = __builtin_amdgcn_mfma_i32_4x4x4i8(KFmt<KF>::a_op(R.krow, g * PER + n), (int)qh[g * PER + n],
-                                                   acc[g], 0, 0, 0);
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
+    for (int c = 0; c < NC; ++c) {
+      // the offset-binary correction -8 * sum(q16) of the chain's group rides in the low half
       int corr = 0;
-      if constexpr (KF == KVQ_INT4) corr = -8 * (int)qsum[g];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[g][r] = acc[g][r] * 256 + corr;
+      if constexpr (KF == KVQ_INT4) corr = (NG == 1) ? (c == 0 ? -8 * (int)qsum[0] : 0) : -8 * (int)qsum[c];
+      ah[c] = i4{0, 0, 0, 0};
+      al[c] = i4{corr, corr, corr, corr};
     }
 #pragma unroll
     for (int n = 0; n < PER; ++n)
 #pragma unroll
-      for (int g = 0; g < NG; ++g)
-        acc[g] = __builtin_amdgcn_mfma_i32_4x4x4i8(KFmt<KF>::a_op(R.krow, g * PER + n), (int)ql[g * PER + n],
-                                                   acc[g], 0, 0, 0);
+      for (int c = 0; c < NC; ++c) {
+        const int av = KFmt<KF>::a_op(R.krow, c * PER + n);
+        ah[c] = __builtin_amdgcn_mfma_i32_4x4x4i8(av, (int)qh[c * PER + n], ah[c], 0, 0, 0);
+        al[c] = __builtin_amdgcn_mfma_i32_4x4x4i8(av, (int)ql[c * PER + n], al[c], 0, 0, 0);
+      }
+    i4 acc[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (NG == 1) {
+          acc[g][r] = 0;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) acc[g][r] += ah[c][r] * 256 + al[c][r];
+        } else {
+          acc[g][r] = ah[g][r] * 256 + al[g][r];
+        }
+      }
     // ---- group scales of tokens pi(s, r), held by lanes 4s + r (A role): quad broadcast
     float l[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll

@@ -170,6 +170,11 @@ kvq_status kvq_buffer_bytes(const kvq_params* p, size_t* out_bytes);
  * (order them on one stream). */
 size_t kvq_decode_workspace_bytes(const kvq_params* p);
 
+/* Number of context splits kvq_decode_attn uses for these params and sequence
+ * lengths (the split kernel's grid is splits x (Hkv * ceil(Hq/Hkv / 4)) x B
+ * workgroups).  Host only, informational; 0 on invalid input. */
+int32_t kvq_decode_splits(const kvq_params* p, const int32_t* seq_len_host);
+
 /*
  * Append n_new tokens to every sequence: positions [start_pos_host[b],
  * start_pos_host[b] + n_new) of sequence b are (over)written.
