@@ -21,6 +21,8 @@
 
 #include "kvq_common.h"
 
+#include <type_traits>
+
 namespace kvq {
 
 namespace {
@@ -536,8 +538,342 @@ __global__ __launch_bounds__(NT) void append_kernel(AppendArgs a) {
   }
 }
 
+// ================================================================ fast path
+// Symmetric int4/int8 codes with the sign + Walsh-Hadamard rotation (or none).
+// Same thread layout and the same fp32 operations in the same order as the
+// generic kernel above, with the work per element cut down:
+//  * sign flips are xors of the fp16/bf16 sign bits before widening (exact);
+//  * the cross-lane butterflies negate the own value and add the partner's
+//    (fl32(p + (-v)) is fl32(p - v));
+//  * the quotient y / s is rounded with one refinement of y * (1/s) by its exact
+//    residual, then a magic-number add that rounds half to even (see
+//    quot_magic);
+//  * codes are packed with byte permutes, and V codes reach the channel-major
+//    tile through an 8x8 nibble transpose of LDS words.
+namespace {
+
+constexpr float MAGIC = 8388608.0f;  // 2^23
+
+// RNE(y / sf) + offset, as the low mantissa bits of 2^23 + offset + RNE(y / sf),
+// clamped to [offset - qmax, offset + qmax].  r = rcp(sf) (<= 1 ulp).  t = y r
+// is within |q| 2^-22 of q = y / sf; one step with the exact residual brings
+// the error below |q| 2^-43, and a quotient that is not a midpoint k + 1/2 lies
+// at least one fp32 ulp of q away from every midpoint (y has 24 significant
+// bits, sf 11), so rounding the refined value is rounding q.
+template <int OFF, int QMAX>
+__device__ __forceinline__ float quot_magic(float y, float sf, float r) {
+  const float t = y * r;
+  const float e = __builtin_fmaf(-t, sf, y);
+  const float tq = __builtin_fmaf(e, r, t);
+  const float m = tq + (MAGIC + (float)OFF);  // ulp 1: round half to even
+  return __builtin_amdgcn_fmed3f(m, MAGIC + (float)(OFF - QMAX), MAGIC + (float)(OFF + QMAX));
+}
+
+// gather the low bytes of 4 floats into one dword (byte i = x[i] low byte)
+__device__ __forceinline__ uint32_t low_bytes4(float x0, float x1, float x2, float x3) {
+  const uint32_t a = __builtin_amdgcn_perm(__float_as_uint(x1), __float_as_uint(x0), 0x0C0C0400u);
+  const uint32_t b = __builtin_amdgcn_perm(__float_as_uint(x3), __float_as_uint(x2), 0x0C0C0400u);
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+
+struct __align__(16) FastSmem {
+  uint32_t smask[4][16];     // per quarter: sign masks of 16 fp16 pairs
+  uint32_t vt[TILE][17];     // V: per token 16 nibble words (8 channels each), padded
+};
+
+// 8x8 transpose of nibbles: w[e] nibble j -> w[j] nibble e
+__device__ __forceinline__ void transpose8x8_nibbles(uint32_t w[8]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {  // 4-nibble blocks
+    const uint32_t a = w[e], b = w[e + 4];
+    w[e] = __builtin_amdgcn_perm(b, a, 0x05040100u);
+    w[e + 4] = __builtin_amdgcn_perm(b, a, 0x07060302u);
+  }
+#pragma unroll
+  for (int e0 = 0; e0 < 8; e0 += 4)
+#pragma unroll
+    for (int e = e0; e < e0 + 2; ++e) {  // 2-nibble blocks (bytes)
+      const uint32_t a = w[e], b = w[e + 2];
+      w[e] = __builtin_amdgcn_perm(b, a, 0x06020400u);
+      w[e + 2] = __builtin_amdgcn_perm(b, a, 0x07030501u);
+    }
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {  // single nibbles
+    const uint32_t a = w[e], b = w[e + 1];
+    w[e] = (a & 0x0F0F0F0Fu) | ((b << 4) & 0xF0F0F0F0u);
+    w[e + 1] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+  }
+}
+
+}  // namespace
+
+// One workgroup per (tensor, tile, kv head, sequence) unit; the tensor is the
+// fastest-varying index so that the K and V workgroups of a tile are adjacent.
+struct FastUnit {
+  int b, h, tensor, tile, lo, hi, pos;
+  bool valid;
+  size_t stream_idx;
+  const uint16_t* src;
+};
+
+__device__ __forceinline__ FastUnit fast_unit(const AppendArgs& a, int u, int ntiles) {
+  FastUnit U;
+  const int tau = threadIdx.x >> 2, q = threadIdx.x & 3;
+  U.tensor = u & 1;
+  const int r = u >> 1;
+  const int ti = r % ntiles, r2 = r / ntiles;
+  U.h = r2 % a.H;
+  U.b = r2 / a.H;
+  const int start = a.start.v[U.b];
+  U.tile = start / TILE + ti;
+  U.lo = max(start, U.tile * TILE);
+  U.hi = min(start + a.n_new, U.tile * TILE + TILE);
+  U.pos = U.tile * TILE + tau;
+  U.valid = U.pos >= U.lo && U.pos < U.hi;
+  U.stream_idx = (size_t)U.b * a.H + U.h;
+  U.src = (U.tensor ? a.v_new : a.k_new) + ((U.stream_idx * a.n_new + (U.valid ? U.pos - start : 0)) * D + 32 * q);
+  return U;
+}
+
+__device__ __forceinline__ void fast_load(const uint16_t* src, uint32_t w[16]) {
+  const uint4* p4 = reinterpret_cast<const uint4*>(src);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 u = p4[i];
+    w[4 * i] = u.x; w[4 * i + 1] = u.y; w[4 * i + 2] = u.z; w[4 * i + 3] = u.w;
+  }
+}
+
+// quantize 32 rotated values of one lane (its group of 32, or a quarter of a
+// group of 128) into packed code dwords; optional residual and norm sums
+template <int FMT, int GROUP>
+__device__ __forceinline__ void fast_quantize(const float y[32], bool want_sums, uint32_t packed[8], uint16_t& meta,
+                                              float& res2, float& ynorm2) {
+  constexpr int QMAX = FMT == KVQ_INT4 ? 7 : 127;
+  constexpr int OFF = FMT == KVQ_INT4 ? 8 : 128;
+  float am = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) am = fmaxf(am, fabsf(y[j]));
+  if constexpr (GROUP == 128) {
+    am = fmaxf(am, dpp_f<KVQ_DPP_XOR1>(am));
+    am = fmaxf(am, dpp_f<KVQ_DPP_XOR2>(am));
+  }
+  const uint16_t sb = f16_sat_bits(am / (float)QMAX);  // correctly rounded fp32 divide
+  const float sf = f16_bits_to_f32(sb);
+  meta = sb;
+  // a zero scale gives code 0 for every element: divisor 1 and reciprocal 0 do that
+  const float sq = sf != 0.0f ? sf : 1.0f;
+  const float r = sf != 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f;
+  float acc = 0.0f, yn = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {  // 8 elements at a time
+    float m[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m[e] = quot_magic<OFF, QMAX>(y[8 * k + e], sq, r);
+    if (want_sums) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float cj = m[e] - (MAGIC + (float)OFF);  // exact
+        const float d = y[8 * k + e] - cj * sf;
+        acc = acc + d * d;
+        yn = yn + y[8 * k + e] * y[8 * k + e];
+      }
+    }
+    if constexpr (FMT == KVQ_INT4) {
+      // offset-binary nibbles: bytes of even / odd elements, then nibble-merged; ^8 -> two's complement
+      const uint32_t ev = low_bytes4(m[0], m[2], m[4], m[6]);
+      const uint32_t od = low_bytes4(m[1], m[3], m[5], m[7]);
+      packed[k] = ((od << 4) | (ev & 0x0F0F0F0Fu)) ^ 0x88888888u;
+    } else {
+      packed[2 * k] = low_bytes4(m[0], m[1], m[2], m[3]) ^ 0x80808080u;
+      packed[2 * k + 1] = low_bytes4(m[4], m[5], m[6], m[7]) ^ 0x80808080u;
+    }
+  }
+  res2 = acc;
+  ynorm2 = yn;
+}
+
+template <int KF, int KG, int VF, int VG, bool BF16>
+__device__ __forceinline__ void fast_process(const AppendArgs& a, FastSmem& sm, const FastUnit& U, const uint32_t w[16]) {
+  const int t = threadIdx.x, tau = t >> 2, q = t & 3;
+  const int tensor = U.tensor, tile = U.tile, pos = U.pos;
+  const bool valid = U.valid;
+  const size_t stream_idx = U.stream_idx;
+  const bool fwht = a.rotation == KVQ_ROT_SIGN_FWHT;
+  const bool desc = a.desc != nullptr;
+
+  // originals and the input norm first, so the raw words are dead after the rotation
+  float xnorm2 = 0.0f;
+  if (desc) {
+    if (valid) {
+      uint16_t* orig = tensor ? a.v_orig : a.k_orig;
+      uint4* d4 = reinterpret_cast<uint4*>(orig + ((stream_idx * a.Tmax + pos) * D + 32 * q));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d4[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float x0 = widen((uint16_t)(w[k] & 0xFFFF), BF16), x1 = widen((uint16_t)(w[k] >> 16), BF16);
+      xnorm2 = xnorm2 + x0 * x0;
+      xnorm2 = xnorm2 + x1 * x1;
+    }
+  }
+
+  float y[32];
+  if (fwht) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t ws = w[k] ^ sm.smask[q][k];
+      y[2 * k] = widen((uint16_t)(ws & 0xFFFF), BF16);
+      y[2 * k + 1] = widen((uint16_t)(ws >> 16), BF16);
+    }
+#pragma unroll
+    for (int hh = 1; hh < 32; hh *= 2)
+#pragma unroll
+      for (int j = 0; j < 32; ++j)
+        if ((j & hh) == 0) {
+          const float u = y[j], v = y[j + hh];
+          y[j] = u + v;
+          y[j + hh] = u - v;
+        }
+    // lower index: own + partner; upper index: partner - own = fma(own, -1, partner)
+    const float s1 = (q & 1) ? -1.0f : 1.0f, s2 = (q & 2) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) y[j] = __builtin_fmaf(y[j], s1, dpp_f<KVQ_DPP_XOR1>(y[j]));
+#pragma unroll
+    for (int j = 0; j < 32; ++j) y[j] = __builtin_fmaf(y[j], s2, dpp_f<KVQ_DPP_XOR2>(y[j]));
+    const float c = bits_to_f32(KVQ_INV_SQRT_D_BITS);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) y[j] = y[j] * c;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      y[2 * k] = widen((uint16_t)(w[k] & 0xFFFF), BF16);
+      y[2 * k + 1] = widen((uint16_t)(w[k] >> 16), BF16);
+    }
+  }
+
+  uint32_t packed[8];
+  uint16_t meta = 0;
+  float res2 = 0.0f, ynorm2 = 0.0f;
+  if (tensor == 0)
+    fast_quantize<KF, KG>(y, desc, packed, meta, res2, ynorm2);
+  else
+    fast_quantize<VF, VG>(y, desc, packed, meta, res2, ynorm2);
+
+  if (desc) {  // outward-rounded norms, as in the generic kernel
+    const float slack = fwht ? 9.5367431640625e-7f : 0.0f;
+    float rn = sqrtf(quad_sum(res2)) * 1.0009765625f + sqrtf(quad_sum(ynorm2)) * slack;
+    float vn = sqrtf(quad_sum(xnorm2)) * 1.0009765625f;
+    if (!valid) {
+      rn = 0.0f;
+      vn = 0.0f;
+    }
+    rn = wave_quad_max(rn);
+    vn = wave_quad_max(vn);
+    if ((t & 63) == 0) {
+      unsigned int* dsc = reinterpret_cast<unsigned int*>(a.desc + (stream_idx * (a.Tmax / TILE) + tile) * 3);
+      atomicMax(dsc + (tensor ? 1 : 0), __float_as_uint(rn));
+      if (tensor) atomicMax(dsc + 2, __float_as_uint(vn));
+    }
+  }
+
+  if (tensor == 0) {
+    if (valid) {
+      constexpr int KB = row_bytes(KF);
+      uint8_t* row = a.k_codes + (stream_idx * a.Tmax + pos) * KB + q * (KB / 4);
+      if constexpr (KF == KVQ_INT8) {
+        uint4* r4 = reinterpret_cast<uint4*>(row);
+        r4[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        r4[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+      } else {
+        *reinterpret_cast<uint4*>(row) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+      }
+      uint16_t* m16 = reinterpret_cast<uint16_t*>(a.k_meta + (stream_idx * a.Tmax + pos) * meta_bytes(KF, KG));
+      if constexpr (KG == 32) m16[q] = meta;
+      else if (q == 0) m16[0] = meta;
+    }
+    return;
+  }
+
+  // V: metadata straight to the tile ([element][64 tokens] fp16), codes via LDS
+  {
+    constexpr int NM = meta_elems(VF, VG);
+    uint16_t* mtile = reinterpret_cast<uint16_t*>(a.v_meta + (stream_idx * (a.Tmax / TILE) + tile) * (size_t)(NM * TILE * 2));
+    if (valid) {
+      if constexpr (VG == 32) mtile[q * TILE + tau] = meta;
+      else if (q == 0) mtile[tau] = meta;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) sm.vt[tau][4 * q + k] = packed[k];
+  __syncthreads();
+  if (t < 128) {
+    const int k = t >> 3, d = t & 7;  // channels 8k..8k+7, tokens 8d..8d+7
+    const int tlo = U.lo - tile * TILE, thi = U.hi - tile * TILE;
+    if (8 * d + 8 > tlo && 8 * d < thi) {
+      uint32_t wv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wv[e] = sm.vt[8 * d + e][k];
+      transpose8x8_nibbles(wv);
+      uint32_t mask = 0xFFFFFFFFu;
+      if (8 * d < tlo || 8 * d + 8 > thi) {
+        mask = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (8 * d + e >= tlo && 8 * d + e < thi) mask |= 0xFu << (4 * e);
+      }
+      uint32_t* vtile = reinterpret_cast<uint32_t*>(a.v_codes + (stream_idx * (a.Tmax / TILE) + tile) * (size_t)(D * chan_bytes(VF)));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t* dst = vtile + (8 * k + j) * (TILE / 8) + d;
+        *dst = mask == 0xFFFFFFFFu ? wv[j] : ((*dst & ~mask) | (wv[j] & mask));
+      }
+    }
+  }
+}
+
+template <int KF, int KG, int VF, int VG, bool BF16>
+__global__ __launch_bounds__(NT) void append_fast_kernel(AppendArgs a, int ntiles) {
+  static_assert(VF == KVQ_INT4, "V codes of the fast path are int4");
+  __shared__ FastSmem sm;
+  const int t = threadIdx.x;
+  const FastUnit U = fast_unit(a, blockIdx.x, ntiles);
+  if (U.lo >= U.hi) return;  // uniform over the workgroup
+  uint32_t w[16];
+  fast_load(U.src, w);
+  // sign masks: bit 15 / bit 31 of pair k of quarter q set where the sign is negative
+  if (a.rotation == KVQ_ROT_SIGN_FWHT && t < 64) {
+    const int qq = t >> 4, k = t & 15;
+    const uint16_t sp = *reinterpret_cast<const uint16_t*>(a.signs + 32 * qq + 2 * k);
+    sm.smask[qq][k] = ((uint32_t)(sp & 0x80u) << 8) | ((uint32_t)(sp & 0x8000u) << 16);
+  }
+  __syncthreads();
+  fast_process<KF, KG, VF, VG, BF16>(a, sm, U, w);
+}
+
 hipError_t launch_append(const AppendArgs& a, int grid_x, hipStream_t s) {
   dim3 grid(grid_x, a.H, 2 * a.B);  // K and V of every sequence in one launch
+  if (a.rotation != KVQ_ROT_DENSE) {
+    const dim3 fgrid(grid_x * a.H * 2 * a.B);
+#define KVQ_FAST(KF, KG, VF, VG)                                                       \
+    if (a.k_fmt == KF && a.k_group == KG && a.v_fmt == VF && a.v_group == VG) {         \
+      if (a.in_bf16)                                                                    \
+        hipLaunchKernelGGL((append_fast_kernel<KF, KG, VF, VG, true>), fgrid, dim3(NT), 0, s, a, grid_x); \
+      else                                                                              \
+        hipLaunchKernelGGL((append_fast_kernel<KF, KG, VF, VG, false>), fgrid, dim3(NT), 0, s, a, grid_x); \
+      return hipGetLastError();                                                         \
+    }
+    KVQ_FAST(KVQ_INT4, 32, KVQ_INT4, 32)
+    KVQ_FAST(KVQ_INT4, 128, KVQ_INT4, 128)
+    KVQ_FAST(KVQ_INT8, 128, KVQ_INT4, 128)
+    KVQ_FAST(KVQ_INT8, 32, KVQ_INT4, 32)
+    KVQ_FAST(KVQ_INT4, 32, KVQ_INT4, 128)
+    KVQ_FAST(KVQ_INT4, 128, KVQ_INT4, 32)
+    KVQ_FAST(KVQ_INT8, 128, KVQ_INT4, 32)
+    KVQ_FAST(KVQ_INT8, 32, KVQ_INT4, 128)
+#undef KVQ_FAST
+  }
   if (a.rotation == KVQ_ROT_DENSE)
     hipLaunchKernelGGL(append_kernel<true>, grid, dim3(NT), 0, s, a);
   else
