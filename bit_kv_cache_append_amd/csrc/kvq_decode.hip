@@ -54,6 +54,7 @@ __device__ __forceinline__ h4 cat(h2 a, h2 b) { return h4{a.x, a.y, b.x, b.y}; }
 template <int VF>
 __device__ __forceinline__ int tok_of(int s, int r) {
   if constexpr (VF == KVQ_INT2) return 16 * (s >> 2) + 2 * (s & 3) + ((r & 1) << 3) + (r >> 1);
+  if constexpr (VF == KVQ_FP4) return 4 * s + r;  // the hardware FP4 pair conversion keeps token order
   return 8 * (s >> 1) + 2 * (s & 1) + ((r & 1) << 2) + (r >> 1);
 }
 // inverse: token tau -> position 4s + r
@@ -91,6 +92,23 @@ struct KFmt<KVQ_INT8> {
   static constexpr int MDW = 2;
   __device__ static __forceinline__ int a_op(const uint32_t* row, int n) { return (int)row[n]; }
   __device__ static __forceinline__ int chan(int n, int m) { return 4 * n + m; }
+  __device__ static __forceinline__ int slot(int c) { return c; }
+};
+template <>
+struct KFmt<KVQ_FP4> {
+  static constexpr int DW = 16;  // 128 E2M1 nibbles
+  static constexpr int MDW = 2;  // 8 E4M3 block scales
+  // fp16 values of channels 4n..4n+3 (E2M1 is exact in fp16)
+  __device__ static __forceinline__ h4 a_op_f16(const uint32_t* row, int n) {
+    const uint32_t w = row[n >> 1];
+    const h2 lo = (n & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2)
+                          : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+    const h2 hi = (n & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3)
+                          : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+    return h4{lo.x, lo.y, hi.x, hi.y};
+  }
+  // the integer-operand interface is not used for FP4 keys (fp16 operands instead)
+  __device__ static __forceinline__ int a_op(const uint32_t*, int) { return 0; }
   __device__ static __forceinline__ int slot(int c) { return c; }
 };
 template <>
@@ -144,6 +162,19 @@ struct VFmt<KVQ_INT2> {
   static constexpr int CDW = 4;
   static constexpr int NMAX = 8;
 };
+template <>
+struct VFmt<KVQ_FP4> {
+  static constexpr int CDW = 8;
+  static constexpr int NMAX = 8;  // 8 blocks of 16 channels, one E4M3 scale each
+};
+
+// E4M3 (non-negative) byte pair -> fp16 pair, exact: the byte shifted into an
+// fp16 is the value / 2^8 (normal and subnormal codes alike), so one packed
+// multiply by 256 finishes it
+__device__ __forceinline__ h2 e4m3x2_to_h2(uint32_t b0, uint32_t b1) {
+  const uint32_t bits = (b0 << 7) | (b1 << 23);
+  return as_h2(bits) * h2{(_Float16)256.0f, (_Float16)256.0f};
+}
 
 // ------------------------------------------------------------------ reductions
 __device__ __forceinline__ float max_same_head(float v) {  // over lanes with equal (lane & 3)
@@ -185,6 +216,7 @@ struct __align__(16) DecodeSmem {
   float qo[4][D];          // original query * scale * log2e (certified recompute)
   uint32_t qh[4][32];      // high int8 halves, MFMA operand order
   uint32_t ql[4][32];      // low int8 halves
+  uint32_t qf4[4][32][4];  // FP4 keys: per head and 4-channel step, fp16 query high then low parts
   float qs[4];             // per-head dequantization of the 16-bit query
   float qsum[4][4];        // per head, per group: sum of 16-bit query codes
   uint16_t vmeta[4][8][16][4];  // per wave: V metadata by (element, slice, r)
@@ -260,6 +292,27 @@ __device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryI
   y0 = y0 * norm * pre;
   y1 = y1 * norm * pre;
   float mx = wave_max(fmaxf(fabsf(y0), fabsf(y1)));
+  if constexpr (KF == KVQ_FP4) {
+    // FP4 keys: the query as two fp16 parts (high + residual) after an exact
+    // power-of-two scaling to |y| < 2^14; products with E2M1 codes are exact
+    int ex = 0;
+    frexpf(mx, &ex);  // mx = f 2^ex, f in [0.5, 1)
+    const float qs = mx > 0.0f ? ldexpf(1.0f, ex - 14) : 1.0f;
+    const float inv = mx > 0.0f ? ldexpf(1.0f, 14 - ex) : 1.0f;
+    uint16_t* qp = reinterpret_cast<uint16_t*>(&sm.qf4[j][0][0]);
+    const float ys[2] = {y0 * inv, y1 * inv};
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int c = 2 * l + e, n = c >> 2, mm = c & 3;
+      const _Float16 hh = (_Float16)ys[e];
+      const _Float16 ll = (_Float16)(ys[e] - (float)hh);
+      qp[n * 8 + mm] = __builtin_bit_cast(uint16_t, hh);
+      qp[n * 8 + 4 + mm] = __builtin_bit_cast(uint16_t, ll);
+    }
+    if (l == 0) sm.qs[j] = qs;
+    __syncthreads();
+    return;
+  }
   const float qs = mx > 0.0f ? mx / 32000.0f : 1.0f;
   const int q0 = (int)rintf(y0 / qs), q1 = (int)rintf(y1 / qs);
   // scatter int8 halves into MFMA operand order
@@ -488,11 +541,11 @@ __device__ __forceinline__ void load_chunk(const DecodeArgs& a, size_t stream, i
     R.vw[4 * i] = u.x; R.vw[4 * i + 1] = u.y; R.vw[4 * i + 2] = u.z; R.vw[4 * i + 3] = u.w;
   }
   constexpr int NM = meta_elems(VF, VG);
-  const uint8_t* vm = a.v_meta + (stream * a.nt + ch) * (size_t)(NM * TILE * 2);
+  const uint8_t* vm = a.v_meta + (stream * a.nt + ch) * (size_t)(NM * TILE * meta_esize(VF));
   if constexpr (VF == KVQ_INT2) {  // 8 elements x 64 tokens: 16 bytes per lane
     const uint4 u = reinterpret_cast<const uint4*>(vm)[lane];
     R.vmeta[0] = u.x; R.vmeta[1] = u.y; R.vmeta[2] = u.z; R.vmeta[3] = u.w;
-  } else if constexpr (NM == 4) {  // 4 groups x 64 tokens: 8 bytes per lane
+  } else if constexpr (NM == 4 || VF == KVQ_FP4) {  // 8 bytes per lane
     const uint2 u = reinterpret_cast<const uint2*>(vm)[lane];
     R.vmeta[0] = u.x; R.vmeta[1] = u.y;
   } else {  // one scale per token
@@ -505,7 +558,16 @@ __device__ __forceinline__ void load_chunk(const DecodeArgs& a, size_t stream, i
 template <int VF, int VG>
 __device__ __forceinline__ void stage_vmeta(uint16_t* L, int lane, const uint32_t* vmeta) {
   constexpr int NM = meta_elems(VF, VG);
-  if constexpr (VF == KVQ_INT2) {
+  if constexpr (VF == KVQ_FP4) {  // block mm = lane / 8, tokens 8u..8u+7 (natural order), E4M3 -> fp16
+    const int mm = lane >> 3, u = lane & 7;
+    uint4 o;
+    const uint32_t w0 = vmeta[0], w1 = vmeta[1];
+    o.x = as_u(e4m3x2_to_h2(w0 & 0xFF, (w0 >> 8) & 0xFF));
+    o.y = as_u(e4m3x2_to_h2((w0 >> 16) & 0xFF, w0 >> 24));
+    o.z = as_u(e4m3x2_to_h2(w1 & 0xFF, (w1 >> 8) & 0xFF));
+    o.w = as_u(e4m3x2_to_h2((w1 >> 16) & 0xFF, w1 >> 24));
+    *reinterpret_cast<uint4*>(L + mm * 64 + 8 * u) = o;
+  } else if constexpr (VF == KVQ_INT2) {
     const int mm = lane >> 3, u = lane & 7;  // tokens 8u..8u+7 of element mm
     const int base = (mm * 16 + 4 * (u >> 1)) * 4 + (u & 1);
 #pragma unroll
@@ -553,7 +615,8 @@ __global__ __launch_bounds__(NT, 2) void decode_split(DecodeArgs a) {
   const int tok_a = tok_of<VF>(s_a, r_a);
   const size_t stream = (size_t)b * a.H + hkv;
   constexpr int CDW = VFmt<VF>::CDW;
-  const int vgrp = (VG == 128) ? 0 : (lane >> 4);  // V group of channels 2*lane, 2*lane+1
+  // V scale element of channels 2*lane, 2*lane+1: 32-channel group, one per token, or 16-channel block
+  const int vgrp = (VF == KVQ_FP4) ? (lane >> 3) : (VG == 128) ? 0 : (lane >> 4);
   uint16_t* vml = &sm.vmeta[wv][0][0][0];
 
   // The first chunk's loads are in flight during the query prologue.  Every
@@ -569,10 +632,12 @@ __global__ __launch_bounds__(NT, 2) void decode_split(DecodeArgs a) {
   query_prologue<KF>(a, sm, qin, nh, KG);
 
   uint32_t qh[32], ql[32];
+  if constexpr (KF != KVQ_FP4) {
 #pragma unroll
-  for (int n = 0; n < 32; ++n) {
-    qh[n] = sm.qh[j][n];
-    ql[n] = sm.ql[j][n];
+    for (int n = 0; n < 32; ++n) {
+      qh[n] = sm.qh[j][n];
+      ql[n] = sm.ql[j][n];
+    }
   }
   const float qs = sm.qs[j];
   float qsum[4];
@@ -592,63 +657,96 @@ __global__ __launch_bounds__(NT, 2) void decode_split(DecodeArgs a) {
   auto quant_chunk = [&](const ChunkRegs<KF, VF>& R, int ch, float ev_c) {
     const int tok0 = ch * TILE;
     stage_vmeta<VF, VG>(vml, lane, R.vmeta);
-    // ---- QK^T: exact integer dot products.  Four independent accumulator
-    // chains per query half (chain c covers channels 32c..32c+31, i.e. one
-    // 32-channel group); each K operand is unpacked once and feeds both halves.
-    constexpr int NG = (KG == 128) ? 1 : 4;
-    constexpr int NC = 4, PER = 32 / NC;
-    i4 ah[NC], al[NC];
+    float l[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (KF == KVQ_FP4) {
+      // ---- QK^T with E2M1 keys in fp16 (exact) against the two fp16 query
+      // parts, one fp32 accumulator per 16-channel block (8 chains), then the
+      // E4M3 block scales of tokens 4s + r (quad broadcast)
+      f4 ab[8];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      // the offset-binary correction -8 * sum(q16) of the chain's group rides in the low half
-      int corr = 0;
-      if constexpr (KF == KVQ_INT4) corr = (NG == 1) ? (c == 0 ? -8 * (int)qsum[0] : 0) : -8 * (int)qsum[c];
-      ah[c] = i4{0, 0, 0, 0};
-      al[c] = i4{corr, corr, corr, corr};
-    }
+      for (int bk = 0; bk < 8; ++bk) ab[bk] = f4{0, 0, 0, 0};
+      const uint4* qrow = reinterpret_cast<const uint4*>(&sm.qf4[j][0][0]);
 #pragma unroll
-    for (int n = 0; n < PER; ++n)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const int av = KFmt<KF>::a_op(R.krow, c * PER + n);
-        ah[c] = __builtin_amdgcn_mfma_i32_4x4x4i8(av, (int)qh[c * PER + n], ah[c], 0, 0, 0);
-        al[c] = __builtin_amdgcn_mfma_i32_4x4x4i8(av, (int)ql[c * PER + n], al[c], 0, 0, 0);
-      }
-    i4 acc[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g)
+        for (int bk = 0; bk < 8; ++bk) {
+          const int n = 4 * bk + i;
+          const uint4 qv = qrow[n];
+          const h4 av = KFmt<KVQ_FP4>::a_op_f16(R.krow, n);
+          ab[bk] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, cat(as_h2(qv.x), as_h2(qv.y)), ab[bk], 0, 0, 0);
+          ab[bk] = __builtin_amdgcn_mfma_f32_4x4x4f16(av, cat(as_h2(qv.z), as_h2(qv.w)), ab[bk], 0, 0, 0);
+        }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if constexpr (NG == 1) {
-          acc[g][r] = 0;
+        uint32_t sw[2];
 #pragma unroll
-          for (int c = 0; c < NC; ++c) acc[g][r] += ah[c][r] * 256 + al[c][r];
-        } else {
-          acc[g][r] = ah[g][r] * 256 + al[g][r];
+        for (int w = 0; w < 2; ++w)
+          sw[w] = r == 0 ? quad_bcast_u<0>(R.kmeta[w]) : r == 1 ? quad_bcast_u<1>(R.kmeta[w])
+                : r == 2 ? quad_bcast_u<2>(R.kmeta[w]) : quad_bcast_u<3>(R.kmeta[w]);
+#pragma unroll
+        for (int bk = 0; bk < 8; ++bk) {
+          const uint32_t sb = (sw[bk >> 2] >> (8 * (bk & 3))) & 0xFFu;
+          l[r] = fmaf(ab[bk][r], f16_bits_to_f32((uint16_t)(sb << 7)) * 256.0f, l[r]);
         }
       }
-    // ---- group scales of tokens pi(s, r), held by lanes 4s + r (A role): quad broadcast
-    float l[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      uint32_t sw[2], zw[2] = {0u, 0u};
-#pragma unroll
-      for (int w = 0; w < (NG == 1 ? 1 : 2); ++w) {
-        sw[w] = r == 0 ? quad_bcast_u<0>(R.kmeta[w]) : r == 1 ? quad_bcast_u<1>(R.kmeta[w])
-              : r == 2 ? quad_bcast_u<2>(R.kmeta[w]) : quad_bcast_u<3>(R.kmeta[w]);
-        if constexpr (KF == KVQ_INT2)
-          zw[w] = r == 0 ? quad_bcast_u<0>(R.kmeta[2 + w]) : r == 1 ? quad_bcast_u<1>(R.kmeta[2 + w])
-                : r == 2 ? quad_bcast_u<2>(R.kmeta[2 + w]) : quad_bcast_u<3>(R.kmeta[2 + w]);
+    } else {
+      // ---- QK^T: exact integer dot products.  Four independent accumulator
+      // chains per query half (chain c covers channels 32c..32c+31, i.e. one
+      // 32-channel group); each K operand is unpacked once and feeds both halves.
+      constexpr int NG = (KG == 128) ? 1 : 4;
+      constexpr int NC = 4, PER = 32 / NC;
+      i4 ah[NC], al[NC];
+  #pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        // the offset-binary correction -8 * sum(q16) of the chain's group rides in the low half
+        int corr = 0;
+        if constexpr (KF == KVQ_INT4) corr = (NG == 1) ? (c == 0 ? -8 * (int)qsum[0] : 0) : -8 * (int)qsum[c];
+        ah[c] = i4{0, 0, 0, 0};
+        al[c] = i4{corr, corr, corr, corr};
       }
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        const uint16_t sb = (uint16_t)(sw[g >> 1] >> (16 * (g & 1)));
-        float v = (float)acc[g][r] * f16_bits_to_f32(sb);
-        if constexpr (KF == KVQ_INT2) {
-          const uint16_t zb = (uint16_t)(zw[g >> 1] >> (16 * (g & 1)));
-          v = fmaf(f16_bits_to_f32(zb), qsum[g], v);
+  #pragma unroll
+      for (int n = 0; n < PER; ++n)
+  #pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int av = KFmt<KF>::a_op(R.krow, c * PER + n);
+          ah[c] = __builtin_amdgcn_mfma_i32_4x4x4i8(av, (int)qh[c * PER + n], ah[c], 0, 0, 0);
+          al[c] = __builtin_amdgcn_mfma_i32_4x4x4i8(av, (int)ql[c * PER + n], al[c], 0, 0, 0);
         }
-        l[r] += v;
+      i4 acc[NG];
+  #pragma unroll
+      for (int g = 0; g < NG; ++g)
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (NG == 1) {
+            acc[g][r] = 0;
+  #pragma unroll
+            for (int c = 0; c < NC; ++c) acc[g][r] += ah[c][r] * 256 + al[c][r];
+          } else {
+            acc[g][r] = ah[g][r] * 256 + al[g][r];
+          }
+        }
+      // ---- group scales of tokens pi(s, r), held by lanes 4s + r (A role): quad broadcast
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        uint32_t sw[2], zw[2] = {0u, 0u};
+  #pragma unroll
+        for (int w = 0; w < (NG == 1 ? 1 : 2); ++w) {
+          sw[w] = r == 0 ? quad_bcast_u<0>(R.kmeta[w]) : r == 1 ? quad_bcast_u<1>(R.kmeta[w])
+                : r == 2 ? quad_bcast_u<2>(R.kmeta[w]) : quad_bcast_u<3>(R.kmeta[w]);
+          if constexpr (KF == KVQ_INT2)
+            zw[w] = r == 0 ? quad_bcast_u<0>(R.kmeta[2 + w]) : r == 1 ? quad_bcast_u<1>(R.kmeta[2 + w])
+                  : r == 2 ? quad_bcast_u<2>(R.kmeta[2 + w]) : quad_bcast_u<3>(R.kmeta[2 + w]);
+        }
+  #pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          const uint16_t sb = (uint16_t)(sw[g >> 1] >> (16 * (g & 1)));
+          float v = (float)acc[g][r] * f16_bits_to_f32(sb);
+          if constexpr (KF == KVQ_INT2) {
+            const uint16_t zb = (uint16_t)(zw[g >> 1] >> (16 * (g & 1)));
+            v = fmaf(f16_bits_to_f32(zb), qsum[g], v);
+          }
+          l[r] += v;
+        }
       }
     }
 #pragma unroll
@@ -682,7 +780,24 @@ __global__ __launch_bounds__(NT, 2) void decode_split(DecodeArgs a) {
     const uint32_t P0 = as_u(h2{(_Float16)p[0], (_Float16)p[1]});
     const uint32_t P1 = as_u(h2{(_Float16)p[2], (_Float16)p[3]});
     const uint2* sc2 = reinterpret_cast<const uint2*>(vml) + vgrp * 16;
-    if constexpr (VF == KVQ_INT4) {
+    if constexpr (VF == KVQ_FP4) {
+      // tokens 4s..4s+3 of step s are the byte pairs 2(s&1), 2(s&1)+1 of word s/2
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const uint32_t w0 = R.vw[s >> 1], w1 = R.vw[CDW + (s >> 1)];
+        const h2 c00 = (s & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 2) : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 0);
+        const h2 c01 = (s & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 3) : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 1);
+        const h2 c10 = (s & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 2) : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 0);
+        const h2 c11 = (s & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 3) : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 1);
+        const int src = (4 * s + j) << 2;
+        const uint32_t A0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)P0);
+        const uint32_t A1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)P1);
+        const uint2 sc = sc2[s];
+        const h4 A = cat(as_h2(A0) * as_h2(sc.x), as_h2(A1) * as_h2(sc.y));
+        o[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, cat(c00, c01), o[0], 0, 0, 0);
+        o[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, cat(c10, c11), o[1], 0, 0, 0);
+      }
+    } else if constexpr (VF == KVQ_INT4) {
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
         h2 c0[4], c1[4];
@@ -995,6 +1110,7 @@ hipError_t launch_decode(const DecodeArgs& a, int k_fmt, int v_fmt, bool dense, 
   KVQ_LAUNCH(KVQ_INT8, 32, KVQ_INT4, 32)
   KVQ_LAUNCH(KVQ_INT8, 32, KVQ_INT4, 128)
   KVQ_LAUNCH(KVQ_INT2, 32, KVQ_INT2, 32)
+  KVQ_LAUNCH(KVQ_FP4, 16, KVQ_FP4, 16)
 #undef KVQ_LAUNCH
   return hipErrorNotSupported;
 }

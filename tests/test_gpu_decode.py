@@ -38,6 +38,7 @@ def _filled(c, seq):
 def _check_rows(got, ref, rows, tag):
     err = attention.row_rel_err(got, ref)
     worst = max(err[b, hq] for b, hq in rows)
+    print(f"[decode] {tag}: max row rel err {worst:.3e}", flush=True)
     assert worst <= TOL, f"{tag}: max row rel err {worst:.3e}"
     return worst
 
@@ -50,6 +51,8 @@ CASES = {
     "c3-int8k-int4v": (synth.config(3, B=2, T=2048), [2048, 1500]),
     "c4-int2-dense": (synth.config(4, B=2, T=1024), [1024, 777]),
     "g1-and-g2": (synth.config(2, B=2, Hq=4, Hkv=2, T=512), [512, 333]),
+    "c5-fp4-search-bf16": (synth.config(5, B=2, T=1024), [1024, 701]),
+    "fp4-absmax-f16-ragged": (synth.config(5, B=3, Hq=8, Hkv=2, T=512, dtype="f16", scale_mode="absmax"), [512, 129, 1]),
 }
 
 
