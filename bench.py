@@ -49,7 +49,25 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workers", type=int, default=min(16, os.cpu_count() or 1))
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="end with one plain 256 MiB device copy (reference for hardware byte counters)")
     return ap.parse_args()
+
+
+def kernel_traffic(roofline_kernel_src):
+    """HBM bytes per decode call from the committed counter summary, if it was taken on this kernel source."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    prof = os.path.join(here, "profiles", "decode_int4_c2_traffic.json")
+    src = os.path.join(here, roofline_kernel_src)
+    try:
+        rec = json.load(open(prof))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_call")
 
 
 def cpu_baseline(c, sample_b):
@@ -97,6 +115,10 @@ def main():
     import synth
 
     kvq.lib()  # fail loudly if the HIP library is missing
+
+    def progress(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
     dev = torch.device("cuda:0")
     c = synth.config(2)
     B, Hq, H, T, P = c["B"], c["Hq"], c["Hkv"], c["T"], c["prefill"]
@@ -105,6 +127,7 @@ def main():
     v_all = synth.kv_all(c, 1, 0, T, workers=args.workers)
     q_np = synth.queries(c)
     t_gen = time.perf_counter() - t_gen
+    progress(f"inputs generated in {t_gen:.1f} s")
     k_dev = kvq.to_device_bits(k_all)
     v_dev = kvq.to_device_bits(v_all)
     del k_all, v_all
@@ -133,6 +156,7 @@ def main():
     flush_buf = torch.ones(1 << 27, dtype=torch.int64, device=dev)  # 1 GiB
     sink = torch.zeros((), dtype=torch.int64, device=dev)
     torch.cuda.synchronize()
+    progress("caches filled")
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
@@ -167,6 +191,7 @@ def main():
     t0 = time.perf_counter()
     step_ms = batch_time(lambda i: step(args.warmup + i), args.steps)
     wall = time.perf_counter() - t0
+    progress(f"{args.steps} steps timed")
     # each kernel sequence on its own over the rotating buffers
     n_each = max(args.steps, 4 * NROT)
     batch_time(do_decode, NROT)
@@ -175,6 +200,7 @@ def main():
     app_ms = batch_time(do_append, n_each)
     batch_time(do_dense, 2)
     f16_ms = batch_time(do_dense, n_each)
+    progress("per-kernel batches timed")
     # isolated calls: 1 GiB read flush, events around each call
     iso = []
     for i in range(args.warmup + args.steps):
@@ -240,6 +266,13 @@ def main():
         "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
         "input_gen_s": round(t_gen, 2),
     }
+    result["roofline"]["traffic"] = kernel_traffic("bit_kv_cache_append_amd/csrc/kvq_decode.hip")
+    if args.copy_calibration:
+        src = torch.full((256 << 20,), 3, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(c, sample_b=8)
     print(json.dumps(result))
