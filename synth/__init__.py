@@ -166,14 +166,18 @@ def kv_slice(c, tensor, b, h, t0, n):
     return to_bits(out, c["dtype"])
 
 
-def kv_all(c, tensor, t0, n, workers=1):
-    """[B, Hkv, n, 128] uint16 for tokens [t0, t0+n) of every stream."""
+def kv_all(c, tensor, t0, n, workers=1, start_method="fork"):
+    """[B, Hkv, n, 128] uint16 for tokens [t0, t0+n) of every stream.
+
+    workers > 1 draws the streams in a process pool; use start_method="spawn" in a
+    process that has already initialised the GPU (the workers only run NumPy).
+    """
     B, H = c["B"], c["Hkv"]
     out = np.empty((B, H, n, D), dtype=np.uint16)
     jobs = [(b, h) for b in range(B) for h in range(H)]
     if workers > 1 and len(jobs) > 1:
         import multiprocessing as mp
-        ctx = mp.get_context("fork")
+        ctx = mp.get_context(start_method)
         with ctx.Pool(min(workers, len(jobs))) as pool:
             res = pool.starmap(kv_slice, [(c, tensor, b, h, t0, n) for b, h in jobs])
         for (b, h), r in zip(jobs, res):
