@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--workers", type=int, default=min(16, os.cpu_count() or 1))
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with one plain 256 MiB device copy (reference for hardware byte counters)")
+    ap.add_argument("--workload", type=int, default=2, choices=(2, 3, 4, 5),
+                    help="2 (default): the GQA int4 line; 3/4/5: the certified, int2 and FP4 workloads")
     return ap.parse_args()
 
 
@@ -104,12 +106,198 @@ def cpu_baseline(c, sample_b):
     }
 
 
+def bench_workload(cfg_id, args):
+    """Decode and append throughput of workload 3 (certified int8/int4), 4 (int2, dense rotation)
+    or 5 (FP4 with scale search) at full shape, same timing method as the default line.
+
+    Inputs are drawn on the GPU from a seeded generator with the workload's law (the host
+    generator would take minutes at these sizes; the values only have to have the right
+    distribution and structure for timing).  The full context is filled by appending one
+    4096-token piece repeatedly; the timed append is a 4096-token prefill at the end of the
+    context, as in the default line.
+    """
+    import torch
+    import bit_kv_cache_append_amd as kvq
+    import synth
+
+    kvq.lib()
+    dev = torch.device("cuda:0")
+    c = synth.config(cfg_id)
+    B, Hq, H, T, P = c["B"], c["Hq"], c["Hkv"], c["T"], c["prefill"]
+    nrot = 4
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234 + cfg_id)
+
+    def progress(msg):
+        print(f"[bench w{cfg_id}] {msg}", file=sys.stderr, flush=True)
+
+    def draw(tensor):
+        shape = (B, H, P, 128)
+        if c["data"] == "certified":
+            x = torch.randn(shape, generator=g, device=dev) * (c["k_sigma"] if tensor == 0 else c["v_sigma"])
+            # one planted token (x10) in each of two seeded blocks per (b, head) of the piece
+            for _ in range(2):
+                t = torch.randint(0, P, (B, H), generator=g, device=dev)
+                idx = t[..., None, None].expand(B, H, 1, 128)
+                x.scatter_(2, idx, x.gather(2, idx) * c["plant_factor"])
+            return x.half().view(torch.int16)
+        if c["data"] == "anisotropic":
+            z = torch.randn(shape, generator=g, device=dev)
+            d = torch.arange(1, 129, device=dev, dtype=torch.float32).rsqrt()
+            u, _ = torch.linalg.qr(torch.randn((H, 128, 128), generator=g, device=dev))
+            x = torch.einsum("bhtc,hdc->bhtd", z * d, u.contiguous())
+            return x.half().view(torch.int16)
+        # Student-t(nu) = N(0,1) / sqrt(chi2(nu) / nu), chi2(nu) = sum of nu squared normals (nu = 4)
+        nu = int(c["nu"])
+        z = torch.randn(shape, generator=g, device=dev)
+        chi = sum(torch.randn(shape, generator=g, device=dev) ** 2 for _ in range(nu))
+        x = z / torch.sqrt(chi / nu)
+        return x.bfloat16().view(torch.int16)
+
+    s_dev = torch.from_numpy(synth.signs(c).copy()).to(dev)
+    r_dev = kvq.to_device_bits(synth.dense_rotation_f16(c)) if c["rotation"] == "dense" else None
+    p = kvq.params_from_config(c)
+    caches = [kvq.Cache(p, signs=s_dev, rot_f16=r_dev) for _ in range(nrot)]
+    if c["k_fmt"] == "int2" or c["v_fmt"] == "int2":
+        ck = np.stack([synth.calibration(c, 0, h) for h in range(H)])
+        cv = np.stack([synth.calibration(c, 1, h) for h in range(H)])
+        tk, tv = kvq.calibrate_clip(p, caches[0], kvq.to_device_bits(ck), kvq.to_device_bits(cv),
+                                    ratio=c["clip_ratio"])
+        for cc in caches:
+            cc.clip_k, cc.clip_v = tk, tv
+    kin = [draw(0) for _ in range(nrot)]
+    vin = [draw(1) for _ in range(nrot)]
+    for cc in caches:
+        for t0 in range(0, T, P):
+            kvq.append(p, cc, kin[(t0 // P) % nrot], vin[(t0 // P) % nrot], [t0] * B)
+    torch.cuda.synchronize()
+    progress("caches filled")
+    q = torch.randn((B, Hq, 128), generator=g, device=dev)
+    q = (q.bfloat16() if c["dtype"] == "bf16" else q.half()).view(torch.int16)
+    seq = [T] * B
+    ws = kvq.workspace(p)
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+    cert = torch.empty((B, Hq), dtype=torch.float32, device=dev) if c["keep"] else None
+    nt = T // 64
+    bnd = torch.empty((B, H, nt), dtype=torch.float32, device=dev)
+    flg = torch.empty((B, H, nt), dtype=torch.uint8, device=dev)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def batch_time(fn, n):
+        e0, e1 = ev(), ev()
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    def do_decode(i):
+        cc = caches[i % nrot]
+        if c["keep"]:
+            kvq.error_bound(p, cc, q, seq, c["tau"], bound=bnd, flags=flg)
+            kvq.decode_attn(p, cc, q, seq, flags=flg, certificate=True, ws=ws, out=out, cert=cert)
+        else:
+            kvq.decode_attn(p, cc, q, seq, ws=ws, out=out)
+
+    def do_append(i):
+        kvq.append(p, caches[i % nrot], kin[i % nrot], vin[i % nrot], [T - P] * B)
+
+    n_each = max(args.steps, 4 * nrot)
+    for i in range(args.warmup):
+        do_append(i)
+        do_decode(i + 2)
+    torch.cuda.synchronize()
+    step_ms = batch_time(lambda i: (do_append(i), do_decode(i + 2)), args.steps)
+    progress(f"{args.steps} steps timed")
+    batch_time(do_decode, nrot)
+    dec_ms = batch_time(do_decode, n_each)
+    batch_time(do_append, nrot)
+    app_ms = batch_time(do_append, n_each)
+    # the fp16/bf16 same-shape baseline: the certified workload's own originals, else fresh tensors
+    if c["keep"]:
+        dense = [(caches[i].bufs["k_orig"], caches[i].bufs["v_orig"]) for i in range(2)]
+    else:
+        dense = []
+        for i in range(2):
+            kd = torch.empty((B, H, T, 128), dtype=torch.int16, device=dev)
+            vd = torch.empty_like(kd)
+            for t0 in range(0, T, P):
+                kd[:, :, t0:t0 + P] = kin[(t0 // P + i) % nrot]
+                vd[:, :, t0:t0 + P] = vin[(t0 // P + i) % nrot]
+            dense.append((kd, vd))
+    dws = kvq.workspace(p)
+    dout = torch.empty_like(out)
+    batch_time(lambda i: kvq.decode_attn_dense(p, dense[i % 2][0], dense[i % 2][1], q, seq, ws=dws, out=dout), 2)
+    f16_ms = batch_time(lambda i: kvq.decode_attn_dense(p, dense[i % 2][0], dense[i % 2][1], q, seq, ws=dws,
+                                                        out=dout), n_each)
+    progress("batches timed")
+    sizes = kvq.buffer_bytes(p)
+    packed = sizes["k_codes"] + sizes["k_meta"] + sizes["v_codes"] + sizes["v_meta"]
+    io = B * Hq * 128 * 2 + B * Hq * 128 * 4
+    extra = ""
+    if c["keep"]:
+        do_decode(0)
+        torch.cuda.synchronize()
+        nflag = int(flg.sum().item())
+        kb_tok = 128 + 2
+        vb_tok = 64 + 2
+        packed += sizes["blk_desc"] - nflag * 64 * (kb_tok + vb_tok) + nflag * 64 * 512
+        io += B * Hq * 4
+        extra = f"; {nflag} of {flg.numel()} blocks flagged ({100.0 * nflag / flg.numel():.2f}%), recomputed from fp16"
+    dense_bytes = 2 * B * H * T * 128 * 2
+    vecs = B * H * P * 2
+    in_bytes = vecs * 256
+    out_bytes = vecs // 2 * (sizes["k_codes"] + sizes["k_meta"] + sizes["v_codes"] + sizes["v_meta"]) // (B * H * T)
+    if c["keep"]:
+        out_bytes += vecs * 256  # fp16 copies
+    app_bytes = in_bytes + out_bytes
+    dec_s, app_s, f16_s = dec_ms / 1e3, app_ms / 1e3, f16_ms / 1e3
+    achieved = (packed + io) / dec_s / 1e9
+    fmt = f"{c['k_fmt']} K / {c['v_fmt']} V"
+    result = {
+        "metric": METRIC,
+        "value": round(packed / dec_s / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"int8": "int8", "int4": "int4", "int2": "int2", "fp4": "fp4"}[c["k_fmt"]],
+        "data": f"synthetic, drawn on the GPU from a seeded generator ({c['data']}){extra}",
+        "config": {"workload": c["name"], "B": B, "Hq": Hq, "Hkv": H, "head_dim": 128, "context": T,
+                   "prefill_tokens": P, "formats": fmt, "rotation": c["rotation"], "input": c["dtype"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_split + combine_kernel" + (" + bound_kernel" if c["keep"] else ""),
+                     "bytes_per_call": packed + io},
+        "decode_us": round(dec_s * 1e6, 2),
+        "decode_grid": [kvq.decode_splits(p, seq), H * ((Hq // H + 3) // 4), B],
+        "fp16_decode_us": round(f16_s * 1e6, 2),
+        "fp16_decode_pct_hbm_peak": round(100 * dense_bytes / f16_s / 1e9 / HBM_PEAK_GBS, 2),
+        "speedup_vs_fp16": round(f16_s / dec_s, 3),
+        "append_us": round(app_s * 1e6, 2),
+        "append_mvec_s": round(vecs / app_s / 1e6, 1),
+        "append_gbs": round(app_bytes / app_s / 1e9, 1),
+        "append_pct_hbm_peak": round(100 * app_bytes / app_s / 1e9 / HBM_PEAK_GBS, 2),
+    }
+    print(json.dumps(result))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one MI355X; --gpus {args.gpus} is not supported (this build runs on one GPU).",
               file=sys.stderr)
         sys.exit(2)
+    if args.workload != 2:
+        bench_workload(args.workload, args)
+        return
     import torch
     import bit_kv_cache_append_amd as kvq
     import synth

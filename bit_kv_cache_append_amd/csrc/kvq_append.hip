@@ -21,6 +21,7 @@
 
 #include "kvq_common.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace kvq {
@@ -318,6 +319,61 @@ struct __align__(16) DenseSmem {
   float ys[TILE][D + 4];  // rotated vectors
 };
 
+
+// Rows lane and lane + 64 of the dense rotation for the 16 vectors of wave wv, NV
+// vectors at a time (2 NV independent fma chains per lane)
+template <bool BF16>
+__device__ __forceinline__ void dense_rows(const uint16_t (*xs)[D], float (*ys)[D + 4], const uint32_t r0[64],
+                                           const uint32_t r1[64], int wv, int lane, int tile0, int lo, int hi) {
+  typedef _Float16 hh2 __attribute__((ext_vector_type(2)));
+  constexpr int NV = 1;
+  for (int v0 = 0; v0 < 16; v0 += NV) {
+    const int vec0 = wv * 16 + v0;
+    if (tile0 + vec0 + NV <= lo || tile0 + vec0 >= hi) continue;  // uniform over the wave
+    float acc0[NV], acc1[NV];
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      acc0[e] = 0.0f;
+      acc1[e] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      uint32_t xw[NV][4];
+#pragma unroll
+      for (int e = 0; e < NV; ++e) {
+        const uint4 u = reinterpret_cast<const uint4*>(&xs[vec0 + e][0])[i];
+        xw[e][0] = u.x; xw[e][1] = u.y; xw[e][2] = u.z; xw[e][3] = u.w;
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int kp = 4 * i + jj;  // channels 2kp, 2kp+1
+        const hh2 ra = __builtin_bit_cast(hh2, r0[kp]), rb = __builtin_bit_cast(hh2, r1[kp]);
+#pragma unroll
+        for (int e = 0; e < NV; ++e) {
+          float x0, x1;
+          if constexpr (BF16) {
+            x0 = __uint_as_float(xw[e][jj] << 16);
+            x1 = __uint_as_float(xw[e][jj] & 0xFFFF0000u);
+          } else {
+            const hh2 xv = __builtin_bit_cast(hh2, xw[e][jj]);
+            x0 = (float)xv.x;
+            x1 = (float)xv.y;
+          }
+          acc0[e] = __builtin_fmaf((float)ra.x, x0, acc0[e]);
+          acc1[e] = __builtin_fmaf((float)rb.x, x0, acc1[e]);
+          acc0[e] = __builtin_fmaf((float)ra.y, x1, acc0[e]);
+          acc1[e] = __builtin_fmaf((float)rb.y, x1, acc1[e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      ys[vec0 + e][lane] = acc0[e];
+      ys[vec0 + e][lane + 64] = acc1[e];
+    }
+  }
+}
+
 }  // namespace
 
 template <bool DENSE>
@@ -377,30 +433,12 @@ __global__ __launch_bounds__(NT) void append_kernel(AppendArgs a) {
         r1[4 * i] = w.x; r1[4 * i + 1] = w.y; r1[4 * i + 2] = w.z; r1[4 * i + 3] = w.w;
       }
     }
-    for (int vv = 0; vv < 16; ++vv) {
-      const int vec = wv * 16 + vv;
-      const int vpos = tile * TILE + vec;
-      if (vpos < lo || vpos >= hi) continue;  // uniform over the wave
-      float acc0 = 0.0f, acc1 = 0.0f;
-      const uint4* xr = reinterpret_cast<const uint4*>(&sm.xs[vec][0]);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        uint4 u = xr[i];
-        uint32_t xw[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int k = 8 * i + 2 * jj;
-          float x0 = widen((uint16_t)(xw[jj] & 0xFFFF), bf16), x1 = widen((uint16_t)(xw[jj] >> 16), bf16);
-          uint32_t p0 = r0[k / 2], p1 = r1[k / 2];
-          acc0 = __builtin_fmaf(f16_bits_to_f32((uint16_t)(p0 & 0xFFFF)), x0, acc0);
-          acc0 = __builtin_fmaf(f16_bits_to_f32((uint16_t)(p0 >> 16)), x1, acc0);
-          acc1 = __builtin_fmaf(f16_bits_to_f32((uint16_t)(p1 & 0xFFFF)), x0, acc1);
-          acc1 = __builtin_fmaf(f16_bits_to_f32((uint16_t)(p1 >> 16)), x1, acc1);
-        }
-      }
-      sm.ys[vec][lane] = acc0;
-      sm.ys[vec][lane + 64] = acc1;
-    }
+    // y_j = fma chain over k = 0..127 in order (the oracle's chain); with fp16 inputs
+    // both operands go straight into a mixed-precision fma (exact conversions)
+    if (bf16)
+      dense_rows<true>(sm.xs, sm.ys, r0, r1, wv, lane, tile * TILE, lo, hi);
+    else
+      dense_rows<false>(sm.xs, sm.ys, r0, r1, wv, lane, tile * TILE, lo, hi);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < 32; ++j) y[j] = sm.ys[tau][32 * q + j];
@@ -852,6 +890,259 @@ __global__ __launch_bounds__(NT) void append_fast_kernel(AppendArgs a, int ntile
   fast_process<KF, KG, VF, VG, BF16>(a, sm, U, w);
 }
 
+// ================================================================ dense rotation on matrix cores
+// The dense rotation y_j = chain over k = 0..127 of fma(R[j][k], x_k, acc) runs
+// as 128 rank-1 steps of the fp32 MFMA with K = 1: each step adds one exact-input
+// product to every accumulator with a single rounding, which is the same fused
+// multiply-add, in the same k order, as the scalar chain.  A workgroup rotates a
+// 64-token tile: wave w owns output channels [32w, 32w + 32) (the quantization
+// group w), the rotation rows it needs stay in registers for the whole
+// (persistent) launch, and the tile's inputs are read from LDS.  The product
+// lands in the MFMA's own layout: lane l holds tokens l % 32 and 32 + l % 32
+// for 16 channels of the group, so a group's min/max needs one exchange between
+// lanes l and l ^ 32; K rows are merged from the two halves with byte permutes
+// and V tiles come out of a 16 x 16 transpose of 2-bit fields inside each row of
+// 16 lanes.  Asymmetric int2 with groups of 32 (the 2-bit workload); other
+// formats with the dense rotation use the generic kernel.
+namespace {
+
+typedef float f32x32 __attribute__((ext_vector_type(32)));
+
+struct __align__(16) DenseMfmaSmem {
+  uint32_t xs[TILE][68];  // input vectors as fp16/bf16 pairs; rows padded to 272 bytes
+};
+
+template <bool BF16>
+__device__ __forceinline__ float half_lo(uint32_t w) {
+  if constexpr (BF16) return __uint_as_float(w << 16);
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+template <bool BF16>
+__device__ __forceinline__ float half_hi(uint32_t w) {
+  if constexpr (BF16) return __uint_as_float(w & 0xFFFF0000u);
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// channel (within the group) of accumulator v, v = 0..15, for lanes of half hf
+__device__ __forceinline__ int mfma_row(int v, int hf) { return 8 * (v >> 2) + 4 * hf + (v & 3); }
+
+// RNE(y / sf) clamped to [0, 3], as 2^23 + code (see quot_magic)
+__device__ __forceinline__ float quot_magic_u2(float y, float sf, float r) {
+  const float t = y * r;
+  const float e = __builtin_fmaf(-t, sf, y);
+  const float tq = __builtin_fmaf(e, r, t);
+  return __builtin_amdgcn_fmed3f(tq + MAGIC, MAGIC, MAGIC + 3.0f);
+}
+
+// 16 codes held as 2^23 + c (c < 4) -> c_v at bits 2v
+__device__ __forceinline__ uint32_t pack16_u2(const float m[16]) {
+  uint32_t p2[8], p4[4], p8[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p2[i] = (__float_as_uint(m[2 * i + 1]) << 2) | __float_as_uint(m[2 * i]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p4[i] = (p2[2 * i + 1] << 4) | p2[2 * i];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) p8[i] = (p4[2 * i + 1] << 8) | p4[2 * i];
+  return __builtin_amdgcn_perm(p8[1], p8[0], 0x05040100u);  // bits 0..15 of each
+}
+
+// one stage of the 16 x 16 transpose of 2-bit fields across a row of 16 lanes:
+// fields whose index bit S differs from the lane's bit S swap with lane ^ S
+template <int S>
+__device__ __forceinline__ uint32_t t16_stage(uint32_t w, int lane) {
+  constexpr uint32_t ML = S == 1 ? 0x33333333u : S == 2 ? 0x0F0F0F0Fu : S == 4 ? 0x00FF00FFu : 0x0000FFFFu;
+  uint32_t p;
+  if constexpr (S == 1)
+    p = (uint32_t)__builtin_amdgcn_mov_dpp((int)w, KVQ_DPP_XOR1, 0xF, 0xF, false);
+  else if constexpr (S == 2)
+    p = (uint32_t)__builtin_amdgcn_mov_dpp((int)w, KVQ_DPP_XOR2, 0xF, 0xF, false);
+  else
+    p = (uint32_t)__builtin_amdgcn_ds_swizzle((int)w, (S << 10) | 0x1F);  // lane ^ S within 32
+  if (lane & S) return (w & ~ML) | ((p >> (2 * S)) & ML);
+  return (w & ML) | ((p << (2 * S)) & ~ML);
+}
+
+__device__ __forceinline__ uint32_t transpose16_u2(uint32_t w, int lane) {
+  w = t16_stage<8>(w, lane);
+  w = t16_stage<4>(w, lane);
+  w = t16_stage<2>(w, lane);
+  return t16_stage<1>(w, lane);
+}
+
+// next unit at or after u (stride gridDim.x) that has tokens in this call; nunits if none
+__device__ __forceinline__ int next_dense_unit(const AppendArgs& a, int u, int ntiles, int nunits, FastUnit& U) {
+  for (; u < nunits; u += gridDim.x) {
+    U = fast_unit(a, u, ntiles);
+    if (U.lo < U.hi) break;
+  }
+  return u;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void dense_int2_store(const AppendArgs& a, const FastUnit& C, const f32x32& acc, int wv,
+                                                 int lane) {
+  const int hf = lane >> 5, col = lane & 31;
+  const int tensor = C.tensor;
+  const float* clip = tensor ? a.clip_v : a.clip_k;
+  float tc[16];
+  if (clip) {
+    const float* cp = clip + (size_t)C.h * D + 32 * wv + 4 * hf;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 c4 = *reinterpret_cast<const float4*>(cp + 8 * g);
+      tc[4 * g] = c4.x; tc[4 * g + 1] = c4.y; tc[4 * g + 2] = c4.z; tc[4 * g + 3] = c4.w;
+    }
+  }
+  uint32_t P[2];
+  uint16_t sbits[2], zbits[2];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {  // token col (blk 0) and 32 + col (blk 1)
+    float yc[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float y = acc[16 * blk + v];
+      yc[v] = clip ? fminf(fmaxf(y, -tc[v]), tc[v]) : y;
+    }
+    float lo = yc[0], hi = yc[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) {
+      lo = fminf(lo, yc[v]);
+      hi = fmaxf(hi, yc[v]);
+    }
+    lo = fminf(lo, __shfl_xor(lo, 32));
+    hi = fmaxf(hi, __shfl_xor(hi, 32));
+    const uint16_t sb = f16_sat_bits((hi - lo) / 3.0f);  // correctly rounded fp32 divide
+    const uint16_t zb = f16_sat_bits(lo);
+    const float sf = f16_bits_to_f32(sb), zf = f16_bits_to_f32(zb);
+    const float sq = sf != 0.0f ? sf : 1.0f;
+    const float r = sf != 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f;
+    float m[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) m[v] = quot_magic_u2(yc[v] - zf, sq, r);
+    P[blk] = pack16_u2(m);
+    sbits[blk] = sb;
+    zbits[blk] = zb;
+  }
+  // this lane stores token `kt` (col for the lower half, 32 + col for the upper)
+  const int kt = 32 * hf + col;
+  const int pos = C.tile * TILE + kt;
+  const bool valid = pos >= C.lo && pos < C.hi;
+  const uint16_t sk = hf ? sbits[1] : sbits[0], zk = hf ? zbits[1] : zbits[0];
+  if (tensor == 0) {
+    const uint32_t give = hf ? P[0] : P[1], keep = hf ? P[1] : P[0];
+    const uint32_t recv = (uint32_t)__shfl_xor((int)give, 32);
+    const uint32_t p0 = hf ? recv : keep, p1 = hf ? keep : recv;  // halves 0 and 1 of the kept token
+    const uint32_t d0 = __builtin_amdgcn_perm(p1, p0, 0x05010400u);
+    const uint32_t d1 = __builtin_amdgcn_perm(p1, p0, 0x07030602u);
+    if (valid) {
+      const size_t row = C.stream_idx * a.Tmax + pos;
+      *reinterpret_cast<uint2*>(a.k_codes + row * row_bytes(KVQ_INT2) + 8 * wv) = make_uint2(d0, d1);
+      uint16_t* m16 = reinterpret_cast<uint16_t*>(a.k_meta + row * meta_bytes(KVQ_INT2, 32));
+      m16[wv] = sk;
+      m16[4 + wv] = zk;
+    }
+    return;
+  }
+  // V: metadata [element][64 tokens]; codes channel-major, 16 tokens per dword
+  const size_t tile_idx = C.stream_idx * (a.Tmax / TILE) + C.tile;
+  if (valid) {
+    uint16_t* mtile = reinterpret_cast<uint16_t*>(a.v_meta + tile_idx * (size_t)(meta_elems(KVQ_INT2, 32) * TILE * 2));
+    mtile[wv * TILE + kt] = sk;
+    mtile[(4 + wv) * TILE + kt] = zk;
+  }
+  const int x = lane & 15, r16 = (lane >> 4) & 1;
+  const int c = 32 * wv + mfma_row(x, hf);
+  uint32_t* vt = reinterpret_cast<uint32_t*>(a.v_codes + tile_idx * (size_t)(D * chan_bytes(KVQ_INT2))) + 4 * c;
+  const int tlo = C.lo - C.tile * TILE, thi = C.hi - C.tile * TILE;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const uint32_t wt = transpose16_u2(P[blk], lane);
+    const int d = 2 * blk + r16;  // tokens 16d .. 16d + 15
+    if (16 * d + 16 <= tlo || 16 * d >= thi) continue;
+    if (16 * d >= tlo && 16 * d + 16 <= thi) {
+      vt[d] = wt;
+    } else {
+      uint32_t mask = 0u;
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (16 * d + e >= tlo && 16 * d + e < thi) mask |= 3u << (2 * e);
+      vt[d] = (vt[d] & ~mask) | (wt & mask);
+    }
+  }
+}
+
+}  // namespace
+
+template <bool BF16>
+__global__ __launch_bounds__(NT) void append_dense_int2_kernel(AppendArgs a, int ntiles, int nunits) {
+  __shared__ DenseMfmaSmem sm;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int tau = t >> 2, q = t & 3;
+  // rotation row 32 wv + lane % 32 as fp16 pairs (channels 2p, 2p + 1)
+  uint32_t rrow[64];
+  {
+    const uint4* r4 = reinterpret_cast<const uint4*>(a.rot + (size_t)(32 * wv + (lane & 31)) * D);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint4 u = r4[i];
+      rrow[4 * i] = u.x; rrow[4 * i + 1] = u.y; rrow[4 * i + 2] = u.z; rrow[4 * i + 3] = u.w;
+    }
+  }
+  FastUnit U;
+  int u = next_dense_unit(a, blockIdx.x, ntiles, nunits, U);
+  uint32_t w[16];
+  if (u < nunits) fast_load(U.src, w);
+  while (u < nunits) {
+    const FastUnit C = U;
+    {
+      uint4* d4 = reinterpret_cast<uint4*>(&sm.xs[tau][16 * q]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        d4[i] = C.valid ? make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]) : make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();
+    u = next_dense_unit(a, u + gridDim.x, ntiles, nunits, U);
+    if (u < nunits) fast_load(U.src, w);  // next tile's inputs, in flight during the products
+    f32x32 acc;
+#pragma unroll
+    for (int v = 0; v < 32; ++v) acc[v] = 0.0f;
+    // keep the rotation rows packed: their widening stays inside the loop
+#pragma unroll
+    for (int i = 0; i < 64; ++i) asm volatile("" : "+v"(rrow[i]));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint4 xv = *reinterpret_cast<const uint4*>(&sm.xs[lane][4 * i]);
+      const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const uint32_t rw = rrow[4 * i + jj];
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(half_lo<false>(rw), half_lo<BF16>(xw[jj]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(half_hi<false>(rw), half_hi<BF16>(xw[jj]), acc, 0, 0, 0);
+      }
+    }
+    __syncthreads();  // every wave is done with the staged tile
+    dense_int2_store<BF16>(a, C, acc, wv, lane);
+  }
+}
+
+// resident workgroups of the persistent dense kernel on the current device
+static int dense_grid_limit(bool bf16) {
+  static int cached[2][64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int& c = cached[bf16 ? 1 : 0][dev];
+  if (c == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    hipError_t e = bf16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, append_dense_int2_kernel<true>, NT, 0)
+                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, append_dense_int2_kernel<false>, NT, 0);
+    if (e != hipSuccess || per_cu <= 0) per_cu = 1;
+    c = cus * per_cu;
+  }
+  return c;
+}
+
 hipError_t launch_append(const AppendArgs& a, int grid_x, hipStream_t s) {
   dim3 grid(grid_x, a.H, 2 * a.B);  // K and V of every sequence in one launch
   if (a.rotation != KVQ_ROT_DENSE) {
@@ -873,6 +1164,16 @@ hipError_t launch_append(const AppendArgs& a, int grid_x, hipStream_t s) {
     KVQ_FAST(KVQ_INT8, 128, KVQ_INT4, 32)
     KVQ_FAST(KVQ_INT8, 32, KVQ_INT4, 128)
 #undef KVQ_FAST
+  }
+  if (a.rotation == KVQ_ROT_DENSE && a.desc == nullptr && a.k_fmt == KVQ_INT2 && a.v_fmt == KVQ_INT2 &&
+      a.k_group == 32 && a.v_group == 32) {
+    const int nunits = grid_x * a.H * 2 * a.B;
+    const int g = std::min(nunits, dense_grid_limit(a.in_bf16 != 0));
+    if (a.in_bf16)
+      hipLaunchKernelGGL(append_dense_int2_kernel<true>, dim3(g), dim3(NT), 0, s, a, grid_x, nunits);
+    else
+      hipLaunchKernelGGL(append_dense_int2_kernel<false>, dim3(g), dim3(NT), 0, s, a, grid_x, nunits);
+    return hipGetLastError();
   }
   if (a.rotation == KVQ_ROT_DENSE)
     hipLaunchKernelGGL(append_kernel<true>, grid, dim3(NT), 0, s, a);

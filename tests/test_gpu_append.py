@@ -20,6 +20,8 @@ CASES = {
     "int4-g32-gqa": synth.config(2, B=2, Hq=8, Hkv=2, T=320),
     "int8k-int4v-cert": synth.config(3, B=2, Hq=8, Hkv=2, T=256, n_plant=2),
     "int2-dense": synth.config(4, B=2, Hq=8, Hkv=2, T=256),
+    "int2-dense-bf16": synth.config(4, B=3, Hq=8, Hkv=2, T=320, dtype="bf16"),
+    "int2-dense-noclip": synth.config(4, B=1, Hq=4, Hkv=2, T=192, no_clip=True),
     "fp4-search-bf16": synth.config(5, B=2, Hq=8, Hkv=2, T=256),
     "fp4-absmax": synth.config(5, B=2, Hq=8, Hkv=2, T=192, scale_mode="absmax"),
     "int4-g128-none": synth.config(1, B=2, Hq=2, Hkv=2, T=192, rotation="none", k_group=128, v_group=128),
@@ -31,7 +33,7 @@ CASES = {
 
 
 def _clip(c, p, gcache, s, r16):
-    if c["k_fmt"] != "int2" and c["v_fmt"] != "int2":
+    if (c["k_fmt"] != "int2" and c["v_fmt"] != "int2") or c.get("no_clip"):
         return None, None
     ck = np.stack([synth.calibration(c, 0, h) for h in range(c["Hkv"])])
     cv = np.stack([synth.calibration(c, 1, h) for h in range(c["Hkv"])])
@@ -83,7 +85,8 @@ def test_append_full_bit_exact(name):
         assert np.all(got <= want * (1 + 2.0 ** -8) + 1e-6 * np.abs(want).max()), "descriptors too loose"
 
 
-@pytest.mark.parametrize("name", ["int4-g32-gqa", "int8k-int4v-cert", "fp4-search-bf16", "int2-dense"])
+@pytest.mark.parametrize("name", ["int4-g32-gqa", "int8k-int4v-cert", "fp4-search-bf16", "int2-dense",
+                                  "int2-dense-bf16"])
 def test_append_ragged_pieces(name):
     c = CASES[name]
     print(f"[append-ragged] case {name}", flush=True)
