@@ -910,6 +910,8 @@ typedef float f32x32 __attribute__((ext_vector_type(32)));
 
 struct __align__(16) DenseMfmaSmem {
   uint32_t xs[TILE][68];  // input vectors as fp16/bf16 pairs; rows padded to 272 bytes
+  uint32_t rs[D][68];     // the rotation as fp16 pairs, same padding
+  float clip[2][D];       // clipping thresholds of the unit, double-buffered by parity
 };
 
 template <bool BF16>
@@ -980,13 +982,13 @@ __device__ __forceinline__ int next_dense_unit(const AppendArgs& a, int u, int n
 
 template <bool BF16>
 __device__ __forceinline__ void dense_int2_store(const AppendArgs& a, const FastUnit& C, const f32x32& acc, int wv,
-                                                 int lane) {
+                                                 int lane, const float* sclip) {
   const int hf = lane >> 5, col = lane & 31;
   const int tensor = C.tensor;
-  const float* clip = tensor ? a.clip_v : a.clip_k;
+  const bool clip = (tensor ? a.clip_v : a.clip_k) != nullptr;
   float tc[16];
   if (clip) {
-    const float* cp = clip + (size_t)C.h * D + 32 * wv + 4 * hf;
+    const float* cp = sclip + 32 * wv + 4 * hf;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const float4 c4 = *reinterpret_cast<const float4*>(cp + 8 * g);
@@ -1074,25 +1076,33 @@ __device__ __forceinline__ void dense_int2_store(const AppendArgs& a, const Fast
 }  // namespace
 
 template <bool BF16>
-__global__ __launch_bounds__(NT) void append_dense_int2_kernel(AppendArgs a, int ntiles, int nunits) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void append_dense_int2_kernel(AppendArgs a, int ntiles,
+                                                                                                   int nunits) {
   __shared__ DenseMfmaSmem sm;
   const int t = threadIdx.x, lane = t & 63;
   const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
   const int tau = t >> 2, q = t & 3;
-  // rotation row 32 wv + lane % 32 as fp16 pairs (channels 2p, 2p + 1)
-  uint32_t rrow[64];
+  // the rotation to LDS once (made visible by the first barrier of the loop)
   {
-    const uint4* r4 = reinterpret_cast<const uint4*>(a.rot + (size_t)(32 * wv + (lane & 31)) * D);
+    const uint4* r4 = reinterpret_cast<const uint4*>(a.rot);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint4 u = r4[i];
-      rrow[4 * i] = u.x; rrow[4 * i + 1] = u.y; rrow[4 * i + 2] = u.z; rrow[4 * i + 3] = u.w;
+    for (int i = 0; i < D * 16 / NT; ++i) {
+      const int c = t + NT * i;  // 16-byte chunk: row c / 16, column chunk c % 16
+      *reinterpret_cast<uint4*>(&sm.rs[c >> 4][4 * (c & 15)]) = r4[c];
     }
   }
+  const int rrow = 32 * wv + (lane & 31);  // the rotation row this lane feeds
   FastUnit U;
   int u = next_dense_unit(a, blockIdx.x, ntiles, nunits, U);
   uint32_t w[16];
-  if (u < nunits) fast_load(U.src, w);
+  float4 cl = make_float4(0.0f, 0.0f, 0.0f, 0.0f);  // lanes t < 32: 4 clipping thresholds
+  auto load_unit = [&]() {
+    fast_load(U.src, w);
+    const float* clip = U.tensor ? a.clip_v : a.clip_k;
+    if (clip && t < D / 4) cl = *reinterpret_cast<const float4*>(clip + (size_t)U.h * D + 4 * t);
+  };
+  if (u < nunits) load_unit();
+  int par = 0;
   while (u < nunits) {
     const FastUnit C = U;
     {
@@ -1100,29 +1110,35 @@ __global__ __launch_bounds__(NT) void append_dense_int2_kernel(AppendArgs a, int
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         d4[i] = C.valid ? make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]) : make_uint4(0, 0, 0, 0);
+      if (t < D / 4) *reinterpret_cast<float4*>(&sm.clip[par][4 * t]) = cl;
     }
     __syncthreads();
     u = next_dense_unit(a, u + gridDim.x, ntiles, nunits, U);
-    if (u < nunits) fast_load(U.src, w);  // next tile's inputs, in flight during the products
+    if (u < nunits) load_unit();  // the next tile's inputs, in flight during the products
     f32x32 acc;
 #pragma unroll
     for (int v = 0; v < 32; ++v) acc[v] = 0.0f;
-    // keep the rotation rows packed: their widening stays inside the loop
-#pragma unroll
-    for (int i = 0; i < 64; ++i) asm volatile("" : "+v"(rrow[i]));
+    // eight channels per LDS read, the next reads in flight during the current eight steps
+    uint4 xv = *reinterpret_cast<const uint4*>(&sm.xs[lane][0]);
+    uint4 rv = *reinterpret_cast<const uint4*>(&sm.rs[rrow][0]);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const uint4 xv = *reinterpret_cast<const uint4*>(&sm.xs[lane][4 * i]);
+      const uint4 xn = *reinterpret_cast<const uint4*>(&sm.xs[lane][4 * ((i + 1) & 15)]);
+      const uint4 rn = *reinterpret_cast<const uint4*>(&sm.rs[rrow][4 * ((i + 1) & 15)]);
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of this step's products
       const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+      const uint32_t rw[4] = {rv.x, rv.y, rv.z, rv.w};
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const uint32_t rw = rrow[4 * i + jj];
-        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(half_lo<false>(rw), half_lo<BF16>(xw[jj]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(half_hi<false>(rw), half_hi<BF16>(xw[jj]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(half_lo<false>(rw[jj]), half_lo<BF16>(xw[jj]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(half_hi<false>(rw[jj]), half_hi<BF16>(xw[jj]), acc, 0, 0, 0);
       }
+      xv = xn;
+      rv = rn;
     }
     __syncthreads();  // every wave is done with the staged tile
-    dense_int2_store<BF16>(a, C, acc, wv, lane);
+    dense_int2_store<BF16>(a, C, acc, wv, lane, sm.clip[par]);
+    par ^= 1;
   }
 }
 
