@@ -731,6 +731,106 @@ __device__ __forceinline__ void fast_quantize(const float y[32], bool want_sums,
   ynorm2 = yn;
 }
 
+// FP4 E2M1 codes with E4M3 scales, two blocks of 16 per lane.  The scale search
+// visits the distinct E4M3 codes of fl32(t * m), m = 0.900, 0.925, ..., 1.100 in
+// that order; those codes are consecutive (a step of m moves t by at most 2.8%,
+// while every E4M3 rounding interval is at least 6.4% wide), so the candidates
+// are the codes c_lo .. c_hi of m = 0.9 and m = 1.1, in increasing order, and
+// the first strictly smallest error wins as in a skip-duplicates scan.  Errors
+// use the same fp32 operations as the generic quantizer: per element
+// d = |y| - Q(|y|), squared, summed over elements 0..7 and 8..15, then added.
+__device__ __forceinline__ float fp4_err16(const float ay[16], float S) {
+  const float t0 = 0.25f * S, t1 = 0.75f * S, t2 = 1.25f * S, t3 = 1.75f * S, t4 = 2.5f * S, t5 = 3.5f * S,
+              t6 = 5.0f * S;
+  const float v1 = 0.5f * S, v2 = S, v3 = 1.5f * S, v4 = 2.0f * S, v5 = 3.0f * S, v6 = 4.0f * S, v7 = 6.0f * S;
+  float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const float x = ay[j];
+    // thresholds pass as a prefix (ties go to the even code), so the last one passed names the value
+    float q = x > t0 ? v1 : 0.0f;
+    q = x >= t1 ? v2 : q;
+    q = x > t2 ? v3 : q;
+    q = x >= t3 ? v4 : q;
+    q = x > t4 ? v5 : q;
+    q = x >= t5 ? v6 : q;
+    q = x > t6 ? v7 : q;
+    const float d = x - q;
+    const float sq = d * d;
+    if (j < 8)
+      lo = lo + sq;
+    else
+      hi = hi + sq;
+  }
+  return lo + hi;
+}
+
+__device__ __forceinline__ void fast_quantize_fp4(const float y[32], bool search, bool want_sums, uint32_t packed[4],
+                                                  uint16_t& meta, float& res2, float& ynorm2) {
+  float acc = 0.0f;
+  uint32_t sc[2];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    float ay[16];
+    float am = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      ay[j] = fabsf(y[16 * blk + j]);
+      am = fmaxf(am, ay[j]);
+    }
+    const float t = am / 6.0f;  // correctly rounded fp32 divide
+    uint32_t best = e4m3_encode_nonneg(search ? t * 0.9f : t);
+    if (search) {
+      const uint32_t chi = e4m3_encode_nonneg(t * 1.1f);
+      float best_e = fp4_err16(ay, e4m3_value(best));
+      for (uint32_t c = best + 1; c <= chi; ++c) {
+        const float e = fp4_err16(ay, e4m3_value(c));
+        if (e < best_e) {
+          best_e = e;
+          best = c;
+        }
+      }
+    }
+    sc[blk] = best;
+    const float S = e4m3_value(best);
+    const float t0 = 0.25f * S, t1 = 0.75f * S, t2 = 1.25f * S, t3 = 1.75f * S, t4 = 2.5f * S, t5 = 3.5f * S,
+                t6 = 5.0f * S;
+    uint32_t nib[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float x = ay[j];
+      uint32_t idx = x > t0 ? 1u : 0u;
+      idx = x >= t1 ? 2u : idx;
+      idx = x > t2 ? 3u : idx;
+      idx = x >= t3 ? 4u : idx;
+      idx = x > t4 ? 5u : idx;
+      idx = x >= t5 ? 6u : idx;
+      idx = x > t6 ? 7u : idx;
+      idx = S != 0.0f ? idx | ((__float_as_uint(y[16 * blk + j]) >> 31) << 3) : 0u;
+      nib[j] = idx;
+      if (want_sums) {
+        const float d = x - e2m1_mag((int)(idx & 7u)) * S;
+        acc = acc + d * d;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w |= nib[8 * k + e] << (4 * e);
+      packed[2 * blk + k] = w;
+    }
+  }
+  meta = (uint16_t)(sc[0] | (sc[1] << 8));
+  res2 = acc;
+  float yn = 0.0f;
+  if (want_sums) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) yn = yn + y[j] * y[j];
+  }
+  ynorm2 = yn;
+}
+
 template <int KF, int KG, int VF, int VG, bool BF16>
 __device__ __forceinline__ void fast_process(const AppendArgs& a, FastSmem& sm, const FastUnit& U, const uint32_t w[16]) {
   const int t = threadIdx.x, tau = t >> 2, q = t & 3;
@@ -794,10 +894,18 @@ __device__ __forceinline__ void fast_process(const AppendArgs& a, FastSmem& sm, 
   uint32_t packed[8];
   uint16_t meta = 0;
   float res2 = 0.0f, ynorm2 = 0.0f;
-  if (tensor == 0)
-    fast_quantize<KF, KG>(y, desc, packed, meta, res2, ynorm2);
-  else
-    fast_quantize<VF, VG>(y, desc, packed, meta, res2, ynorm2);
+  const bool search = a.scale_mode == KVQ_SCALE_SEARCH9;
+  if (tensor == 0) {
+    if constexpr (KF == KVQ_FP4)
+      fast_quantize_fp4(y, search, desc, packed, meta, res2, ynorm2);
+    else
+      fast_quantize<KF, KG>(y, desc, packed, meta, res2, ynorm2);
+  } else {
+    if constexpr (VF == KVQ_FP4)
+      fast_quantize_fp4(y, search, desc, packed, meta, res2, ynorm2);
+    else
+      fast_quantize<VF, VG>(y, desc, packed, meta, res2, ynorm2);
+  }
 
   if (desc) {  // outward-rounded norms, as in the generic kernel
     const float slack = fwht ? 9.5367431640625e-7f : 0.0f;
@@ -828,7 +936,7 @@ __device__ __forceinline__ void fast_process(const AppendArgs& a, FastSmem& sm, 
         *reinterpret_cast<uint4*>(row) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
       }
       uint16_t* m16 = reinterpret_cast<uint16_t*>(a.k_meta + (stream_idx * a.Tmax + pos) * meta_bytes(KF, KG));
-      if constexpr (KG == 32) m16[q] = meta;
+      if constexpr (KF == KVQ_FP4 || KG == 32) m16[q] = meta;  // FP4: E4M3 bytes of blocks 2q, 2q + 1
       else if (q == 0) m16[0] = meta;
     }
     return;
@@ -837,10 +945,16 @@ __device__ __forceinline__ void fast_process(const AppendArgs& a, FastSmem& sm, 
   // V: metadata straight to the tile ([element][64 tokens] fp16), codes via LDS
   {
     constexpr int NM = meta_elems(VF, VG);
-    uint16_t* mtile = reinterpret_cast<uint16_t*>(a.v_meta + (stream_idx * (a.Tmax / TILE) + tile) * (size_t)(NM * TILE * 2));
+    uint8_t* mbase = a.v_meta + (stream_idx * (a.Tmax / TILE) + tile) * (size_t)(NM * TILE * meta_esize(VF));
     if (valid) {
-      if constexpr (VG == 32) mtile[q * TILE + tau] = meta;
-      else if (q == 0) mtile[tau] = meta;
+      if constexpr (VF == KVQ_FP4) {
+        mbase[(2 * q) * TILE + tau] = (uint8_t)(meta & 0xFF);
+        mbase[(2 * q + 1) * TILE + tau] = (uint8_t)(meta >> 8);
+      } else {
+        uint16_t* mtile = reinterpret_cast<uint16_t*>(mbase);
+        if constexpr (VG == 32) mtile[q * TILE + tau] = meta;
+        else if (q == 0) mtile[tau] = meta;
+      }
     }
   }
 #pragma unroll
@@ -873,7 +987,7 @@ __device__ __forceinline__ void fast_process(const AppendArgs& a, FastSmem& sm, 
 
 template <int KF, int KG, int VF, int VG, bool BF16>
 __global__ __launch_bounds__(NT) void append_fast_kernel(AppendArgs a, int ntiles) {
-  static_assert(VF == KVQ_INT4, "V codes of the fast path are int4");
+  static_assert(VF == KVQ_INT4 || VF == KVQ_FP4, "V codes of the fast path are nibbles");
   __shared__ FastSmem sm;
   const int t = threadIdx.x;
   const FastUnit U = fast_unit(a, blockIdx.x, ntiles);
@@ -1180,6 +1294,13 @@ hipError_t launch_append(const AppendArgs& a, int grid_x, hipStream_t s) {
     KVQ_FAST(KVQ_INT8, 128, KVQ_INT4, 32)
     KVQ_FAST(KVQ_INT8, 32, KVQ_INT4, 128)
 #undef KVQ_FAST
+    if (a.k_fmt == KVQ_FP4 && a.v_fmt == KVQ_FP4) {  // group fields are not used by FP4
+      if (a.in_bf16)
+        hipLaunchKernelGGL((append_fast_kernel<KVQ_FP4, 16, KVQ_FP4, 16, true>), fgrid, dim3(NT), 0, s, a, grid_x);
+      else
+        hipLaunchKernelGGL((append_fast_kernel<KVQ_FP4, 16, KVQ_FP4, 16, false>), fgrid, dim3(NT), 0, s, a, grid_x);
+      return hipGetLastError();
+    }
   }
   if (a.rotation == KVQ_ROT_DENSE && a.desc == nullptr && a.k_fmt == KVQ_INT2 && a.v_fmt == KVQ_INT2 &&
       a.k_group == 32 && a.v_group == 32) {
