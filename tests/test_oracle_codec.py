@@ -140,6 +140,27 @@ def test_fp4_search_never_worse_than_absmax():
         assert np.all(es <= e * (1 + 1e-5) + 1e-30)
 
 
+def test_fp4_search_codes_are_consecutive():
+    """The nine candidate scales E4M3(fl32(t * m)), m = 0.900 .. 1.100, take every E4M3 code
+    between code(t * 0.9) and code(t * 1.1) and no other (the write kernel scans that range):
+    each step of m moves t by at most 2.8%, every E4M3 rounding interval is wider than 6.4%."""
+    rng = np.random.default_rng(5)
+    t = np.concatenate([
+        np.exp(rng.uniform(np.log(2.0 ** -14), np.log(600.0), 200000)),
+        # t placed so that t * m lands on or next to a rounding midpoint of E4M3, for every m
+        np.outer((nx.e4m3_value(np.arange(0, 126)) + nx.e4m3_value(np.arange(1, 127))) / 2.0,
+                 1.0 / codec.SEARCH_M.astype(np.float64)).ravel(),
+        np.array([0.0, 1e-30, 2.0 ** -10, 448.0 / 1.1, 448.0 / 0.9, 1000.0]),
+    ]).astype(np.float32)
+    codes = np.stack([nx.e4m3_encode_nonneg(nx.f32(t * m)) for m in codec.SEARCH_M]).astype(np.int64)
+    lo, hi = codes[0], codes[-1]
+    assert np.all(np.diff(codes, axis=0) >= 0), "codes are non-decreasing in m"
+    for c in range(0, 127):
+        hit = np.any(codes == c, axis=0)
+        inside = (lo <= c) & (c <= hi)
+        assert np.array_equal(hit, inside), f"code {c}: candidate set is not the range"
+
+
 def test_fp4_element_bound():
     rng = np.random.default_rng(14)
     y = rng.standard_normal((100, 128)).astype(np.float32)
