@@ -38,6 +38,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F32_PEAK_TFLOPS = 157.3
 METRIC = "decode-attn effective KV GB/s & % HBM peak (int4 vs fp16); append Mvec/s"
 NROT = 4
 
@@ -144,8 +145,10 @@ def bench_workload(cfg_id, args):
         if c["data"] == "anisotropic":
             z = torch.randn(shape, generator=g, device=dev)
             d = torch.arange(1, 129, device=dev, dtype=torch.float32).rsqrt()
-            u, _ = torch.linalg.qr(torch.randn((H, 128, 128), generator=g, device=dev))
-            x = torch.einsum("bhtc,hdc->bhtd", z * d, u.contiguous())
+            # Haar bases per kv head from a QR on the host (small), then to the device
+            gh = torch.Generator().manual_seed(int(torch.randint(0, 2 ** 31, (1,), generator=g, device=dev).item()))
+            u = torch.linalg.qr(torch.randn((H, 128, 128), generator=gh, dtype=torch.float64))[0].float().to(dev)
+            x = torch.matmul(z * d, u.transpose(1, 2).contiguous())  # x[b,h,t] = U_h (d * z)
             return x.half().view(torch.int16)
         # Student-t(nu) = N(0,1) / sqrt(chi2(nu) / nu), chi2(nu) = sum of nu squared normals (nu = 4)
         nu = int(c["nu"])
@@ -286,6 +289,26 @@ def bench_workload(cfg_id, args):
         "append_gbs": round(app_bytes / app_s / 1e9, 1),
         "append_pct_hbm_peak": round(100 * app_bytes / app_s / 1e9 / HBM_PEAK_GBS, 2),
     }
+    if c["rotation"] == "dense":
+        # the write side is bound by the exact fp32 rotation: 2 * 128 * 128 flops per vector on
+        # fp32 K=1 MFMA chains (dense fp32 matrix peak 157.3 TFLOP/s)
+        tf = vecs * 2 * 128 * 128 / app_s / 1e12
+        result["append_roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_F32_PEAK_TFLOPS,
+                                     "unit": "TFLOP/s", "frac": round(tf / MFMA_F32_PEAK_TFLOPS, 4),
+                                     "kernel": "append_dense_int2_kernel"}
+    elif c["k_fmt"] == "fp4" and c["scale_mode"] == "search9":
+        # the scale search is VALU work: per 16-element block and candidate scale, 7 compares and
+        # selects plus the squared error per element (see the FP4 quantizer); reported against the
+        # fp32 vector issue rate of 256 CUs x 4 SIMDs x 16 lanes at 2.4 GHz
+        result["append_roofline"] = {"bound": "alu", "achieved_gbs": round(app_bytes / app_s / 1e9, 1),
+                                     "hbm_frac": round(app_bytes / app_s / 1e9 / HBM_PEAK_GBS, 4),
+                                     "kernel": "append_fast_kernel<fp4, fp4>"}
+    if args.copy_calibration:
+        src = torch.full((256 << 20,), 3, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
     print(json.dumps(result))
 
 
