@@ -49,7 +49,8 @@ kvq_status check_params(const kvq_params* p) {
     return fail(KVQ_ERR_INVALID_ARG, "k_group must be 32 or 128");
   if (p->v_fmt == KVQ_INT4 && p->v_group != 32 && p->v_group != 128)
     return fail(KVQ_ERR_INVALID_ARG, "v_group must be 32 or 128");
-  if (p->scale_mode != KVQ_SCALE_ABSMAX && p->scale_mode != KVQ_SCALE_SEARCH9)
+  if (p->scale_mode != KVQ_SCALE_ABSMAX && p->scale_mode != KVQ_SCALE_SEARCH9 &&
+      p->scale_mode != KVQ_SCALE_SEARCH_OFFSETS)
     return fail(KVQ_ERR_INVALID_ARG, "bad scale_mode");
   if (p->rotation != KVQ_ROT_NONE && p->rotation != KVQ_ROT_SIGN_FWHT && p->rotation != KVQ_ROT_DENSE)
     return fail(KVQ_ERR_INVALID_ARG, "bad rotation");

@@ -216,8 +216,10 @@ __device__ __forceinline__ float fp4_zero_err(const float* y) {
   return lo + hi;
 }
 
-// FP4 with E4M3 block scales (two blocks of 16 per lane)
-__device__ __forceinline__ void quant_fp4(const float y[32], int search, int codes[32], uint8_t sc[2],
+// FP4 with E4M3 block scales (two blocks of 16 per lane).  Candidates: E4M3(t * m_k) for the
+// multiplicative search, the bit patterns c0 - 2 .. c0 + 6 of c0 = E4M3(t) (kept inside
+// 0x00..0x7E) for the offset search, c0 alone for absmax.
+__device__ __forceinline__ void quant_fp4(const float y[32], int mode, int codes[32], uint8_t sc[2],
                                           float& res2) {
   const float mults[9] = {0.9f, 0.925f, 0.95f, 0.975f, 1.0f, 1.025f, 1.05f, 1.075f, 1.1f};
   float acc = 0.0f;
@@ -232,10 +234,12 @@ __device__ __forceinline__ void quant_fp4(const float y[32], int search, int cod
     float best_e = 0.0f;
     bool have = false;
     uint32_t prev_c = 0xFFFFFFFFu;
+    const int c0 = (int)e4m3_encode_nonneg(t);
 #pragma unroll
     for (int k = 0; k < 9; ++k) {
-      if (!search && k != 4) continue;
-      uint32_t c = e4m3_encode_nonneg(t * mults[k]);
+      if (mode == KVQ_SCALE_ABSMAX && k != 4) continue;
+      uint32_t c = mode == KVQ_SCALE_SEARCH_OFFSETS ? (uint32_t)min(max(c0 + k - 2, 0), 0x7E)
+                                                    : e4m3_encode_nonneg(t * mults[k]);
       if (c == prev_c) continue;  // same stored scale as the previous candidate: same error
       prev_c = c;
       float S = e4m3_value(c);
@@ -458,7 +462,7 @@ __global__ __launch_bounds__(NT) void append_kernel(AppendArgs a) {
     quant_asym2(y, clip ? clip + (size_t)h * D + 32 * q : nullptr, codes, m0, m1, res2);
   } else {
     uint8_t sc[2];
-    quant_fp4(y, a.scale_mode == KVQ_SCALE_SEARCH9, codes, sc, res2);
+    quant_fp4(y, a.scale_mode, codes, sc, res2);
     m0 = (uint16_t)(sc[0] | (sc[1] << 8));
   }
 
@@ -736,7 +740,9 @@ __device__ __forceinline__ void fast_quantize(const float y[32], bool want_sums,
 // that order; those codes are consecutive (a step of m moves t by at most 2.8%,
 // while every E4M3 rounding interval is at least 6.4% wide), so the candidates
 // are the codes c_lo .. c_hi of m = 0.9 and m = 1.1, in increasing order, and
-// the first strictly smallest error wins as in a skip-duplicates scan.  Errors
+// the first strictly smallest error wins as in a skip-duplicates scan.  The
+// bit-offset search scans the patterns c0 - 2 .. c0 + 6 of c0 = E4M3(t) the
+// same way (clamped to 0x00..0x7E, which only drops repeats).  Errors
 // use the same fp32 operations as the generic quantizer: per element
 // d = |y| - Q(|y|), squared, summed over elements 0..7 and 8..15, then added.
 __device__ __forceinline__ float fp4_err16(const float ay[16], float S) {
@@ -765,7 +771,7 @@ __device__ __forceinline__ float fp4_err16(const float ay[16], float S) {
   return lo + hi;
 }
 
-__device__ __forceinline__ void fast_quantize_fp4(const float y[32], bool search, bool want_sums, uint32_t packed[4],
+__device__ __forceinline__ void fast_quantize_fp4(const float y[32], int mode, bool want_sums, uint32_t packed[4],
                                                   uint16_t& meta, float& res2, float& ynorm2) {
   float acc = 0.0f;
   uint32_t sc[2];
@@ -779,9 +785,16 @@ __device__ __forceinline__ void fast_quantize_fp4(const float y[32], bool search
       am = fmaxf(am, ay[j]);
     }
     const float t = am / 6.0f;  // correctly rounded fp32 divide
-    uint32_t best = e4m3_encode_nonneg(search ? t * 0.9f : t);
-    if (search) {
-      const uint32_t chi = e4m3_encode_nonneg(t * 1.1f);
+    uint32_t best, chi;
+    if (mode == KVQ_SCALE_SEARCH9) {
+      best = e4m3_encode_nonneg(t * 0.9f);
+      chi = e4m3_encode_nonneg(t * 1.1f);
+    } else {
+      const uint32_t c0 = e4m3_encode_nonneg(t);
+      best = mode == KVQ_SCALE_SEARCH_OFFSETS ? (c0 > 2u ? c0 - 2u : 0u) : c0;
+      chi = mode == KVQ_SCALE_SEARCH_OFFSETS ? min(c0 + 6u, 0x7Eu) : c0;
+    }
+    if (chi > best) {
       float best_e = fp4_err16(ay, e4m3_value(best));
       for (uint32_t c = best + 1; c <= chi; ++c) {
         const float e = fp4_err16(ay, e4m3_value(c));
@@ -894,15 +907,15 @@ __device__ __forceinline__ void fast_process(const AppendArgs& a, FastSmem& sm, 
   uint32_t packed[8];
   uint16_t meta = 0;
   float res2 = 0.0f, ynorm2 = 0.0f;
-  const bool search = a.scale_mode == KVQ_SCALE_SEARCH9;
+  const int smode = a.scale_mode;
   if (tensor == 0) {
     if constexpr (KF == KVQ_FP4)
-      fast_quantize_fp4(y, search, desc, packed, meta, res2, ynorm2);
+      fast_quantize_fp4(y, smode, desc, packed, meta, res2, ynorm2);
     else
       fast_quantize<KF, KG>(y, desc, packed, meta, res2, ynorm2);
   } else {
     if constexpr (VF == KVQ_FP4)
-      fast_quantize_fp4(y, search, desc, packed, meta, res2, ynorm2);
+      fast_quantize_fp4(y, smode, desc, packed, meta, res2, ynorm2);
     else
       fast_quantize<VF, VG>(y, desc, packed, meta, res2, ynorm2);
   }

@@ -82,6 +82,10 @@ typedef int32_t kvq_status;
 /* FP4 scale selection */
 #define KVQ_SCALE_ABSMAX 0  /* S = E4M3(absmax / 6) */
 #define KVQ_SCALE_SEARCH9 1 /* best of E4M3(absmax/6 * m), m = 0.900, 0.925, ..., 1.100 */
+/* best of the E4M3 bit patterns c0 + f, c0 = E4M3(absmax/6), f = -2, ..., 6 (patterns
+ * 0x00..0x7E only): the bit-offset search of "Search Your Block Floating Point Scales!",
+ * Methodology, ScaleSearch */
+#define KVQ_SCALE_SEARCH_OFFSETS 2
 
 /* indices into the array filled by kvq_buffer_bytes */
 #define KVQ_BUF_K_CODES 0

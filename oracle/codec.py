@@ -33,6 +33,12 @@ fp4 E2M1 with an E4M3 scale per 16, absmax or searched
     bit-offset search (the configured workload asks for it); 9 points so that
     x1.00 is a candidate; candidates are rounded to E4M3 before their error is
     measured, since the stored scale is what dequantization uses.
+    Mode "offsets" is the search as the page states it: the candidates are the
+    E4M3 bit patterns c0 + f of the absmax scale c0 = E4M3(t), for the integer
+    offsets f = -2, ..., 6 in that order (the page's reinterpret-add-reinterpret),
+    keeping only non-negative finite patterns 0x00..0x7E.  Readings: the page
+    prints no range; [-2, 6] covers the ~1.5x larger scales it finds optimal
+    for many blocks (absmax mapped to 4 instead of 6) plus two smaller ones.
 
 Layout of the cache buffers (bytes; little-endian; B batch, H kv heads,
 Tmax positions, a multiple of 64):
@@ -58,6 +64,8 @@ from .rotation import rotate_input_f32, D
 
 FORMATS = ("int4", "int8", "int2", "fp4")
 SEARCH_M = np.array([0.9, 0.925, 0.95, 0.975, 1.0, 1.025, 1.05, 1.075, 1.1], dtype=np.float32)
+SEARCH_OFFSETS = tuple(range(-2, 7))  # f in the page's s(f) = reinterpret(reinterpret(s, int8) + f)
+SCALE_MODES = ("absmax", "search9", "offsets")
 TILE = 64
 
 
@@ -180,16 +188,24 @@ def quantize_fp4(y, scale_mode="search9"):
 
     Returns (codes uint8 nibbles [..., 128], scale codes uint8 [..., 8]).
     """
+    if scale_mode not in SCALE_MODES:
+        raise ValueError(scale_mode)
     y = np.asarray(y, dtype=np.float32)
     yb = y.reshape(y.shape[:-1] + (8, 16))
     a = np.max(np.abs(yb), axis=-1)
     t = nx.f32(nx.f32(a) / np.float32(6.0))
-    mults = SEARCH_M if scale_mode == "search9" else np.array([1.0], dtype=np.float32)
+    if scale_mode == "offsets":
+        c0 = nx.e4m3_encode_nonneg(t).astype(np.int64)
+        # patterns outside 0x00..0x7E are not candidates: clamping them onto the ends repeats
+        # a candidate already tried (same error), so the first-smallest choice is unchanged
+        cands = [np.clip(c0 + f, 0, 0x7E).astype(np.uint8) for f in SEARCH_OFFSETS]
+    else:
+        mults = SEARCH_M if scale_mode == "search9" else np.array([1.0], dtype=np.float32)
+        cands = [nx.e4m3_encode_nonneg(nx.f32(t * m)) for m in mults]
     best_err = None
     best_codes = None
     best_sc = None
-    for m in mults:
-        sc = nx.e4m3_encode_nonneg(nx.f32(t * m))
+    for sc in cands:
         S = nx.e4m3_value(sc)
         Ssafe = np.where(S == 0, 1.0, S)
         codes = nx.e2m1_quantize(yb, Ssafe[..., None])

@@ -29,6 +29,9 @@ CASES = {
     "int4-bf16": synth.config(2, B=1, Hq=4, Hkv=2, T=128, dtype="bf16"),
     "fp4-f16-absmax": synth.config(5, B=1, Hq=4, Hkv=2, T=128, dtype="f16", scale_mode="absmax"),
     "fp4-f16-search": synth.config(5, B=1, Hq=4, Hkv=2, T=128, dtype="f16"),
+    "fp4-offsets-bf16": synth.config(5, B=2, Hq=8, Hkv=2, T=256, scale_mode="offsets"),
+    "fp4-offsets-dense-f16": synth.config(5, B=1, Hq=4, Hkv=2, T=192, dtype="f16", scale_mode="offsets",
+                                          rotation="dense"),
 }
 
 

@@ -53,6 +53,7 @@ CASES = {
     "g1-and-g2": (synth.config(2, B=2, Hq=4, Hkv=2, T=512), [512, 333]),
     "c5-fp4-search-bf16": (synth.config(5, B=2, T=1024), [1024, 701]),
     "fp4-absmax-f16-ragged": (synth.config(5, B=3, Hq=8, Hkv=2, T=512, dtype="f16", scale_mode="absmax"), [512, 129, 1]),
+    "fp4-offsets-search": (synth.config(5, B=2, Hq=8, Hkv=2, T=512, scale_mode="offsets"), [512, 300]),
 }
 
 

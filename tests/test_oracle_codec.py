@@ -140,6 +140,62 @@ def test_fp4_search_never_worse_than_absmax():
         assert np.all(es <= e * (1 + 1e-5) + 1e-30)
 
 
+def _e2m1_err_f64(yb, S):
+    """Squared error of the nearest E2M1 value x S per element (ties to the even magnitude
+    index), summed per block, in fp64; written independently of the oracle's encoder."""
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    ay = np.abs(yb.astype(np.float64))[..., None]
+    grid = mags * S[..., None, None]
+    dist = np.abs(ay - grid)
+    best = dist.min(-1, keepdims=True)
+    tied = dist == best
+    idx = np.where(tied.sum(-1) > 1, np.argmax(tied & (np.arange(8) % 2 == 0), -1), np.argmin(dist, -1))
+    q = np.take_along_axis(grid, idx[..., None], -1)[..., 0]
+    return ((ay[..., 0] - q) ** 2).sum(-1)
+
+
+def test_fp4_offsets_brute_force():
+    """ScaleSearch as printed: the kept scale is a pattern c0 + f, f in [-2, 6], of the absmax
+    scale c0 = E4M3(a / 6), and no pattern in that range has a smaller error."""
+    rng = np.random.default_rng(21)
+    y = np.concatenate([rng.standard_normal((150, 128)), rng.standard_t(4, (150, 128)) * 0.01,
+                        rng.standard_normal((10, 128)) * 300.0]).astype(np.float32)
+    n = y.shape[0]
+    codes, sc = codec.quantize_fp4(y, "offsets")
+    yb = y.reshape(n, 8, 16)
+    t = (np.abs(yb).max(-1) / np.float32(6)).astype(np.float32)
+    c0 = nx.e4m3_encode_nonneg(t).astype(np.int64)
+    f = sc.astype(np.int64) - c0
+    assert np.all((f >= -2) & (f <= 6)), "kept scale outside the offset range"
+    assert np.all(sc <= 0x7E)
+    e_kept = _e2m1_err_f64(yb, nx.e4m3_value(sc))
+    for off in range(-2, 7):
+        cand = c0 + off
+        ok = (cand >= 0) & (cand <= 0x7E)
+        e = _e2m1_err_f64(yb, nx.e4m3_value(np.clip(cand, 0, 0x7E)))
+        assert np.all(~ok | (e_kept <= e * (1 + 1e-5) + 1e-30)), f"offset {off} beats the kept scale"
+    # the kept codes are the nearest E2M1 values for the kept scale
+    got = codec.dequant_fp4(codes, sc).reshape(n, 8, 16)
+    assert np.allclose(((got - yb.astype(np.float64)) ** 2).sum(-1), e_kept, rtol=1e-12, atol=0)
+
+
+def test_fp4_offsets_bimodal_on_gaussian_blocks():
+    """The page finds the best offsets bimodal: the absmax scale (f = 0) for some blocks and
+    a ~1.5x larger one (absmax mapped to E2M1 4 instead of 6: f = +4, +5) for many others."""
+    rng = np.random.default_rng(3)
+    y = rng.standard_normal((2000, 128)).astype(np.float32)
+    _, sc = codec.quantize_fp4(y, "offsets")
+    t = (np.abs(y.reshape(2000, 8, 16)).max(-1) / np.float32(6)).astype(np.float32)
+    f = sc.astype(np.int64) - nx.e4m3_encode_nonneg(t).astype(np.int64)
+    cnt = np.bincount((f + 2).ravel(), minlength=9)
+    near0, near15, valley = cnt[1:4].sum(), cnt[6:8].sum(), cnt[4:6].sum()
+    assert near0 > 0.3 * f.size and near15 > 0.25 * f.size and valley < 0.1 * f.size
+    # and the search lowers the error against the absmax scale
+    cs, ss = codec.quantize_fp4(y, "offsets")
+    ca, sa = codec.quantize_fp4(y, "absmax")
+    assert ((codec.dequant_fp4(cs, ss) - y) ** 2).sum() < 0.8 * ((codec.dequant_fp4(ca, sa) - y) ** 2).sum()
+
+
 def test_fp4_search_codes_are_consecutive():
     """The nine candidate scales E4M3(fl32(t * m)), m = 0.900 .. 1.100, take every E4M3 code
     between code(t * 0.9) and code(t * 1.1) and no other (the write kernel scans that range):
