@@ -92,12 +92,16 @@ float softmax_scale(const kvq_params* p) { return p->softmax_scale > 0.0f ? p->s
 
 // split count for decode: about two workgroups per CU (256 CUs), at
 // least 8 chunks (512 tokens) per workgroup, at most MAX_SPLITS
-int choose_splits(const kvq_params* p, int max_chunks) {
+// Context splits per (sequence, kv head, group of 4 query heads): enough workgroups
+// to fill the GPU (quantized path: 8-wave workgroups, one per CU; fp16 baseline:
+// 4-wave workgroups, two per CU), each with at least 2 chunks per wave.
+int choose_splits(const kvq_params* p, int max_chunks, bool dense = false) {
   const int G = p->n_q_heads / p->n_kv_heads;
   const int hg = (G + 3) / 4;
   const long units = (long)p->batch * p->n_kv_heads * hg;
-  long target = (512 + units - 1) / units;
-  long by_len = max_chunks / 8;
+  const long wgs = dense ? 512 : 256;
+  long target = (wgs + units - 1) / units;
+  long by_len = max_chunks / (dense ? 8 : 16);
   if (by_len < 1) by_len = 1;
   long s = target < by_len ? target : by_len;
   if (s < 1) s = 1;
@@ -105,7 +109,10 @@ int choose_splits(const kvq_params* p, int max_chunks) {
   return (int)s;
 }
 
-int max_splits_for(const kvq_params* p) { return choose_splits(p, p->max_ctx / TILE); }
+int max_splits_for(const kvq_params* p) {
+  const int a = choose_splits(p, p->max_ctx / TILE, false), b = choose_splits(p, p->max_ctx / TILE, true);
+  return a > b ? a : b;
+}
 
 }  // namespace
 
@@ -289,7 +296,7 @@ static kvq_status decode_common(const kvq_params* p, const kvq_cache* c, const v
     const int ch = (a.seq.v[b] + TILE - 1) / TILE;
     if (ch > max_chunks) max_chunks = ch;
   }
-  const int n_splits = choose_splits(p, max_chunks > 0 ? max_chunks : 1);
+  const int n_splits = choose_splits(p, max_chunks > 0 ? max_chunks : 1, dense);
   a.q = (const uint16_t*)q;
   if (dense) {
     if (!kd || !vd || !aligned16(kd) || !aligned16(vd))

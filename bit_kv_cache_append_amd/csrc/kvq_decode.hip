@@ -41,7 +41,9 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef int i4 __attribute__((ext_vector_type(4)));
 
-constexpr int NT = 256;
+constexpr int NT = 256;   // combine kernel, fp16 baseline split kernel
+constexpr int NTS = 512;  // quantized split kernel: 8 waves, one workgroup per CU
+constexpr int NWS = NTS / 64;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float NEG_INF = -__builtin_huge_valf();
 
@@ -214,17 +216,18 @@ struct __align__(16) DecodeSmem {
   float qf[4][D];          // query (fp32), rotated in place
   float qr[4][D];          // dense rotation output
   float qo[4][D];          // original query * scale * log2e (certified recompute)
-  uint32_t qh[4][32];      // high int8 halves, MFMA operand order
-  uint32_t ql[4][32];      // low int8 halves
+  uint32_t qh[4][32];      // high int8 halves: dword 4n + c = MFMA operand of chain c, step n
+  uint32_t ql[4][32];      // low int8 halves, same order
   uint32_t qf4[4][32][4];  // FP4 keys: per head and 4-channel step, fp16 query high then low parts
   float qs[4];             // per-head dequantization of the 16-bit query
   float qsum[4][4];        // per head, per group: sum of 16-bit query codes
-  uint16_t vmeta[4][8][16][4];  // per wave: V metadata by (element, slice, r)
-  float pb[4][TILE][4];    // per wave: probabilities by token (certified recompute)
-  float mrg_m[4][4], mrg_l[4][4], mrg_e[4][4];
-  float mrg_ek[4], mrg_vn[4];
-  float mrg_o[4][4][D];    // per wave, head, channel
-  float mrg_oo[4][4][D];
+  uint16_t vmeta[NWS][8][16][4];  // per wave: V metadata by (element, slice, r)
+  float pb[NWS][TILE][4];    // per wave: probabilities by token (certified recompute)
+  float mrg_m[NWS][4], mrg_l[NWS][4], mrg_e[NWS][4];
+  float mrg_ek[NWS], mrg_vn[NWS];
+  float mrg_o[NWS][4][D];    // per wave, head, channel
+  float mrg_oo[NWS][4][D];
+  int next;                  // next chunk (offset from the split's first) to claim
 };
 
 // ------------------------------------------------------------------ prologue
@@ -251,16 +254,21 @@ __device__ __forceinline__ QueryIn query_loads(const DecodeArgs& a, int b, int h
 
 template <int KF>
 __device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryIn& qin, int nh, int kgroup) {
-  const int t = threadIdx.x, j = t >> 6, l = t & 63;
+  // waves 0..3 own query heads 0..3; further waves only join the barriers
+  const int t = threadIdx.x, l = t & 63;
+  const bool own = (t >> 6) < 4;
+  const int j = (t >> 6) & 3;
   const bool bf16 = a.in_bf16 != 0;
   float x0 = 0.0f, x1 = 0.0f;
-  if (j < nh) {
+  if (own && j < nh) {
     x0 = widen(qin.q0, bf16);
     x1 = widen(qin.q1, bf16);
   }
   const float pre = a.scale * LOG2E;
-  sm.qo[j][2 * l] = x0 * pre;
-  sm.qo[j][2 * l + 1] = x1 * pre;
+  if (own) {
+    sm.qo[j][2 * l] = x0 * pre;
+    sm.qo[j][2 * l + 1] = x1 * pre;
+  }
   float y0 = x0, y1 = x1;
   if (a.rotation == KVQ_ROT_SIGN_FWHT) {
     x0 = (qin.sg & 0x80u) ? -x0 : x0;
@@ -274,16 +282,19 @@ __device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryI
       y1 = up ? p1 - y1 : y1 + p1;
     }
   } else if (a.rotation == KVQ_ROT_DENSE) {
-    sm.qf[j][2 * l] = x0;
-    sm.qf[j][2 * l + 1] = x1;
-    __syncthreads();
-    for (int rr = 0; rr < 2; ++rr) {
-      const int row = l + 64 * rr;
-      const uint16_t* rp = a.rot + (size_t)row * D;
-      float acc = 0.0f;
-      for (int k = 0; k < D; ++k) acc = fmaf(f16_bits_to_f32(rp[k]), sm.qf[j][k], acc);
-      sm.qr[j][row] = acc;
+    if (own) {
+      sm.qf[j][2 * l] = x0;
+      sm.qf[j][2 * l + 1] = x1;
     }
+    __syncthreads();
+    if (own)
+      for (int rr = 0; rr < 2; ++rr) {
+        const int row = l + 64 * rr;
+        const uint16_t* rp = a.rot + (size_t)row * D;
+        float acc = 0.0f;
+        for (int k = 0; k < D; ++k) acc = fmaf(f16_bits_to_f32(rp[k]), sm.qf[j][k], acc);
+        sm.qr[j][row] = acc;
+      }
     __syncthreads();
     y0 = sm.qr[j][2 * l];
     y1 = sm.qr[j][2 * l + 1];
@@ -301,15 +312,16 @@ __device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryI
     const float inv = mx > 0.0f ? ldexpf(1.0f, 14 - ex) : 1.0f;
     uint16_t* qp = reinterpret_cast<uint16_t*>(&sm.qf4[j][0][0]);
     const float ys[2] = {y0 * inv, y1 * inv};
+    if (own)
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int c = 2 * l + e, n = c >> 2, mm = c & 3;
-      const _Float16 hh = (_Float16)ys[e];
-      const _Float16 ll = (_Float16)(ys[e] - (float)hh);
-      qp[n * 8 + mm] = __builtin_bit_cast(uint16_t, hh);
-      qp[n * 8 + 4 + mm] = __builtin_bit_cast(uint16_t, ll);
-    }
-    if (l == 0) sm.qs[j] = qs;
+      for (int e = 0; e < 2; ++e) {
+        const int c = 2 * l + e, n = c >> 2, mm = c & 3;
+        const _Float16 hh = (_Float16)ys[e];
+        const _Float16 ll = (_Float16)(ys[e] - (float)hh);
+        qp[n * 8 + mm] = __builtin_bit_cast(uint16_t, hh);
+        qp[n * 8 + 4 + mm] = __builtin_bit_cast(uint16_t, ll);
+      }
+    if (own && l == 0) sm.qs[j] = qs;
     __syncthreads();
     return;
   }
@@ -319,14 +331,18 @@ __device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryI
   uint8_t* hb = reinterpret_cast<uint8_t*>(&sm.qh[j][0]);
   uint8_t* lb = reinterpret_cast<uint8_t*>(&sm.ql[j][0]);
   const int qv[2] = {q0, q1};
+  if (own)
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int c = 2 * l + e;
     const int hi = (qv[e] + 128) >> 8;
     const int lo = qv[e] - 256 * hi;
+    // operand dword d = 8 c + n of the QK chains is stored at 4 n + c, so that one 16-byte
+    // LDS read gives step n of all four chains
     const int sl = KFmt<KF>::slot(c);
-    hb[sl] = (uint8_t)(hi & 0xFF);
-    lb[sl] = (uint8_t)(lo & 0xFF);
+    const int d = sl >> 2, ps = (((d & 7) << 2) | (d >> 3)) * 4 + (sl & 3);
+    hb[ps] = (uint8_t)(hi & 0xFF);
+    lb[ps] = (uint8_t)(lo & 0xFF);
   }
   // per-group sums of the 16-bit codes (groups of 32 channels = 16 lanes)
   float gs = (float)(q0 + q1);
@@ -338,28 +354,28 @@ __device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryI
     gs += __shfl_xor(gs, 16);
     gs += __shfl_xor(gs, 32);
   }
-  if ((l & 15) == 0) sm.qsum[j][l >> 4] = gs;
-  if (l == 0) sm.qs[j] = qs;
+  if (own && (l & 15) == 0) sm.qsum[j][l >> 4] = gs;
+  if (own && l == 0) sm.qs[j] = qs;
   __syncthreads();
 }
 
 // ------------------------------------------------------------------ split record
-// Merges the 4 waves of this workgroup (in LDS, log-sum-exp weights) and writes
+// Merges the NW waves of this workgroup (in LDS, log-sum-exp weights) and writes
 // the record of (sequence, query head, split) for the combine kernel.
-template <bool CERT>
+template <bool CERT, int NW>
 __device__ void write_record(const DecodeArgs& a, DecodeSmem& sm, int b, int hq0, int nh, int split) {
   const int t = threadIdx.x, hh = t >> 6, l = t & 63, c = 2 * l;
   if (hh >= nh) return;
   float M = NEG_INF;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) M = fmaxf(M, sm.mrg_m[w][hh]);
-  float wgt[4];
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.mrg_m[w][hh]);
+  float wgt[NW];
 #pragma unroll
-  for (int w = 0; w < 4; ++w) wgt[w] = (M == NEG_INF) ? 0.0f : exp2f(sm.mrg_m[w][hh] - M);
+  for (int w = 0; w < NW; ++w) wgt[w] = (M == NEG_INF) ? 0.0f : exp2f(sm.mrg_m[w][hh] - M);
   float* rec = a.part + (((size_t)b * a.Hq + hq0 + hh) * a.n_splits + split) * PART_FLOATS;
   float o0 = 0.0f, o1 = 0.0f, p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     o0 += wgt[w] * sm.mrg_o[w][hh][c];
     o1 += wgt[w] * sm.mrg_o[w][hh][c + 1];
     if constexpr (CERT) {
@@ -380,7 +396,7 @@ __device__ void write_record(const DecodeArgs& a, DecodeSmem& sm, int b, int hq0
   if (l == 0) {
     float L = 0.0f, E = 0.0f, ek = 0.0f, vn = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       L += wgt[w] * sm.mrg_l[w][hh];
       E += wgt[w] * sm.mrg_e[w][hh];
       ek = fmaxf(ek, sm.mrg_ek[w]);
@@ -595,7 +611,7 @@ __device__ __forceinline__ float max_same_head_fast(float v) {
 }
 
 template <int KF, int KG, int VF, int VG, bool CERT>
-__global__ __launch_bounds__(NT, 2) void decode_split(DecodeArgs a) {
+__global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   __shared__ DecodeSmem sm;
   const int b = blockIdx.z;
   const int HG = (a.G + 3) >> 2;
@@ -625,20 +641,23 @@ __global__ __launch_bounds__(NT, 2) void decode_split(DecodeArgs a) {
   // same on every path.
   const QueryIn qin = query_loads(a, b, hq0, nh);
   __builtin_amdgcn_sched_barrier(0);
+  // Chunk schedule inside the workgroup: wave w starts with chunk c0 + w; every
+  // further chunk is claimed from a counter in LDS, one claim ahead of the chunk
+  // being loaded.  The two waves sharing a SIMD do not progress equally (the
+  // older one wins issue slots), so the faster one simply claims more chunks.
+  if (t == 0) sm.next = NWS;  // published by the prologue's barrier
+  auto claim = [&]() -> int {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&sm.next, 1);
+    return v;
+  };
   ChunkRegs<KF, VF> RA, RB;
-  int ch = c0 + wv;
-  load_chunk<KF, KG, VF, VG>(a, stream, ch < c1 ? ch : 0, lane, tok_a, RA);
+  int cA = c0 + wv;
+  load_chunk<KF, KG, VF, VG>(a, stream, cA < c1 ? cA : 0, lane, tok_a, RA);
   __builtin_amdgcn_sched_barrier(0);
   query_prologue<KF>(a, sm, qin, nh, KG);
+  int pB = claim();
 
-  uint32_t qh[32], ql[32];
-  if constexpr (KF != KVQ_FP4) {
-#pragma unroll
-    for (int n = 0; n < 32; ++n) {
-      qh[n] = sm.qh[j][n];
-      ql[n] = sm.ql[j][n];
-    }
-  }
   const float qs = sm.qs[j];
   float qsum[4];
 #pragma unroll
@@ -704,14 +723,21 @@ __global__ __launch_bounds__(NT, 2) void decode_split(DecodeArgs a) {
         ah[c] = i4{0, 0, 0, 0};
         al[c] = i4{corr, corr, corr, corr};
       }
+      static_assert(NC == 4, "query operand layout: 4 chains per 16-byte LDS read");
   #pragma unroll
-      for (int n = 0; n < PER; ++n)
+      for (int n = 0; n < PER; ++n) {
+        // the query operands stay in LDS (registers go to deeper chunk prefetch)
+        const uint4 qhv = *reinterpret_cast<const uint4*>(&sm.qh[j][4 * n]);
+        const uint4 qlv = *reinterpret_cast<const uint4*>(&sm.ql[j][4 * n]);
+        const int qhc[4] = {(int)qhv.x, (int)qhv.y, (int)qhv.z, (int)qhv.w};
+        const int qlc[4] = {(int)qlv.x, (int)qlv.y, (int)qlv.z, (int)qlv.w};
   #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const int av = KFmt<KF>::a_op(R.krow, c * PER + n);
-          ah[c] = __builtin_amdgcn_mfma_i32_4x4x4i8(av, (int)qh[c * PER + n], ah[c], 0, 0, 0);
-          al[c] = __builtin_amdgcn_mfma_i32_4x4x4i8(av, (int)ql[c * PER + n], al[c], 0, 0, 0);
+          ah[c] = __builtin_amdgcn_mfma_i32_4x4x4i8(av, qhc[c], ah[c], 0, 0, 0);
+          al[c] = __builtin_amdgcn_mfma_i32_4x4x4i8(av, qlc[c], al[c], 0, 0, 0);
         }
+      }
       i4 acc[NG];
   #pragma unroll
       for (int g = 0; g < NG; ++g)
@@ -901,8 +927,8 @@ __global__ __launch_bounds__(NT, 2) void decode_split(DecodeArgs a) {
   };
 
   // ---------------------------------------------------------------- software-pipelined walk
-  // Chunks c0+wv, c0+wv+4, ...: the loads of the next chunk are in flight while
-  // the current one is computed (two register sets used alternately).
+  // The loads of the next chunk are in flight while the current one is computed
+  // (two register sets used alternately).
   auto is_flagged = [&](int ch) -> bool {
     if constexpr (CERT) return a.flags != nullptr && a.flags[stream * a.nt + ch] != 0;
     return false;
@@ -921,22 +947,32 @@ __global__ __launch_bounds__(NT, 2) void decode_split(DecodeArgs a) {
       quant_chunk(R, ch, ev_c);
     }
   };
-  // Pairs of chunks, then an odd last one: the loop has a single exit, so the
-  // loads in flight at its head are the same on entry and on every iteration.
-  const int n_my = c1 > ch ? (c1 - ch + 3) / 4 : 0;
-  for (int k = 0; k + 1 < n_my; k += 2) {
-    load_chunk<KF, KG, VF, VG>(a, stream, ch + 4, lane, tok_a, RB);
+  // Every iteration issues the same claims and loads (a load past the stream's
+  // last chunk reloads the current, valid chunk), so the number of memory
+  // operations in flight at the loop head is the same on entry and on every
+  // iteration; the wave leaves as soon as a claimed index is past the end.
+  // (claims only grow, so once one is past the end the next is too: the loop
+  // leaves at its head, its single exit.)
+  while (cA < c1) {
+    const int cB = c0 + __builtin_amdgcn_readfirstlane(pB);
+    const int pC = claim();
+    load_chunk<KF, KG, VF, VG>(a, stream, cB < c1 ? cB : cA, lane, tok_a, RB);
     __builtin_amdgcn_sched_barrier(0);
-    visit(RA, ch, is_flagged(ch));
-    const int nx2 = ch + 8;
-    load_chunk<KF, KG, VF, VG>(a, stream, nx2 < c1 ? nx2 : ch, lane, tok_a, RA);
+    visit(RA, cA, is_flagged(cA));
+    // read the claim only after this chunk's work (an empty asm that takes the register
+    // keeps the read, and the wait for the atomic, from being hoisted above the work)
+    int pCv = pC;
+    asm volatile("" : "+v"(pCv));
+    const int cC = c0 + __builtin_amdgcn_readfirstlane(pCv);
+    pB = claim();
+    load_chunk<KF, KG, VF, VG>(a, stream, cC < c1 ? cC : cA, lane, tok_a, RA);
     __builtin_amdgcn_sched_barrier(0);
-    visit(RB, ch + 4, is_flagged(ch + 4));
-    ch = nx2;
+    if (cB < c1) visit(RB, cB, is_flagged(cB));
+    asm volatile("" : "+v"(pB));
+    cA = cC;
   }
-  if (n_my & 1) visit(RA, ch, is_flagged(ch));
 
-  // ---------------- per-wave totals, then merge the 4 waves in LDS
+  // ---------------- per-wave totals, then merge the waves in LDS
   const float lt = sum_same_head(lsum);
   const float et = CERT ? sum_same_head(eta) : 0.0f;
   if (lane < 4) {
@@ -960,7 +996,7 @@ __global__ __launch_bounds__(NT, 2) void decode_split(DecodeArgs a) {
     }
   }
   __syncthreads();
-  write_record<CERT>(a, sm, b, hq0, nh, split);
+  write_record<CERT, NWS>(a, sm, b, hq0, nh, split);
 }
 
 // ------------------------------------------------------------------ dense fp16 baseline
@@ -1075,7 +1111,7 @@ __global__ __launch_bounds__(NT, 2) void decode_dense_split(DecodeArgs a) {
     sm.mrg_o[wv][hh][2 * lane + 1] = o[1][hh];
   }
   __syncthreads();
-  write_record<false>(a, sm, b, hq0, nh, split);
+  write_record<false, 4>(a, sm, b, hq0, nh, split);
 }
 
 }  // namespace
@@ -1093,10 +1129,10 @@ hipError_t launch_decode(const DecodeArgs& a, int k_fmt, int v_fmt, bool dense, 
 #define KVQ_LAUNCH(KF, KG, VF, VG)                                                            \
   if (k_fmt == KF && a.k_group == KG && v_fmt == VF && a.v_group == VG) {                     \
     if (cert) {                                                                               \
-      hipLaunchKernelGGL((decode_split<KF, KG, VF, VG, true>), grid, dim3(NT), 0, s, a);      \
+      hipLaunchKernelGGL((decode_split<KF, KG, VF, VG, true>), grid, dim3(NTS), 0, s, a);     \
       hipLaunchKernelGGL(combine_kernel<true>, cgrid, dim3(NT), 0, s, a);                     \
     } else {                                                                                  \
-      hipLaunchKernelGGL((decode_split<KF, KG, VF, VG, false>), grid, dim3(NT), 0, s, a);     \
+      hipLaunchKernelGGL((decode_split<KF, KG, VF, VG, false>), grid, dim3(NTS), 0, s, a);    \
       hipLaunchKernelGGL(combine_kernel<false>, cgrid, dim3(NT), 0, s, a);                    \
     }                                                                                         \
     return hipGetLastError();                                                                 \

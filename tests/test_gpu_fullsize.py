@@ -88,7 +88,8 @@ def test_c2_gqa_int4_bench_shape():
     ws = kvq.workspace(p)
     out = kvq.decode_attn(p, gcache, dev_bits(q), [T] * B, ws=ws)
     torch.cuda.synchronize()
-    assert kvq.decode_splits(p, [T] * B) == 4
+    # the launch configuration bench.py times: 2 splits x 8 kv heads x 16 sequences = 256 workgroups
+    assert kvq.decode_splits(p, [T] * B) == 2
     _log("c2: bytes of sampled streams")
     for b, h in ((0, 0), (5, 3), (10, 7), (15, 4)):
         _stream_bytes_match(c, gcache, k[b, h], v[b, h], b, h, s, r16)
