@@ -277,7 +277,7 @@ def bench_workload(cfg_id, args):
                    "prefill_tokens": P, "formats": fmt, "rotation": c["rotation"], "input": c["dtype"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_split + combine_kernel" + (" + bound_kernel" if c["keep"] else ""),
+                     "kernel": "decode_split (splits merged by their last workgroup)" + (" + bound_kernel" if c["keep"] else ""),
                      "bytes_per_call": packed + io},
         "decode_us": round(dec_s * 1e6, 2),
         "decode_grid": [kvq.decode_splits(p, seq), H * ((Hq // H + 3) // 4), B],
@@ -458,7 +458,7 @@ def main():
                    "rotation": "sign+fwht"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_split<int4 g32, int4 g32> + combine_kernel (one kvq_decode_attn call)",
+                     "kernel": "decode_split<int4 g32, int4 g32> (one kvq_decode_attn call: one launch, splits merged by their last workgroup)",
                      "bytes_per_call": kv_bytes + io_bytes},
         "decode_us": round(dec_s * 1e6, 2),
         "decode_pct_hbm_peak": round(100 * dec_gbs / HBM_PEAK_GBS, 2),

@@ -190,10 +190,10 @@ def error_bound(p, cache, q, seq_len, tau, bound=None, flags=None, stream=None):
 
 
 def workspace(p, device="cuda"):
-    """A decode workspace (split records; its contents on entry do not matter)."""
+    """A decode workspace: split arrival counters (zero between calls) and split records."""
     import torch
     n = decode_workspace_bytes(p)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def decode_attn(p, cache, q, seq_len, flags=None, certificate=False, ws=None, out=None, cert=None, stream=None):

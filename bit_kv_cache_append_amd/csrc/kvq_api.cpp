@@ -163,9 +163,17 @@ int32_t kvq_decode_splits(const kvq_params* p, const int32_t* seq_len_host) {
   return choose_splits(p, max_chunks > 0 ? max_chunks : 1);
 }
 
+// workspace: [arrival counters, one int32 per (sequence, kv head, group of 4 query heads),
+// padded to 256 bytes][split records]
+static size_t ctr_bytes(const kvq_params* p) {
+  const int G = p->n_q_heads / p->n_kv_heads;
+  const size_t n = (size_t)p->batch * p->n_kv_heads * ((G + 3) / 4);
+  return (n * sizeof(int32_t) + 255) & ~(size_t)255;
+}
+
 size_t kvq_decode_workspace_bytes(const kvq_params* p) {
   if (check_params(p)) return 0;
-  return (size_t)p->batch * p->n_q_heads * max_splits_for(p) * PART_FLOATS * sizeof(float);
+  return ctr_bytes(p) + (size_t)p->batch * p->n_q_heads * max_splits_for(p) * PART_FLOATS * sizeof(float);
 }
 
 kvq_status kvq_append(const kvq_params* p, const kvq_cache* c, const void* k_new, const void* v_new,
@@ -316,7 +324,8 @@ static kvq_status decode_common(const kvq_params* p, const kvq_cache* c, const v
     a.signs = c->signs;
     a.rot = c->rot_f16;
   }
-  a.part = (float*)ws;
+  a.ctr = (int*)ws;
+  a.part = (float*)((char*)ws + ctr_bytes(p));
   a.out = out;
   a.cert = dense ? nullptr : cert;
   a.B = p->batch;

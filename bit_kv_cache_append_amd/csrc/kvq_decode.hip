@@ -1,8 +1,9 @@
 // Read side: single-token decode attention over the packed cache.
 //
-// Split kernel: one workgroup (4 waves) per (context split, kv head, group of 4
-// query heads, sequence).  Each wave walks 64-token chunks of its split (the
-// chunk is also the V tile and the descriptor block).  Per chunk:
+// Split kernel: one workgroup (8 waves, one workgroup per CU) per (context
+// split, kv head, group of 4 query heads, sequence).  The waves share out the
+// 64-token chunks of the split through a counter in LDS (the chunk is also the
+// V tile and the descriptor block).  Per chunk:
 //
 //  QK^T  -- 4x4x4 (16-block) int8 MFMA.  Lane 4s+r loads the packed K row of
 //           token pi(s, r); the query is rotated once, prescaled by
@@ -27,8 +28,11 @@
 // Methodology sections 1 and 3) into a separate accumulator; the value-error
 // mass sum p * ev and the descriptor maxima are tracked for the certificate.
 //
-// Combine kernel: log-sum-exp merge of the splits, inverse rotation back to the
-// original basis ("OSCAR", section 2.2B), certificate.
+// Merge: log-sum-exp merge of the splits, inverse rotation back to the original
+// basis ("OSCAR", section 2.2B), certificate; done by the last split workgroup of
+// each (sequence, kv head, query-head group) to finish, found with an arrival
+// counter, on records written and read with agent-coherent accesses.  The fp16
+// baseline uses a separate combine launch for the same merge.
 
 #include "kvq_common.h"
 
@@ -228,6 +232,7 @@ struct __align__(16) DecodeSmem {
   float mrg_o[NWS][4][D];    // per wave, head, channel
   float mrg_oo[NWS][4][D];
   int next;                  // next chunk (offset from the split's first) to claim
+  int last;                  // this workgroup is the last of its stream to finish
 };
 
 // ------------------------------------------------------------------ prologue
@@ -359,10 +364,25 @@ __device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryI
   __syncthreads();
 }
 
+// ------------------------------------------------------------------ coherent record access
+// Split records read by the last workgroup of a stream (on any XCD) are written and
+// read with agent-scope atomic accesses, which the hardware keeps coherent across
+// the L2s of all XCDs; plain accesses when a separate launch does the merge.
+template <bool COH>
+__device__ __forceinline__ void rec_st(float* p, float v) {
+  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+template <bool COH>
+__device__ __forceinline__ float rec_ld(const float* p) {
+  if constexpr (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
+}
+
 // ------------------------------------------------------------------ split record
 // Merges the NW waves of this workgroup (in LDS, log-sum-exp weights) and writes
 // the record of (sequence, query head, split) for the combine kernel.
-template <bool CERT, int NW>
+template <bool CERT, int NW, bool COH>
 __device__ void write_record(const DecodeArgs& a, DecodeSmem& sm, int b, int hq0, int nh, int split) {
   const int t = threadIdx.x, hh = t >> 6, l = t & 63, c = 2 * l;
   if (hh >= nh) return;
@@ -383,8 +403,12 @@ __device__ void write_record(const DecodeArgs& a, DecodeSmem& sm, int b, int hq0
       p1 += wgt[w] * sm.mrg_oo[w][hh][c + 1];
     }
   }
-  *reinterpret_cast<float2*>(rec + 8 + c) = make_float2(o0, o1);
-  if constexpr (CERT) *reinterpret_cast<float2*>(rec + 8 + D + c) = make_float2(p0, p1);
+  rec_st<COH>(rec + 8 + c, o0);
+  rec_st<COH>(rec + 8 + c + 1, o1);
+  if constexpr (CERT) {
+    rec_st<COH>(rec + 8 + D + c, p0);
+    rec_st<COH>(rec + 8 + D + c + 1, p1);
+  }
   float qn = 0.0f;
   if constexpr (CERT) {
     // ||q|| * scale from the prologue's q * scale * log2(e)
@@ -402,21 +426,19 @@ __device__ void write_record(const DecodeArgs& a, DecodeSmem& sm, int b, int hq0
       ek = fmaxf(ek, sm.mrg_ek[w]);
       vn = fmaxf(vn, sm.mrg_vn[w]);
     }
-    *reinterpret_cast<float4*>(rec) = make_float4(M, L, E, ek);
-    *reinterpret_cast<float4*>(rec + 4) = make_float4(vn, qn, 0.0f, 0.0f);
+    const float hdr[6] = {M, L, E, ek, vn, qn};
+#pragma unroll
+    for (int i = 0; i < 6; ++i) rec_st<COH>(rec + i, hdr[i]);
   }
 }
 
-// ------------------------------------------------------------------ combine kernel
+// ------------------------------------------------------------------ combine
 // One wave per (sequence, query head): log-sum-exp merge of the split records,
 // inverse rotation back to the original basis ("OSCAR", section 2.2B), and the
-// certificate.  A separate launch on the same stream orders it after every split.
-template <bool CERT>
-__global__ __launch_bounds__(NT) void combine_kernel(DecodeArgs a) {
-  __shared__ float zs[4][D];
-  const int t = threadIdx.x, w = t >> 6, l = t & 63, c = 2 * l;
-  const int row = blockIdx.x * 4 + w;
-  if (row >= a.B * a.Hq) return;  // whole waves; no barrier below
+// certificate.  zsw: 128 floats of LDS private to the wave.
+template <bool CERT, bool COH>
+__device__ void combine_row(const DecodeArgs& a, int row, float* zsw) {
+  const int l = threadIdx.x & 63, c = 2 * l;
   const int b = row / a.Hq;
   float* out = a.out + (size_t)row * D;
   if (a.seq.v[b] == 0) {
@@ -437,10 +459,17 @@ __global__ __launch_bounds__(NT) void combine_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < SB; ++i) {
       const float* rec = rec0 + (size_t)min(s0 + i, a.n_splits - 1) * PART_FLOATS;
-      hd[i] = *reinterpret_cast<const float4*>(rec);
-      vs[i] = rec[4];
-      ov[i] = *reinterpret_cast<const float2*>(rec + 8 + c);
-      if constexpr (CERT) pv[i] = *reinterpret_cast<const float2*>(rec + 8 + D + c);
+      if constexpr (COH) {
+        hd[i] = make_float4(rec_ld<true>(rec), rec_ld<true>(rec + 1), rec_ld<true>(rec + 2), rec_ld<true>(rec + 3));
+        vs[i] = rec_ld<true>(rec + 4);
+        ov[i] = make_float2(rec_ld<true>(rec + 8 + c), rec_ld<true>(rec + 8 + c + 1));
+        if constexpr (CERT) pv[i] = make_float2(rec_ld<true>(rec + 8 + D + c), rec_ld<true>(rec + 8 + D + c + 1));
+      } else {
+        hd[i] = *reinterpret_cast<const float4*>(rec);
+        vs[i] = rec[4];
+        ov[i] = *reinterpret_cast<const float2*>(rec + 8 + c);
+        if constexpr (CERT) pv[i] = *reinterpret_cast<const float2*>(rec + 8 + D + c);
+      }
     }
     float Mb = M;
 #pragma unroll
@@ -490,13 +519,13 @@ __global__ __launch_bounds__(NT) void combine_kernel(DecodeArgs a) {
     r0 *= a.signs[c] < 0 ? -cn : cn;
     r1 *= a.signs[c + 1] < 0 ? -cn : cn;
   } else if (a.rotation == KVQ_ROT_DENSE) {
-    zs[w][c] = o0;
-    zs[w][c + 1] = o1;
+    zsw[c] = o0;
+    zsw[c + 1] = o1;
     __builtin_amdgcn_wave_barrier();
     lds_wait();
     float acc0 = 0.0f, acc1 = 0.0f;
     for (int k = 0; k < D; ++k) {
-      const float z = zs[w][k];
+      const float z = zsw[k];
       const uint32_t rr = *reinterpret_cast<const uint32_t*>(a.rot + (size_t)k * D + c);
       acc0 = fmaf(f16_bits_to_f32((uint16_t)(rr & 0xFFFF)), z, acc0);
       acc1 = fmaf(f16_bits_to_f32((uint16_t)(rr >> 16)), z, acc1);
@@ -510,9 +539,20 @@ __global__ __launch_bounds__(NT) void combine_kernel(DecodeArgs a) {
   }
   *reinterpret_cast<float2*>(out + c) = make_float2(r0, r1);
   if (CERT && a.cert && l == 0) {
-    const float dstar = rec0[5] * ek;
+    const float dstar = rec_ld<COH>(rec0 + 5) * ek;
     a.cert[row] = 2.0f * (1.0f - expf(-2.0f * dstar)) * vn + E * inv;
   }
+}
+
+// The separate combine launch (fp16 baseline path): one wave per row, ordered
+// after every split workgroup by the stream.
+template <bool CERT>
+__global__ __launch_bounds__(NT) void combine_kernel(DecodeArgs a) {
+  __shared__ float zs[4][D];
+  const int w = threadIdx.x >> 6;
+  const int row = blockIdx.x * 4 + w;
+  if (row >= a.B * a.Hq) return;  // whole waves; no barrier in combine_row
+  combine_row<CERT, false>(a, row, zs[w]);
 }
 
 // ------------------------------------------------------------------ split kernel
@@ -996,7 +1036,26 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
     }
   }
   __syncthreads();
-  write_record<CERT, NWS>(a, sm, b, hq0, nh, split);
+  write_record<CERT, NWS, true>(a, sm, b, hq0, nh, split);
+
+  // ---------------- the last workgroup of the stream to finish merges its splits
+  // The records are agent-coherent atomic stores; every thread waits for its own
+  // stores to complete before the barrier, so they are performed before the
+  // arrival is counted.  The last arrival reads every split's record with
+  // agent-coherent loads.  (No cache write-back or invalidate is needed: only
+  // the records cross workgroups, and they never sit in a non-coherent cache.)
+  const int sidx = blockIdx.z * gridDim.y + blockIdx.y;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (t == 0) {
+    const int prev = __hip_atomic_fetch_add(a.ctr + sidx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.last = prev == a.n_splits - 1;
+  }
+  __syncthreads();
+  if (sm.last) {
+    if (wv < nh) combine_row<CERT, true>(a, b * a.Hq + hq0 + wv, &sm.qf[wv][0]);
+    if (t == 0) __hip_atomic_store(a.ctr + sidx, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // ------------------------------------------------------------------ dense fp16 baseline
@@ -1111,7 +1170,7 @@ __global__ __launch_bounds__(NT, 2) void decode_dense_split(DecodeArgs a) {
     sm.mrg_o[wv][hh][2 * lane + 1] = o[1][hh];
   }
   __syncthreads();
-  write_record<false, 4>(a, sm, b, hq0, nh, split);
+  write_record<false, 4, false>(a, sm, b, hq0, nh, split);
 }
 
 }  // namespace
@@ -1128,13 +1187,10 @@ hipError_t launch_decode(const DecodeArgs& a, int k_fmt, int v_fmt, bool dense, 
   const bool cert = a.desc != nullptr;
 #define KVQ_LAUNCH(KF, KG, VF, VG)                                                            \
   if (k_fmt == KF && a.k_group == KG && v_fmt == VF && a.v_group == VG) {                     \
-    if (cert) {                                                                               \
+    if (cert)                                                                                 \
       hipLaunchKernelGGL((decode_split<KF, KG, VF, VG, true>), grid, dim3(NTS), 0, s, a);     \
-      hipLaunchKernelGGL(combine_kernel<true>, cgrid, dim3(NT), 0, s, a);                     \
-    } else {                                                                                  \
+    else                                                                                      \
       hipLaunchKernelGGL((decode_split<KF, KG, VF, VG, false>), grid, dim3(NTS), 0, s, a);    \
-      hipLaunchKernelGGL(combine_kernel<false>, cgrid, dim3(NT), 0, s, a);                    \
-    }                                                                                         \
     return hipGetLastError();                                                                 \
   }
   KVQ_LAUNCH(KVQ_INT4, 32, KVQ_INT4, 32)

@@ -92,6 +92,7 @@ struct DecodeArgs {
   const int8_t* signs;
   const uint16_t* rot;
   float* part;              // [B][Hq][n_splits][PART_FLOATS]
+  int* ctr;                 // [B][Hkv * head groups] split arrival counters, zero between calls
   float* out;               // [B][Hq][128]
   float* cert;              // [B][Hq] or null
   int32_t B, Hq, H, G, Tmax, nt;

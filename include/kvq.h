@@ -168,10 +168,15 @@ kvq_status kvq_buffer_bytes(const kvq_params* p, size_t* out_bytes);
 
 /* Workspace bytes kvq_decode_attn / kvq_decode_attn_dense need for these params
  * (depends on batch, heads and max_ctx only).  Host only; 0 on invalid params.
- * The workspace holds one partial-result record per (sequence, query head,
- * context split); every call writes all records it reads, so its initial
- * contents do not matter.  Calls that share one workspace must not overlap
- * (order them on one stream). */
+ * The workspace holds one arrival counter per (sequence, kv head, group of 4
+ * query heads), through which the last split workgroup of a sequence learns that
+ * it is last and merges the others' results, and one partial-result record per
+ * (sequence, query head, context split).  It must be zero-filled before its
+ * first use; every call leaves the counters zero again (the records' contents
+ * do not matter), so one workspace serves call after call.  Calls that share a
+ * workspace must not overlap (order them on one stream).  The split workgroups
+ * share out 64-token chunks at run time, so the fp32 summation order, and with
+ * it the last bits of the output, can differ from call to call. */
 size_t kvq_decode_workspace_bytes(const kvq_params* p);
 
 /* Number of context splits kvq_decode_attn uses for these params and sequence
@@ -212,8 +217,8 @@ kvq_status kvq_error_bound(const kvq_params* p, const kvq_cache* cache, const vo
  *     seq_len 0 are written as zeros.
  *   certificate: device fp32 [B][Hq] or NULL (needs keep_fp16_copy): an upper bound
  *     on ||out - dense attention over the originals||_2 for that row.
- *   workspace: device, >= kvq_decode_workspace_bytes(p) bytes, 256-byte aligned
- *     (scratch for the split records; any contents).
+ *   workspace: device, >= kvq_decode_workspace_bytes(p) bytes, 256-byte aligned,
+ *     zero-filled before its first use (see kvq_decode_workspace_bytes).
  * Attention output differs from exact fp64 attention over the decoded cache by
  * fp16 rounding of the query/probabilities and fp32 accumulation only.
  */
