@@ -154,3 +154,29 @@ def test_certified_decode(certified, mode):
     if mode == "all":
         assert not E.any()
         assert attention.row_rel_err(got, dense).max() <= TOL
+
+
+@pytest.mark.parametrize("B,T", [(1, 16384), (2, 8192)])
+def test_split_merge_repeatable(B, T):
+    """Many splits, many calls on one workspace, alternating between two queries: the last
+    split workgroup must see every other split's record of *this* call (a record left from
+    the previous call, made with the other query, would show as a gross error) and must
+    leave the arrival counters at zero (the next call merges again).  Chunks are shared out
+    at run time, so calls differ at the level of the fp16 probabilities, within the bar."""
+    c = synth.config(2, B=B, T=T)
+    seq = [T] * B
+    print(f"[decode] merge repeatable B={B} T={T}", flush=True)
+    s, r16, p, gcache, k, v = _filled(c, seq)
+    qs = [synth.queries(c), synth.queries(synth.config(1, B=B, Hq=c["Hq"]))]
+    ws = kvq.workspace(p)
+    assert kvq.decode_splits(p, seq) >= 4
+    oc = oracle_view_of_gpu(c, gcache)
+    refs = [attention.decode_attention(oc, q, c["dtype"], np.array(seq), c["rotation"], s, r16)[0] for q in qs]
+    qd = [dev_bits(q) for q in qs]
+    outs = [torch.empty((B, c["Hq"], 128), dtype=torch.float32, device="cuda") for _ in range(100)]
+    for i in range(100):
+        kvq.decode_attn(p, gcache, qd[i % 2], seq, ws=ws, out=outs[i])
+    torch.cuda.synchronize()
+    worst = max(float(attention.row_rel_err(outs[i].cpu().numpy(), refs[i % 2]).max()) for i in range(100))
+    print(f"[decode] merge repeatable: worst row rel err over 100 alternating calls {worst:.2e}", flush=True)
+    assert worst <= TOL
