@@ -54,6 +54,8 @@ CASES = {
     "c5-fp4-search-bf16": (synth.config(5, B=2, T=1024), [1024, 701]),
     "fp4-absmax-f16-ragged": (synth.config(5, B=3, Hq=8, Hkv=2, T=512, dtype="f16", scale_mode="absmax"), [512, 129, 1]),
     "fp4-offsets-search": (synth.config(5, B=2, Hq=8, Hkv=2, T=512, scale_mode="offsets"), [512, 300]),
+    "gqa8-two-head-groups": (synth.config(2, B=2, Hq=16, Hkv=2, T=640), [640, 513]),
+    "gqa6-partial-group-bf16": (synth.config(2, B=1, Hq=12, Hkv=2, T=384, dtype="bf16"), [384]),
 }
 
 
