@@ -20,7 +20,7 @@ F16, BF16 = 0, 1
 INT4, INT8, INT2, FP4 = 0, 1, 2, 3
 ROT_NONE, ROT_SIGN_FWHT, ROT_DENSE = 0, 1, 2
 SCALE_ABSMAX, SCALE_SEARCH9, SCALE_SEARCH_OFFSETS = 0, 1, 2
-BUF_NAMES = ("k_codes", "k_meta", "v_codes", "v_meta", "blk_desc", "k_orig", "v_orig")
+BUF_NAMES = ("k_codes", "k_meta", "v_codes", "v_meta", "blk_desc", "k_orig", "v_orig", "k_win", "v_win")
 
 _FMT = {"int4": INT4, "int8": INT8, "int2": INT2, "fp4": FP4}
 _ROT = {"none": ROT_NONE, "sign_fwht": ROT_SIGN_FWHT, "dense": ROT_DENSE}
@@ -41,12 +41,14 @@ class Params(ctypes.Structure):
         ("k_fmt", ctypes.c_int32), ("v_fmt", ctypes.c_int32), ("k_group", ctypes.c_int32),
         ("v_group", ctypes.c_int32), ("scale_mode", ctypes.c_int32), ("rotation", ctypes.c_int32),
         ("keep_fp16_copy", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("sink_blocks", ctypes.c_int32), ("recent_blocks", ctypes.c_int32),
     ]
 
 
 class CacheStruct(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("k_codes", "k_meta", "v_codes", "v_meta", "blk_desc",
-                                               "k_orig", "v_orig", "signs", "rot_f16", "clip_k", "clip_v")]
+                                               "k_orig", "v_orig", "signs", "rot_f16", "clip_k", "clip_v",
+                                               "k_win", "v_win")]
 
 
 _lib = None
@@ -91,26 +93,28 @@ def _check(status):
 
 
 def make_params(B, Hq, Hkv, max_ctx, k_fmt="int4", v_fmt="int4", k_group=32, v_group=32, dtype="f16",
-                scale_mode="absmax", rotation="sign_fwht", keep_fp16_copy=False, softmax_scale=0.0):
+                scale_mode="absmax", rotation="sign_fwht", keep_fp16_copy=False, softmax_scale=0.0,
+                sink_blocks=0, recent_blocks=0):
     """Build the C params struct (format names as strings or the integer constants)."""
     def enum(v, table):
         return table[v] if isinstance(v, str) else int(v)
     return Params(B, Hq, Hkv, 128, max_ctx, enum(dtype, _DT), enum(k_fmt, _FMT), enum(v_fmt, _FMT), k_group,
                   v_group, enum(scale_mode, _SM), enum(rotation, _ROT), int(bool(keep_fp16_copy)),
-                  float(softmax_scale))
+                  float(softmax_scale), int(sink_blocks), int(recent_blocks))
 
 
 def params_from_config(c, **over):
     """Params for a workload dict of the synth module (shape and format fields only)."""
     d = dict(B=c["B"], Hq=c["Hq"], Hkv=c["Hkv"], max_ctx=c["T"], k_fmt=c["k_fmt"], v_fmt=c["v_fmt"],
              k_group=c["k_group"], v_group=c["v_group"], dtype=c["dtype"], scale_mode=c["scale_mode"],
-             rotation=c["rotation"], keep_fp16_copy=c["keep"])
+             rotation=c["rotation"], keep_fp16_copy=c["keep"], sink_blocks=c.get("sink_blocks", 0),
+             recent_blocks=c.get("recent_blocks", 0))
     d.update(over)
     return make_params(**d)
 
 
 def buffer_bytes(p):
-    out = (ctypes.c_size_t * 7)()
+    out = (ctypes.c_size_t * len(BUF_NAMES))()
     _check(lib().kvq_buffer_bytes(ctypes.byref(p), out))
     return {n: int(out[i]) for i, n in enumerate(BUF_NAMES)}
 
@@ -160,11 +164,9 @@ class Cache:
 
     def struct(self):
         b = self.bufs
-        return CacheStruct(*[None if b[n] is None else b[n].data_ptr() for n in BUF_NAMES],
-                           None if self.signs is None else self.signs.data_ptr(),
-                           None if self.rot_f16 is None else self.rot_f16.data_ptr(),
-                           None if self.clip_k is None else self.clip_k.data_ptr(),
-                           None if self.clip_v is None else self.clip_v.data_ptr())
+        ptr = lambda t: None if t is None else t.data_ptr()
+        return CacheStruct(*[ptr(b[n]) for n in BUF_NAMES[:7]], ptr(self.signs), ptr(self.rot_f16),
+                           ptr(self.clip_k), ptr(self.clip_v), ptr(b["k_win"]), ptr(b["v_win"]))
 
 
 def append(p, cache, k_new, v_new, start_pos, stream=None):

@@ -55,6 +55,9 @@ kvq_status check_params(const kvq_params* p) {
   if (p->rotation != KVQ_ROT_NONE && p->rotation != KVQ_ROT_SIGN_FWHT && p->rotation != KVQ_ROT_DENSE)
     return fail(KVQ_ERR_INVALID_ARG, "bad rotation");
   if (!(p->softmax_scale >= 0.0f) || isinf(p->softmax_scale)) return fail(KVQ_ERR_INVALID_ARG, "bad softmax_scale");
+  if (p->sink_blocks < 0 || p->recent_blocks < 0 || (long)p->sink_blocks + p->recent_blocks > p->max_ctx / TILE)
+    return fail(KVQ_ERR_INVALID_ARG, "sink_blocks (%d) and recent_blocks (%d) must be >= 0 with sum <= max_ctx / 64",
+                p->sink_blocks, p->recent_blocks);
   return KVQ_OK;
 }
 
@@ -75,6 +78,9 @@ kvq_status check_cache(const kvq_params* p, const kvq_cache* c, bool need_desc) 
   } else if (need_desc) {
     return fail(KVQ_ERR_INVALID_ARG, "this call needs keep_fp16_copy");
   }
+  if (p->sink_blocks + p->recent_blocks > 0 &&
+      (!c->k_win || !c->v_win || !aligned16(c->k_win) || !aligned16(c->v_win)))
+    return fail(KVQ_ERR_INVALID_ARG, "a window (sink_blocks + recent_blocks > 0) needs k_win and v_win, 16-byte aligned");
   return KVQ_OK;
 }
 
@@ -148,6 +154,9 @@ kvq_status kvq_buffer_bytes(const kvq_params* p, size_t* out) {
   out[KVQ_BUF_BLK_DESC] = keep ? streams * nt * 3 * sizeof(float) : 0;
   out[KVQ_BUF_K_ORIG] = keep ? streams * T * D * 2 : 0;
   out[KVQ_BUF_V_ORIG] = keep ? streams * T * D * 2 : 0;
+  const size_t win = (size_t)(p->sink_blocks + p->recent_blocks) * TILE;
+  out[KVQ_BUF_K_WIN] = streams * win * D * 2;
+  out[KVQ_BUF_V_WIN] = streams * win * D * 2;
   return KVQ_OK;
 }
 
@@ -226,6 +235,14 @@ kvq_status kvq_append(const kvq_params* p, const kvq_cache* c, const void* k_new
   a.rotation = p->rotation;
   hipError_t e = launch_append(a, max_tiles, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "append launch");
+  if (p->sink_blocks + p->recent_blocks > 0) {
+    a.k_win = (uint16_t*)c->k_win;
+    a.v_win = (uint16_t*)c->v_win;
+    a.n_sink = p->sink_blocks;
+    a.n_recent = p->recent_blocks;
+    e = launch_window_copy(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "window copy launch");
+  }
   return KVQ_OK;
 }
 
@@ -317,10 +334,18 @@ static kvq_status decode_common(const kvq_params* p, const kvq_cache* c, const v
     a.k_meta = (const uint8_t*)c->k_meta;
     a.v_codes = (const uint8_t*)c->v_codes;
     a.v_meta = (const uint8_t*)c->v_meta;
-    a.desc = c->blk_desc;
-    a.k_orig = (const uint16_t*)c->k_orig;
-    a.v_orig = (const uint16_t*)c->v_orig;
+    if (p->keep_fp16_copy) {
+      a.desc = c->blk_desc;
+      a.k_orig = (const uint16_t*)c->k_orig;
+      a.v_orig = (const uint16_t*)c->v_orig;
+    }
     a.flags = flags;
+    if (p->sink_blocks + p->recent_blocks > 0) {
+      a.k_win = (const uint16_t*)c->k_win;
+      a.v_win = (const uint16_t*)c->v_win;
+      a.n_sink = p->sink_blocks;
+      a.n_recent = p->recent_blocks;
+    }
     a.signs = c->signs;
     a.rot = c->rot_f16;
   }

@@ -1332,6 +1332,38 @@ hipError_t launch_append(const AppendArgs& a, int grid_x, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- full-precision window
+// Copies the originals of the window blocks this append reaches ("OSCAR", section
+// 2.2B, mixed-precision layout: sink and recent tokens kept at full precision).
+// Workgroup w < n_sink takes sink block w; workgroup n_sink + i takes block
+// jlast - i, the i-th newest block of the call (skipped if it is a sink block), so
+// the ring slots written by one call are distinct.  Rows are 256-byte copies.
+__global__ __launch_bounds__(NT) void window_copy_kernel(AppendArgs a) {
+  const int b = blockIdx.z >> 1, h = blockIdx.y, tensor = blockIdx.z & 1;
+  const int start = a.start.v[b], end = start + a.n_new;
+  const int w = blockIdx.x;
+  const int jlast = (end - 1) / TILE;
+  int j = w;
+  if (w >= a.n_sink) {
+    j = jlast - (w - a.n_sink);
+    if (j < a.n_sink) return;  // a sink block, or before position 0
+  }
+  const int lo = max(start, j * TILE), hi = min(end, j * TILE + TILE);
+  if (lo >= hi) return;  // uniform over the workgroup
+  const int slot = j < a.n_sink ? j : a.n_sink + j % a.n_recent;
+  const size_t stream = (size_t)b * a.H + h;
+  const uint4* src = reinterpret_cast<const uint4*>((tensor ? a.v_new : a.k_new) + (stream * a.n_new + (lo - start)) * D);
+  uint4* dst = reinterpret_cast<uint4*>((tensor ? a.v_win : a.k_win) +
+                                        ((stream * (a.n_sink + a.n_recent) + slot) * TILE + (lo - j * TILE)) * D);
+  const int n16 = (hi - lo) * (D * 2 / 16);
+  for (int i = threadIdx.x; i < n16; i += NT) dst[i] = src[i];
+}
+
+hipError_t launch_window_copy(const AppendArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(window_copy_kernel, dim3(a.n_sink + a.n_recent, a.H, 2 * a.B), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- clip calibration
 // t[h][c] = fl32(ratio * max_t |y_t,c|): one workgroup per kv head, 64 tokens per step.
 __global__ __launch_bounds__(NT) void calibrate_kernel(CalibArgs a) {

@@ -908,13 +908,27 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   };
 
   // ---------------------------------------------------------------- one exactly recomputed chunk
+  // Window blocks: the first n_sink and the last n_recent blocks of the sequence,
+  // kept at full precision in k_win/v_win ("OSCAR", section 2.2B, mixed-precision
+  // layout).  They are attended exactly, like blocks flagged by the error bound.
+  auto in_window = [&](int ch) -> bool {
+    return a.k_win != nullptr && (ch < a.n_sink || ch >= nchunks - a.n_recent);
+  };
+  // first row of chunk ch's originals: its window slot, else the full copy
+  auto orig_rows = [&](const uint16_t* full, const uint16_t* win, int ch) -> const uint16_t* {
+    if (in_window(ch)) {
+      const int slot = ch < a.n_sink ? ch : a.n_sink + ch % a.n_recent;
+      return win + (stream * (size_t)(a.n_sink + a.n_recent) + slot) * TILE * D;
+    }
+    return full + (stream * a.Tmax + (size_t)ch * TILE) * D;
+  };
   auto exact_chunk = [&](int ch) {
     const int tok0 = ch * TILE;
     const bool bf16 = a.in_bf16 != 0;
     const int tau = lane;
     const bool live = tok0 + tau < T;
     float lh[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    const uint4* kp = reinterpret_cast<const uint4*>(a.k_orig + (stream * a.Tmax + tok0 + tau) * D);
+    const uint4* kp = reinterpret_cast<const uint4*>(orig_rows(a.k_orig, a.k_win, ch) + (size_t)tau * D);
     for (int i = 0; i < 16; ++i) {
       const uint4 u = kp[i];
       const uint32_t ws[4] = {u.x, u.y, u.z, u.w};
@@ -955,7 +969,7 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
     }
     if constexpr (VF == KVQ_INT2) oz *= av;
     lds_wait();
-    const uint32_t* vp = reinterpret_cast<const uint32_t*>(a.v_orig + (stream * a.Tmax + tok0) * D) + lane;
+    const uint32_t* vp = reinterpret_cast<const uint32_t*>(orig_rows(a.v_orig, a.v_win, ch)) + lane;
     for (int tt = 0; tt < TILE; ++tt) {
       const uint32_t vv = vp[(size_t)tt * (D / 2)];
       const float v0 = widen((uint16_t)(vv & 0xFFFF), bf16), v1 = widen((uint16_t)(vv >> 16), bf16);
@@ -970,16 +984,18 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   // The loads of the next chunk are in flight while the current one is computed
   // (two register sets used alternately).
   auto is_flagged = [&](int ch) -> bool {
-    if constexpr (CERT) return a.flags != nullptr && a.flags[stream * a.nt + ch] != 0;
+    if constexpr (CERT) return in_window(ch) || (a.flags != nullptr && a.flags[stream * a.nt + ch] != 0);
     return false;
   };
   auto visit = [&](const ChunkRegs<KF, VF>& R, int ch, bool fl) {
     float ev_c = 0.0f;
     if constexpr (CERT) {
-      const float* dsc = a.desc + (stream * a.nt + ch) * 3;
-      ev_c = dsc[1];
-      vnmax = fmaxf(vnmax, dsc[2]);
-      if (!fl) ekmax = fmaxf(ekmax, dsc[0]);
+      if (a.desc != nullptr) {
+        const float* dsc = a.desc + (stream * a.nt + ch) * 3;
+        ev_c = dsc[1];
+        vnmax = fmaxf(vnmax, dsc[2]);
+        if (!fl) ekmax = fmaxf(ekmax, dsc[0]);
+      }
     }
     if (fl) {
       if constexpr (CERT) exact_chunk(ch);
@@ -1184,7 +1200,8 @@ hipError_t launch_decode(const DecodeArgs& a, int k_fmt, int v_fmt, bool dense, 
     hipLaunchKernelGGL(combine_kernel<false>, cgrid, dim3(NT), 0, s, a);
     return hipGetLastError();
   }
-  const bool cert = a.desc != nullptr;
+  // the exact-recompute instantiation serves the certified cache and the window
+  const bool cert = a.desc != nullptr || a.k_win != nullptr;
 #define KVQ_LAUNCH(KF, KG, VF, VG)                                                            \
   if (k_fmt == KF && a.k_group == KG && v_fmt == VF && a.v_group == VG) {                     \
     if (cert)                                                                                 \

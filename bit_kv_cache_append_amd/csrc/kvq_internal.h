@@ -45,9 +45,12 @@ struct AppendArgs {
   const uint16_t* rot;  // fp16 bits [128][128]
   const float* clip_k;
   const float* clip_v;
+  uint16_t* k_win;  // may be null
+  uint16_t* v_win;
   int32_t B, H, Tmax, n_new;
   int32_t in_bf16;
   int32_t k_fmt, v_fmt, k_group, v_group, scale_mode, rotation;
+  int32_t n_sink, n_recent;  // window blocks
   SeqArray start;
 };
 
@@ -89,6 +92,8 @@ struct DecodeArgs {
   const uint16_t* k_orig;
   const uint16_t* v_orig;
   const uint8_t* flags;  // [B][H][nt] or null
+  const uint16_t* k_win;  // [B][H][(n_sink + n_recent) * 64][128] or null
+  const uint16_t* v_win;
   const int8_t* signs;
   const uint16_t* rot;
   float* part;              // [B][Hq][n_splits][PART_FLOATS]
@@ -98,6 +103,7 @@ struct DecodeArgs {
   int32_t B, Hq, H, G, Tmax, nt;
   int32_t in_bf16, rotation, k_group, v_group;
   int32_t n_splits, chunks_per_split;
+  int32_t n_sink, n_recent;  // window blocks (0, 0 = none)
   float scale;  // softmax scale
   SeqArray seq;
 };
@@ -105,6 +111,7 @@ struct DecodeArgs {
 
 // host-side launchers (defined in the .hip files)
 hipError_t launch_append(const AppendArgs& a, int grid_x, hipStream_t s);
+hipError_t launch_window_copy(const AppendArgs& a, hipStream_t s);
 hipError_t launch_calibrate(const CalibArgs& a, hipStream_t s);
 hipError_t launch_bound(const BoundArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int k_fmt, int v_fmt, bool dense, hipStream_t s);

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 1
+#define KVQ_ABI_VERSION 2
 
 typedef int32_t kvq_status;
 #define KVQ_OK 0
@@ -95,7 +95,9 @@ typedef int32_t kvq_status;
 #define KVQ_BUF_BLK_DESC 4
 #define KVQ_BUF_K_ORIG 5
 #define KVQ_BUF_V_ORIG 6
-#define KVQ_NUM_BUFS 7
+#define KVQ_BUF_K_WIN 7
+#define KVQ_BUF_V_WIN 8
+#define KVQ_NUM_BUFS 9
 
 /* Shapes and formats of one cache (one layer).  Plain values, passed by pointer. */
 typedef struct kvq_params {
@@ -112,6 +114,13 @@ typedef struct kvq_params {
   int32_t rotation;       /* KVQ_ROT_* */
   int32_t keep_fp16_copy; /* nonzero: store originals + per-block descriptors */
   float softmax_scale;    /* 0 => 1/sqrt(head_dim) */
+  /* Full-precision window ("OSCAR", section 2.2B, mixed-precision layout; "Search Your
+   * Block Floating Point Scales!", attention-sink-aware mixed-precision caching): the
+   * first sink_blocks and the last recent_blocks 64-token blocks of every sequence
+   * are attended from their in_dtype originals, the blocks between from the codes.
+   * Both 0 = no window.  sink_blocks + recent_blocks <= max_ctx / 64. */
+  int32_t sink_blocks;
+  int32_t recent_blocks;
 } kvq_params;
 
 /*
@@ -137,7 +146,12 @@ typedef struct kvq_params {
  *   signs   [128] int8 of +1/-1                 needed for KVQ_ROT_SIGN_FWHT
  *   rot_f16 [128][128] fp16 bits, row-major     needed for KVQ_ROT_DENSE
  *   clip_k, clip_v [Hkv][128] fp32 thresholds   optional, INT2 only (NULL = none)
- * Code and metadata buffers must be 16-byte aligned.
+ *   k_win, v_win [B][Hkv][NW * 64][128]  in_dtype originals of the window blocks,
+ *                                   NW = sink_blocks + recent_blocks; block j sits
+ *                                   in slot j if j < sink_blocks, else in slot
+ *                                   sink_blocks + j % recent_blocks (a ring), at row
+ *                                   position % 64; needed iff NW > 0
+ * Code, metadata, original and window buffers must be 16-byte aligned.
  */
 typedef struct kvq_cache {
   void* k_codes;
@@ -151,6 +165,8 @@ typedef struct kvq_cache {
   const uint16_t* rot_f16;
   const float* clip_k;
   const float* clip_v;
+  void* k_win;
+  void* v_win;
 } kvq_cache;
 
 /* Returns KVQ_ABI_VERSION. */
@@ -192,6 +208,11 @@ int32_t kvq_decode_splits(const kvq_params* p, const int32_t* seq_len_host);
  * Codes and scales are bit-exact functions of the inputs (fp32 arithmetic in a
  * fixed order, round-half-to-even of exact quotients).  Other positions of the
  * cache are left unchanged.  n_new == 0 is a no-op.
+ * With a window, every position is still quantized; in addition the originals of
+ * the positions in blocks j < sink_blocks, and in the last recent_blocks blocks
+ * that this call reaches (blocks j > (start + n_new - 1) / 64 - recent_blocks),
+ * are copied into the window.  Appending in position order therefore keeps the
+ * window holding the sink blocks and the most recent blocks appended.
  */
 kvq_status kvq_append(const kvq_params* p, const kvq_cache* cache, const void* k_new, const void* v_new,
                       const int32_t* start_pos_host, int32_t n_new, void* stream);
@@ -219,6 +240,10 @@ kvq_status kvq_error_bound(const kvq_params* p, const kvq_cache* cache, const vo
  *     on ||out - dense attention over the originals||_2 for that row.
  *   workspace: device, >= kvq_decode_workspace_bytes(p) bytes, 256-byte aligned,
  *     zero-filled before its first use (see kvq_decode_workspace_bytes).
+ * With a window (sink_blocks + recent_blocks > 0), blocks j < sink_blocks and
+ * j >= ceil(seq_len / 64) - recent_blocks are attended exactly from k_win/v_win in
+ * the original basis (like flagged blocks), so seq_len must be the number of
+ * positions appended in order (the ring holds the most recent blocks appended).
  * Attention output differs from exact fp64 attention over the decoded cache by
  * fp16 rounding of the query/probabilities and fp32 accumulation only.
  */

@@ -19,7 +19,16 @@ for the newest query token.  The plain definition is evaluated directly:
 * for blocks flagged for exact recompute (64 tokens each), the fp16 originals
   are used instead, in the original basis, for both the logits and the values
   ("Runtime-Certified ...", Methodology sections 1 and 3: fetch the fp16 data
-  and compute exact dense attention for what the bound does not cover).
+  and compute exact dense attention for what the bound does not cover);
+* with a full-precision window, the first n_sink and the last n_recent 64-token
+  blocks of the sequence are likewise taken from the full-precision originals,
+  in the original basis ("OSCAR", section 2.2B: sink and recent tokens kept in
+  BF16, the historical middle in INT2; "Search Your Block Floating Point
+  Scales!", attention-sink-aware mixed-precision caching: the first and last
+  blocks at full precision, the middle blocks in NVFP4).  Reading: "blocks" are
+  the 64-token blocks of the position grid, and "last" counts back from the block
+  holding the newest token, so with T tokens the window is the blocks j with
+  j < n_sink or j >= ceil(T / 64) - n_recent.
 
 Grouped-query attention: query head hq reads kv head hq // (Hq / Hkv).
 No mask: the query attends to positions [0, seq_len), which include the token
@@ -33,12 +42,22 @@ from .codec import decode_k, decode_v, TILE
 from .rotation import rotation_matrix_f64, D
 
 
+def window_blocks(T, n_sink, n_recent):
+    """Boolean mask over the ceil(T / 64) blocks of a T-token sequence: True for
+    the blocks kept at full precision (the first n_sink, the last n_recent)."""
+    nb = (int(T) + TILE - 1) // TILE
+    j = np.arange(nb)
+    return (j < n_sink) | (j >= nb - n_recent)
+
+
 def decode_attention(cache, q_bits, dtype, seq_len, rotation, signs=None, r16=None,
-                     flags=None, softmax_scale=None, rows=None):
+                     flags=None, softmax_scale=None, rows=None, window=None, originals=None):
     """Decode attention for every (b, hq) (or the given (b, hq) rows).
 
     q_bits: uint16 [B, Hq, 128] (fp16/bf16 bit patterns); seq_len: [B];
     flags: uint8 [B, Hkv, nblk] or None.
+    window: (n_sink, n_recent) blocks kept at full precision, or None; then
+    originals = (k_bits, v_bits), uint16 [B, Hkv, >= T, 128], the appended inputs.
     Returns (out fp64 [B, Hq, 128], block_mass fp64 [B, Hq, nblk]); rows that
     were not requested are left zero.
     """
@@ -67,9 +86,14 @@ def decode_attention(cache, q_bits, dtype, seq_len, rotation, signs=None, r16=No
             for blk in range((T + TILE - 1) // TILE):
                 if flags[b, h, blk]:
                     exact[blk * TILE:min(T, (blk + 1) * TILE)] = True
+        if window is not None:
+            for blk in np.nonzero(window_blocks(T, *window))[0]:
+                exact[blk * TILE:min(T, (blk + 1) * TILE)] = True
         if exact.any():
-            ko = nx.widen_input(cache.k_orig[b, h, :T], dtype).astype(np.float64)
-            vo = nx.widen_input(cache.v_orig[b, h, :T], dtype).astype(np.float64)
+            # the originals: the kept copy, or the inputs (identical where both exist)
+            src_k, src_v = (cache.k_orig, cache.v_orig) if originals is None else originals
+            ko = nx.widen_input(src_k[b, h, :T], dtype).astype(np.float64)
+            vo = nx.widen_input(src_v[b, h, :T], dtype).astype(np.float64)
         for hq in hqs:
             qr = R @ q[b, hq]
             logits = (kh @ qr) * sigma

@@ -22,7 +22,7 @@ def test_library_exports_every_declared_symbol():
     assert "kvq_append" in names and "kvq_decode_attn" in names and "kvq_error_bound" in names
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
-    assert L.kvq_abi_version() == 1
+    assert L.kvq_abi_version() == 2
 
 
 def test_buffer_sizes():
@@ -44,7 +44,31 @@ def test_buffer_sizes():
     p5 = kvq.make_params(8, 32, 8, 131072, "fp4", "fp4", dtype="bf16", scale_mode="search9")
     s5 = kvq.buffer_bytes(p5)
     assert s5["k_codes"] == 64 * 131072 * 64 and s5["v_meta"] == 64 * 131072 * 8
+    assert s5["k_win"] == 0 and s5["v_win"] == 0
     assert kvq.decode_workspace_bytes(p) > 0
+    # full-precision window: (sink + recent) blocks of 64 rows of 128 16-bit values per stream
+    pw = kvq.make_params(64, 32, 8, 32768, "int2", "int2", rotation="dense", sink_blocks=1, recent_blocks=2)
+    sw = kvq.buffer_bytes(pw)
+    assert sw["k_win"] == sw["v_win"] == 512 * 3 * 64 * 256
+    assert sw["k_codes"] == s4["k_codes"]
+
+
+@pytest.mark.parametrize("sink,recent", [(-1, 0), (0, -2), (3, 2)])
+def test_invalid_window_rejected(sink, recent):
+    p = kvq.make_params(2, 8, 2, 256, sink_blocks=sink, recent_blocks=recent)  # 4 blocks of 64
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.buffer_bytes(p)
+    assert e.value.status == -1
+
+
+def test_window_needs_buffers_without_gpu():
+    L = kvq.lib()
+    p = kvq.make_params(2, 8, 2, 256, sink_blocks=1, recent_blocks=1)
+    fake = 1 << 20  # never dereferenced: validation fails first
+    cs = kvq.CacheStruct(k_codes=fake, k_meta=fake, v_codes=fake, v_meta=fake, signs=fake)
+    starts = (ctypes.c_int32 * 2)(0, 0)
+    st = L.kvq_append(ctypes.byref(p), ctypes.byref(cs), fake, fake, starts, 4, None)
+    assert st == -1 and b"k_win" in L.kvq_last_error()
 
 
 @pytest.mark.parametrize("field,value", [("head_dim", 64), ("max_ctx", 100), ("batch", 0), ("n_q_heads", 7),

@@ -102,6 +102,62 @@ def test_all_flagged_is_dense_attention():
         assert np.allclose(dense[b], _sdpa(qf[b], k, v, 2), rtol=1e-10, atol=1e-12)
 
 
+@pytest.mark.parametrize("T,window,want", [
+    (323, (1, 2), [1, 0, 0, 0, 1, 1]),   # 6 blocks, the last one partial
+    (100, (1, 2), [1, 1]),               # window wider than the sequence
+    (640, (0, 1), [0] * 9 + [1]),
+    (640, (2, 0), [1, 1] + [0] * 8),
+    (64, (0, 0), [0]),
+    (0, (1, 1), []),
+])
+def test_window_blocks_examples(T, window, want):
+    # "Search Your Block Floating Point Scales!": first and last blocks at full precision
+    assert attention.window_blocks(T, *window).astype(int).tolist() == want
+
+
+def test_window_covering_all_is_dense_attention():
+    rng = np.random.default_rng(24)
+    s = np.where(rng.integers(0, 2, 128) == 1, 1, -1)
+    cache = _cache("int4", "int4", B=2, H=2, T=192)
+    kb, vb = _fill(cache, rng, signs=s)
+    q = synth.to_bits(rng.standard_normal((2, 4, 128)), "f16")
+    seq = np.array([192, 70])
+    out, _ = attention.decode_attention(cache, q, "f16", seq, "sign_fwht", s, window=(3, 0), originals=(kb, vb))
+    dense = attention.dense_attention(kb, vb, q, "f16", seq)
+    assert np.allclose(out, dense, rtol=1e-12, atol=1e-14)
+    none, _ = attention.decode_attention(cache, q, "f16", seq, "sign_fwht", s, window=(0, 0), originals=(kb, vb))
+    plain, _ = attention.decode_attention(cache, q, "f16", seq, "sign_fwht", s)
+    assert np.array_equal(none, plain)
+
+
+@pytest.mark.parametrize("fk,fv,dtype,rotation", [("int4", "int4", "f16", "sign_fwht"),
+                                                  ("fp4", "fp4", "bf16", "sign_fwht"),
+                                                  ("int2", "int2", "f16", "none")])
+def test_window_matches_mixed_cache_sdpa(fk, fv, dtype, rotation):
+    # sink block 0 and the two newest blocks exact, the middle decoded from codes: the same
+    # attention as SDPA over one key/value matrix in the original basis that holds the
+    # originals at those positions and the derotated decoded rows elsewhere
+    rng = np.random.default_rng(25)
+    s = np.where(rng.integers(0, 2, 128) == 1, 1, -1)
+    cache = _cache(fk, fv, B=2, H=2, T=384)
+    kb, vb = _fill(cache, rng, dtype=dtype, rotation=rotation, signs=s)
+    Hq = 4
+    q = synth.to_bits(rng.standard_normal((2, Hq, 128)), dtype)
+    seq = np.array([323, 384])
+    exact_ranges = {323: [(0, 64), (256, 323)], 384: [(0, 64), (256, 384)]}
+    out, _ = attention.decode_attention(cache, q, dtype, seq, rotation, s, window=(1, 2), originals=(kb, vb))
+    R = rot.rotation_matrix_f64(rotation, s)
+    qf = nx.widen_input(q, dtype).astype(np.float64)
+    for b in range(2):
+        T = seq[b]
+        k = np.stack([codec.decode_k(cache, b, h, 0, T) @ R for h in range(2)])
+        v = np.stack([codec.decode_v(cache, b, h, 0, T) @ R for h in range(2)])
+        for lo, hi in exact_ranges[T]:
+            k[:, lo:hi] = nx.widen_input(kb[b, :, lo:hi], dtype)
+            v[:, lo:hi] = nx.widen_input(vb[b, :, lo:hi], dtype)
+        assert np.allclose(out[b], _sdpa(qf[b], k, v, Hq // 2), rtol=1e-10, atol=1e-12)
+
+
 def test_row_rel_err_metric():
     ref = np.array([[1.0, -2.0, 0.5]])
     got = np.array([[1.0, -2.004, 0.5]])
