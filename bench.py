@@ -54,7 +54,24 @@ def parse():
                     help="end with one plain 256 MiB device copy (reference for hardware byte counters)")
     ap.add_argument("--workload", type=int, default=2, choices=(2, 3, 4, 5),
                     help="2 (default): the GQA int4 line; 3/4/5: the certified, int2 and FP4 workloads")
-    return ap.parse_args()
+    ap.add_argument("--window", type=str, default=None, metavar="SINK,RECENT",
+                    help="workloads 3/4/5: keep the first SINK and last RECENT 64-token blocks of every "
+                         "sequence at full precision")
+    args = ap.parse_args()
+    if args.window is not None:
+        if args.workload == 2:
+            ap.error("--window applies to workloads 3, 4 and 5")
+        args.window = tuple(int(x) for x in args.window.split(","))
+        if len(args.window) != 2 or min(args.window) < 0:
+            ap.error("--window takes SINK,RECENT (two non-negative block counts)")
+    return args
+
+
+def attention_window_tokens(T, n_sink, n_recent):
+    """Tokens of a T-token sequence in its first n_sink and last n_recent 64-token blocks."""
+    nb = (T + 63) // 64
+    blocks = [j for j in range(nb) if j < n_sink or j >= nb - n_recent]
+    return sum(min(T, 64 * j + 64) - 64 * j for j in blocks)
 
 
 def kernel_traffic(roofline_kernel_src):
@@ -124,6 +141,8 @@ def bench_workload(cfg_id, args):
     kvq.lib()
     dev = torch.device("cuda:0")
     c = synth.config(cfg_id)
+    if args.window is not None:
+        c["sink_blocks"], c["recent_blocks"] = args.window
     B, Hq, H, T, P = c["B"], c["Hq"], c["Hkv"], c["T"], c["prefill"]
     nrot = 4
     g = torch.Generator(device=dev)
@@ -250,6 +269,13 @@ def bench_workload(cfg_id, args):
         packed += sizes["blk_desc"] - nflag * 64 * (kb_tok + vb_tok) + nflag * 64 * 512
         io += B * Hq * 4
         extra = f"; {nflag} of {flg.numel()} blocks flagged ({100.0 * nflag / flg.numel():.2f}%), recomputed from fp16"
+    if args.window is not None:
+        # window blocks are read from the full-precision copy (512 B per token) instead of the codes
+        nwin = int(attention_window_tokens(T, *args.window))
+        per_tok = (sizes["k_codes"] + sizes["k_meta"] + sizes["v_codes"] + sizes["v_meta"]) // (B * H * T)
+        packed += B * H * nwin * (512 - per_tok)
+        extra += (f"; window: first {args.window[0]} and last {args.window[1]} blocks of 64 tokens at full "
+                  f"precision ({nwin} tokens per sequence and kv head)")
     dense_bytes = 2 * B * H * T * 128 * 2
     vecs = B * H * P * 2
     in_bytes = vecs * 256
@@ -274,7 +300,8 @@ def bench_workload(cfg_id, args):
         "dtype": {"int8": "int8", "int4": "int4", "int2": "int2", "fp4": "fp4"}[c["k_fmt"]],
         "data": f"synthetic, drawn on the GPU from a seeded generator ({c['data']}){extra}",
         "config": {"workload": c["name"], "B": B, "Hq": Hq, "Hkv": H, "head_dim": 128, "context": T,
-                   "prefill_tokens": P, "formats": fmt, "rotation": c["rotation"], "input": c["dtype"]},
+                   "prefill_tokens": P, "formats": fmt, "rotation": c["rotation"], "input": c["dtype"],
+                   **({"window_blocks": list(args.window)} if args.window is not None else {})},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "decode_split (splits merged by their last workgroup)" + (" + bound_kernel" if c["keep"] else ""),

@@ -565,6 +565,15 @@ struct ChunkRegs {
   uint32_t vmeta[VF == KVQ_INT2 ? 4 : 2]; // this lane's share of the V metadata tile
 };
 
+// Flag and error descriptor of one chunk (exact-recompute kernels only).
+template <bool CERT>
+struct ChunkAux {};
+template <>
+struct ChunkAux<true> {
+  uint32_t flag;
+  float ek, ev, vn;
+};
+
 // Issue the loads of chunk ch (no waits: the caller consumes them one chunk later).
 template <int KF, int KG, int VF, int VG>
 __device__ __forceinline__ void load_chunk(const DecodeArgs& a, size_t stream, int ch, int lane, int tok_a,
@@ -650,8 +659,14 @@ __device__ __forceinline__ float max_same_head_fast(float v) {
   return v;
 }
 
-template <int KF, int KG, int VF, int VG, bool CERT>
+// MODE 0: codes only.  MODE 1: blocks of the full-precision window recomputed
+// exactly from their originals.  MODE 2: certified cache: window blocks and blocks
+// flagged by the error bound recomputed exactly, per-block descriptors for the
+// certificate.
+template <int KF, int KG, int VF, int VG, int MODE>
 __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
+  constexpr bool EXACT = MODE != 0;  // exact recompute of some chunks
+  constexpr bool CERT = MODE == 2;   // flags and descriptors
   __shared__ DecodeSmem sm;
   const int b = blockIdx.z;
   const int HG = (a.G + 3) >> 2;
@@ -691,9 +706,30 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
     if (lane == 0) v = atomicAdd(&sm.next, 1);
     return v;
   };
+  // With exact recompute, a chunk's flag and descriptor are loaded right after its
+  // codes, unconditionally (from a stand-in address when the buffer is absent), so
+  // that the wait for them is the wait for the chunk itself, never for the chunk
+  // loaded after it.
+  auto load_aux = [&](int ch, ChunkAux<CERT>& X) {
+    if constexpr (CERT) {
+      // The offset is taken through an empty asm: the loaded values are then not
+      // known to be wave-uniform, so they stay in vector registers (no read into a
+      // scalar register, and no wait, at the load) until the visit reads them.
+      uint32_t blk = (uint32_t)(stream * a.nt + ch);
+      asm volatile("" : "+v"(blk));
+      const uint8_t* fp = a.flags != nullptr ? a.flags + blk : a.k_meta;
+      const float* dp = a.desc != nullptr ? a.desc + (size_t)blk * 3 : reinterpret_cast<const float*>(a.k_meta);
+      X.flag = *fp;
+      X.ek = dp[0];
+      X.ev = dp[1];
+      X.vn = dp[2];
+    }
+  };
   ChunkRegs<KF, VF> RA, RB;
+  ChunkAux<CERT> XA, XB;
   int cA = c0 + wv;
   load_chunk<KF, KG, VF, VG>(a, stream, cA < c1 ? cA : 0, lane, tok_a, RA);
+  load_aux(cA < c1 ? cA : 0, XA);
   __builtin_amdgcn_sched_barrier(0);
   query_prologue<KF>(a, sm, qin, nh, KG);
   int pB = claim();
@@ -838,7 +874,7 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       o[hf] *= av;
-      if constexpr (CERT) oo[hf] *= av;
+      if constexpr (EXACT) oo[hf] *= av;
     }
     if constexpr (VF == KVQ_INT2) oz *= av;
     // ---- PV
@@ -928,9 +964,27 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
     const int tau = lane;
     const bool live = tok0 + tau < T;
     float lh[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    // Loads are issued in batches ahead of their use (the token's key row in two
+    // halves, the value rows 16 at a time), a few memory round trips per chunk
+    // rather than one per row.
     const uint4* kp = reinterpret_cast<const uint4*>(orig_rows(a.k_orig, a.k_win, ch) + (size_t)tau * D);
+    const uint32_t* vp = reinterpret_cast<const uint32_t*>(orig_rows(a.v_orig, a.v_win, ch)) + lane;
+    uint4 kr[8];
+    uint32_t vr[2][16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kr[i] = kp[i];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const uint4 u = kp[i];
+      if (i == 8) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kr[e] = kp[8 + e];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) vr[0][k] = vp[(size_t)k * (D / 2)];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const uint4 u = kr[i & 7];
       const uint32_t ws[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -969,13 +1023,21 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
     }
     if constexpr (VF == KVQ_INT2) oz *= av;
     lds_wait();
-    const uint32_t* vp = reinterpret_cast<const uint32_t*>(orig_rows(a.v_orig, a.v_win, ch)) + lane;
-    for (int tt = 0; tt < TILE; ++tt) {
-      const uint32_t vv = vp[(size_t)tt * (D / 2)];
-      const float v0 = widen((uint16_t)(vv & 0xFFFF), bf16), v1 = widen((uint16_t)(vv >> 16), bf16);
-      const float4 pp = *reinterpret_cast<const float4*>(&sm.pb[wv][tt][0]);
-      oo[0] += f4{pp.x, pp.y, pp.z, pp.w} * v0;
-      oo[1] += f4{pp.x, pp.y, pp.z, pp.w} * v1;
+    // value rows in batches of 16, the next batch in flight while one is accumulated
+#pragma unroll
+    for (int bt = 0; bt < TILE / 16; ++bt) {
+      if (bt + 1 < TILE / 16) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) vr[(bt + 1) & 1][k] = vp[(size_t)(16 * (bt + 1) + k) * (D / 2)];
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const uint32_t vv = vr[bt & 1][k];
+        const float v0 = widen((uint16_t)(vv & 0xFFFF), bf16), v1 = widen((uint16_t)(vv >> 16), bf16);
+        const float4 pp = *reinterpret_cast<const float4*>(&sm.pb[wv][16 * bt + k][0]);
+        oo[0] += f4{pp.x, pp.y, pp.z, pp.w} * v0;
+        oo[1] += f4{pp.x, pp.y, pp.z, pp.w} * v1;
+      }
     }
     lds_wait();
   };
@@ -983,22 +1045,20 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   // ---------------------------------------------------------------- software-pipelined walk
   // The loads of the next chunk are in flight while the current one is computed
   // (two register sets used alternately).
-  auto is_flagged = [&](int ch) -> bool {
-    if constexpr (CERT) return in_window(ch) || (a.flags != nullptr && a.flags[stream * a.nt + ch] != 0);
-    return false;
-  };
-  auto visit = [&](const ChunkRegs<KF, VF>& R, int ch, bool fl) {
+  auto visit = [&](const ChunkRegs<KF, VF>& R, int ch, const ChunkAux<CERT>& X) {
     float ev_c = 0.0f;
+    bool fl = false;
+    if constexpr (EXACT) fl = in_window(ch);
     if constexpr (CERT) {
+      fl = fl || (a.flags != nullptr && __builtin_amdgcn_readfirstlane(X.flag) != 0);
       if (a.desc != nullptr) {
-        const float* dsc = a.desc + (stream * a.nt + ch) * 3;
-        ev_c = dsc[1];
-        vnmax = fmaxf(vnmax, dsc[2]);
-        if (!fl) ekmax = fmaxf(ekmax, dsc[0]);
+        ev_c = X.ev;
+        vnmax = fmaxf(vnmax, X.vn);
+        if (!fl) ekmax = fmaxf(ekmax, X.ek);
       }
     }
     if (fl) {
-      if constexpr (CERT) exact_chunk(ch);
+      if constexpr (EXACT) exact_chunk(ch);
     } else {
       quant_chunk(R, ch, ev_c);
     }
@@ -1013,8 +1073,9 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
     const int cB = c0 + __builtin_amdgcn_readfirstlane(pB);
     const int pC = claim();
     load_chunk<KF, KG, VF, VG>(a, stream, cB < c1 ? cB : cA, lane, tok_a, RB);
+    load_aux(cB < c1 ? cB : cA, XB);
     __builtin_amdgcn_sched_barrier(0);
-    visit(RA, cA, is_flagged(cA));
+    visit(RA, cA, XA);
     // read the claim only after this chunk's work (an empty asm that takes the register
     // keeps the read, and the wait for the atomic, from being hoisted above the work)
     int pCv = pC;
@@ -1022,8 +1083,9 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
     const int cC = c0 + __builtin_amdgcn_readfirstlane(pCv);
     pB = claim();
     load_chunk<KF, KG, VF, VG>(a, stream, cC < c1 ? cC : cA, lane, tok_a, RA);
+    load_aux(cC < c1 ? cC : cA, XA);
     __builtin_amdgcn_sched_barrier(0);
-    if (cB < c1) visit(RB, cB, is_flagged(cB));
+    if (cB < c1) visit(RB, cB, XB);
     asm volatile("" : "+v"(pB));
     cA = cC;
   }
@@ -1046,13 +1108,13 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
     if constexpr (VF == KVQ_INT2) zb = oz[hh];
     sm.mrg_o[wv][hh][2 * lane] = o[0][hh] + zb;
     sm.mrg_o[wv][hh][2 * lane + 1] = o[1][hh] + zb;
-    if constexpr (CERT) {
+    if constexpr (EXACT) {
       sm.mrg_oo[wv][hh][2 * lane] = oo[0][hh];
       sm.mrg_oo[wv][hh][2 * lane + 1] = oo[1][hh];
     }
   }
   __syncthreads();
-  write_record<CERT, NWS, true>(a, sm, b, hq0, nh, split);
+  write_record<EXACT, NWS, true>(a, sm, b, hq0, nh, split);
 
   // ---------------- the last workgroup of the stream to finish merges its splits
   // The records are agent-coherent atomic stores; every thread waits for its own
@@ -1069,7 +1131,7 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   }
   __syncthreads();
   if (sm.last) {
-    if (wv < nh) combine_row<CERT, true>(a, b * a.Hq + hq0 + wv, &sm.qf[wv][0]);
+    if (wv < nh) combine_row<EXACT, true>(a, b * a.Hq + hq0 + wv, &sm.qf[wv][0]);
     if (t == 0) __hip_atomic_store(a.ctr + sidx, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -1201,13 +1263,21 @@ hipError_t launch_decode(const DecodeArgs& a, int k_fmt, int v_fmt, bool dense, 
     return hipGetLastError();
   }
   // the exact-recompute instantiation serves the certified cache and the window
-  const bool cert = a.desc != nullptr || a.k_win != nullptr;
+  // 2: certified cache; 1: full-precision window only; 0: codes only.  (With 8-bit
+  // keys the window-only variant would need more than 256 registers per lane, so
+  // those caches take the certified variant, whose flag and descriptor loads then
+  // read a stand-in address and are ignored.)
+  const int mode = a.desc != nullptr ? 2 : (a.k_win != nullptr ? (k_fmt == KVQ_INT8 ? 2 : 1) : 0);
 #define KVQ_LAUNCH(KF, KG, VF, VG)                                                            \
   if (k_fmt == KF && a.k_group == KG && v_fmt == VF && a.v_group == VG) {                     \
-    if (cert)                                                                                 \
-      hipLaunchKernelGGL((decode_split<KF, KG, VF, VG, true>), grid, dim3(NTS), 0, s, a);     \
-    else                                                                                      \
-      hipLaunchKernelGGL((decode_split<KF, KG, VF, VG, false>), grid, dim3(NTS), 0, s, a);    \
+    if (mode == 2) {                                                                          \
+      hipLaunchKernelGGL((decode_split<KF, KG, VF, VG, 2>), grid, dim3(NTS), 0, s, a);        \
+    } else if (mode == 1) {                                                                   \
+      if constexpr (KF != KVQ_INT8)                                                           \
+        hipLaunchKernelGGL((decode_split<KF, KG, VF, VG, 1>), grid, dim3(NTS), 0, s, a);      \
+    } else {                                                                                  \
+      hipLaunchKernelGGL((decode_split<KF, KG, VF, VG, 0>), grid, dim3(NTS), 0, s, a);        \
+    }                                                                                         \
     return hipGetLastError();                                                                 \
   }
   KVQ_LAUNCH(KVQ_INT4, 32, KVQ_INT4, 32)
