@@ -21,11 +21,14 @@ What it computes, in the order the pages give it:
 * ``bound``     -- per-block error descriptors, the certified per-block bound
   and the output certificate ("Runtime-Certified Bounded-Error Quantized
   Attention", Methodology section 2).
+* ``adaptive``  -- the adaptive-precision steps of the same page (Methodology
+  section 3): block attention mass estimated from the quantized keys, the
+  top-K* blocks covering a mass fraction, and the dense fallback of a head.
 
 Every function names the passage it follows in its docstring.  Where a page is
-silent, the reading taken is stated there and collected in the design doc.
+silent, the reading taken is stated there.
 """
 
-from . import numerics, rotation, codec, attention, bound  # noqa: F401
+from . import numerics, rotation, codec, attention, bound, adaptive  # noqa: F401
 
 __all__ = ["numerics", "rotation", "codec", "attention", "bound"]
