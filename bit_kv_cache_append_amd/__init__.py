@@ -3,8 +3,8 @@
 Every computation runs in the HIP kernels of libkvq.so; this module turns torch
 tensors into device pointers and the current HIP stream, calls the C entry
 points of the same names (kvq_append, kvq_error_bound, kvq_decode_attn,
-kvq_decode_attn_dense, kvq_calibrate_clip, kvq_buffer_bytes,
-kvq_decode_workspace_bytes, kvq_decode_splits) and raises KvqError on a non-zero status.  There is
+kvq_decode_attn_dense, kvq_calibrate_clip, kvq_block_mass, kvq_select_blocks,
+kvq_dense_fallback, kvq_buffer_bytes, kvq_decode_workspace_bytes, kvq_decode_splits) and raises KvqError on a non-zero status.  There is
 no fallback: if the library is not built, importing the functions raises.
 """
 
@@ -80,6 +80,12 @@ def lib():
         L.kvq_decode_attn.argtypes = [P(Params), P(CacheStruct), vp, P(i32), vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.kvq_decode_attn_dense.restype = i32
         L.kvq_decode_attn_dense.argtypes = [P(Params), vp, vp, vp, P(i32), vp, vp, ctypes.c_size_t, vp]
+        L.kvq_block_mass.restype = i32
+        L.kvq_block_mass.argtypes = [P(Params), P(CacheStruct), vp, P(i32), vp, vp]
+        L.kvq_select_blocks.restype = i32
+        L.kvq_select_blocks.argtypes = [P(Params), vp, P(i32), ctypes.c_float, vp, vp, vp]
+        L.kvq_dense_fallback.restype = i32
+        L.kvq_dense_fallback.argtypes = [P(Params), P(CacheStruct), vp, P(i32), ctypes.c_float, vp, vp, vp]
         L.kvq_calibrate_clip.restype = i32
         L.kvq_calibrate_clip.argtypes = [P(Params), P(CacheStruct), vp, vp, i32, ctypes.c_float, vp, vp, vp]
         _lib = L
@@ -224,6 +230,35 @@ def decode_attn_dense(p, k, v, q, seq_len, ws=None, out=None, stream=None):
     _check(lib().kvq_decode_attn_dense(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(q), _i32(seq_len), _ptr(out), _ptr(ws),
                                        ws.numel() * ws.element_size(), stream if stream is not None else _stream()))
     return out
+
+
+def block_mass(p, cache, q, seq_len, mass=None, stream=None):
+    """kvq_block_mass: estimated attention mass per block, fp32 [B, Hq, max_ctx // 64]."""
+    import torch
+    if mass is None:
+        mass = torch.empty((p.batch, p.n_q_heads, p.max_ctx // 64), dtype=torch.float32, device=q.device)
+    cs = cache.struct()
+    _check(lib().kvq_block_mass(ctypes.byref(p), ctypes.byref(cs), _ptr(q), _i32(seq_len), _ptr(mass),
+                                stream if stream is not None else _stream()))
+    return mass
+
+
+def select_blocks(p, mass, seq_len, tau_cov, flags_in=None, flags_out=None, stream=None):
+    """kvq_select_blocks: promotion flags uint8 [B, Hkv, max_ctx // 64] (flags_out may be flags_in)."""
+    import torch
+    if flags_out is None:
+        flags_out = torch.empty((p.batch, p.n_kv_heads, p.max_ctx // 64), dtype=torch.uint8, device=mass.device)
+    _check(lib().kvq_select_blocks(ctypes.byref(p), _ptr(mass), _i32(seq_len), float(tau_cov), _ptr(flags_in),
+                                   _ptr(flags_out), stream if stream is not None else _stream()))
+    return flags_out
+
+
+def dense_fallback(p, cache, q, seq_len, eps, out, cert, stream=None):
+    """kvq_dense_fallback: rows with cert > eps recomputed densely from the originals (in place)."""
+    cs = cache.struct()
+    _check(lib().kvq_dense_fallback(ctypes.byref(p), ctypes.byref(cs), _ptr(q), _i32(seq_len), float(eps), _ptr(out),
+                                    _ptr(cert), stream if stream is not None else _stream()))
+    return out, cert
 
 
 def calibrate_clip(p, cache, calib_k, calib_v, ratio=0.9, stream=None):

@@ -32,6 +32,7 @@ SOURCES = {
     "kvq_append.hip": ["-ffp-contract=off"],
     "kvq_decode.hip": [],
     "kvq_bound.hip": [],
+    "kvq_adaptive.hip": [],
     "kvq_api.cpp": [],
 }
 

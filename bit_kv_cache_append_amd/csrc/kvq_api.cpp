@@ -374,6 +374,85 @@ static kvq_status decode_common(const kvq_params* p, const kvq_cache* c, const v
   return KVQ_OK;
 }
 
+static void adapt_common(const kvq_params* p, AdaptArgs& a) {
+  a.B = p->batch;
+  a.Hq = p->n_q_heads;
+  a.H = p->n_kv_heads;
+  a.G = p->n_q_heads / p->n_kv_heads;
+  a.Tmax = p->max_ctx;
+  a.nt = p->max_ctx / TILE;
+  a.in_bf16 = p->in_dtype == KVQ_BF16;
+  a.rotation = p->rotation;
+  a.k_fmt = p->k_fmt;
+  a.k_group = eff_group(p->k_fmt, p->k_group);
+  a.scale = softmax_scale(p);
+}
+
+kvq_status kvq_block_mass(const kvq_params* p, const kvq_cache* c, const void* q, const int32_t* seq_len_host,
+                          float* mass, void* stream) {
+  kvq_status st = check_params(p);
+  if (st) return st;
+  if ((st = check_cache(p, c, false))) return st;
+  if (!q || !mass) return fail(KVQ_ERR_INVALID_ARG, "q/mass are NULL");
+  AdaptArgs a;
+  memset(&a, 0, sizeof(a));
+  if ((st = check_seq(p, seq_len_host, a.seq))) return st;
+  adapt_common(p, a);
+  a.q = (const uint16_t*)q;
+  a.k_codes = (const uint8_t*)c->k_codes;
+  a.k_meta = (const uint8_t*)c->k_meta;
+  a.signs = c->signs;
+  a.rot = c->rot_f16;
+  a.mass = mass;
+  hipError_t e = launch_block_mass(a, (hipStream_t)stream);
+  if (e == hipErrorNotSupported) return fail(KVQ_ERR_UNSUPPORTED, "key format not supported by the scoring pass");
+  if (e != hipSuccess) return hip_fail(e, "block mass launch");
+  return KVQ_OK;
+}
+
+kvq_status kvq_select_blocks(const kvq_params* p, const float* mass, const int32_t* seq_len_host, float tau_cov,
+                             const uint8_t* flags_in, uint8_t* flags_out, void* stream) {
+  kvq_status st = check_params(p);
+  if (st) return st;
+  if (!mass || !flags_out) return fail(KVQ_ERR_INVALID_ARG, "mass/flags_out are NULL");
+  if (!(tau_cov >= 0.0f && tau_cov <= 1.0f)) return fail(KVQ_ERR_INVALID_ARG, "tau_cov must be in [0, 1]");
+  if (p->max_ctx / TILE > MAX_SELECT_BLOCKS)
+    return fail(KVQ_ERR_UNSUPPORTED, "selection supports max_ctx / 64 <= %d blocks", MAX_SELECT_BLOCKS);
+  AdaptArgs a;
+  memset(&a, 0, sizeof(a));
+  if ((st = check_seq(p, seq_len_host, a.seq))) return st;
+  adapt_common(p, a);
+  a.mass = const_cast<float*>(mass);
+  a.flags_in = flags_in;
+  a.flags_out = flags_out;
+  a.tau_cov = tau_cov;
+  hipError_t e = launch_select(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  return KVQ_OK;
+}
+
+kvq_status kvq_dense_fallback(const kvq_params* p, const kvq_cache* c, const void* q, const int32_t* seq_len_host,
+                              float eps, float* out, float* certificate, void* stream) {
+  kvq_status st = check_params(p);
+  if (st) return st;
+  if ((st = check_cache(p, c, true))) return st;
+  if (!q || !out || !certificate) return fail(KVQ_ERR_INVALID_ARG, "q/out/certificate are NULL");
+  if (!(eps >= 0.0f)) return fail(KVQ_ERR_INVALID_ARG, "eps must be >= 0");
+  AdaptArgs a;
+  memset(&a, 0, sizeof(a));
+  if ((st = check_seq(p, seq_len_host, a.seq))) return st;
+  adapt_common(p, a);
+  a.q = (const uint16_t*)q;
+  a.k_orig = (const uint16_t*)c->k_orig;
+  a.v_orig = (const uint16_t*)c->v_orig;
+  a.out = out;
+  a.cert = certificate;
+  a.eps = eps;
+  hipError_t e = launch_fallback(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fallback launch");
+  return KVQ_OK;
+}
+
 kvq_status kvq_decode_attn(const kvq_params* p, const kvq_cache* c, const void* q, const int32_t* seq_len_host,
                            const uint8_t* block_flags, float* out, float* certificate, void* workspace,
                            size_t workspace_bytes, void* stream) {

@@ -73,6 +73,27 @@ struct BoundArgs {
   SeqArray seq;
 };
 
+// Adaptive precision: scoring pass, top-K* selection, per-head dense fallback.
+struct AdaptArgs {
+  const uint16_t* q;  // [B][Hq][128]
+  const uint8_t* k_codes;
+  const uint8_t* k_meta;
+  const uint16_t* k_orig;  // [B][H][Tmax][128] (fallback)
+  const uint16_t* v_orig;
+  const int8_t* signs;
+  const uint16_t* rot;
+  float* mass;               // [B][Hq][nt]
+  const uint8_t* flags_in;   // [B][H][nt] or null
+  uint8_t* flags_out;        // [B][H][nt]
+  float* out;                // [B][Hq][128] (fallback)
+  float* cert;               // [B][Hq] (fallback)
+  int32_t B, Hq, H, G, Tmax, nt;
+  int32_t in_bf16, rotation, k_fmt, k_group;
+  float scale, tau_cov, eps;
+  SeqArray seq;
+};
+constexpr int MAX_SELECT_BLOCKS = 4096;  // selection sorts one head's blocks in LDS
+
 // Workspace of a decode call: one partial-result record per (b, hq, split),
 // written by the split kernel and read by the combine kernel:
 // [0] m: running max (log2 domain), [1] l: sum of exp2, [2] eta: sum of p * ev
@@ -115,5 +136,8 @@ hipError_t launch_window_copy(const AppendArgs& a, hipStream_t s);
 hipError_t launch_calibrate(const CalibArgs& a, hipStream_t s);
 hipError_t launch_bound(const BoundArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int k_fmt, int v_fmt, bool dense, hipStream_t s);
+hipError_t launch_block_mass(const AdaptArgs& a, hipStream_t s);
+hipError_t launch_select(const AdaptArgs& a, hipStream_t s);
+hipError_t launch_fallback(const AdaptArgs& a, hipStream_t s);
 
 }  // namespace kvq

@@ -252,6 +252,47 @@ kvq_status kvq_decode_attn(const kvq_params* p, const kvq_cache* cache, const vo
                            float* certificate, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Adaptive precision ("Runtime-Certified Bounded-Error Quantized Attention",
+ * Methodology section 3): a scoring pass over the quantized keys estimates each
+ * block's attention mass; the blocks covering a fraction tau_cov of it are
+ * promoted to exact recompute (kvq_select_blocks, then kvq_decode_attn with the
+ * flags); a head whose certificate still exceeds eps is recomputed densely
+ * (kvq_dense_fallback).
+ *
+ * kvq_block_mass: mass[b][hq][j] = sum over the tokens t of block j of
+ *   softmax_t(scale * (R q) . k_hat_t), the softmax over positions [0,
+ *   seq_len_host[b]) of the quantized keys alone (fp32; 0 past the sequence).
+ *   q: device [B][Hq][128] in_dtype; mass: device fp32 [B][Hq][max_ctx/64].
+ *   Key formats as for kvq_decode_attn.
+ */
+kvq_status kvq_block_mass(const kvq_params* p, const kvq_cache* cache, const void* q,
+                          const int32_t* seq_len_host, float* mass, void* stream);
+
+/*
+ * kvq_select_blocks: flags_out[b][h][j] = 1 if block j is among the top-K* blocks
+ * of any query head of kv head h, or flags_in[b][h][j] != 0 (flags_in may be NULL
+ * or equal flags_out).  Top-K* of a query head: its blocks below seq_len sorted by
+ * decreasing mass (equal masses: lower index first), K* the shortest prefix whose
+ * fp32 running sum, accumulated in that order, reaches tau_cov (all blocks if it
+ * never does).  mass: device fp32 [B][Hq][max_ctx/64] (from kvq_block_mass);
+ * flags: device uint8 [B][Hkv][max_ctx/64]; tau_cov in [0, 1].
+ * max_ctx / 64 must not exceed 4096 (KVQ_ERR_UNSUPPORTED otherwise).
+ */
+kvq_status kvq_select_blocks(const kvq_params* p, const float* mass, const int32_t* seq_len_host,
+                             float tau_cov, const uint8_t* flags_in, uint8_t* flags_out, void* stream);
+
+/*
+ * kvq_dense_fallback: for every (b, hq) with certificate[b][hq] > eps, out[b][hq]
+ * is replaced by attention over k_orig/v_orig (positions [0, seq_len_host[b]),
+ * fp32 arithmetic, original basis) and certificate[b][hq] is set to 0; other rows
+ * are left unchanged.  Needs keep_fp16_copy.  out/certificate: device, as
+ * written by kvq_decode_attn.  eps >= 0.
+ */
+kvq_status kvq_dense_fallback(const kvq_params* p, const kvq_cache* cache, const void* q,
+                              const int32_t* seq_len_host, float eps, float* out, float* certificate,
+                              void* stream);
+
+/*
  * Decode attention over uncompressed K/V in the layout of k_orig/v_orig
  * ([B][Hkv][Tmax][128] in_dtype); no rotation.  Same q/out/workspace contract as
  * kvq_decode_attn.  Only the shape fields and in_dtype of p are used.

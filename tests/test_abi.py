@@ -92,3 +92,20 @@ def test_null_pointers_rejected_without_gpu():
     st = L.kvq_decode_attn(ctypes.byref(p), ctypes.byref(cs), None, seq, None, None, None, None, 0, None)
     assert st == -1
     assert L.kvq_status_str(-3) == b"KVQ_ERR_WORKSPACE"
+
+
+def test_adaptive_entry_points_validate_without_gpu():
+    L = kvq.lib()
+    p = kvq.make_params(2, 8, 2, 256)
+    seq = (ctypes.c_int32 * 2)(10, 10)
+    fake = 1 << 20  # never dereferenced: validation fails first
+    cs = kvq.CacheStruct(k_codes=fake, k_meta=fake, v_codes=fake, v_meta=fake, signs=fake)
+    assert L.kvq_block_mass(ctypes.byref(p), ctypes.byref(cs), None, seq, None, None) == -1
+    assert L.kvq_select_blocks(ctypes.byref(p), fake, seq, ctypes.c_float(1.5), None, fake, None) == -1
+    assert b"tau_cov" in L.kvq_last_error()
+    big = kvq.make_params(1, 8, 2, 64 * 8192)
+    one = (ctypes.c_int32 * 1)(10)
+    assert L.kvq_select_blocks(ctypes.byref(big), fake, one, ctypes.c_float(0.9), None, fake, None) == -2
+    # the dense fallback reads the originals: it needs keep_fp16_copy
+    st = L.kvq_dense_fallback(ctypes.byref(p), ctypes.byref(cs), fake, seq, ctypes.c_float(0.1), fake, fake, None)
+    assert st == -1 and b"keep_fp16_copy" in L.kvq_last_error()
