@@ -57,7 +57,17 @@ def parse():
     ap.add_argument("--window", type=str, default=None, metavar="SINK,RECENT",
                     help="workloads 3/4/5: keep the first SINK and last RECENT 64-token blocks of every "
                          "sequence at full precision")
+    ap.add_argument("--adaptive", type=str, default=None, metavar="TAU_COV,EPS",
+                    help="workload 3: also time the adaptive-precision ladder (scoring pass, top-K* promotion "
+                         "covering TAU_COV of the estimated mass, decode, dense fallback of heads whose "
+                         "certificate exceeds EPS)")
     args = ap.parse_args()
+    if args.adaptive is not None:
+        if args.workload != 3:
+            ap.error("--adaptive applies to workload 3 (the certified cache)")
+        args.adaptive = tuple(float(x) for x in args.adaptive.split(","))
+        if len(args.adaptive) != 2:
+            ap.error("--adaptive takes TAU_COV,EPS")
     if args.window is not None:
         if args.workload == 2:
             ap.error("--window applies to workloads 3, 4 and 5")
@@ -330,6 +340,9 @@ def bench_workload(cfg_id, args):
         result["append_roofline"] = {"bound": "alu", "achieved_gbs": round(app_bytes / app_s / 1e9, 1),
                                      "hbm_frac": round(app_bytes / app_s / 1e9 / HBM_PEAK_GBS, 4),
                                      "kernel": "append_fast_kernel<fp4, fp4>"}
+    if args.adaptive is not None:
+        result["adaptive"] = adaptive_ladder(args, c, p, caches, q, seq, ws, out, cert, bnd, flg, batch_time, n_each)
+        progress("adaptive ladder timed")
     if args.copy_calibration:
         src = torch.full((256 << 20,), 3, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -337,6 +350,63 @@ def bench_workload(cfg_id, args):
         dst.copy_(src)
         torch.cuda.synchronize()
     print(json.dumps(result))
+
+
+def adaptive_ladder(args, c, p, caches, q, seq, ws, out, cert, bnd, flg, batch_time, n_each):
+    """Times of the adaptive-precision ladder on the certified cache, stage by stage."""
+    import torch
+    import bit_kv_cache_append_amd as kvq
+    tau_cov, eps = args.adaptive
+    B, Hq, H, T = c["B"], c["Hq"], c["Hkv"], c["T"]
+    nrot = len(caches)
+    mass = torch.empty((B, Hq, T // 64), dtype=torch.float32, device=q.device)
+    prom = torch.empty_like(flg)
+
+    def stages(i, which):
+        cc = caches[i % nrot]
+        if "bound" in which:
+            kvq.error_bound(p, cc, q, seq, c["tau"], bound=bnd, flags=flg)
+        if "mass" in which:
+            kvq.block_mass(p, cc, q, seq, mass=mass)
+        if "select" in which:
+            kvq.select_blocks(p, mass, seq, tau_cov, flags_in=flg, flags_out=prom)
+        if "decode" in which:
+            kvq.decode_attn(p, cc, q, seq, flags=prom, certificate=True, ws=ws, out=out, cert=cert)
+        if "fallback" in which:
+            kvq.dense_fallback(p, cc, q, seq, eps, out, cert)
+
+    allst = ("bound", "mass", "select", "decode", "fallback")
+    for i in range(nrot):
+        stages(i, allst)
+    torch.cuda.synchronize()
+    step_ms = batch_time(lambda i: stages(i, allst), n_each)
+    mass_ms = batch_time(lambda i: stages(i, ("mass",)), n_each)
+    sel_ms = batch_time(lambda i: stages(i, ("select",)), n_each)
+    stages(0, ("bound", "mass", "select"))
+    dec_ms = batch_time(lambda i: kvq.decode_attn(p, caches[0], q, seq, flags=prom, certificate=True, ws=ws, out=out,
+                                                  cert=cert), n_each)
+    c0 = cert.clone()
+    fb_ms = batch_time(lambda i: (cert.copy_(c0), kvq.dense_fallback(p, caches[0], q, seq, eps, out, cert)), n_each)
+    torch.cuda.synchronize()
+    nprom = int(prom.sum().item())
+    nbound = int(flg.sum().item())
+    nfall = int((c0 > eps).sum().item())
+    sizes = kvq.buffer_bytes(p)
+    kbytes = sizes["k_codes"] + sizes["k_meta"] + B * Hq * 128 * 2 + B * Hq * (T // 64) * 4
+    return {
+        "tau_cov": tau_cov, "eps": eps,
+        "step_us": round(step_ms * 1e3, 2),
+        "block_mass_us": round(mass_ms * 1e3, 2),
+        "select_us": round(sel_ms * 1e3, 2),
+        "decode_promoted_us": round(dec_ms * 1e3, 2),
+        "fallback_us_incl_cert_copy": round(fb_ms * 1e3, 2),
+        "blocks_promoted": nprom, "blocks_flagged_by_bound": nbound, "blocks": int(prom.numel()),
+        "heads_fallen_back": nfall, "heads": B * Hq,
+        "block_mass_roofline": {"bound": "hbm", "achieved": round(kbytes / (mass_ms / 1e3) / 1e9, 1),
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(kbytes / (mass_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                                "kernel": "score_kernel + mass_kernel", "bytes_per_call": kbytes},
+    }
 
 
 def main():

@@ -4,6 +4,8 @@
 // it are promoted to the full-precision originals (through the decode pass's
 // exact-recompute flags), and a head whose certificate still exceeds a tolerance
 // is recomputed with dense attention over the originals.
+#include <algorithm>
+
 #include "kvq_common.h"
 
 namespace kvq {
@@ -66,105 +68,116 @@ __device__ __forceinline__ void rotated_query(const AdaptArgs& a, int b, int hq,
 
 typedef float v2f __attribute__((ext_vector_type(2)));
 
+// the two E2M1 codes of byte s of w as floats (the selector must be a constant)
+__device__ __forceinline__ v2f fp4_byte(uint32_t w, int s) {
+  switch (s) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  }
+}
+
 // Dequantized key channel values times the rotated query, summed per head:
-// acc[h] += sum_c qr[h][c] * k_hat[c] for the token's packed row.
+// acc[h] += sum_c qr[h][c] * k_hat[c] for the token's packed row.  Codes enter as
+// exact small floats; each group's sum is scaled once (INT2: plus offset times the
+// group's query sum, qsum[h][g]).  All four heads are computed (rows past the
+// group's last query head are zero).
+// One token's packed key row and its metadata, in registers.
 template <int KF, int KG>
-__device__ __forceinline__ void key_dot(const uint8_t* row, const uint8_t* meta, const float (*qr)[D], int nh,
+struct KeyRow {
+  static constexpr int NW = D * fmt_bits(KF) / 32;                   // 32-bit words of codes
+  static constexpr int NM = (meta_bytes(KF, fmt_group(KF, KG)) + 3) / 4;  // 32-bit words of metadata
+  uint32_t w[NW];
+  uint32_t m[NM];
+};
+
+template <int KF, int KG>
+__device__ __forceinline__ void load_key_row(const uint8_t* row, const uint8_t* meta, KeyRow<KF, KG>& r) {
+  const uint4* rp = reinterpret_cast<const uint4*>(row);
+#pragma unroll
+  for (int i = 0; i < KeyRow<KF, KG>::NW / 4; ++i) {
+    const uint4 u = rp[i];
+    r.w[4 * i] = u.x; r.w[4 * i + 1] = u.y; r.w[4 * i + 2] = u.z; r.w[4 * i + 3] = u.w;
+  }
+  constexpr int KM = meta_bytes(KF, fmt_group(KF, KG));
+  if constexpr (KM >= 16) {
+    const uint4 u = *reinterpret_cast<const uint4*>(meta);
+    r.m[0] = u.x; r.m[1] = u.y; r.m[2] = u.z; r.m[3] = u.w;
+  } else if constexpr (KM == 8) {
+    const uint2 u = *reinterpret_cast<const uint2*>(meta);
+    r.m[0] = u.x; r.m[1] = u.y;
+  } else {
+    r.m[0] = *reinterpret_cast<const uint16_t*>(meta);
+  }
+}
+
+// Dequantized key channel values times the rotated query, summed per head:
+// acc[h] = sum_c qr[h][c] * k_hat[c].  Codes enter as exact small floats; each
+// group's sum is scaled once (INT2: plus offset times the group's query sum,
+// qsum[h][g]).  All four heads are computed (rows past the group's last query
+// head are zero).
+template <int KF, int KG>
+__device__ __forceinline__ void key_dot(const KeyRow<KF, KG>& r, const float (*qr)[D], const float (*qsum)[4],
                                         float acc[4]) {
-  auto add = [&](int c, float v) {
+  constexpr int GS = fmt_group(KF, KG);  // channels per scale
+  constexpr int NG = D / GS;
+  float sc[NG], z[NG];
 #pragma unroll
-    for (int h = 0; h < 4; ++h)
-      if (h < nh) acc[h] = fmaf(qr[h][c], v, acc[h]);
-  };
-  if constexpr (KF == KVQ_INT4 || KF == KVQ_INT8) {
-    constexpr int NG = D / KG;
-    const uint16_t* mp = reinterpret_cast<const uint16_t*>(meta);
-    float sc[NG];
+  for (int g = 0; g < NG; ++g) {
+    if constexpr (KF == KVQ_FP4) {
+      sc[g] = e4m3_value((r.m[g >> 2] >> (8 * (g & 3))) & 0xFFu);
+    } else {
+      sc[g] = f16_bits_to_f32((uint16_t)(r.m[g >> 1] >> (16 * (g & 1))));
+      if constexpr (KF == KVQ_INT2) z[g] = f16_bits_to_f32((uint16_t)(r.m[(NG + g) >> 1] >> (16 * ((NG + g) & 1))));
+    }
+  }
+  constexpr int CPW = 32 / fmt_bits(KF);  // channels per 32-bit word
 #pragma unroll
-    for (int g = 0; g < NG; ++g) sc[g] = f16_bits_to_f32(mp[g]);
-    constexpr int NW = KF == KVQ_INT4 ? 16 : 32;  // 32-bit words per row
-    const uint4* rp = reinterpret_cast<const uint4*>(row);
+  for (int h = 0; h < 4; ++h) acc[h] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NW / 4; ++i) {
-      const uint4 u = rp[i];
-      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+  for (int g = 0; g < NG; ++g) {
+    float ag[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t w = w4[e];
-        if constexpr (KF == KVQ_INT4) {
+    for (int c = g * GS; c < (g + 1) * GS; ++c) {
+      const uint32_t ww = r.w[c / CPW];
+      const int n = c % CPW;
+      float v;
+      if constexpr (KF == KVQ_INT4) {
+        v = (float)(((int)(ww << (28 - 4 * n))) >> 28);
+      } else if constexpr (KF == KVQ_INT8) {
+        v = (float)(((int)(ww << (24 - 8 * n))) >> 24);
+      } else if constexpr (KF == KVQ_INT2) {
+        v = (float)((ww >> (2 * n)) & 3u);
+      } else {  // FP4: the gfx950 conversion of the two E2M1 codes of one byte (exact, scale 1)
+        if ((n & 1) != 0) continue;  // both channels of the byte are taken at the even one
+        const v2f p = fp4_byte(ww, n >> 1);
 #pragma unroll
-          for (int n = 0; n < 8; ++n) {
-            const int c = (4 * i + e) * 8 + n;
-            const int code = ((int)(w << (28 - 4 * n))) >> 28;
-            add(c, (float)code * sc[c / KG]);
-          }
-        } else {
-#pragma unroll
-          for (int n = 0; n < 4; ++n) {
-            const int c = (4 * i + e) * 4 + n;
-            const int code = ((int)(w << (24 - 8 * n))) >> 24;
-            add(c, (float)code * sc[c / KG]);
-          }
-        }
+        for (int h = 0; h < 4; ++h) ag[h] = fmaf(qr[h][c + 1], p.y, fmaf(qr[h][c], p.x, ag[h]));
+        continue;
       }
+#pragma unroll
+      for (int h = 0; h < 4; ++h) ag[h] = fmaf(qr[h][c], v, ag[h]);
     }
-  } else if constexpr (KF == KVQ_INT2) {
-    const uint16_t* mp = reinterpret_cast<const uint16_t*>(meta);
-    float sc[4], z[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      sc[g] = f16_bits_to_f32(mp[g]);
-      z[g] = f16_bits_to_f32(mp[4 + g]);
-    }
-    const uint4* rp = reinterpret_cast<const uint4*>(row);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint4 u = rp[i];
-      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int n = 0; n < 16; ++n) {
-          const int c = (4 * i + e) * 16 + n;
-          const float code = (float)((w4[e] >> (2 * n)) & 3u);
-          add(c, fmaf(code, sc[c / 32], z[c / 32]));
-        }
-    }
-  } else {  // FP4: E2M1 nibbles (even channel in the low nibble), one E4M3 scale per 16 channels
-    float sc[8];
-#pragma unroll
-    for (int g = 0; g < 8; ++g) sc[g] = e4m3_value(meta[g]);
-    const uint4* rp = reinterpret_cast<const uint4*>(row);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 u = rp[i];
-      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c0 = (4 * i + e) * 8;
-        const float s = sc[c0 / 16];
-        // the gfx950 conversion of the two E2M1 codes of one byte (exact, scale 1)
-        const v2f r0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w4[e], 1.0f, 0);
-        const v2f r1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w4[e], 1.0f, 1);
-        const v2f r2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w4[e], 1.0f, 2);
-        const v2f r3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w4[e], 1.0f, 3);
-        add(c0 + 0, r0.x * s); add(c0 + 1, r0.y * s);
-        add(c0 + 2, r1.x * s); add(c0 + 3, r1.y * s);
-        add(c0 + 4, r2.x * s); add(c0 + 5, r2.y * s);
-        add(c0 + 6, r3.x * s); add(c0 + 7, r3.y * s);
-      }
+    for (int h = 0; h < 4; ++h) {
+      acc[h] = fmaf(ag[h], sc[g], acc[h]);
+      if constexpr (KF == KVQ_INT2) acc[h] = fmaf(qsum[h][g], z[g], acc[h]);
     }
   }
 }
 
 // Scoring pass: log of the softmax numerator mass of every 64-token block,
 // lse_b = log sum_{t in b} exp(scale * q_rot . k_hat_t), per query head.  One
-// workgroup per (4 blocks, kv head, group of 4 query heads, sequence); one wave
+// workgroup per (4 blocks, kv head, group of 4 query heads, sequence), one wave
 // per block, one lane per token.  Written into mass, normalised by mass_kernel.
+// (VALU-bound: about 1000 vector instructions per block and wave, most of them the
+// 512 fma of four heads times 128 channels.)
 template <int KF, int KG>
 __global__ __launch_bounds__(NTA) void score_kernel(AdaptArgs a) {
   __shared__ float qr[4][D];
   __shared__ float tmp[4][D];
+  __shared__ float qsum[4][4];  // per head, per 32-channel group (INT2 offsets)
   const int b = blockIdx.z;
   const int HG = (a.G + 3) >> 2;
   const int hkv = blockIdx.y / HG, hg = blockIdx.y % HG;
@@ -174,16 +187,32 @@ __global__ __launch_bounds__(NTA) void score_kernel(AdaptArgs a) {
   const int T = a.seq.v[b];
   const int nchunks = (T + TILE - 1) / TILE;
   if ((int)blockIdx.x * 4 >= nchunks) return;  // uniform over the workgroup
-  if (wv < nh) rotated_query(a, b, hq0 + wv, qr[wv], tmp[wv]);
+  if (wv < nh) {
+    rotated_query(a, b, hq0 + wv, qr[wv], tmp[wv]);
+  } else {
+    qr[wv][2 * lane] = 0.0f;
+    qr[wv][2 * lane + 1] = 0.0f;
+  }
+  if constexpr (KF == KVQ_INT2) {
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    float v = qr[wv][2 * lane] + qr[wv][2 * lane + 1];  // lanes 16g..16g+15 hold group g
+    for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
+    if ((lane & 15) == 0) qsum[wv][lane >> 4] = v;
+  }
   __syncthreads();
   const int c = blockIdx.x * 4 + wv;
   if (c >= nchunks) return;  // no barrier follows
   constexpr int KB = row_bytes(KF);
-  constexpr int KM = meta_bytes(KF, KG);
+  constexpr int KM = meta_bytes(KF, fmt_group(KF, KG));
   const size_t stream = (size_t)b * a.H + hkv;
   const int t = c * TILE + lane;
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (t < T) key_dot<KF, KG>(a.k_codes + (stream * a.Tmax + t) * KB, a.k_meta + (stream * a.Tmax + t) * KM, qr, nh, acc);
+  if (t < T) {
+    KeyRow<KF, KG> R;
+    load_key_row<KF, KG>(a.k_codes + (stream * a.Tmax + t) * KB, a.k_meta + (stream * a.Tmax + t) * KM, R);
+    key_dot<KF, KG>(R, qr, qsum, acc);
+  }
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
     if (h >= nh) break;
@@ -218,59 +247,71 @@ __global__ __launch_bounds__(NTA) void mass_kernel(AdaptArgs a) {
   for (int j = t; j < a.nt; j += NTA) m[j] = j < nb ? expf(m[j] - lse) : 0.0f;
 }
 
-// Promotion flags of one (sequence, kv head): for each of its query heads, the
-// blocks sorted by decreasing mass (equal masses: lower index first) and the
-// shortest prefix whose fp32 running sum, taken in that order, reaches tau_cov;
-// the union over the query heads, OR the flags given.  The running sum is one
-// thread's sequential fp32 additions, so the choice is reproducible bit for bit.
+// Promotion flags.  flags_init_kernel writes the given flags (or zeros); then one
+// workgroup per (sequence, query head) sorts that head's blocks by decreasing mass
+// (equal masses: lower index first) and marks the shortest prefix whose fp32
+// running sum, taken in that order, reaches tau_cov.  The query heads of a kv head
+// mark the same flag row; they only ever store 1, so their order does not matter.
+// The running sum is one thread's sequential fp32 additions, so the choice is
+// reproducible bit for bit.
+__global__ __launch_bounds__(NTA) void flags_init_kernel(AdaptArgs a) {
+  const size_t n = (size_t)a.B * a.H * a.nt;
+  for (size_t j = (size_t)blockIdx.x * NTA + threadIdx.x; j < n; j += (size_t)gridDim.x * NTA)
+    a.flags_out[j] = (a.flags_in != nullptr && a.flags_in[j] != 0) ? 1 : 0;
+}
+
 __global__ __launch_bounds__(NTA) void select_kernel(AdaptArgs a) {
   __shared__ unsigned long long key[MAX_SELECT_BLOCKS];
-  __shared__ uint8_t fl[MAX_SELECT_BLOCKS];
   __shared__ int kstar;
-  const int b = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int row = blockIdx.x, b = row / a.Hq, h = (row % a.Hq) / a.G;
   const int t = threadIdx.x;
   const int nb = (a.seq.v[b] + TILE - 1) / TILE;
-  const size_t base = ((size_t)b * a.H + h) * a.nt;
-  for (int j = t; j < a.nt; j += NTA) fl[j] = (a.flags_in != nullptr && a.flags_in[base + j] != 0) ? 1 : 0;
+  if (nb == 0) return;  // uniform
   int npow = 2;
   while (npow < nb) npow <<= 1;
-  for (int g = 0; g < a.G && nb > 0; ++g) {
-    const float* m = a.mass + ((size_t)b * a.Hq + h * a.G + g) * a.nt;
-    __syncthreads();
-    for (int j = t; j < npow; j += NTA)
-      key[j] = j < nb ? (((unsigned long long)__float_as_uint(m[j]) << 32) | (0xFFFFFFFFu - (uint32_t)j)) : 0ull;
-    __syncthreads();
-    for (int k = 2; k <= npow; k <<= 1) {
-      for (int jj = k >> 1; jj > 0; jj >>= 1) {
-        for (int i = t; i < npow; i += NTA) {
-          const int ixj = i ^ jj;
-          if (ixj > i) {
-            const unsigned long long x = key[i], y = key[ixj];
-            const bool desc = (i & k) == 0;
-            if (desc ? (x < y) : (x > y)) {
-              key[i] = y;
-              key[ixj] = x;
-            }
+  const float* m = a.mass + (size_t)row * a.nt;
+  for (int j = t; j < npow; j += NTA)
+    key[j] = j < nb ? (((unsigned long long)__float_as_uint(m[j]) << 32) | (0xFFFFFFFFu - (uint32_t)j)) : 0ull;
+  __syncthreads();
+  for (int k = 2; k <= npow; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int i = t; i < npow; i += NTA) {
+        const int ixj = i ^ jj;
+        if (ixj > i) {
+          const unsigned long long x = key[i], y = key[ixj];
+          const bool desc = (i & k) == 0;
+          if (desc ? (x < y) : (x > y)) {
+            key[i] = y;
+            key[ixj] = x;
           }
         }
-        __syncthreads();
+      }
+      __syncthreads();
+    }
+  }
+  if (t == 0) {
+    // the masses are read 16 at a time (the LDS loads overlap) and added one by one
+    float run = 0.0f;
+    int k = 0;
+    bool done = false;
+    for (int k0 = 0; k0 < nb && !done; k0 += 16) {
+      float mk[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mk[i] = k0 + i < npow ? __uint_as_float((uint32_t)(key[k0 + i] >> 32)) : 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (!done && k0 + i < nb) {
+          run = run + mk[i];
+          k = k0 + i + 1;
+          done = run >= a.tau_cov;
+        }
       }
     }
-    if (t == 0) {
-      float run = 0.0f;
-      int k = 0;
-      while (k < nb) {
-        run = run + __uint_as_float((uint32_t)(key[k] >> 32));
-        ++k;
-        if (run >= a.tau_cov) break;
-      }
-      kstar = k;
-    }
-    __syncthreads();
-    for (int j = t; j < kstar; j += NTA) fl[0xFFFFFFFFu - (uint32_t)key[j]] = 1;
+    kstar = k;
   }
   __syncthreads();
-  for (int j = t; j < a.nt; j += NTA) a.flags_out[base + j] = fl[j];
+  uint8_t* fl = a.flags_out + ((size_t)b * a.H + h) * a.nt;
+  for (int j = t; j < kstar; j += NTA) fl[0xFFFFFFFFu - (uint32_t)key[j]] = 1;
 }
 
 // Dense fallback of one (sequence, query head): if its certificate exceeds eps,
@@ -382,7 +423,11 @@ hipError_t launch_block_mass(const AdaptArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_select(const AdaptArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(select_kernel, dim3(a.B * a.H), dim3(NTA), 0, s, a);
+  const size_t n = (size_t)a.B * a.H * a.nt;
+  hipLaunchKernelGGL(flags_init_kernel, dim3((unsigned)std::min<size_t>((n + NTA - 1) / NTA, 1024)), dim3(NTA), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(select_kernel, dim3(a.B * a.Hq), dim3(NTA), 0, s, a);
   return hipGetLastError();
 }
 
