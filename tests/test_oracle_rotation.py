@@ -103,3 +103,72 @@ def test_dense_rotation_close_to_matvec():
     # fp16 rounding of an orthogonal matrix keeps it orthogonal to ~1e-3
     R = rot.rotation_matrix_f64("dense", r16=r16)
     assert np.abs(R @ R.T - np.eye(128)).max() < 2e-3
+
+
+# ---- SRFT ("When Quantization Is Free", Methodology sections 1 and 2)
+
+def _signs(seed):
+    rng = np.random.default_rng(seed)
+    return np.where(rng.integers(0, 2, 128) == 1, 1, -1)
+
+
+def test_srft_matrix_is_orthonormal_and_the_packed_real_dft():
+    s = _signs(50)
+    R = rot.srft_matrix_f64(s)
+    assert np.abs(R @ R.T - np.eye(128)).max() < 1e-13
+    # against numpy's real FFT (a library routine): rows are DC, Nyquist, then Re/Im pairs
+    x = np.random.default_rng(51).standard_normal((4, 128))
+    X = np.fft.rfft(x * s, axis=-1)
+    y = x @ R.T
+    assert np.allclose(y[:, 0], X[:, 0].real / np.sqrt(128), atol=1e-12)
+    assert np.allclose(y[:, 1], X[:, 64].real / np.sqrt(128), atol=1e-12)
+    assert np.allclose(y[:, 2::2], X[:, 1:64].real * np.sqrt(2 / 128), atol=1e-12)
+    assert np.allclose(y[:, 3::2], X[:, 1:64].imag * np.sqrt(2 / 128), atol=1e-12)
+
+
+def test_stockham_fft_matches_numpy_fft():
+    rng = np.random.default_rng(52)
+    re = rng.standard_normal((8, 64)).astype(np.float32)
+    im = rng.standard_normal((8, 64)).astype(np.float32)
+    zr, zi = rot.stockham_fft64_f32(re, im)
+    Z = np.fft.fft(re.astype(np.float64) + 1j * im.astype(np.float64), axis=-1)
+    # fp32 butterflies: error grows like log2(64) roundings of values of size sqrt(64)
+    assert np.abs(zr - Z.real).max() < 2e-5 and np.abs(zi - Z.imag).max() < 2e-5
+    # an impulse at n gives W64^(k n) exactly in magnitude
+    e = np.zeros((64,), np.float32)
+    e[5] = 1.0
+    zr, zi = rot.stockham_fft64_f32(e, np.zeros_like(e))
+    assert np.allclose(zr + 1j * zi, np.exp(-2j * np.pi * 5 * np.arange(64) / 64), atol=1e-6)
+
+
+def test_srft_f32_close_to_the_matrix():
+    s = _signs(53)
+    x = np.random.default_rng(54).standard_normal((16, 128)).astype(np.float32) * 3
+    y = rot.srft_f32(x, s)
+    ref = x.astype(np.float64) @ rot.srft_matrix_f64(s).T
+    assert np.abs(y - ref).max() < 1e-5 * np.abs(ref).max() + 1e-7
+    assert np.allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x.astype(np.float64), axis=-1), rtol=1e-5)
+
+
+def test_srft_first_unit_vector_closed_form_exact():
+    # x = e_0: Z_k = s_0 for every k (only twiddles W^0 = 1 are applied), so X_k = s_0:
+    # y = s_0 (c0, c0, 1/8, 0, 1/8, 0, ...) exactly
+    s = _signs(55)
+    x = np.zeros(128, np.float32)
+    x[0] = 1.0
+    y = rot.srft_f32(x, s)
+    c0 = rot.INV_SQRT_D_F32
+    want = np.zeros(128, np.float32)
+    want[0] = want[1] = s[0] * c0
+    want[2::2] = s[0] * np.float32(0.125)
+    assert np.array_equal(y, want)  # +0 == -0
+
+
+def test_twiddles_are_the_rounded_fp64_values():
+    wr, wi = rot.twiddles_f32(128, 65)
+    assert wr[0] == 1.0 and wi[0] == 0.0 and wr[64] == -1.0
+    assert wr[32] == np.float32(np.cos(np.pi / 2)) and wi[32] == -1.0
+    for k in (1, 17, 45):
+        ang = 2 * np.pi * k / 128
+        assert wr[k] == np.float32(np.cos(ang)) and wi[k] == np.float32(-np.sin(ang))
+        assert abs(float(wr[k]) - np.cos(ang)) <= abs(np.spacing(np.float32(wr[k]))) / 2
