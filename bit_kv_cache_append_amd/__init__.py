@@ -18,12 +18,12 @@ LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
 F16, BF16 = 0, 1
 INT4, INT8, INT2, FP4 = 0, 1, 2, 3
-ROT_NONE, ROT_SIGN_FWHT, ROT_DENSE = 0, 1, 2
+ROT_NONE, ROT_SIGN_FWHT, ROT_DENSE, ROT_SRFT = 0, 1, 2, 3
 SCALE_ABSMAX, SCALE_SEARCH9, SCALE_SEARCH_OFFSETS = 0, 1, 2
 BUF_NAMES = ("k_codes", "k_meta", "v_codes", "v_meta", "blk_desc", "k_orig", "v_orig", "k_win", "v_win")
 
 _FMT = {"int4": INT4, "int8": INT8, "int2": INT2, "fp4": FP4}
-_ROT = {"none": ROT_NONE, "sign_fwht": ROT_SIGN_FWHT, "dense": ROT_DENSE}
+_ROT = {"none": ROT_NONE, "sign_fwht": ROT_SIGN_FWHT, "dense": ROT_DENSE, "srft": ROT_SRFT}
 _DT = {"f16": F16, "bf16": BF16}
 _SM = {"absmax": SCALE_ABSMAX, "search9": SCALE_SEARCH9, "offsets": SCALE_SEARCH_OFFSETS}
 

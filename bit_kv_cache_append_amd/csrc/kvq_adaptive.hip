@@ -26,11 +26,40 @@ __device__ __forceinline__ float wsum(float v) {
 // The query of head hq rotated like the cache (y = R q) and multiplied by the
 // softmax scale, into dst[128]; one wave, lane l computes channels 2l, 2l+1 (the
 // dense rotation: rows l and l + 64).  tmp: 128 floats of LDS private to the wave.
-__device__ __forceinline__ void rotated_query(const AdaptArgs& a, int b, int hq, float* dst, float* tmp) {
+__device__ __forceinline__ void rotated_query(const AdaptArgs& a, int b, int hq, float* dst, float* tmp,
+                                              const float* ctab) {
   const int l = threadIdx.x & 63;
   const bool bf16 = a.in_bf16 != 0;
   const uint16_t* qp = a.q + ((size_t)b * a.Hq + hq) * D;
   float x0 = widen(qp[2 * l], bf16), x1 = widen(qp[2 * l + 1], bf16);
+  if (a.rotation == KVQ_ROT_SRFT) {
+    // y = R q, R the packed unitary DFT times diag(s): lane l forms X_l (lane 0: X_0, X_64)
+    tmp[2 * l] = a.signs[2 * l] < 0 ? -x0 : x0;
+    tmp[2 * l + 1] = a.signs[2 * l + 1] < 0 ? -x1 : x1;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    float re = 0.0f, im = 0.0f, y0, y1;
+    if (l == 0) {
+      for (int n = 0; n < D; n += 2) {
+        re += tmp[n] + tmp[n + 1];
+        im += tmp[n] - tmp[n + 1];
+      }
+      const float c0 = bits_to_f32(KVQ_INV_SQRT_D_BITS);
+      y0 = re * c0;
+      y1 = im * c0;
+    } else {
+      for (int n = 0; n < D; ++n) {
+        const int ix = (l * n) & 127;
+        re = fmaf(tmp[n], ctab[ix], re);
+        im = fmaf(tmp[n], ctab[(ix + 96) & 127], im);
+      }
+      y0 = re * 0.125f;
+      y1 = -im * 0.125f;
+    }
+    dst[2 * l] = y0 * a.scale;
+    dst[2 * l + 1] = y1 * a.scale;
+    return;
+  }
   if (a.rotation == KVQ_ROT_DENSE) {
     tmp[2 * l] = x0;
     tmp[2 * l + 1] = x1;
@@ -178,6 +207,7 @@ __global__ __launch_bounds__(NTA) void score_kernel(AdaptArgs a) {
   __shared__ float qr[4][D];
   __shared__ float tmp[4][D];
   __shared__ float qsum[4][4];  // per head, per 32-channel group (INT2 offsets)
+  __shared__ float ctab[128];   // cos(2 pi k / 128) (SRFT)
   const int b = blockIdx.z;
   const int HG = (a.G + 3) >> 2;
   const int hkv = blockIdx.y / HG, hg = blockIdx.y % HG;
@@ -187,8 +217,12 @@ __global__ __launch_bounds__(NTA) void score_kernel(AdaptArgs a) {
   const int T = a.seq.v[b];
   const int nchunks = (T + TILE - 1) / TILE;
   if ((int)blockIdx.x * 4 >= nchunks) return;  // uniform over the workgroup
+  if (a.rotation == KVQ_ROT_SRFT) {
+    if (threadIdx.x < 128) ctab[threadIdx.x] = a.cos128[threadIdx.x];
+    __syncthreads();
+  }
   if (wv < nh) {
-    rotated_query(a, b, hq0 + wv, qr[wv], tmp[wv]);
+    rotated_query(a, b, hq0 + wv, qr[wv], tmp[wv], ctab);
   } else {
     qr[wv][2 * lane] = 0.0f;
     qr[wv][2 * lane + 1] = 0.0f;

@@ -52,7 +52,8 @@ kvq_status check_params(const kvq_params* p) {
   if (p->scale_mode != KVQ_SCALE_ABSMAX && p->scale_mode != KVQ_SCALE_SEARCH9 &&
       p->scale_mode != KVQ_SCALE_SEARCH_OFFSETS)
     return fail(KVQ_ERR_INVALID_ARG, "bad scale_mode");
-  if (p->rotation != KVQ_ROT_NONE && p->rotation != KVQ_ROT_SIGN_FWHT && p->rotation != KVQ_ROT_DENSE)
+  if (p->rotation != KVQ_ROT_NONE && p->rotation != KVQ_ROT_SIGN_FWHT && p->rotation != KVQ_ROT_DENSE &&
+      p->rotation != KVQ_ROT_SRFT)
     return fail(KVQ_ERR_INVALID_ARG, "bad rotation");
   if (!(p->softmax_scale >= 0.0f) || isinf(p->softmax_scale)) return fail(KVQ_ERR_INVALID_ARG, "bad softmax_scale");
   if (p->sink_blocks < 0 || p->recent_blocks < 0 || (long)p->sink_blocks + p->recent_blocks > p->max_ctx / TILE)
@@ -67,7 +68,8 @@ kvq_status check_cache(const kvq_params* p, const kvq_cache* c, bool need_desc) 
     return fail(KVQ_ERR_INVALID_ARG, "code/metadata buffers must be non-NULL");
   if (!aligned16(c->k_codes) || !aligned16(c->k_meta) || !aligned16(c->v_codes) || !aligned16(c->v_meta))
     return fail(KVQ_ERR_INVALID_ARG, "code/metadata buffers must be 16-byte aligned");
-  if (p->rotation == KVQ_ROT_SIGN_FWHT && !c->signs) return fail(KVQ_ERR_INVALID_ARG, "signs required for SIGN_FWHT");
+  if ((p->rotation == KVQ_ROT_SIGN_FWHT || p->rotation == KVQ_ROT_SRFT) && !c->signs)
+    return fail(KVQ_ERR_INVALID_ARG, "signs required for SIGN_FWHT and SRFT");
   if (p->rotation == KVQ_ROT_DENSE && (!c->rot_f16 || !aligned16(c->rot_f16)))
     return fail(KVQ_ERR_INVALID_ARG, "rot_f16 (16-byte aligned) required for DENSE");
   if (p->keep_fp16_copy) {
@@ -92,6 +94,20 @@ kvq_status check_seq(const kvq_params* p, const int32_t* seq_host, SeqArray& out
     out.v[b] = seq_host[b];
   }
   return KVQ_OK;
+}
+
+// SRFT twiddles W128^k = (fl32(cos(2 pi k / 128)), fl32(-sin(2 pi k / 128))), k = 0..64: the
+// fp64 values (angle computed as (2 pi) k / 128) rounded once
+void srft_twiddles(float* re, float* im) {
+  for (int k = 0; k <= 64; ++k) {
+    const double ang = 2.0 * M_PI * (double)k / 128.0;
+    re[k] = (float)cos(ang);
+    im[k] = (float)(-sin(ang));
+  }
+}
+// cos(2 pi k / 128), k = 0..127: entries of the SRFT matrix (query and output rotations)
+void srft_cos_table(float* c) {
+  for (int k = 0; k < 128; ++k) c[k] = (float)cos(2.0 * M_PI * (double)k / 128.0);
 }
 
 float softmax_scale(const kvq_params* p) { return p->softmax_scale > 0.0f ? p->softmax_scale : 1.0f / sqrtf((float)D); }
@@ -233,6 +249,7 @@ kvq_status kvq_append(const kvq_params* p, const kvq_cache* c, const void* k_new
   a.v_group = eff_group(p->v_fmt, p->v_group);
   a.scale_mode = p->scale_mode;
   a.rotation = p->rotation;
+  if (p->rotation == KVQ_ROT_SRFT) srft_twiddles(a.tw_re, a.tw_im);
   hipError_t e = launch_append(a, max_tiles, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "append launch");
   if (p->sink_blocks + p->recent_blocks > 0) {
@@ -251,7 +268,8 @@ kvq_status kvq_calibrate_clip(const kvq_params* p, const kvq_cache* c, const voi
   kvq_status st = check_params(p);
   if (st) return st;
   if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
-  if (p->rotation == KVQ_ROT_SIGN_FWHT && !c->signs) return fail(KVQ_ERR_INVALID_ARG, "signs required");
+  if ((p->rotation == KVQ_ROT_SIGN_FWHT || p->rotation == KVQ_ROT_SRFT) && !c->signs)
+    return fail(KVQ_ERR_INVALID_ARG, "signs required");
   if (p->rotation == KVQ_ROT_DENSE && !c->rot_f16) return fail(KVQ_ERR_INVALID_ARG, "rot_f16 required");
   if (n_tokens < 1) return fail(KVQ_ERR_INVALID_ARG, "n_tokens must be >= 1");
   if (!(ratio > 0.0f) || isinf(ratio)) return fail(KVQ_ERR_INVALID_ARG, "ratio must be positive and finite");
@@ -266,6 +284,7 @@ kvq_status kvq_calibrate_clip(const kvq_params* p, const kvq_cache* c, const voi
   a.in_bf16 = p->in_dtype == KVQ_BF16;
   a.rotation = p->rotation;
   a.ratio = ratio;
+  if (p->rotation == KVQ_ROT_SRFT) srft_twiddles(a.tw_re, a.tw_im);
   hipStream_t s = (hipStream_t)stream;
   a.x = (const uint16_t*)calib_k;
   a.out = clip_k_out;
@@ -367,6 +386,7 @@ static kvq_status decode_common(const kvq_params* p, const kvq_cache* c, const v
   a.chunks_per_split = (max_chunks + n_splits - 1) / n_splits;
   if (a.chunks_per_split < 1) a.chunks_per_split = 1;
   a.scale = softmax_scale(p);
+  if (a.rotation == KVQ_ROT_SRFT) srft_cos_table(a.cos128);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_decode(a, p->k_fmt, p->v_fmt, dense, s);
   if (e == hipErrorNotSupported) return fail(KVQ_ERR_UNSUPPORTED, "format combination not supported by decode");
@@ -386,6 +406,7 @@ static void adapt_common(const kvq_params* p, AdaptArgs& a) {
   a.k_fmt = p->k_fmt;
   a.k_group = eff_group(p->k_fmt, p->k_group);
   a.scale = softmax_scale(p);
+  if (p->rotation == KVQ_ROT_SRFT) srft_cos_table(a.cos128);
 }
 
 kvq_status kvq_block_mass(const kvq_params* p, const kvq_cache* c, const void* q, const int32_t* seq_len_host,

@@ -322,6 +322,88 @@ struct __align__(16) DenseSmem {
   uint16_t xs[TILE][D];  // input vectors (fp16/bf16 bits)
   float ys[TILE][D + 4];  // rotated vectors
 };
+struct __align__(16) SrftSmem {
+  float zre[TILE][65], zim[TILE][65];  // the 64 complex points of each vector
+  float twr[65], twi[65];              // W128^k
+};
+
+// SRFT ("When Quantization Is Free", Methodology sections 1-2) of the vector held by
+// a quad (lane q: channels 32q..32q+31), returned in the same layout: the sign flip,
+// z_n = u_2n + i u_2n+1 into LDS, six radix-2 Stockham passes of the 64-point FFT
+// (lane q computes butterflies 8q..8q+7 of each pass), the Hermitian unpack of
+// X_0..X_64 and the orthonormal packing.  All fp32 operations in the stated order
+// (this unit is compiled without contraction), so the result is bit-exact.
+// Every thread of the workgroup must call it (barriers); sm.twr/twi must be set
+// before the call.
+__device__ void srft_quad(float v[32], const int8_t* signs, int q, int vec, SrftSmem& sm) {
+  const int8_t* s = signs + 32 * q;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) v[j] = s[j] < 0 ? -v[j] : v[j];
+  float* zre = sm.zre[vec];
+  float* zim = sm.zim[vec];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    zre[16 * q + e] = v[2 * e];
+    zim[16 * q + e] = v[2 * e + 1];
+  }
+  __syncthreads();
+  int lm = 0;  // log2 of the stride m
+#pragma unroll
+  for (int pass = 0; pass < 6; ++pass, ++lm) {
+    const int m = 1 << lm, half = 32 >> lm;  // sub-length L = 64 >> pass, half = L / 2
+    float ar[8], ai[8], br[8], bi[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int bf = 8 * q + e, j = bf >> lm, k = bf & (m - 1);
+      ar[e] = zre[j * m + k];
+      ai[e] = zim[j * m + k];
+      br[e] = zre[(j + half) * m + k];
+      bi[e] = zim[(j + half) * m + k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int bf = 8 * q + e, j = bf >> lm, k = bf & (m - 1);
+      const float wr = sm.twr[2 * j * m], wi = sm.twi[2 * j * m];  // W64^(j m) = W128^(2 j m)
+      zre[2 * j * m + k] = ar[e] + br[e];
+      zim[2 * j * m + k] = ai[e] + bi[e];
+      const float dr = ar[e] - br[e], di = ai[e] - bi[e];
+      zre[(2 * j + 1) * m + k] = dr * wr - di * wi;
+      zim[(2 * j + 1) * m + k] = dr * wi + di * wr;
+    }
+    __syncthreads();
+  }
+  // X_k = E + W128^k O with A = Z_k, B = conj(Z_(64-k)), E = (A + B) / 2, O = (A - B) / 2i
+  auto unpack = [&](int k, float& xr, float& xi) {
+    const int ia = k & 63, ib = (64 - k) & 63;
+    const float a_re = zre[ia], a_im = zim[ia];
+    const float b_re = zre[ib], b_im = -zim[ib];
+    const float e_re = 0.5f * (a_re + b_re), e_im = 0.5f * (a_im + b_im);
+    const float o_re = 0.5f * (a_im - b_im), o_im = -(0.5f * (a_re - b_re));
+    const float wr = sm.twr[k], wi = sm.twi[k];
+    const float t_re = o_re * wr - o_im * wi, t_im = o_re * wi + o_im * wr;
+    xr = e_re + t_re;
+    xi = e_im + t_im;
+  };
+  const float c0 = bits_to_f32(KVQ_INV_SQRT_D_BITS);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int k = 16 * q + e;
+    float xr, xi;
+    if (k == 0) {
+      float nr, ni;
+      unpack(0, xr, xi);
+      unpack(64, nr, ni);
+      v[0] = xr * c0;
+      v[1] = nr * c0;
+    } else {
+      unpack(k, xr, xi);
+      v[2 * e] = xr * 0.125f;
+      v[2 * e + 1] = xi * 0.125f;
+    }
+  }
+  __syncthreads();  // the rows may be reused
+}
 
 
 // Rows lane and lane + 64 of the dense rotation for the 16 vectors of wave wv, NV
@@ -380,7 +462,7 @@ __device__ __forceinline__ void dense_rows(const uint16_t (*xs)[D], float (*ys)[
 
 }  // namespace
 
-template <bool DENSE>
+template <bool DENSE, bool SRFT>
 __global__ __launch_bounds__(NT) void append_kernel(AppendArgs a) {
   __shared__ StageSmem sm;
   const int b = blockIdx.z >> 1, h = blockIdx.y;
@@ -411,7 +493,16 @@ __global__ __launch_bounds__(NT) void append_kernel(AppendArgs a) {
   for (int j = 0; j < 32; ++j) xnorm2 = xnorm2 + x[j] * x[j];
 
   float y[32];
-  if (a.rotation == KVQ_ROT_SIGN_FWHT) {
+  if constexpr (SRFT) {
+    __shared__ SrftSmem ss;
+    if (t < 65) {
+      ss.twr[t] = a.tw_re[t];
+      ss.twi[t] = a.tw_im[t];
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) y[j] = x[j];
+    srft_quad(y, a.signs, q, tau, ss);
+  } else if (a.rotation == KVQ_ROT_SIGN_FWHT) {
 #pragma unroll
     for (int j = 0; j < 32; ++j) y[j] = x[j];
     sign_fwht(y, a.signs, q);
@@ -479,7 +570,11 @@ __global__ __launch_bounds__(NT) void append_kernel(AppendArgs a) {
 #pragma unroll
     for (int j = 0; j < 32; ++j) ynorm2 = ynorm2 + y[j] * y[j];
     // outward-rounded norms: fp32 sum/sqrt error and the rotation's own rounding
-    const float slack = a.rotation == KVQ_ROT_DENSE ? 2.44140625e-4f : (a.rotation == KVQ_ROT_SIGN_FWHT ? 9.5367431640625e-7f : 0.0f);
+    // (SRFT: six butterfly passes and the unpack, each a few fp32 roundings of values no
+    // larger than the vector norm, twiddles within half an ulp: far below 4e-6 relative)
+    const float slack = a.rotation == KVQ_ROT_DENSE ? 2.44140625e-4f
+                      : a.rotation == KVQ_ROT_SIGN_FWHT ? 9.5367431640625e-7f
+                      : a.rotation == KVQ_ROT_SRFT ? 4.0e-6f : 0.0f;
     float rn = sqrtf(quad_sum(res2)) * 1.0009765625f + sqrtf(quad_sum(ynorm2)) * slack;
     float vn = sqrtf(quad_sum(xnorm2)) * 1.0009765625f;
     if (!valid) {
@@ -1288,7 +1383,7 @@ static int dense_grid_limit(bool bf16) {
 
 hipError_t launch_append(const AppendArgs& a, int grid_x, hipStream_t s) {
   dim3 grid(grid_x, a.H, 2 * a.B);  // K and V of every sequence in one launch
-  if (a.rotation != KVQ_ROT_DENSE) {
+  if (a.rotation == KVQ_ROT_NONE || a.rotation == KVQ_ROT_SIGN_FWHT) {
     const dim3 fgrid(grid_x * a.H * 2 * a.B);
 #define KVQ_FAST(KF, KG, VF, VG)                                                       \
     if (a.k_fmt == KF && a.k_group == KG && a.v_fmt == VF && a.v_group == VG) {         \
@@ -1326,9 +1421,11 @@ hipError_t launch_append(const AppendArgs& a, int grid_x, hipStream_t s) {
     return hipGetLastError();
   }
   if (a.rotation == KVQ_ROT_DENSE)
-    hipLaunchKernelGGL(append_kernel<true>, grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((append_kernel<true, false>), grid, dim3(NT), 0, s, a);
+  else if (a.rotation == KVQ_ROT_SRFT)
+    hipLaunchKernelGGL((append_kernel<false, true>), grid, dim3(NT), 0, s, a);
   else
-    hipLaunchKernelGGL(append_kernel<false>, grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((append_kernel<false, false>), grid, dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1369,10 +1466,16 @@ hipError_t launch_window_copy(const AppendArgs& a, hipStream_t s) {
 __global__ __launch_bounds__(NT) void calibrate_kernel(CalibArgs a) {
   __shared__ DenseSmem sm;
   __shared__ unsigned int amax[D];
+  static_assert(sizeof(SrftSmem) <= sizeof(DenseSmem), "the SRFT rows share the dense staging area");
+  SrftSmem& ss = *reinterpret_cast<SrftSmem*>(&sm);  // used only by the SRFT rotation
   const int h = blockIdx.x;
   const int t = threadIdx.x, tau = t >> 2, q = t & 3;
   const bool bf16 = a.in_bf16 != 0;
   if (t < D) amax[t] = 0u;
+  if (a.rotation == KVQ_ROT_SRFT && t < 65) {
+    ss.twr[t] = a.tw_re[t];
+    ss.twi[t] = a.tw_im[t];
+  }
   float run[32];
 #pragma unroll
   for (int j = 0; j < 32; ++j) run[j] = 0.0f;
@@ -1415,6 +1518,7 @@ __global__ __launch_bounds__(NT) void calibrate_kernel(CalibArgs a) {
         for (int j = 0; j < 32; ++j) y[j] = 0.0f;
       }
       if (a.rotation == KVQ_ROT_SIGN_FWHT) sign_fwht(y, a.signs, q);
+      if (a.rotation == KVQ_ROT_SRFT) srft_quad(y, a.signs, q, t >> 2, ss);  // uniform: every thread
     }
     if (valid) {
 #pragma unroll

@@ -219,6 +219,7 @@ __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)"
 struct __align__(16) DecodeSmem {
   float qf[4][D];          // query (fp32), rotated in place
   float qr[4][D];          // dense rotation output
+  float ctab[128];         // cos(2 pi k / 128) for the SRFT rotation
   float qo[4][D];          // original query * scale * log2e (certified recompute)
   uint32_t qh[4][32];      // high int8 halves: dword 4n + c = MFMA operand of chain c, step n
   uint32_t ql[4][32];      // low int8 halves, same order
@@ -249,7 +250,8 @@ struct QueryIn {
 __device__ __forceinline__ QueryIn query_loads(const DecodeArgs& a, int b, int hq0, int nh) {
   const int t = threadIdx.x, j = t >> 6, l = t & 63;
   const uint16_t* qp = a.q + ((size_t)b * a.Hq + hq0 + (j < nh ? j : 0)) * D;
-  const int8_t* sp = a.rotation == KVQ_ROT_SIGN_FWHT ? a.signs : reinterpret_cast<const int8_t*>(a.q);
+  const int8_t* sp = (a.rotation == KVQ_ROT_SIGN_FWHT || a.rotation == KVQ_ROT_SRFT) ? a.signs
+                                                                                   : reinterpret_cast<const int8_t*>(a.q);
   QueryIn r;
   r.q0 = qp[2 * l];
   r.q1 = qp[2 * l + 1];
@@ -286,6 +288,37 @@ __device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryI
       y0 = up ? p0 - y0 : y0 + p0;
       y1 = up ? p1 - y1 : y1 + p1;
     }
+  } else if (a.rotation == KVQ_ROT_SRFT) {
+    // y = R q with R the packed unitary DFT times diag(s): lane l forms X_l =
+    // sum_n u_n e^(-2 pi i l n / 128), u = s * q, which gives channels 2l, 2l + 1
+    // (lane 0: X_0 and X_64)
+    if (own) {
+      sm.qf[j][2 * l] = (qin.sg & 0x80u) ? -x0 : x0;
+      sm.qf[j][2 * l + 1] = (qin.sg & 0x8000u) ? -x1 : x1;
+    }
+    if (t < 128) sm.ctab[t] = a.cos128[t];
+    __syncthreads();
+    if (own) {
+      float re = 0.0f, im = 0.0f;
+      if (l == 0) {
+        for (int n = 0; n < D; n += 2) {
+          re += sm.qf[j][n] + sm.qf[j][n + 1];
+          im += sm.qf[j][n] - sm.qf[j][n + 1];
+        }
+        const float c0 = bits_to_f32(KVQ_INV_SQRT_D_BITS);
+        y0 = re * c0;
+        y1 = im * c0;
+      } else {
+        for (int n = 0; n < D; ++n) {
+          const int ix = (l * n) & 127;
+          re = fmaf(sm.qf[j][n], sm.ctab[ix], re);
+          im = fmaf(sm.qf[j][n], sm.ctab[(ix + 96) & 127], im);  // sin = cos(. - pi/2)
+        }
+        y0 = re * 0.125f;
+        y1 = -im * 0.125f;
+      }
+    }
+    __syncthreads();
   } else if (a.rotation == KVQ_ROT_DENSE) {
     if (own) {
       sm.qf[j][2 * l] = x0;
@@ -437,7 +470,7 @@ __device__ void write_record(const DecodeArgs& a, DecodeSmem& sm, int b, int hq0
 // inverse rotation back to the original basis ("OSCAR", section 2.2B), and the
 // certificate.  zsw: 128 floats of LDS private to the wave.
 template <bool CERT, bool COH>
-__device__ void combine_row(const DecodeArgs& a, int row, float* zsw) {
+__device__ void combine_row(const DecodeArgs& a, int row, float* zsw, const float* ctab) {
   const int l = threadIdx.x & 63, c = 2 * l;
   const int b = row / a.Hq;
   float* out = a.out + (size_t)row * D;
@@ -518,6 +551,23 @@ __device__ void combine_row(const DecodeArgs& a, int row, float* zsw) {
     const float cn = bits_to_f32(KVQ_INV_SQRT_D_BITS);
     r0 *= a.signs[c] < 0 ? -cn : cn;
     r1 *= a.signs[c + 1] < 0 ? -cn : cn;
+  } else if (a.rotation == KVQ_ROT_SRFT) {
+    // R^T o: o_n = s_n (c0 (z_0 + (-1)^n z_1) + sum_{m=1..63} (z_2m cos - z_2m+1 sin)(2 pi m n / 128) / 8)
+    zsw[c] = o0;
+    zsw[c + 1] = o1;
+    __builtin_amdgcn_wave_barrier();
+    lds_wait();
+    const float c0 = bits_to_f32(KVQ_INV_SQRT_D_BITS);
+    float acc0 = 0.0f, acc1 = 0.0f;
+    for (int m = 1; m < 64; ++m) {
+      const int i0 = (m * c) & 127, i1 = (m * (c + 1)) & 127;
+      acc0 = fmaf(zsw[2 * m], ctab[i0], fmaf(-zsw[2 * m + 1], ctab[(i0 + 96) & 127], acc0));
+      acc1 = fmaf(zsw[2 * m], ctab[i1], fmaf(-zsw[2 * m + 1], ctab[(i1 + 96) & 127], acc1));
+    }
+    r0 = fmaf(c0, zsw[0] + zsw[1], 0.125f * acc0);   // n = c is even
+    r1 = fmaf(c0, zsw[0] - zsw[1], 0.125f * acc1);   // n = c + 1 is odd
+    if (a.signs[c] < 0) r0 = -r0;
+    if (a.signs[c + 1] < 0) r1 = -r1;
   } else if (a.rotation == KVQ_ROT_DENSE) {
     zsw[c] = o0;
     zsw[c + 1] = o1;
@@ -552,7 +602,7 @@ __global__ __launch_bounds__(NT) void combine_kernel(DecodeArgs a) {
   const int w = threadIdx.x >> 6;
   const int row = blockIdx.x * 4 + w;
   if (row >= a.B * a.Hq) return;  // whole waves; no barrier in combine_row
-  combine_row<CERT, false>(a, row, zs[w]);
+  combine_row<CERT, false>(a, row, zs[w], nullptr);  // the fp16 baseline has no rotation
 }
 
 // ------------------------------------------------------------------ split kernel
@@ -918,7 +968,6 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
         }
       }
     } else {  // INT2 values: codes 0..3, value = c * s + z
-      const h4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
       const uint2* zc2 = reinterpret_cast<const uint2*>(vml) + (4 + vgrp) * 16;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -934,10 +983,13 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
           const uint2 sc = sc2[s];
           const uint2 zc = zc2[s];
           const h4 A = cat(as_h2(A0) * as_h2(sc.x), as_h2(A1) * as_h2(sc.y));
-          const h4 Az = cat(as_h2(A0) * as_h2(zc.x), as_h2(A1) * as_h2(zc.y));
+          // zero points: P and z enter as separate operands, so each product p z is exact
+          // (a rounded fp16 p z would not cancel against the code term as it should)
+          const h4 Ap = cat(as_h2(A0), as_h2(A1));
+          const h4 Bz = cat(as_h2(zc.x), as_h2(zc.y));
           o[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, cat(c0[2 * kk], c0[2 * kk + 1]), o[0], 0, 0, 0);
           o[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, cat(c1[2 * kk], c1[2 * kk + 1]), o[1], 0, 0, 0);
-          oz = __builtin_amdgcn_mfma_f32_4x4x4f16(Az, ones, oz, 0, 0, 0);
+          oz = __builtin_amdgcn_mfma_f32_4x4x4f16(Ap, Bz, oz, 0, 0, 0);
         }
       }
     }
@@ -1131,7 +1183,7 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   }
   __syncthreads();
   if (sm.last) {
-    if (wv < nh) combine_row<EXACT, true>(a, b * a.Hq + hq0 + wv, &sm.qf[wv][0]);
+    if (wv < nh) combine_row<EXACT, true>(a, b * a.Hq + hq0 + wv, &sm.qf[wv][0], sm.ctab);
     if (t == 0) __hip_atomic_store(a.ctr + sidx, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }

@@ -51,6 +51,7 @@ struct AppendArgs {
   int32_t in_bf16;
   int32_t k_fmt, v_fmt, k_group, v_group, scale_mode, rotation;
   int32_t n_sink, n_recent;  // window blocks
+  float tw_re[65], tw_im[65];  // SRFT twiddles W128^k = (fl32(cos), fl32(-sin)) of 2 pi k / 128
   SeqArray start;
 };
 
@@ -61,6 +62,7 @@ struct CalibArgs {
   const uint16_t* rot;
   int32_t H, n, in_bf16, rotation;
   float ratio;
+  float tw_re[65], tw_im[65];  // SRFT twiddles
 };
 
 struct BoundArgs {
@@ -90,6 +92,7 @@ struct AdaptArgs {
   int32_t B, Hq, H, G, Tmax, nt;
   int32_t in_bf16, rotation, k_fmt, k_group;
   float scale, tau_cov, eps;
+  float cos128[128];  // fl32(cos(2 pi k / 128)): the SRFT matrix entries
   SeqArray seq;
 };
 constexpr int MAX_SELECT_BLOCKS = 4096;  // selection sorts one head's blocks in LDS
@@ -126,6 +129,7 @@ struct DecodeArgs {
   int32_t n_splits, chunks_per_split;
   int32_t n_sink, n_recent;  // window blocks (0, 0 = none)
   float scale;  // softmax scale
+  float cos128[128];  // fl32(cos(2 pi k / 128)): the SRFT matrix entries
   SeqArray seq;
 };
 

@@ -78,6 +78,13 @@ typedef int32_t kvq_status;
 #define KVQ_ROT_NONE 0
 #define KVQ_ROT_SIGN_FWHT 1 /* y = fl32(FWHT(s * x) * fl32(1/sqrt(128))) */
 #define KVQ_ROT_DENSE 2     /* y_j = sum_k R16[j][k] x_k, fp32 chain in k order */
+/* y = pack(F diag(s) x), F the unitary DFT ("When Quantization Is Free", Methodology
+ * sections 1-2): signs, the 64-point FFT of the channel pairs (x_2n + i x_2n+1) by
+ * six radix-2 Stockham passes, Hermitian unpack to the real DFT X_0..X_64, then
+ * y_0 = X_0 / sqrt(128), y_1 = X_64 / sqrt(128), y_2k = Re X_k / 8, y_2k+1 = Im X_k / 8
+ * (an orthonormal packing), all in fp32 in a fixed order with twiddles
+ * fl32(cos), fl32(-sin) of 2 pi k / 128 */
+#define KVQ_ROT_SRFT 3
 
 /* FP4 scale selection */
 #define KVQ_SCALE_ABSMAX 0  /* S = E4M3(absmax / 6) */
@@ -111,7 +118,7 @@ typedef struct kvq_params {
   int32_t k_group;        /* INT4/INT8: 32 or 128; ignored otherwise */
   int32_t v_group;        /* INT4: 32 or 128; ignored otherwise */
   int32_t scale_mode;     /* KVQ_SCALE_*: FP4 only */
-  int32_t rotation;       /* KVQ_ROT_* */
+  int32_t rotation;       /* KVQ_ROT_* (SIGN_FWHT and SRFT need signs) */
   int32_t keep_fp16_copy; /* nonzero: store originals + per-block descriptors */
   float softmax_scale;    /* 0 => 1/sqrt(head_dim) */
   /* Full-precision window ("OSCAR", section 2.2B, mixed-precision layout; "Search Your

@@ -32,6 +32,11 @@ CASES = {
     "fp4-offsets-bf16": synth.config(5, B=2, Hq=8, Hkv=2, T=256, scale_mode="offsets"),
     "fp4-offsets-dense-f16": synth.config(5, B=1, Hq=4, Hkv=2, T=192, dtype="f16", scale_mode="offsets",
                                           rotation="dense"),
+    # SRFT ("When Quantization Is Free", Methodology sections 1-2): the Stockham FFT write side
+    "int4-srft-f16": synth.config(1, B=2, Hq=2, Hkv=2, T=256, rotation="srft"),
+    "int8k-int4v-srft-cert": synth.config(3, B=2, Hq=8, Hkv=2, T=256, n_plant=2, rotation="srft"),
+    "int2-srft-bf16": synth.config(4, B=2, Hq=8, Hkv=2, T=256, dtype="bf16", rotation="srft"),
+    "fp4-srft": synth.config(5, B=2, Hq=8, Hkv=2, T=192, rotation="srft"),
 }
 
 
@@ -89,7 +94,7 @@ def test_append_full_bit_exact(name):
 
 
 @pytest.mark.parametrize("name", ["int4-g32-gqa", "int8k-int4v-cert", "fp4-search-bf16", "int2-dense",
-                                  "int2-dense-bf16"])
+                                  "int2-dense-bf16", "int4-srft-f16"])
 def test_append_ragged_pieces(name):
     c = CASES[name]
     print(f"[append-ragged] case {name}", flush=True)
