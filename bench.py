@@ -61,7 +61,12 @@ def parse():
                     help="workload 3: also time the adaptive-precision ladder (scoring pass, top-K* promotion "
                          "covering TAU_COV of the estimated mass, decode, dense fallback of heads whose "
                          "certificate exceeds EPS)")
+    ap.add_argument("--rotation", default="sign_fwht", choices=("sign_fwht", "srft"),
+                    help="workload 2: the rotation applied before quantization (sign + Walsh-Hadamard, or the "
+                         "sign + real-packed FFT form)")
     args = ap.parse_args()
+    if args.rotation != "sign_fwht" and args.workload != 2:
+        ap.error("--rotation applies to workload 2")
     if args.adaptive is not None:
         if args.workload != 3:
             ap.error("--adaptive applies to workload 3 (the certified cache)")
@@ -108,20 +113,20 @@ def cpu_baseline(c, sample_b):
     T, P = c["T"], c["prefill"]
     H = c["Hkv"]
     with threadpool_limits(1):
-        cs = synth.config(2, B=sample_b)
+        cs = synth.config(2, B=sample_b, rotation=c["rotation"])
         k = synth.kv_all(cs, 0, 0, T)
         v = synth.kv_all(cs, 1, 0, T)
         s = synth.signs(cs)
         oc = codec.Cache(sample_b, H, T, cs["k_fmt"], cs["v_fmt"], cs["k_group"], cs["v_group"])
-        codec.append(oc, k[:, :, :T - P], v[:, :, :T - P], np.zeros(sample_b, int), "f16", "sign_fwht", s,
+        codec.append(oc, k[:, :, :T - P], v[:, :, :T - P], np.zeros(sample_b, int), "f16", cs["rotation"], s,
                      scale_mode=cs["scale_mode"])
         t0 = time.perf_counter()
-        codec.append(oc, k[:, :, T - P:], v[:, :, T - P:], np.full(sample_b, T - P), "f16", "sign_fwht", s,
+        codec.append(oc, k[:, :, T - P:], v[:, :, T - P:], np.full(sample_b, T - P), "f16", cs["rotation"], s,
                      scale_mode=cs["scale_mode"])
         t_app = time.perf_counter() - t0
         q = synth.queries(cs)
         t0 = time.perf_counter()
-        attention.decode_attention(oc, q, "f16", np.full(sample_b, T), "sign_fwht", s)
+        attention.decode_attention(oc, q, "f16", np.full(sample_b, T), cs["rotation"], s)
         t_dec = time.perf_counter() - t0
     kv_bytes = sample_b * H * T * 144
     vecs = sample_b * H * P * 2
@@ -428,7 +433,7 @@ def main():
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     dev = torch.device("cuda:0")
-    c = synth.config(2)
+    c = synth.config(2, rotation=args.rotation)
     B, Hq, H, T, P = c["B"], c["Hq"], c["Hkv"], c["T"], c["prefill"]
     t_gen = time.perf_counter()
     k_all = synth.kv_all(c, 0, 0, T, workers=args.workers)
@@ -552,7 +557,7 @@ def main():
         "data": "synthetic (seeded fp16 N(0,1) K/V with outlier channels; no model weights)",
         "config": {"workload": "llama3-8b-shaped GQA int4 decode + prefill append", "B": B, "Hq": Hq, "Hkv": H,
                    "head_dim": 128, "context": T, "prefill_tokens": P, "k_fmt": "int4 g32", "v_fmt": "int4 g32",
-                   "rotation": "sign+fwht"},
+                   "rotation": {"sign_fwht": "sign+fwht", "srft": "sign+srft"}[args.rotation]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "decode_split<int4 g32, int4 g32> (one kvq_decode_attn call: one launch, splits merged by their last workgroup)",

@@ -301,9 +301,13 @@ def bytes_to_meta(b, fmt):
 class Cache:
     """Host mirror of the cache buffers, with the byte layout in the module doc."""
 
-    def __init__(self, B, H, Tmax, k_fmt, v_fmt, k_group=32, v_group=32, keep_fp16_copy=False):
+    def __init__(self, B, H, Tmax, k_fmt, v_fmt, k_group=32, v_group=32, keep_fp16_copy=False, lam_k=None,
+                 lam_v=None):
         if Tmax % TILE:
             raise ValueError("Tmax must be a multiple of 64")
+        # per-channel rescale factors [H, 128] (fp32) of K and V, or None
+        self.lam_k = None if lam_k is None else np.asarray(lam_k, np.float32)
+        self.lam_v = None if lam_v is None else np.asarray(lam_v, np.float32)
         self.B, self.H, self.Tmax = B, H, Tmax
         self.k_fmt, self.v_fmt, self.k_group, self.v_group = k_fmt, v_fmt, k_group, v_group
         nt = Tmax // TILE
@@ -365,13 +369,21 @@ def append(cache, k_bits, v_bits, start_pos, dtype, rotation, signs=None, r16=No
     order of "When Quantization Is Free", Methodology section 2: widen, sign flip,
     transform, per-group scale, round, pack.  clip_k/clip_v: per (kv head,
     channel) fp32 thresholds for int2 ("OSCAR", section 2.2A).
-    Returns the fp32 rotated vectors (yk, yv) for the caller's checks.
+    With per-channel rescale factors on the cache ("When Quantization Is Free",
+    Methodology sections 2 and 3: one scale per coordinate, then the per-group
+    scales), the rotated vectors are multiplied by them in fp32 before clipping
+    and quantization: y'_c = fl32(y_c * lambda_c).
+    Returns the fp32 rotated (and rescaled) vectors (yk, yv) for the caller's checks.
     """
     B, H, n, _ = k_bits.shape
     xk = nx.widen_input(k_bits, dtype)
     xv = nx.widen_input(v_bits, dtype)
     yk = rotate_input_f32(xk, rotation, signs, r16)
     yv = rotate_input_f32(xv, rotation, signs, r16)
+    if cache.lam_k is not None:
+        yk = nx.f32(yk * cache.lam_k[None, :, None, :])
+    if cache.lam_v is not None:
+        yv = nx.f32(yv * cache.lam_v[None, :, None, :])
     for b in range(B):
         t0 = int(start_pos[b])
         if t0 < 0 or t0 + n > cache.Tmax:
@@ -391,11 +403,15 @@ def append(cache, k_bits, v_bits, start_pos, dtype, rotation, signs=None, r16=No
 
 
 def decode_k(cache, b, h, t0, t1):
-    """Dequantized K (rotated basis, fp64) for positions [t0, t1) of stream (b, h)."""
+    """Dequantized K (rotated basis, fp64) for positions [t0, t1) of stream (b, h);
+    with per-channel rescale factors, the dequantized values divided by them."""
     signed = cache.k_fmt in ("int4", "int8")
     codes = unpack_elems(cache.k_codes[b, h, t0:t1], cache.k_fmt, signed)
     meta = bytes_to_meta(cache.k_meta[b, h, t0:t1], cache.k_fmt)
-    return dequantize(codes, meta, cache.k_fmt, cache.k_group)
+    out = dequantize(codes, meta, cache.k_fmt, cache.k_group)
+    if cache.lam_k is not None:
+        out = out / cache.lam_k[h].astype(np.float64)
+    return out
 
 
 def decode_v(cache, b, h, t0, t1):
@@ -408,19 +424,41 @@ def decode_v(cache, b, h, t0, t1):
         lo = max(t0, tile * TILE)
         hi = min(t1, (tile + 1) * TILE)
         out[lo - t0:hi - t0] = vals[lo - tile * TILE:hi - tile * TILE]
+    if cache.lam_v is not None:
+        out = out / cache.lam_v[h].astype(np.float64)
     return out
 
 
-def calibrate_clip(calib_bits, dtype, rotation, signs=None, r16=None, ratio=0.9):
+def calibrate_clip(calib_bits, dtype, rotation, signs=None, r16=None, ratio=0.9, lam=None):
     """Per-channel clipping thresholds from rotated calibration vectors.
 
     "OSCAR", section 2.2A: thresholds are estimated from the *rotated*
     calibration activations.  Reading taken: t_c = fl32(ratio * max_t |y_t,c|)
     per (kv head, channel), with y the same fp32 write-side rotation as append
-    and ratio = fl32(0.9) for the configured workload.
+    and ratio = fl32(0.9) for the configured workload; with per-channel rescale
+    factors lam [H, 128], y is rescaled first (the vectors as the quantizer sees them).
+    calib_bits: uint16 [H, n, 128]; returns float32 [H, 128].
+    """
+    x = nx.widen_input(calib_bits, dtype)
+    y = rotate_input_f32(x, rotation, signs, r16)
+    if lam is not None:
+        y = nx.f32(y * np.asarray(lam, np.float32)[:, None, :])
+    a = np.max(np.abs(y), axis=-2)
+    return nx.f32(np.float32(ratio) * a)
+
+
+def calibrate_lambda(calib_bits, dtype, rotation, signs=None, r16=None):
+    """Per-channel rescale factors from rotated calibration vectors.
+
+    "When Quantization Is Free", Methodology section 2 (a per-channel rescale,
+    learned or calibrated, before the per-group absmax) and section 3 (one scale
+    per coordinate combined with per-group scales).  Reading taken (calibrated):
+    lambda_c = fl32(1 / max_t |y_t,c|) per (kv head, channel), 1 where the maximum
+    is 0, so every channel spans [-1, 1] before the group scales.
     calib_bits: uint16 [H, n, 128]; returns float32 [H, 128].
     """
     x = nx.widen_input(calib_bits, dtype)
     y = rotate_input_f32(x, rotation, signs, r16)
     a = np.max(np.abs(y), axis=-2)
-    return nx.f32(np.float32(ratio) * a)
+    one = np.float32(1.0)
+    return np.where(a > 0, nx.f32(one / np.where(a > 0, a, one)), one).astype(np.float32)

@@ -4,6 +4,7 @@ import os
 import numpy as np
 import pytest
 
+import synth
 from oracle import codec, numerics as nx, rotation as rot
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
@@ -284,3 +285,68 @@ def test_calibrate_clip_definition():
     y = x.view(np.float16).astype(np.float64) @ r16.astype(np.float64).T
     ref = 0.9 * np.abs(y).max(axis=1)
     assert np.allclose(t, ref, rtol=1e-5)
+
+
+# ---- per-channel rescale ("When Quantization Is Free", Methodology sections 2 and 3)
+
+def _append_with(lam_k, lam_v, k, v, fmt="int4", group=32, rotation="sign_fwht", signs=None):
+    B, H, T, _ = k.shape
+    c = codec.Cache(B, H, T, fmt, fmt, group, group, lam_k=lam_k, lam_v=lam_v)
+    codec.append(c, synth.to_bits(k, "f16"), synth.to_bits(v, "f16"), np.zeros(B, int), "f16", rotation, signs)
+    return c
+
+
+def test_lambda_of_ones_changes_nothing():
+    rng = np.random.default_rng(60)
+    s = np.where(rng.integers(0, 2, 128) == 1, 1, -1)
+    k, v = rng.standard_normal((2, 1, 2, 64, 128))
+    plain = _append_with(None, None, k, v, signs=s)
+    ones = np.ones((2, 128), np.float32)
+    lam = _append_with(ones, ones, k, v, signs=s)
+    for n in ("k_codes", "k_meta", "v_codes", "v_meta"):
+        assert np.array_equal(getattr(plain, n), getattr(lam, n))
+
+
+def test_lambda_powers_of_two_per_group_are_exact():
+    # multiplying a whole 32-channel group by 2^e scales its absmax and fp16 scale exactly, so
+    # the codes are unchanged and the rescaled-back decode equals the plain one
+    rng = np.random.default_rng(61)
+    k, v = rng.standard_normal((2, 1, 2, 64, 128))
+    lam = np.repeat(np.array([[2.0 ** -3, 2.0, 1.0, 2.0 ** 4], [0.5, 8.0, 2.0 ** -2, 1.0]], np.float32), 32, axis=1)
+    plain = _append_with(None, None, k, v, rotation="none")
+    scaled = _append_with(lam, lam, k, v, rotation="none")
+    assert np.array_equal(plain.k_codes, scaled.k_codes) and np.array_equal(plain.v_codes, scaled.v_codes)
+    for h in range(2):
+        assert np.array_equal(codec.decode_k(plain, 0, h, 0, 64), codec.decode_k(scaled, 0, h, 0, 64))
+        assert np.array_equal(codec.decode_v(plain, 0, h, 0, 64), codec.decode_v(scaled, 0, h, 0, 64))
+
+
+def test_calibrate_lambda_brute_force():
+    rng = np.random.default_rng(62)
+    x = rng.standard_normal((2, 50, 128)).astype(np.float32)
+    x[1, :, 7] = 0.0  # an all-zero channel gets 1
+    lam = codec.calibrate_lambda(synth.to_bits(x, "f16"), "f16", "none")
+    xb = synth.to_bits(x, "f16").view(np.float16).astype(np.float32)
+    for h in range(2):
+        for c in range(128):
+            m = max(abs(float(t)) for t in xb[h, :, c])
+            want = np.float32(1.0) / np.float32(m) if m > 0 else np.float32(1.0)
+            assert lam[h, c] == want
+
+
+def test_lambda_helps_groups_with_an_outlier_channel():
+    # the case of section 3: without a per-channel scale, one large coordinate sets the group's
+    # scale and the other 31 channels of the group lose most of their resolution
+    rng = np.random.default_rng(63)
+    x = rng.standard_normal((1, 1, 512, 128))
+    x[..., ::32] *= 60.0  # one outlier channel per group
+    bits = synth.to_bits(x, "f16")
+    lam = codec.calibrate_lambda(bits[0], "f16", "none")
+    y = bits.view(np.float16).astype(np.float64)[0, 0]
+    plain = _append_with(None, None, x, x, rotation="none")
+    scaled = _append_with(lam, lam, x, x, rotation="none")
+    normal = np.ones(128, bool)
+    normal[::32] = False
+    e_plain = np.mean((codec.decode_k(plain, 0, 0, 0, 512) - y)[:, normal] ** 2)
+    e_lam = np.mean((codec.decode_k(scaled, 0, 0, 0, 512) - y)[:, normal] ** 2)
+    assert e_lam < 0.05 * e_plain, (e_lam, e_plain)
