@@ -4,7 +4,7 @@ Every computation runs in the HIP kernels of libkvq.so; this module turns torch
 tensors into device pointers and the current HIP stream, calls the C entry
 points of the same names (kvq_append, kvq_error_bound, kvq_decode_attn,
 kvq_decode_attn_dense, kvq_calibrate_clip, kvq_block_mass, kvq_select_blocks,
-kvq_dense_fallback, kvq_buffer_bytes, kvq_decode_workspace_bytes, kvq_decode_splits) and raises KvqError on a non-zero status.  There is
+kvq_dense_fallback, kvq_calibrate_lambda, kvq_buffer_bytes, kvq_decode_workspace_bytes, kvq_decode_splits) and raises KvqError on a non-zero status.  There is
 no fallback: if the library is not built, importing the functions raises.
 """
 
@@ -48,7 +48,7 @@ class Params(ctypes.Structure):
 class CacheStruct(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("k_codes", "k_meta", "v_codes", "v_meta", "blk_desc",
                                                "k_orig", "v_orig", "signs", "rot_f16", "clip_k", "clip_v",
-                                               "k_win", "v_win")]
+                                               "k_win", "v_win", "lambda_k", "lambda_v")]
 
 
 _lib = None
@@ -86,6 +86,8 @@ def lib():
         L.kvq_select_blocks.argtypes = [P(Params), vp, P(i32), ctypes.c_float, vp, vp, vp]
         L.kvq_dense_fallback.restype = i32
         L.kvq_dense_fallback.argtypes = [P(Params), P(CacheStruct), vp, P(i32), ctypes.c_float, vp, vp, vp]
+        L.kvq_calibrate_lambda.restype = i32
+        L.kvq_calibrate_lambda.argtypes = [P(Params), P(CacheStruct), vp, vp, i32, vp, vp, vp]
         L.kvq_calibrate_clip.restype = i32
         L.kvq_calibrate_clip.argtypes = [P(Params), P(CacheStruct), vp, vp, i32, ctypes.c_float, vp, vp, vp]
         _lib = L
@@ -151,7 +153,8 @@ def _i32(a):
 class Cache:
     """The device buffers of one cache, allocated with torch (zero-filled)."""
 
-    def __init__(self, p, device="cuda", signs=None, rot_f16=None, clip_k=None, clip_v=None):
+    def __init__(self, p, device="cuda", signs=None, rot_f16=None, clip_k=None, clip_v=None, lambda_k=None,
+                 lambda_v=None):
         import torch
         self.p = p
         sizes = buffer_bytes(p)
@@ -167,12 +170,15 @@ class Cache:
         self.rot_f16 = rot_f16
         self.clip_k = clip_k
         self.clip_v = clip_v
+        self.lambda_k = lambda_k
+        self.lambda_v = lambda_v
 
     def struct(self):
         b = self.bufs
         ptr = lambda t: None if t is None else t.data_ptr()
         return CacheStruct(*[ptr(b[n]) for n in BUF_NAMES[:7]], ptr(self.signs), ptr(self.rot_f16),
-                           ptr(self.clip_k), ptr(self.clip_v), ptr(b["k_win"]), ptr(b["v_win"]))
+                           ptr(self.clip_k), ptr(self.clip_v), ptr(b["k_win"]), ptr(b["v_win"]),
+                           ptr(self.lambda_k), ptr(self.lambda_v))
 
 
 def append(p, cache, k_new, v_new, start_pos, stream=None):
@@ -271,6 +277,18 @@ def calibrate_clip(p, cache, calib_k, calib_v, ratio=0.9, stream=None):
                                     int(calib_k.shape[1]), float(ratio), _ptr(ck), _ptr(cv),
                                     stream if stream is not None else _stream()))
     return ck, cv
+
+
+def calibrate_lambda(p, cache, calib_k, calib_v, stream=None):
+    """kvq_calibrate_lambda: per-channel rescale factors fp32 [Hkv, 128] of K and V."""
+    import torch
+    lk = torch.empty((p.n_kv_heads, 128), dtype=torch.float32, device=calib_k.device)
+    lv = torch.empty((p.n_kv_heads, 128), dtype=torch.float32, device=calib_k.device)
+    cs = cache.struct()
+    _check(lib().kvq_calibrate_lambda(ctypes.byref(p), ctypes.byref(cs), _ptr(calib_k), _ptr(calib_v),
+                                      int(calib_k.shape[1]), _ptr(lk), _ptr(lv),
+                                      stream if stream is not None else _stream()))
+    return lk, lv
 
 
 def to_device_bits(a, device="cuda"):

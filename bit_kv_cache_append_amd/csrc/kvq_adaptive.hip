@@ -223,6 +223,13 @@ __global__ __launch_bounds__(NTA) void score_kernel(AdaptArgs a) {
   }
   if (wv < nh) {
     rotated_query(a, b, hq0 + wv, qr[wv], tmp[wv], ctab);
+    if (a.lam_k != nullptr) {  // keys were stored times lambda_k
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      const float* lp = a.lam_k + (size_t)hkv * D;
+      qr[wv][2 * lane] = qr[wv][2 * lane] / lp[2 * lane];
+      qr[wv][2 * lane + 1] = qr[wv][2 * lane + 1] / lp[2 * lane + 1];
+    }
   } else {
     qr[wv][2 * lane] = 0.0f;
     qr[wv][2 * lane + 1] = 0.0f;

@@ -80,6 +80,8 @@ kvq_status check_cache(const kvq_params* p, const kvq_cache* c, bool need_desc) 
   } else if (need_desc) {
     return fail(KVQ_ERR_INVALID_ARG, "this call needs keep_fp16_copy");
   }
+  if (p->keep_fp16_copy && (c->lambda_k || c->lambda_v))
+    return fail(KVQ_ERR_UNSUPPORTED, "per-channel rescale factors are not supported with keep_fp16_copy");
   if (p->sink_blocks + p->recent_blocks > 0 &&
       (!c->k_win || !c->v_win || !aligned16(c->k_win) || !aligned16(c->v_win)))
     return fail(KVQ_ERR_INVALID_ARG, "a window (sink_blocks + recent_blocks > 0) needs k_win and v_win, 16-byte aligned");
@@ -238,6 +240,8 @@ kvq_status kvq_append(const kvq_params* p, const kvq_cache* c, const void* k_new
   a.rot = c->rot_f16;
   a.clip_k = p->k_fmt == KVQ_INT2 ? c->clip_k : nullptr;
   a.clip_v = p->v_fmt == KVQ_INT2 ? c->clip_v : nullptr;
+  a.lam_k = c->lambda_k;
+  a.lam_v = c->lambda_v;
   a.B = p->batch;
   a.H = p->n_kv_heads;
   a.Tmax = p->max_ctx;
@@ -288,10 +292,45 @@ kvq_status kvq_calibrate_clip(const kvq_params* p, const kvq_cache* c, const voi
   hipStream_t s = (hipStream_t)stream;
   a.x = (const uint16_t*)calib_k;
   a.out = clip_k_out;
+  a.lam = c->lambda_k;
   hipError_t e = launch_calibrate(a, s);
   if (e != hipSuccess) return hip_fail(e, "calibrate launch");
   a.x = (const uint16_t*)calib_v;
   a.out = clip_v_out;
+  a.lam = c->lambda_v;
+  e = launch_calibrate(a, s);
+  if (e != hipSuccess) return hip_fail(e, "calibrate launch");
+  return KVQ_OK;
+}
+
+kvq_status kvq_calibrate_lambda(const kvq_params* p, const kvq_cache* c, const void* calib_k, const void* calib_v,
+                                int32_t n_tokens, float* lambda_k_out, float* lambda_v_out, void* stream) {
+  kvq_status st = check_params(p);
+  if (st) return st;
+  if (!c) return fail(KVQ_ERR_INVALID_ARG, "cache is NULL");
+  if ((p->rotation == KVQ_ROT_SIGN_FWHT || p->rotation == KVQ_ROT_SRFT) && !c->signs)
+    return fail(KVQ_ERR_INVALID_ARG, "signs required");
+  if (p->rotation == KVQ_ROT_DENSE && !c->rot_f16) return fail(KVQ_ERR_INVALID_ARG, "rot_f16 required");
+  if (n_tokens < 1) return fail(KVQ_ERR_INVALID_ARG, "n_tokens must be >= 1");
+  if (!calib_k || !calib_v || !lambda_k_out || !lambda_v_out || !aligned16(calib_k) || !aligned16(calib_v))
+    return fail(KVQ_ERR_INVALID_ARG, "calibration buffers must be non-NULL (inputs 16-byte aligned)");
+  CalibArgs a;
+  memset(&a, 0, sizeof(a));
+  a.signs = c->signs;
+  a.rot = c->rot_f16;
+  a.H = p->n_kv_heads;
+  a.n = n_tokens;
+  a.in_bf16 = p->in_dtype == KVQ_BF16;
+  a.rotation = p->rotation;
+  a.mode = 1;
+  if (p->rotation == KVQ_ROT_SRFT) srft_twiddles(a.tw_re, a.tw_im);
+  hipStream_t s = (hipStream_t)stream;
+  a.x = (const uint16_t*)calib_k;
+  a.out = lambda_k_out;
+  hipError_t e = launch_calibrate(a, s);
+  if (e != hipSuccess) return hip_fail(e, "calibrate launch");
+  a.x = (const uint16_t*)calib_v;
+  a.out = lambda_v_out;
   e = launch_calibrate(a, s);
   if (e != hipSuccess) return hip_fail(e, "calibrate launch");
   return KVQ_OK;
@@ -359,6 +398,8 @@ static kvq_status decode_common(const kvq_params* p, const kvq_cache* c, const v
       a.v_orig = (const uint16_t*)c->v_orig;
     }
     a.flags = flags;
+    a.lam_k = c->lambda_k;
+    a.lam_v = c->lambda_v;
     if (p->sink_blocks + p->recent_blocks > 0) {
       a.k_win = (const uint16_t*)c->k_win;
       a.v_win = (const uint16_t*)c->v_win;
@@ -424,6 +465,7 @@ kvq_status kvq_block_mass(const kvq_params* p, const kvq_cache* c, const void* q
   a.k_meta = (const uint8_t*)c->k_meta;
   a.signs = c->signs;
   a.rot = c->rot_f16;
+  a.lam_k = c->lambda_k;
   a.mass = mass;
   hipError_t e = launch_block_mass(a, (hipStream_t)stream);
   if (e == hipErrorNotSupported) return fail(KVQ_ERR_UNSUPPORTED, "key format not supported by the scoring pass");

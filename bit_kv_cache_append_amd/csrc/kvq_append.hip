@@ -542,6 +542,13 @@ __global__ __launch_bounds__(NT) void append_kernel(AppendArgs a) {
     for (int j = 0; j < 32; ++j) y[j] = x[j];
   }
 
+  // per-channel rescale ("When Quantization Is Free", Methodology sections 2-3), fp32
+  if (const float* lam = tensor ? a.lam_v : a.lam_k) {
+    const float* lp = lam + (size_t)h * D + 32 * q;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) y[j] = y[j] * lp[j];
+  }
+
   // quantize
   int codes[32];
   uint16_t m0 = 0, m1 = 0;  // metadata elements of this lane
@@ -1383,7 +1390,8 @@ static int dense_grid_limit(bool bf16) {
 
 hipError_t launch_append(const AppendArgs& a, int grid_x, hipStream_t s) {
   dim3 grid(grid_x, a.H, 2 * a.B);  // K and V of every sequence in one launch
-  if (a.rotation == KVQ_ROT_NONE || a.rotation == KVQ_ROT_SIGN_FWHT) {
+  const bool rescale = a.lam_k != nullptr || a.lam_v != nullptr;  // the generic kernel applies it
+  if ((a.rotation == KVQ_ROT_NONE || a.rotation == KVQ_ROT_SIGN_FWHT) && !rescale) {
     const dim3 fgrid(grid_x * a.H * 2 * a.B);
 #define KVQ_FAST(KF, KG, VF, VG)                                                       \
     if (a.k_fmt == KF && a.k_group == KG && a.v_fmt == VF && a.v_group == VG) {         \
@@ -1410,7 +1418,7 @@ hipError_t launch_append(const AppendArgs& a, int grid_x, hipStream_t s) {
       return hipGetLastError();
     }
   }
-  if (a.rotation == KVQ_ROT_DENSE && a.desc == nullptr && a.k_fmt == KVQ_INT2 && a.v_fmt == KVQ_INT2 &&
+  if (a.rotation == KVQ_ROT_DENSE && a.desc == nullptr && !rescale && a.k_fmt == KVQ_INT2 && a.v_fmt == KVQ_INT2 &&
       a.k_group == 32 && a.v_group == 32) {
     const int nunits = grid_x * a.H * 2 * a.B;
     const int g = std::min(nunits, dense_grid_limit(a.in_bf16 != 0));
@@ -1520,6 +1528,11 @@ __global__ __launch_bounds__(NT) void calibrate_kernel(CalibArgs a) {
       if (a.rotation == KVQ_ROT_SIGN_FWHT) sign_fwht(y, a.signs, q);
       if (a.rotation == KVQ_ROT_SRFT) srft_quad(y, a.signs, q, t >> 2, ss);  // uniform: every thread
     }
+    if (a.lam != nullptr && a.mode == 0) {  // thresholds of the rescaled vectors
+      const float* lp = a.lam + (size_t)h * D + 32 * q;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) y[j] = y[j] * lp[j];
+    }
     if (valid) {
 #pragma unroll
       for (int j = 0; j < 32; ++j) run[j] = fmaxf(run[j], fabsf(y[j]));
@@ -1529,7 +1542,10 @@ __global__ __launch_bounds__(NT) void calibrate_kernel(CalibArgs a) {
 #pragma unroll
   for (int j = 0; j < 32; ++j) atomicMax(&amax[32 * q + j], __float_as_uint(run[j]));
   __syncthreads();
-  if (t < D) a.out[(size_t)h * D + t] = a.ratio * __uint_as_float(amax[t]);
+  if (t < D) {
+    const float m = __uint_as_float(amax[t]);
+    a.out[(size_t)h * D + t] = a.mode == 0 ? a.ratio * m : (m > 0.0f ? 1.0f / m : 1.0f);
+  }
 }
 
 hipError_t launch_calibrate(const CalibArgs& a, hipStream_t s) {

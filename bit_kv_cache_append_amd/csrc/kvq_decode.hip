@@ -260,7 +260,7 @@ __device__ __forceinline__ QueryIn query_loads(const DecodeArgs& a, int b, int h
 }
 
 template <int KF>
-__device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryIn& qin, int nh, int kgroup) {
+__device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryIn& qin, int nh, int kgroup, int hkv) {
   // waves 0..3 own query heads 0..3; further waves only join the barriers
   const int t = threadIdx.x, l = t & 63;
   const bool own = (t >> 6) < 4;
@@ -336,6 +336,10 @@ __device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryI
     __syncthreads();
     y0 = sm.qr[j][2 * l];
     y1 = sm.qr[j][2 * l + 1];
+  }
+  if (a.lam_k != nullptr) {  // keys were stored times lambda_k: q . y = (q / lambda) . (lambda y)
+    y0 = y0 / a.lam_k[(size_t)hkv * D + 2 * l];
+    y1 = y1 / a.lam_k[(size_t)hkv * D + 2 * l + 1];
   }
   const float norm = a.rotation == KVQ_ROT_SIGN_FWHT ? bits_to_f32(KVQ_INV_SQRT_D_BITS) : 1.0f;
   y0 = y0 * norm * pre;
@@ -537,6 +541,11 @@ __device__ void combine_row(const DecodeArgs& a, int row, float* zsw, const floa
   const float inv = 1.0f / L;
   o0 *= inv;
   o1 *= inv;
+  if (a.lam_v != nullptr) {  // values were stored times lambda_v
+    const float* lp = a.lam_v + (size_t)((row % a.Hq) / a.G) * D;
+    o0 = o0 / lp[c];
+    o1 = o1 / lp[c + 1];
+  }
   float r0 = o0, r1 = o1;
   if (a.rotation == KVQ_ROT_SIGN_FWHT) {
     // R^T o = diag(s) H o / sqrt(128): the butterflies over this head's 64 lanes
@@ -781,7 +790,7 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   load_chunk<KF, KG, VF, VG>(a, stream, cA < c1 ? cA : 0, lane, tok_a, RA);
   load_aux(cA < c1 ? cA : 0, XA);
   __builtin_amdgcn_sched_barrier(0);
-  query_prologue<KF>(a, sm, qin, nh, KG);
+  query_prologue<KF>(a, sm, qin, nh, KG, hkv);
   int pB = claim();
 
   const float qs = sm.qs[j];

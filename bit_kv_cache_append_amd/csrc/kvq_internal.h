@@ -47,6 +47,8 @@ struct AppendArgs {
   const float* clip_v;
   uint16_t* k_win;  // may be null
   uint16_t* v_win;
+  const float* lam_k;  // [H][128] per-channel rescale, or null
+  const float* lam_v;
   int32_t B, H, Tmax, n_new;
   int32_t in_bf16;
   int32_t k_fmt, v_fmt, k_group, v_group, scale_mode, rotation;
@@ -58,6 +60,8 @@ struct AppendArgs {
 struct CalibArgs {
   const uint16_t* x;  // [H][n][128]
   float* out;         // [H][128]
+  const float* lam;   // [H][128] rescale applied before the maxima (clip mode), or null
+  int32_t mode;       // 0: ratio * max |y| (clip thresholds), 1: 1 / max |y| (rescale factors)
   const int8_t* signs;
   const uint16_t* rot;
   int32_t H, n, in_bf16, rotation;
@@ -84,6 +88,7 @@ struct AdaptArgs {
   const uint16_t* v_orig;
   const int8_t* signs;
   const uint16_t* rot;
+  const float* lam_k;        // [H][128] per-channel rescale of the keys, or null
   float* mass;               // [B][Hq][nt]
   const uint8_t* flags_in;   // [B][H][nt] or null
   uint8_t* flags_out;        // [B][H][nt]
@@ -118,6 +123,8 @@ struct DecodeArgs {
   const uint8_t* flags;  // [B][H][nt] or null
   const uint16_t* k_win;  // [B][H][(n_sink + n_recent) * 64][128] or null
   const uint16_t* v_win;
+  const float* lam_k;  // [H][128] per-channel rescale, or null
+  const float* lam_v;
   const int8_t* signs;
   const uint16_t* rot;
   float* part;              // [B][Hq][n_splits][PART_FLOATS]

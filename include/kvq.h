@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 2
+#define KVQ_ABI_VERSION 3
 
 typedef int32_t kvq_status;
 #define KVQ_OK 0
@@ -158,6 +158,12 @@ typedef struct kvq_params {
  *                                   in slot j if j < sink_blocks, else in slot
  *                                   sink_blocks + j % recent_blocks (a ring), at row
  *                                   position % 64; needed iff NW > 0
+ *   lambda_k, lambda_v [Hkv][128] fp32  per-channel rescale factors or NULL: the
+ *                                   rotated vector is multiplied by them (fp32) before
+ *                                   clipping and the group scales ("When Quantization
+ *                                   Is Free", Methodology sections 2 and 3; one scale per
+ *                                   coordinate with per-group scales), and decode
+ *                                   divides them out; not with keep_fp16_copy
  * Code, metadata, original and window buffers must be 16-byte aligned.
  */
 typedef struct kvq_cache {
@@ -174,6 +180,8 @@ typedef struct kvq_cache {
   const float* clip_v;
   void* k_win;
   void* v_win;
+  const float* lambda_k;
+  const float* lambda_v;
 } kvq_cache;
 
 /* Returns KVQ_ABI_VERSION. */
@@ -310,13 +318,25 @@ kvq_status kvq_decode_attn_dense(const kvq_params* p, const void* k, const void*
 
 /*
  * Clipping thresholds for KVQ_INT2: t[h][c] = fl32(ratio * max_t |y_t,c|), with y
- * the same fp32 rotation kvq_append applies.
+ * the same fp32 rotation kvq_append applies (times the cache's lambda_k / lambda_v
+ * when given).
  *   calib_k, calib_v: device [Hkv][n_tokens][128] in_dtype; n_tokens >= 1.
  *   clip_k_out, clip_v_out: device fp32 [Hkv][128].
  */
 kvq_status kvq_calibrate_clip(const kvq_params* p, const kvq_cache* cache, const void* calib_k,
                               const void* calib_v, int32_t n_tokens, float ratio, float* clip_k_out,
                               float* clip_v_out, void* stream);
+
+/*
+ * Per-channel rescale factors (calibrated): lambda[h][c] = fl32(1 / max_t |y_t,c|), 1
+ * where the maximum is 0, with y the same fp32 rotation kvq_append applies (before
+ * any rescale).  Same buffers as kvq_calibrate_clip; the results go into
+ * kvq_cache.lambda_k / lambda_v.  (kvq_calibrate_clip applies a cache's factors
+ * before taking its maxima, so calibrate the factors first.)
+ */
+kvq_status kvq_calibrate_lambda(const kvq_params* p, const kvq_cache* cache, const void* calib_k,
+                                const void* calib_v, int32_t n_tokens, float* lambda_k_out,
+                                float* lambda_v_out, void* stream);
 
 #ifdef __cplusplus
 }

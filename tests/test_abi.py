@@ -22,7 +22,7 @@ def test_library_exports_every_declared_symbol():
     assert "kvq_append" in names and "kvq_decode_attn" in names and "kvq_error_bound" in names
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
-    assert L.kvq_abi_version() == 2
+    assert L.kvq_abi_version() == 3
 
 
 def test_buffer_sizes():
