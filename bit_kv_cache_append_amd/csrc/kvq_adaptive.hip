@@ -453,7 +453,7 @@ hipError_t launch_block_mass(const AdaptArgs& a, hipStream_t s) {
     if (a.k_fmt == KF && a.k_group == KG) {                                        \
       hipLaunchKernelGGL((score_kernel<KF, KG>), grid, dim3(NTA), 0, s, a);        \
     } else
-    KVQ_SCORE(KVQ_INT4, 32) KVQ_SCORE(KVQ_INT4, 128) KVQ_SCORE(KVQ_INT8, 32) KVQ_SCORE(KVQ_INT8, 128)
+    KVQ_SCORE(KVQ_INT4, 16) KVQ_SCORE(KVQ_INT4, 32) KVQ_SCORE(KVQ_INT4, 128) KVQ_SCORE(KVQ_INT8, 32) KVQ_SCORE(KVQ_INT8, 128)
     KVQ_SCORE(KVQ_INT2, 32) KVQ_SCORE(KVQ_FP4, 16) { return hipErrorNotSupported; }
 #undef KVQ_SCORE
     hipError_t e = hipGetLastError();

@@ -45,10 +45,12 @@ kvq_status check_params(const kvq_params* p) {
   if (p->in_dtype != KVQ_F16 && p->in_dtype != KVQ_BF16) return fail(KVQ_ERR_INVALID_ARG, "bad in_dtype");
   if (!valid_fmt(p->k_fmt) || !valid_fmt(p->v_fmt)) return fail(KVQ_ERR_INVALID_ARG, "bad k_fmt/v_fmt");
   if (p->v_fmt == KVQ_INT8) return fail(KVQ_ERR_UNSUPPORTED, "INT8 values are not supported");
-  if ((p->k_fmt == KVQ_INT4 || p->k_fmt == KVQ_INT8) && p->k_group != 32 && p->k_group != 128)
-    return fail(KVQ_ERR_INVALID_ARG, "k_group must be 32 or 128");
-  if (p->v_fmt == KVQ_INT4 && p->v_group != 32 && p->v_group != 128)
-    return fail(KVQ_ERR_INVALID_ARG, "v_group must be 32 or 128");
+  if (p->k_fmt == KVQ_INT8 && p->k_group != 32 && p->k_group != 128)
+    return fail(KVQ_ERR_INVALID_ARG, "INT8 k_group must be 32 or 128");
+  if (p->k_fmt == KVQ_INT4 && p->k_group != 16 && p->k_group != 32 && p->k_group != 128)
+    return fail(KVQ_ERR_INVALID_ARG, "INT4 k_group must be 16, 32 or 128");
+  if (p->v_fmt == KVQ_INT4 && p->v_group != 16 && p->v_group != 32 && p->v_group != 128)
+    return fail(KVQ_ERR_INVALID_ARG, "v_group must be 16, 32 or 128");
   if (p->scale_mode != KVQ_SCALE_ABSMAX && p->scale_mode != KVQ_SCALE_SEARCH9 &&
       p->scale_mode != KVQ_SCALE_SEARCH_OFFSETS)
     return fail(KVQ_ERR_INVALID_ARG, "bad scale_mode");

@@ -103,28 +103,40 @@ __device__ __forceinline__ float rne_quot(float y, float sf, float r) {
 // Each returns packed code dwords for the lane's 32 channels, writes metadata
 // elements (fp16 bits or E4M3 codes) and the squared-residual partial sum.
 
-// symmetric int4/int8; group 32 (in-lane) or 128 (quad)
+// symmetric int4/int8; group 16 (two per lane), 32 (in-lane) or 128 (quad).
+// meta0/meta1: the scales of channels 0..15 and 16..31 of the lane (equal unless group 16)
 __device__ __forceinline__ void quant_sym(const float y[32], int qmax, int group, int codes[32],
-                                          uint16_t& meta, float& res2) {
-  float a = 0.0f;
+                                          uint16_t& meta0, uint16_t& meta1, float& res2) {
+  float a[2] = {0.0f, 0.0f};
 #pragma unroll
-  for (int j = 0; j < 32; ++j) a = fmaxf(a, fabsf(y[j]));
-  if (group == 128) {
-    a = fmaxf(a, dpp_f<KVQ_DPP_XOR1>(a));
-    a = fmaxf(a, dpp_f<KVQ_DPP_XOR2>(a));
+  for (int j = 0; j < 32; ++j) a[j >> 4] = fmaxf(a[j >> 4], fabsf(y[j]));
+  if (group != 16) {
+    a[0] = fmaxf(a[0], a[1]);  // max is exact: any order gives the group's absmax
+    if (group == 128) {
+      a[0] = fmaxf(a[0], dpp_f<KVQ_DPP_XOR1>(a[0]));
+      a[0] = fmaxf(a[0], dpp_f<KVQ_DPP_XOR2>(a[0]));
+    }
+    a[1] = a[0];
   }
-  uint16_t sb = f16_sat_bits(a / (float)qmax);  // correctly rounded fp32 divide
-  float sf = f16_bits_to_f32(sb);
-  meta = sb;
-  float r = __builtin_amdgcn_rcpf(sf);
+  uint16_t sb[2];
+  float sf[2], r[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    sb[i] = f16_sat_bits(a[i] / (float)qmax);  // correctly rounded fp32 divide
+    sf[i] = f16_bits_to_f32(sb[i]);
+    r[i] = __builtin_amdgcn_rcpf(sf[i]);
+  }
+  meta0 = sb[0];
+  meta1 = sb[1];
   float qm = (float)qmax;
   float acc = 0.0f;
 #pragma unroll
   for (int j = 0; j < 32; ++j) {
+    const float s = sf[j >> 4];
     float c = 0.0f;
-    if (sf != 0.0f) c = fminf(fmaxf(rne_quot(y[j], sf, r), -qm), qm);
+    if (s != 0.0f) c = fminf(fmaxf(rne_quot(y[j], s, r[j >> 4]), -qm), qm);
     codes[j] = (int)c;
-    float d = y[j] - c * sf;
+    float d = y[j] - c * s;
     acc = acc + d * d;
   }
   res2 = acc;
@@ -554,7 +566,7 @@ __global__ __launch_bounds__(NT) void append_kernel(AppendArgs a) {
   uint16_t m0 = 0, m1 = 0;  // metadata elements of this lane
   float res2 = 0.0f;
   if (fmt == KVQ_INT4 || fmt == KVQ_INT8) {
-    quant_sym(y, fmt == KVQ_INT4 ? 7 : 127, group, codes, m0, res2);
+    quant_sym(y, fmt == KVQ_INT4 ? 7 : 127, group, codes, m0, m1, res2);
   } else if (fmt == KVQ_INT2) {
     const float* clip = tensor ? a.clip_v : a.clip_k;
     quant_asym2(y, clip ? clip + (size_t)h * D + 32 * q : nullptr, codes, m0, m1, res2);
@@ -621,6 +633,9 @@ __global__ __launch_bounds__(NT) void append_kernel(AppendArgs a) {
         m16[4 + q] = m1;
       } else if (fmt == KVQ_FP4) {
         m16[q] = m0;  // two E4M3 bytes: blocks 2q and 2q+1
+      } else if (group == 16) {
+        m16[2 * q] = m0;
+        m16[2 * q + 1] = m1;
       } else if (group == 32) {
         m16[q] = m0;
       } else if (q == 0) {
@@ -639,6 +654,9 @@ __global__ __launch_bounds__(NT) void append_kernel(AppendArgs a) {
   } else if (fmt == KVQ_FP4) {
     sm.meta[tau][2 * q] = m0 & 0xFF;
     sm.meta[tau][2 * q + 1] = m0 >> 8;
+  } else if (group == 16) {
+    sm.meta[tau][2 * q] = m0;
+    sm.meta[tau][2 * q + 1] = m1;
   } else if (group == 32) {
     sm.meta[tau][q] = m0;
   } else if (q == 0) {

@@ -225,7 +225,7 @@ struct __align__(16) DecodeSmem {
   uint32_t ql[4][32];      // low int8 halves, same order
   uint32_t qf4[4][32][4];  // FP4 keys: per head and 4-channel step, fp16 query high then low parts
   float qs[4];             // per-head dequantization of the 16-bit query
-  float qsum[4][4];        // per head, per group: sum of 16-bit query codes
+  float qsum[4][8];        // per head, per group (of 16, 32 or 128 channels): sum of 16-bit query codes
   uint16_t vmeta[NWS][8][16][4];  // per wave: V metadata by (element, slice, r)
   float pb[NWS][TILE][4];    // per wave: probabilities by token (certified recompute)
   float mrg_m[NWS][4], mrg_l[NWS][4], mrg_e[NWS][4];
@@ -386,17 +386,21 @@ __device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryI
     hb[ps] = (uint8_t)(hi & 0xFF);
     lb[ps] = (uint8_t)(lo & 0xFF);
   }
-  // per-group sums of the 16-bit codes (groups of 32 channels = 16 lanes)
+  // per-group sums of the 16-bit codes (groups of 16 channels = 8 lanes, 32 = 16 lanes)
   float gs = (float)(q0 + q1);
   gs += __shfl_xor(gs, 1);
   gs += __shfl_xor(gs, 2);
   gs += __shfl_xor(gs, 4);
-  gs += __shfl_xor(gs, 8);
-  if (kgroup == 128) {
-    gs += __shfl_xor(gs, 16);
-    gs += __shfl_xor(gs, 32);
+  if (kgroup == 16) {
+    if (own && (l & 7) == 0) sm.qsum[j][l >> 3] = gs;
+  } else {
+    gs += __shfl_xor(gs, 8);
+    if (kgroup == 128) {
+      gs += __shfl_xor(gs, 16);
+      gs += __shfl_xor(gs, 32);
+    }
+    if (own && (l & 15) == 0) sm.qsum[j][l >> 4] = gs;
   }
-  if (own && (l & 15) == 0) sm.qsum[j][l >> 4] = gs;
   if (own && l == 0) sm.qs[j] = qs;
   __syncthreads();
 }
@@ -615,13 +619,19 @@ __global__ __launch_bounds__(NT) void combine_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ split kernel
+// V metadata dwords per lane and chunk: 8 elements x 64 tokens x 2 bytes (INT2 scales and
+// offsets, INT4 groups of 16) is 16 bytes; the others fit in 8.
+__host__ __device__ constexpr int vmeta_words(int vf, int vg) {
+  return (vf == KVQ_INT2 || (vf == KVQ_INT4 && vg == 16)) ? 4 : 2;
+}
+
 // Registers holding one chunk of packed data for one lane.
-template <int KF, int VF>
+template <int KF, int VF, int VMW>
 struct ChunkRegs {
   uint32_t krow[KFmt<KF>::DW];            // K row of token pi(s_a, r_a)
   uint32_t kmeta[4];                      // its metadata (scales [, offsets])
   uint32_t vw[2 * VFmt<VF>::CDW];         // V codes of channels 2*lane, 2*lane+1
-  uint32_t vmeta[VF == KVQ_INT2 ? 4 : 2]; // this lane's share of the V metadata tile
+  uint32_t vmeta[VMW];                    // this lane's share of the V metadata tile
 };
 
 // Flag and error descriptor of one chunk (exact-recompute kernels only).
@@ -636,7 +646,7 @@ struct ChunkAux<true> {
 // Issue the loads of chunk ch (no waits: the caller consumes them one chunk later).
 template <int KF, int KG, int VF, int VG>
 __device__ __forceinline__ void load_chunk(const DecodeArgs& a, size_t stream, int ch, int lane, int tok_a,
-                                           ChunkRegs<KF, VF>& R) {
+                                           ChunkRegs<KF, VF, vmeta_words(VF, VG)>& R) {
   constexpr int KDW = KFmt<KF>::DW;
   constexpr int KM = meta_bytes(KF, KG);
   constexpr int CDW = VFmt<VF>::CDW;
@@ -666,7 +676,7 @@ __device__ __forceinline__ void load_chunk(const DecodeArgs& a, size_t stream, i
   }
   constexpr int NM = meta_elems(VF, VG);
   const uint8_t* vm = a.v_meta + (stream * a.nt + ch) * (size_t)(NM * TILE * meta_esize(VF));
-  if constexpr (VF == KVQ_INT2) {  // 8 elements x 64 tokens: 16 bytes per lane
+  if constexpr (VF == KVQ_INT2 || (VF == KVQ_INT4 && NM == 8)) {  // 8 elements x 64 tokens: 16 bytes per lane
     const uint4 u = reinterpret_cast<const uint4*>(vm)[lane];
     R.vmeta[0] = u.x; R.vmeta[1] = u.y; R.vmeta[2] = u.z; R.vmeta[3] = u.w;
   } else if constexpr (NM == 4 || VF == KVQ_FP4) {  // 8 bytes per lane
@@ -696,6 +706,11 @@ __device__ __forceinline__ void stage_vmeta(uint16_t* L, int lane, const uint32_
     const int base = (mm * 16 + 4 * (u >> 1)) * 4 + (u & 1);
 #pragma unroll
     for (int e = 0; e < 8; ++e) L[base + 2 * e] = (uint16_t)(vmeta[e >> 1] >> (16 * (e & 1)));
+  } else if constexpr (NM == 8) {  // INT4, groups of 16: tokens 8u..8u+7 of group mm, placed as below
+    const int mm = lane >> 3, u = lane & 7;
+    const int base = (mm * 16 + 2 * u) * 4;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) L[base + ((e >> 2) & 1) + 2 * (e & 3)] = (uint16_t)(vmeta[e >> 1] >> (16 * (e & 1)));
   } else if constexpr (NM == 4) {
     const int mm = lane >> 4, t0 = 4 * (lane & 15);  // tokens t0..t0+3 of group mm
     const int base = (mm * 16 + 2 * (t0 >> 3)) * 4 + ((t0 >> 2) & 1);
@@ -746,7 +761,7 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   const size_t stream = (size_t)b * a.H + hkv;
   constexpr int CDW = VFmt<VF>::CDW;
   // V scale element of channels 2*lane, 2*lane+1: 32-channel group, one per token, or 16-channel block
-  const int vgrp = (VF == KVQ_FP4) ? (lane >> 3) : (VG == 128) ? 0 : (lane >> 4);
+  const int vgrp = (VF == KVQ_FP4 || VG == 16) ? (lane >> 3) : (VG == 128) ? 0 : (lane >> 4);
   uint16_t* vml = &sm.vmeta[wv][0][0][0];
 
   // The first chunk's loads are in flight during the query prologue.  Every
@@ -784,7 +799,7 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
       X.vn = dp[2];
     }
   };
-  ChunkRegs<KF, VF> RA, RB;
+  ChunkRegs<KF, VF, vmeta_words(VF, VG)> RA, RB;
   ChunkAux<CERT> XA, XB;
   int cA = c0 + wv;
   load_chunk<KF, KG, VF, VG>(a, stream, cA < c1 ? cA : 0, lane, tok_a, RA);
@@ -794,7 +809,7 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   int pB = claim();
 
   const float qs = sm.qs[j];
-  float qsum[4];
+  float qsum[4];  // (groups of 16 read theirs from LDS when needed: registers are short there)
 #pragma unroll
   for (int g = 0; g < 4; ++g) qsum[g] = sm.qsum[j][g];
 
@@ -808,7 +823,7 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   oz = f4{0, 0, 0, 0};
 
   // ---------------------------------------------------------------- one quantized chunk
-  auto quant_chunk = [&](const ChunkRegs<KF, VF>& R, int ch, float ev_c) {
+  auto quant_chunk = [&](const ChunkRegs<KF, VF, vmeta_words(VF, VG)>& R, int ch, float ev_c) {
     const int tok0 = ch * TILE;
     stage_vmeta<VF, VG>(vml, lane, R.vmeta);
     float l[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -847,56 +862,73 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
       // ---- QK^T: exact integer dot products.  Four independent accumulator
       // chains per query half (chain c covers channels 32c..32c+31, i.e. one
       // 32-channel group); each K operand is unpacked once and feeds both halves.
-      constexpr int NG = (KG == 128) ? 1 : 4;
+      // With groups of 16 each chain is read out, scaled and added after its first
+      // four steps (channels 32c..32c+15, group 2c) and restarted for group 2c + 1.
+      constexpr int NG = (KG == 128) ? 1 : 4;  // groups whose sums wait for the scale step below
       constexpr int NC = 4, PER = 32 / NC;
-      i4 ah[NC], al[NC];
-  #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        // the offset-binary correction -8 * sum(q16) of the chain's group rides in the low half
-        int corr = 0;
-        if constexpr (KF == KVQ_INT4) corr = (NG == 1) ? (c == 0 ? -8 * (int)qsum[0] : 0) : -8 * (int)qsum[c];
-        ah[c] = i4{0, 0, 0, 0};
-        al[c] = i4{corr, corr, corr, corr};
-      }
+      constexpr int NPH = (KG == 16) ? 2 : 1, PPH = PER / NPH;  // phases per chain, steps per phase
+      i4 ah[NC], al[NC], acc[NG];
+      auto kscale_word = [&](int r, int w) -> uint32_t {  // metadata dword w of token pi(s, r)
+        return r == 0 ? quad_bcast_u<0>(R.kmeta[w]) : r == 1 ? quad_bcast_u<1>(R.kmeta[w])
+             : r == 2 ? quad_bcast_u<2>(R.kmeta[w]) : quad_bcast_u<3>(R.kmeta[w]);
+      };
       static_assert(NC == 4, "query operand layout: 4 chains per 16-byte LDS read");
   #pragma unroll
-      for (int n = 0; n < PER; ++n) {
-        // the query operands stay in LDS (registers go to deeper chunk prefetch)
-        const uint4 qhv = *reinterpret_cast<const uint4*>(&sm.qh[j][4 * n]);
-        const uint4 qlv = *reinterpret_cast<const uint4*>(&sm.ql[j][4 * n]);
-        const int qhc[4] = {(int)qhv.x, (int)qhv.y, (int)qhv.z, (int)qhv.w};
-        const int qlc[4] = {(int)qlv.x, (int)qlv.y, (int)qlv.z, (int)qlv.w};
+      for (int ph = 0; ph < NPH; ++ph) {
   #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const int av = KFmt<KF>::a_op(R.krow, c * PER + n);
-          ah[c] = __builtin_amdgcn_mfma_i32_4x4x4i8(av, qhc[c], ah[c], 0, 0, 0);
-          al[c] = __builtin_amdgcn_mfma_i32_4x4x4i8(av, qlc[c], al[c], 0, 0, 0);
+          // the offset-binary correction -8 * sum(q16) of the chain's group rides in the low half
+          int corr = 0;
+          if constexpr (KF == KVQ_INT4)
+            corr = (KG == 16) ? -8 * (int)sm.qsum[j][2 * c + ph]
+                 : (NG == 1) ? (c == 0 ? -8 * (int)qsum[0] : 0) : -8 * (int)qsum[c];
+          ah[c] = i4{0, 0, 0, 0};
+          al[c] = i4{corr, corr, corr, corr};
         }
-      }
-      i4 acc[NG];
   #pragma unroll
-      for (int g = 0; g < NG; ++g)
+        for (int n = ph * PPH; n < (ph + 1) * PPH; ++n) {
+          // the query operands stay in LDS (registers go to deeper chunk prefetch)
+          const uint4 qhv = *reinterpret_cast<const uint4*>(&sm.qh[j][4 * n]);
+          const uint4 qlv = *reinterpret_cast<const uint4*>(&sm.ql[j][4 * n]);
+          const int qhc[4] = {(int)qhv.x, (int)qhv.y, (int)qhv.z, (int)qhv.w};
+          const int qlc[4] = {(int)qlv.x, (int)qlv.y, (int)qlv.z, (int)qlv.w};
   #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if constexpr (NG == 1) {
-            acc[g][r] = 0;
-  #pragma unroll
-            for (int c = 0; c < NC; ++c) acc[g][r] += ah[c][r] * 256 + al[c][r];
-          } else {
-            acc[g][r] = ah[g][r] * 256 + al[g][r];
+          for (int c = 0; c < NC; ++c) {
+            const int av = KFmt<KF>::a_op(R.krow, c * PER + n);
+            ah[c] = __builtin_amdgcn_mfma_i32_4x4x4i8(av, qhc[c], ah[c], 0, 0, 0);
+            al[c] = __builtin_amdgcn_mfma_i32_4x4x4i8(av, qlc[c], al[c], 0, 0, 0);
           }
         }
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (KG == 16) {
+            // group 2c + ph: its fp16 scale is half ph of metadata dword c
+  #pragma unroll
+            for (int c = 0; c < NC; ++c) {
+              const uint16_t sb = (uint16_t)(kscale_word(r, c) >> (16 * ph));
+              l[r] += (float)(ah[c][r] * 256 + al[c][r]) * f16_bits_to_f32(sb);
+            }
+          } else if constexpr (NG == 1) {
+            acc[0][r] = 0;
+  #pragma unroll
+            for (int c = 0; c < NC; ++c) acc[0][r] += ah[c][r] * 256 + al[c][r];
+          } else {
+  #pragma unroll
+            for (int c = 0; c < NC; ++c) acc[c][r] = ah[c][r] * 256 + al[c][r];
+          }
+        }
+        // keep the next phase's chains from starting before this one is read out (both
+        // sets of accumulators live at once would cost 32 registers)
+        if constexpr (NPH > 1) __builtin_amdgcn_sched_barrier(0);
+      }
       // ---- group scales of tokens pi(s, r), held by lanes 4s + r (A role): quad broadcast
   #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < 4 && KG != 16; ++r) {
         uint32_t sw[2], zw[2] = {0u, 0u};
   #pragma unroll
         for (int w = 0; w < (NG == 1 ? 1 : 2); ++w) {
-          sw[w] = r == 0 ? quad_bcast_u<0>(R.kmeta[w]) : r == 1 ? quad_bcast_u<1>(R.kmeta[w])
-                : r == 2 ? quad_bcast_u<2>(R.kmeta[w]) : quad_bcast_u<3>(R.kmeta[w]);
-          if constexpr (KF == KVQ_INT2)
-            zw[w] = r == 0 ? quad_bcast_u<0>(R.kmeta[2 + w]) : r == 1 ? quad_bcast_u<1>(R.kmeta[2 + w])
-                  : r == 2 ? quad_bcast_u<2>(R.kmeta[2 + w]) : quad_bcast_u<3>(R.kmeta[2 + w]);
+          sw[w] = kscale_word(r, w);
+          if constexpr (KF == KVQ_INT2) zw[w] = kscale_word(r, 2 + w);
         }
   #pragma unroll
         for (int g = 0; g < NG; ++g) {
@@ -1106,7 +1138,7 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   // ---------------------------------------------------------------- software-pipelined walk
   // The loads of the next chunk are in flight while the current one is computed
   // (two register sets used alternately).
-  auto visit = [&](const ChunkRegs<KF, VF>& R, int ch, const ChunkAux<CERT>& X) {
+  auto visit = [&](const ChunkRegs<KF, VF, vmeta_words(VF, VG)>& R, int ch, const ChunkAux<CERT>& X) {
     float ev_c = 0.0f;
     bool fl = false;
     if constexpr (EXACT) fl = in_window(ch);
@@ -1342,6 +1374,7 @@ hipError_t launch_decode(const DecodeArgs& a, int k_fmt, int v_fmt, bool dense, 
     return hipGetLastError();                                                                 \
   }
   KVQ_LAUNCH(KVQ_INT4, 32, KVQ_INT4, 32)
+  KVQ_LAUNCH(KVQ_INT4, 16, KVQ_INT4, 16)
   KVQ_LAUNCH(KVQ_INT4, 128, KVQ_INT4, 128)
   KVQ_LAUNCH(KVQ_INT4, 32, KVQ_INT4, 128)
   KVQ_LAUNCH(KVQ_INT4, 128, KVQ_INT4, 32)

@@ -69,7 +69,7 @@ typedef int32_t kvq_status;
 #define KVQ_BF16 1
 
 /* code formats (K and V independently) */
-#define KVQ_INT4 0 /* symmetric, codes -7..7, fp16 scale per group (32 or 128) */
+#define KVQ_INT4 0 /* symmetric, codes -7..7, fp16 scale per group (16, 32 or 128) */
 #define KVQ_INT8 1 /* symmetric, codes -127..127, fp16 scale per group (32 or 128) */
 #define KVQ_INT2 2 /* asymmetric, codes 0..3, fp16 scale + fp16 offset per 32 */
 #define KVQ_FP4 3  /* E2M1 codes, one E4M3 scale per 16 */
@@ -115,8 +115,8 @@ typedef struct kvq_params {
   int32_t max_ctx;        /* Tmax positions per sequence, multiple of 64 */
   int32_t in_dtype;       /* KVQ_F16 | KVQ_BF16 */
   int32_t k_fmt, v_fmt;   /* KVQ_INT4 | KVQ_INT8 | KVQ_INT2 | KVQ_FP4 (V: not INT8) */
-  int32_t k_group;        /* INT4/INT8: 32 or 128; ignored otherwise */
-  int32_t v_group;        /* INT4: 32 or 128; ignored otherwise */
+  int32_t k_group;        /* INT4: 16, 32 or 128; INT8: 32 or 128; ignored otherwise */
+  int32_t v_group;        /* INT4: 16, 32 or 128; ignored otherwise */
   int32_t scale_mode;     /* KVQ_SCALE_*: FP4 only */
   int32_t rotation;       /* KVQ_ROT_* (SIGN_FWHT and SRFT need signs) */
   int32_t keep_fp16_copy; /* nonzero: store originals + per-block descriptors */
@@ -138,7 +138,8 @@ typedef struct kvq_params {
  *                                   even element low), bits 2*(c%4) of byte c/4
  *                                   (INT2), byte c (INT8); INT4/INT8 two's complement
  *   k_meta  [B][Hkv][Tmax][KM]      fp16 scales per group (INT4/INT8: 128/group of
- *                                   them), INT2: 4 fp16 scales then 4 fp16 offsets,
+ *                                   them; groups of 16 follow "When Quantization Is
+ *                                   Free", Methodology section 3), INT2: 4 fp16 scales then 4 fp16 offsets,
  *                                   FP4: 8 E4M3 bytes
  *   v_codes [B][Hkv][nt][128][CB]   per 64-token tile, channel-major: channel c's 64
  *                                   codes packed along tokens with the rules above

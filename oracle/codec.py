@@ -4,7 +4,7 @@ Test infrastructure only: see the package docstring for who may import it.
 
 Formats (d = 128 channels per head vector, y = the fp32 rotated vector):
 
-int4 / int8 symmetric, group G in {32, 128}
+int4 / int8 symmetric, group G in {32, 128} (int4 also 16)
     "When Quantization Is Free", Methodology section 2 (per-group absmax, round to
     signed int4/int8, two int4 per byte) and "Runtime-Certified Bounded-Error
     Quantized Attention", Methodology section 1 (INT8 keys, INT4 values).
@@ -13,6 +13,8 @@ int4 / int8 symmetric, group G in {32, 128}
     exact quotient by the *stored* fp16 scale; s == 0 gives all-zero codes.
     Readings: qmax = 2^(b-1)-1 (symmetric, -8/-128 unused); dividing by the
     stored scale makes |y - c*s| <= s/2 hold against the metadata.
+    Groups of 16 (int4): "When Quantization Is Free", Methodology section 3
+    (per-channel scaling combined with groups of 16 for d = 128).
 
 int2 asymmetric with clipping, group 32
     "OSCAR", section 2.2A (clipping thresholds from rotated calibration
@@ -82,9 +84,9 @@ def group_of(fmt, group):
         return 32
     if fmt == "fp4":
         return 16
-    if group not in (32, 128):
-        raise ValueError("int4/int8 groups are 32 or 128")
-    return group
+    if group in (32, 128) or (fmt == "int4" and group == 16):
+        return group
+    raise ValueError("int4 groups are 16, 32 or 128; int8 groups 32 or 128")
 
 
 def row_bytes(fmt):

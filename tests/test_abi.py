@@ -72,13 +72,26 @@ def test_window_needs_buffers_without_gpu():
 
 
 @pytest.mark.parametrize("field,value", [("head_dim", 64), ("max_ctx", 100), ("batch", 0), ("n_q_heads", 7),
-                                         ("k_group", 16), ("v_fmt", 1), ("rotation", 9)])
+                                         ("k_group", 64), ("v_group", 8), ("v_fmt", 1), ("rotation", 9)])
 def test_invalid_params_rejected(field, value):
     p = kvq.make_params(2, 8, 2, 256)
     setattr(p, field, value)
     with pytest.raises(kvq.KvqError) as e:
         kvq.buffer_bytes(p)
     assert e.value.status in (-1, -2)
+
+
+def test_group_16_is_int4_only():
+    # groups of 16 ("When Quantization Is Free", Methodology section 3): 8 fp16 scales per token
+    p = kvq.make_params(2, 8, 2, 256, k_group=16, v_group=16)
+    q = kvq.make_params(2, 8, 2, 256, k_group=32, v_group=32)
+    sizes16, sizes32 = kvq.buffer_bytes(p), kvq.buffer_bytes(q)
+    assert sizes16["k_meta"] == 2 * 2 * 256 * 16 and sizes32["k_meta"] == 2 * 2 * 256 * 8
+    assert sizes16["v_meta"] == 2 * 2 * 4 * 8 * 64 * 2
+    r = kvq.make_params(2, 8, 2, 256, k_fmt="int8", k_group=16)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.buffer_bytes(r)
+    assert e.value.status == -1
 
 
 def test_null_pointers_rejected_without_gpu():

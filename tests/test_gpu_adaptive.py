@@ -48,6 +48,7 @@ CASES = {
     "int2-dense-bf16": (synth.config(4, B=2, T=1024, dtype="bf16"), [1024, 777]),
     "fp4-search": (synth.config(5, B=2, T=1024), [1024, 701]),
     "int4-srft": (synth.config(2, B=2, T=640, rotation="srft"), [640, 300]),
+    "int4-g16": (synth.config(2, B=2, T=640, k_group=16, v_group=16), [640, 129]),
 }
 
 

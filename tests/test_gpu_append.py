@@ -34,6 +34,9 @@ CASES = {
                                           rotation="dense"),
     # SRFT ("When Quantization Is Free", Methodology sections 1-2): the Stockham FFT write side
     "int4-srft-f16": synth.config(1, B=2, Hq=2, Hkv=2, T=256, rotation="srft"),
+    "int4-g16-fwht": synth.config(2, B=2, Hq=8, Hkv=2, T=256, k_group=16, v_group=16),
+    "int4-g16-srft-bf16-cert": synth.config(2, B=2, Hq=8, Hkv=2, T=192, k_group=16, v_group=16, rotation="srft",
+                                            dtype="bf16", keep=True),
     "int8k-int4v-srft-cert": synth.config(3, B=2, Hq=8, Hkv=2, T=256, n_plant=2, rotation="srft"),
     "int2-srft-bf16": synth.config(4, B=2, Hq=8, Hkv=2, T=256, dtype="bf16", rotation="srft"),
     "fp4-srft": synth.config(5, B=2, Hq=8, Hkv=2, T=192, rotation="srft"),

@@ -57,6 +57,10 @@ CASES = {
     "gqa8-two-head-groups": (synth.config(2, B=2, Hq=16, Hkv=2, T=640), [640, 513]),
     "gqa6-partial-group-bf16": (synth.config(2, B=1, Hq=12, Hkv=2, T=384, dtype="bf16"), [384]),
     "c2-int4-srft": (synth.config(2, B=2, T=640, rotation="srft"), [640, 333]),
+    "int4-g16-gqa": (synth.config(2, B=3, T=640, k_group=16, v_group=16), [640, 577, 1]),
+    "int4-g16-certified": (synth.config(3, B=2, T=1024, k_fmt="int4", k_group=16, v_group=16), [1024, 700]),
+    "int4-g16-none-bf16": (synth.config(1, B=2, Hq=8, Hkv=2, T=384, rotation="none", k_group=16, v_group=16,
+                                        dtype="bf16"), [384, 200]),
     "c3-int8k-int4v-srft": (synth.config(3, B=2, T=1024, rotation="srft"), [1024, 700]),
     "c4-int2-srft": (synth.config(4, B=2, T=512, rotation="srft"), [512, 65]),
     "c5-fp4-srft-bf16": (synth.config(5, B=2, T=512, rotation="srft"), [512, 129]),

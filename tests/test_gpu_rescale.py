@@ -26,6 +26,8 @@ CASES = {
     "int4-g128-none-outliers": synth.config(1, B=2, Hq=8, Hkv=2, T=384, rotation="none", k_group=128, v_group=128),
     "int2-dense-bf16-clip": synth.config(4, B=2, T=384, dtype="bf16"),
     "fp4-srft": synth.config(5, B=2, T=320, rotation="srft"),
+    # the pairing the page describes: per-channel factors with groups of 16
+    "int4-g16-srft": synth.config(2, B=2, T=320, rotation="srft", k_group=16, v_group=16),
 }
 
 

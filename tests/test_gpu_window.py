@@ -130,6 +130,8 @@ CASES = {
     "int4-recent-only-g128": (synth.config(1, B=2, Hq=8, Hkv=2, T=512, k_group=128, v_group=128,
                                            sink_blocks=0, recent_blocks=3), [([0, 0], 300), ([300, 200], 150)]),
     "int4-sink-only": (synth.config(2, B=1, T=640, sink_blocks=2, recent_blocks=0), [([0], 640)]),
+    "int4-g16-ragged": (synth.config(2, B=2, Hq=8, Hkv=2, T=512, k_group=16, v_group=16, sink_blocks=1,
+                                     recent_blocks=1), [([0, 0], 400), ([400, 300], 50)]),
     "int8k-int4v-window-no-copy": (synth.config(3, B=2, T=1024, keep=False, sink_blocks=1, recent_blocks=1),
                                    [([0, 0], 1024), ([1000, 896], 24)]),
     "whole-sequence-in-window": (synth.config(2, B=2, T=256, sink_blocks=2, recent_blocks=2),

@@ -67,7 +67,7 @@ def _brute_sym(y, sf, qmax):
     return out
 
 
-@pytest.mark.parametrize("fmt,group", [("int4", 32), ("int4", 128), ("int8", 128), ("int8", 32)])
+@pytest.mark.parametrize("fmt,group", [("int4", 16), ("int4", 32), ("int4", 128), ("int8", 128), ("int8", 32)])
 def test_sym_quant_brute_force_and_bound(fmt, group):
     rng = np.random.default_rng(11)
     y = (rng.standard_normal((40, 128)) * rng.uniform(0.01, 5, (40, 1))).astype(np.float32)
@@ -89,6 +89,28 @@ def test_sym_quant_brute_force_and_bound(fmt, group):
     err = np.abs(yg - cg * sf)
     assert np.all(err <= sf / 2 * (1 + 2.0 ** -9))
     assert not c[3].any() and not s[3].any()
+
+
+def test_group16_scales_refine_group32():
+    # "When Quantization Is Free", Methodology section 3: groups of 16.  fp16(fl32(a / 7)) is
+    # monotone in a, so the larger of the two 16-channel scales of a 32-channel group is that
+    # group's own scale; a group sliced across the wrong channels breaks this.
+    rng = np.random.default_rng(21)
+    y = (rng.standard_normal((60, 128)) * rng.uniform(0.01, 5, (60, 128))).astype(np.float32)
+    y[5, 16:32] = 0  # one all-zero 16-group next to a non-zero one
+    c16, s16 = codec.quantize_sym(y, "int4", 16)
+    c32, s32 = codec.quantize_sym(y, "int4", 32)
+    assert s16.shape == (60, 8) and s32.shape == (60, 4)
+    assert np.array_equal(np.maximum(s16[:, 0::2], s16[:, 1::2]), s32)
+    assert s16[5, 1] == 0 and not c16[5, 16:32].any() and s16[5, 0] > 0
+    # where the two halves share the scale, the codes agree with the 32-channel ones
+    same = np.repeat(s16[:, 0::2] == s16[:, 1::2], 32, axis=1)
+    assert np.array_equal(c16[same], c32[same])
+    # a finer group never has a larger per-element bound: |y - c s16| <= s16/2 <= s32/2
+    err = np.abs(y.astype(np.float64) - c16 * np.repeat(s16.astype(np.float64), 16, axis=1))
+    assert np.all(err <= np.repeat(s32.astype(np.float64), 32, axis=1) / 2 * (1 + 2.0 ** -9))
+    with pytest.raises(ValueError):
+        codec.quantize_sym(y, "int8", 16)
 
 
 def test_asym2_brute_force_and_bound():
