@@ -743,6 +743,135 @@ struct __align__(16) FastSmem {
   uint32_t vt[TILE][17];     // V: per token 16 nibble words (8 channels each), padded
 };
 
+// SRFT in registers (the fast path).  Twiddles W128^k, k = 0..64, and one
+// 128-float row per vector of the tile for the final reorder.
+struct __align__(16) SrftRegSmem {
+  float twr[65], twi[65];
+  float rows[TILE][D + 4];
+};
+
+__device__ __forceinline__ constexpr int rev4(int i) {
+  return ((i & 1) << 3) | ((i & 2) << 1) | ((i & 4) >> 1) | ((i & 8) >> 3);
+}
+
+// The same fp32 operations as the LDS version above (srft_quad), on values that
+// stay in place.  Lane q of the quad holds the complex points z_n, n = 16q + i, in
+// register i.  Every Stockham pass combines the points whose current index differs
+// in its top bit (32 apart); computed in place, the passes leave the labels moving
+// instead of the data: the pair bit is lane bit 1 in pass 0 and lane bit 0 in pass 1
+// (DPP partners), then register bits 3, 2, 1, 0, and the index of the twiddle
+// W64^(jm) follows from the label of the upper element.  Afterwards register i of
+// lane q holds Z_k, k = 4 rev4(i) + r with r = (q >> 1) + 2 (q & 1); the partner
+// Z_(64-k) of the Hermitian unpack is in the same lane (r = 0, 2) or in lane q ^ 1
+// (r = 1, 3), at register 15 - i (lane 0: rev4(16 - rev4(i))).  The packed output
+// goes through one LDS row per vector back to the natural channel order.  y holds
+// the sign-flipped input on entry and the rotated vector on return.
+__device__ __forceinline__ void srft_regs(float y[32], int q, int vec, SrftRegSmem& sm) {
+  float zr[16], zi[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    zr[i] = y[2 * i];
+    zi[i] = y[2 * i + 1];
+  }
+  const int q0 = q & 1, q1 = q >> 1;
+  // passes 0 and 1: the lower element takes own + partner, the upper one
+  // (partner - own) W, with W64^(jm) = W128^(2jm): 32 q0 + 2i in pass 0, 4i in pass 1
+  {
+    const float sg = q1 ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float vr = __builtin_fmaf(zr[i], sg, dpp_f<KVQ_DPP_XOR2>(zr[i]));
+      const float vi = __builtin_fmaf(zi[i], sg, dpp_f<KVQ_DPP_XOR2>(zi[i]));
+      const int e = 32 * q0 + 2 * i;
+      const float wr = sm.twr[e], wi = sm.twi[e];
+      const float tr = vr * wr - vi * wi, ti = vr * wi + vi * wr;
+      zr[i] = q1 ? tr : vr;
+      zi[i] = q1 ? ti : vi;
+    }
+  }
+  {
+    const float sg = q0 ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float vr = __builtin_fmaf(zr[i], sg, dpp_f<KVQ_DPP_XOR1>(zr[i]));
+      const float vi = __builtin_fmaf(zi[i], sg, dpp_f<KVQ_DPP_XOR1>(zi[i]));
+      const float wr = sm.twr[4 * i], wi = sm.twi[4 * i];
+      const float tr = vr * wr - vi * wi, ti = vr * wi + vi * wr;
+      zr[i] = q0 ? tr : vr;
+      zi[i] = q0 ? ti : vi;
+    }
+  }
+  // passes 2..5 inside the lane: pairs (i, i + h), h = 8, 4, 2, 1
+  auto bfly = [&](int ia, int ib, int e) {
+    const float ar = zr[ia], ai = zi[ia], br = zr[ib], bi = zi[ib];
+    zr[ia] = ar + br;
+    zi[ia] = ai + bi;
+    const float dr = ar - br, di = ai - bi;
+    const float wr = sm.twr[e], wi = sm.twi[e];
+    zr[ib] = dr * wr - di * wi;
+    zi[ib] = dr * wi + di * wr;
+  };
+#pragma unroll
+  for (int i = 0; i < 8; ++i) bfly(i, i + 8, 8 * i);
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if ((i & 4) == 0) bfly(i, i + 4, 16 * (i & 3));
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if ((i & 2) == 0) bfly(i, i + 2, 32 * (i & 1));
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) bfly(i, i + 1, 0);
+  // Hermitian unpack: X_k = E + W128^k O, A = Z_k, B = conj(Z_(64-k)),
+  // E = (A + B) / 2, O = (A - B) / 2i
+  const int r = q1 + 2 * q0;
+  float* row = sm.rows[vec];
+  const float c0 = bits_to_f32(KVQ_INV_SQRT_D_BITS);
+  auto unpack = [&](float a_re, float a_im, float p_re, float p_im, int k, float& xr, float& xi) {
+    const float b_re = p_re, b_im = -p_im;
+    const float e_re = 0.5f * (a_re + b_re), e_im = 0.5f * (a_im + b_im);
+    const float o_re = 0.5f * (a_im - b_im), o_im = -(0.5f * (a_re - b_re));
+    const float wr = sm.twr[k], wi = sm.twi[k];
+    const float t_re = o_re * wr - o_im * wi, t_im = o_re * wi + o_im * wr;
+    xr = e_re + t_re;
+    xi = e_im + t_im;
+  };
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int i1 = 15 - i, i0 = rev4((16 - rev4(i)) & 15);
+    float pr = zr[i1], pi = zi[i1];
+    const float dr = dpp_f<KVQ_DPP_XOR1>(zr[i1]), di = dpp_f<KVQ_DPP_XOR1>(zi[i1]);
+    if (q1) {
+      pr = dr;
+      pi = di;
+    } else if (q == 0) {
+      pr = zr[i0];
+      pi = zi[i0];
+    }
+    const int k = 4 * rev4(i) + r;
+    float xr, xi;
+    unpack(zr[i], zi[i], pr, pi, k, xr, xi);
+    float v0 = xr * 0.125f, v1 = xi * 0.125f;
+    if (i == 0 && q == 0) {  // X_0 and X_64 (both from Z_0) are the two real channels
+      float nr, ni;
+      unpack(zr[0], zi[0], zr[0], zi[0], 64, nr, ni);
+      v0 = xr * c0;
+      v1 = nr * c0;
+    }
+    row[2 * k] = v0;
+    row[2 * k + 1] = v1;
+  }
+  __syncthreads();
+  const float4* rp = reinterpret_cast<const float4*>(row + 32 * q);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 u = rp[i];
+    y[4 * i] = u.x;
+    y[4 * i + 1] = u.y;
+    y[4 * i + 2] = u.z;
+    y[4 * i + 3] = u.w;
+  }
+}
+
 // 8x8 transpose of nibbles: w[e] nibble j -> w[j] nibble e
 __device__ __forceinline__ void transpose8x8_nibbles(uint32_t w[8]) {
 #pragma unroll
@@ -806,37 +935,48 @@ __device__ __forceinline__ void fast_load(const uint16_t* src, uint32_t w[16]) {
   }
 }
 
-// quantize 32 rotated values of one lane (its group of 32, or a quarter of a
-// group of 128) into packed code dwords; optional residual and norm sums
+// quantize 32 rotated values of one lane (its group of 32, its two groups of 16,
+// or a quarter of a group of 128) into packed code dwords; optional residual and
+// norm sums.  meta: the lane's scale (groups of 16: of channels 0..15; meta1 of 16..31)
 template <int FMT, int GROUP>
 __device__ __forceinline__ void fast_quantize(const float y[32], bool want_sums, uint32_t packed[8], uint16_t& meta,
-                                              float& res2, float& ynorm2) {
+                                              uint16_t& meta1, float& res2, float& ynorm2) {
   constexpr int QMAX = FMT == KVQ_INT4 ? 7 : 127;
   constexpr int OFF = FMT == KVQ_INT4 ? 8 : 128;
-  float am = 0.0f;
+  constexpr int NH = GROUP == 16 ? 2 : 1;  // scales per lane
+  float am[NH];
 #pragma unroll
-  for (int j = 0; j < 32; ++j) am = fmaxf(am, fabsf(y[j]));
+  for (int i = 0; i < NH; ++i) am[i] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) am[j * NH / 32] = fmaxf(am[j * NH / 32], fabsf(y[j]));
   if constexpr (GROUP == 128) {
-    am = fmaxf(am, dpp_f<KVQ_DPP_XOR1>(am));
-    am = fmaxf(am, dpp_f<KVQ_DPP_XOR2>(am));
+    am[0] = fmaxf(am[0], dpp_f<KVQ_DPP_XOR1>(am[0]));
+    am[0] = fmaxf(am[0], dpp_f<KVQ_DPP_XOR2>(am[0]));
   }
-  const uint16_t sb = f16_sat_bits(am / (float)QMAX);  // correctly rounded fp32 divide
-  const float sf = f16_bits_to_f32(sb);
-  meta = sb;
-  // a zero scale gives code 0 for every element: divisor 1 and reciprocal 0 do that
-  const float sq = sf != 0.0f ? sf : 1.0f;
-  const float r = sf != 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f;
+  uint16_t sb[NH];
+  float sf[NH], sq[NH], r[NH];
+#pragma unroll
+  for (int i = 0; i < NH; ++i) {
+    sb[i] = f16_sat_bits(am[i] / (float)QMAX);  // correctly rounded fp32 divide
+    sf[i] = f16_bits_to_f32(sb[i]);
+    // a zero scale gives code 0 for every element: divisor 1 and reciprocal 0 do that
+    sq[i] = sf[i] != 0.0f ? sf[i] : 1.0f;
+    r[i] = sf[i] != 0.0f ? __builtin_amdgcn_rcpf(sf[i]) : 0.0f;
+  }
+  meta = sb[0];
+  meta1 = sb[NH - 1];
   float acc = 0.0f, yn = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {  // 8 elements at a time
+  for (int k = 0; k < 4; ++k) {  // 8 elements at a time (one scale: groups of 16 are k = 0, 1 and 2, 3)
+    const int hs = k * NH / 4;
     float m[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) m[e] = quot_magic<OFF, QMAX>(y[8 * k + e], sq, r);
+    for (int e = 0; e < 8; ++e) m[e] = quot_magic<OFF, QMAX>(y[8 * k + e], sq[hs], r[hs]);
     if (want_sums) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float cj = m[e] - (MAGIC + (float)OFF);  // exact
-        const float d = y[8 * k + e] - cj * sf;
+        const float d = y[8 * k + e] - cj * sf[hs];
         acc = acc + d * d;
         yn = yn + y[8 * k + e] * y[8 * k + e];
       }
@@ -964,8 +1104,9 @@ __device__ __forceinline__ void fast_quantize_fp4(const float y[32], int mode, b
   ynorm2 = yn;
 }
 
-template <int KF, int KG, int VF, int VG, bool BF16>
-__device__ __forceinline__ void fast_process(const AppendArgs& a, FastSmem& sm, const FastUnit& U, const uint32_t w[16]) {
+template <int KF, int KG, int VF, int VG, bool BF16, bool SRFT>
+__device__ __forceinline__ void fast_process(const AppendArgs& a, FastSmem& sm, SrftRegSmem* ss, const FastUnit& U,
+                                             const uint32_t w[16]) {
   const int t = threadIdx.x, tau = t >> 2, q = t & 3;
   const int tensor = U.tensor, tile = U.tile, pos = U.pos;
   const bool valid = U.valid;
@@ -991,7 +1132,15 @@ __device__ __forceinline__ void fast_process(const AppendArgs& a, FastSmem& sm, 
   }
 
   float y[32];
-  if (fwht) {
+  if constexpr (SRFT) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t ws = w[k] ^ sm.smask[q][k];
+      y[2 * k] = widen((uint16_t)(ws & 0xFFFF), BF16);
+      y[2 * k + 1] = widen((uint16_t)(ws >> 16), BF16);
+    }
+    srft_regs(y, q, tau, *ss);
+  } else if (fwht) {
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const uint32_t ws = w[k] ^ sm.smask[q][k];
@@ -1025,23 +1174,23 @@ __device__ __forceinline__ void fast_process(const AppendArgs& a, FastSmem& sm, 
   }
 
   uint32_t packed[8];
-  uint16_t meta = 0;
+  uint16_t meta = 0, meta1 = 0;
   float res2 = 0.0f, ynorm2 = 0.0f;
   const int smode = a.scale_mode;
   if (tensor == 0) {
     if constexpr (KF == KVQ_FP4)
       fast_quantize_fp4(y, smode, desc, packed, meta, res2, ynorm2);
     else
-      fast_quantize<KF, KG>(y, desc, packed, meta, res2, ynorm2);
+      fast_quantize<KF, KG>(y, desc, packed, meta, meta1, res2, ynorm2);
   } else {
     if constexpr (VF == KVQ_FP4)
       fast_quantize_fp4(y, smode, desc, packed, meta, res2, ynorm2);
     else
-      fast_quantize<VF, VG>(y, desc, packed, meta, res2, ynorm2);
+      fast_quantize<VF, VG>(y, desc, packed, meta, meta1, res2, ynorm2);
   }
 
   if (desc) {  // outward-rounded norms, as in the generic kernel
-    const float slack = fwht ? 9.5367431640625e-7f : 0.0f;
+    const float slack = SRFT ? 4.0e-6f : fwht ? 9.5367431640625e-7f : 0.0f;
     float rn = sqrtf(quad_sum(res2)) * 1.0009765625f + sqrtf(quad_sum(ynorm2)) * slack;
     float vn = sqrtf(quad_sum(xnorm2)) * 1.0009765625f;
     if (!valid) {
@@ -1070,6 +1219,7 @@ __device__ __forceinline__ void fast_process(const AppendArgs& a, FastSmem& sm, 
       }
       uint16_t* m16 = reinterpret_cast<uint16_t*>(a.k_meta + (stream_idx * a.Tmax + pos) * meta_bytes(KF, KG));
       if constexpr (KF == KVQ_FP4 || KG == 32) m16[q] = meta;  // FP4: E4M3 bytes of blocks 2q, 2q + 1
+      else if constexpr (KG == 16) reinterpret_cast<uint32_t*>(m16)[q] = (uint32_t)meta | ((uint32_t)meta1 << 16);
       else if (q == 0) m16[0] = meta;
     }
     return;
@@ -1085,8 +1235,14 @@ __device__ __forceinline__ void fast_process(const AppendArgs& a, FastSmem& sm, 
         mbase[(2 * q + 1) * TILE + tau] = (uint8_t)(meta >> 8);
       } else {
         uint16_t* mtile = reinterpret_cast<uint16_t*>(mbase);
-        if constexpr (VG == 32) mtile[q * TILE + tau] = meta;
-        else if (q == 0) mtile[tau] = meta;
+        if constexpr (VG == 32) {
+          mtile[q * TILE + tau] = meta;
+        } else if constexpr (VG == 16) {
+          mtile[(2 * q) * TILE + tau] = meta;
+          mtile[(2 * q + 1) * TILE + tau] = meta1;
+        } else if (q == 0) {
+          mtile[tau] = meta;
+        }
       }
     }
   }
@@ -1118,7 +1274,7 @@ __device__ __forceinline__ void fast_process(const AppendArgs& a, FastSmem& sm, 
   }
 }
 
-template <int KF, int KG, int VF, int VG, bool BF16>
+template <int KF, int KG, int VF, int VG, bool BF16, bool SRFT = false>
 __global__ __launch_bounds__(NT) void append_fast_kernel(AppendArgs a, int ntiles) {
   static_assert(VF == KVQ_INT4 || VF == KVQ_FP4, "V codes of the fast path are nibbles");
   __shared__ FastSmem sm;
@@ -1128,13 +1284,23 @@ __global__ __launch_bounds__(NT) void append_fast_kernel(AppendArgs a, int ntile
   uint32_t w[16];
   fast_load(U.src, w);
   // sign masks: bit 15 / bit 31 of pair k of quarter q set where the sign is negative
-  if (a.rotation == KVQ_ROT_SIGN_FWHT && t < 64) {
+  if ((SRFT || a.rotation == KVQ_ROT_SIGN_FWHT) && t < 64) {
     const int qq = t >> 4, k = t & 15;
     const uint16_t sp = *reinterpret_cast<const uint16_t*>(a.signs + 32 * qq + 2 * k);
     sm.smask[qq][k] = ((uint32_t)(sp & 0x80u) << 8) | ((uint32_t)(sp & 0x8000u) << 16);
   }
-  __syncthreads();
-  fast_process<KF, KG, VF, VG, BF16>(a, sm, U, w);
+  if constexpr (SRFT) {
+    __shared__ SrftRegSmem ss;
+    if (t < 65) {
+      ss.twr[t] = a.tw_re[t];
+      ss.twi[t] = a.tw_im[t];
+    }
+    __syncthreads();
+    fast_process<KF, KG, VF, VG, BF16, true>(a, sm, &ss, U, w);
+  } else {
+    __syncthreads();
+    fast_process<KF, KG, VF, VG, BF16, false>(a, sm, nullptr, U, w);
+  }
 }
 
 // ================================================================ dense rotation on matrix cores
@@ -1409,6 +1575,25 @@ static int dense_grid_limit(bool bf16) {
 hipError_t launch_append(const AppendArgs& a, int grid_x, hipStream_t s) {
   dim3 grid(grid_x, a.H, 2 * a.B);  // K and V of every sequence in one launch
   const bool rescale = a.lam_k != nullptr || a.lam_v != nullptr;  // the generic kernel applies it
+  if (a.rotation == KVQ_ROT_SRFT && !rescale) {  // SRFT in registers for the common pairs
+    const dim3 fgrid(grid_x * a.H * 2 * a.B);
+#define KVQ_FAST_SRFT(KF, KG, VF, VG)                                                  \
+    if (a.k_fmt == KF && (KF == KVQ_FP4 || a.k_group == KG) && a.v_fmt == VF &&          \
+        (VF == KVQ_FP4 || a.v_group == VG)) {                                            \
+      if (a.in_bf16)                                                                    \
+        hipLaunchKernelGGL((append_fast_kernel<KF, KG, VF, VG, true, true>), fgrid, dim3(NT), 0, s, a, grid_x); \
+      else                                                                              \
+        hipLaunchKernelGGL((append_fast_kernel<KF, KG, VF, VG, false, true>), fgrid, dim3(NT), 0, s, a, grid_x); \
+      return hipGetLastError();                                                         \
+    }
+    KVQ_FAST_SRFT(KVQ_INT4, 32, KVQ_INT4, 32)
+    KVQ_FAST_SRFT(KVQ_INT4, 16, KVQ_INT4, 16)
+    KVQ_FAST_SRFT(KVQ_INT4, 128, KVQ_INT4, 128)
+    KVQ_FAST_SRFT(KVQ_INT8, 128, KVQ_INT4, 128)
+    KVQ_FAST_SRFT(KVQ_INT8, 32, KVQ_INT4, 32)
+    KVQ_FAST_SRFT(KVQ_FP4, 16, KVQ_FP4, 16)
+#undef KVQ_FAST_SRFT
+  }
   if ((a.rotation == KVQ_ROT_NONE || a.rotation == KVQ_ROT_SIGN_FWHT) && !rescale) {
     const dim3 fgrid(grid_x * a.H * 2 * a.B);
 #define KVQ_FAST(KF, KG, VF, VG)                                                       \
@@ -1420,6 +1605,7 @@ hipError_t launch_append(const AppendArgs& a, int grid_x, hipStream_t s) {
       return hipGetLastError();                                                         \
     }
     KVQ_FAST(KVQ_INT4, 32, KVQ_INT4, 32)
+    KVQ_FAST(KVQ_INT4, 16, KVQ_INT4, 16)
     KVQ_FAST(KVQ_INT4, 128, KVQ_INT4, 128)
     KVQ_FAST(KVQ_INT8, 128, KVQ_INT4, 128)
     KVQ_FAST(KVQ_INT8, 32, KVQ_INT4, 32)

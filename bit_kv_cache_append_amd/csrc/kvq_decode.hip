@@ -309,11 +309,18 @@ __device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryI
         y0 = re * c0;
         y1 = im * c0;
       } else {
-        for (int n = 0; n < D; ++n) {
-          const int ix = (l * n) & 127;
-          re = fmaf(sm.qf[j][n], sm.ctab[ix], re);
-          im = fmaf(sm.qf[j][n], sm.ctab[(ix + 96) & 127], im);  // sin = cos(. - pi/2)
+        // four independent partial sums (n mod 4) keep the fma chains short
+        float pr[4] = {0.0f, 0.0f, 0.0f, 0.0f}, pi[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int n0 = 0; n0 < D; n0 += 4) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int n = n0 + u, ix = (l * n) & 127;
+            pr[u] = fmaf(sm.qf[j][n], sm.ctab[ix], pr[u]);
+            pi[u] = fmaf(sm.qf[j][n], sm.ctab[(ix + 96) & 127], pi[u]);  // sin = cos(. - pi/2)
+          }
         }
+        re = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        im = (pi[0] + pi[1]) + (pi[2] + pi[3]);
         y0 = re * 0.125f;
         y1 = -im * 0.125f;
       }
@@ -571,12 +578,19 @@ __device__ void combine_row(const DecodeArgs& a, int row, float* zsw, const floa
     __builtin_amdgcn_wave_barrier();
     lds_wait();
     const float c0 = bits_to_f32(KVQ_INV_SQRT_D_BITS);
-    float acc0 = 0.0f, acc1 = 0.0f;
-    for (int m = 1; m < 64; ++m) {
-      const int i0 = (m * c) & 127, i1 = (m * (c + 1)) & 127;
-      acc0 = fmaf(zsw[2 * m], ctab[i0], fmaf(-zsw[2 * m + 1], ctab[(i0 + 96) & 127], acc0));
-      acc1 = fmaf(zsw[2 * m], ctab[i1], fmaf(-zsw[2 * m + 1], ctab[(i1 + 96) & 127], acc1));
+    // four independent partial sums (m mod 4; the m = 0 slot holds the DC and Nyquist terms)
+    float a0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, a1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int m0 = 0; m0 < 64; m0 += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int m = m0 + u;
+        if (m == 0) continue;
+        const int i0 = (m * c) & 127, i1 = (m * (c + 1)) & 127;
+        a0[u] = fmaf(zsw[2 * m], ctab[i0], fmaf(-zsw[2 * m + 1], ctab[(i0 + 96) & 127], a0[u]));
+        a1[u] = fmaf(zsw[2 * m], ctab[i1], fmaf(-zsw[2 * m + 1], ctab[(i1 + 96) & 127], a1[u]));
+      }
     }
+    const float acc0 = (a0[0] + a0[1]) + (a0[2] + a0[3]), acc1 = (a1[0] + a1[1]) + (a1[2] + a1[3]);
     r0 = fmaf(c0, zsw[0] + zsw[1], 0.125f * acc0);   // n = c is even
     r1 = fmaf(c0, zsw[0] - zsw[1], 0.125f * acc1);   // n = c + 1 is odd
     if (a.signs[c] < 0) r0 = -r0;
