@@ -259,6 +259,27 @@ __device__ __forceinline__ QueryIn query_loads(const DecodeArgs& a, int b, int h
   return r;
 }
 
+// 64-point complex FFT across the lanes of a wave (lane l holds point l), radix 2,
+// decimation in frequency: stage h pairs lanes l and l ^ h, the lower takes a + b, the
+// upper (a - b) W64^((l mod h) 32 / h).  The result is in bit-reversed order: lane p
+// holds point rev6(p).  Forward: W64 = e^(-2 pi i / 64); inverse (unnormalised): e^(+...).
+// ctab: cos(2 pi k / 128), k = 0..127 (sin x = cos(x - pi/2): index + 96).
+__device__ __forceinline__ void wave_fft64(float& re, float& im, int l, const float* ctab, bool inverse) {
+#pragma unroll
+  for (int h = 32; h >= 1; h >>= 1) {
+    const float pr = __shfl_xor(re, h), pi = __shfl_xor(im, h);
+    const bool up = (l & h) != 0;
+    const float sr = up ? pr - re : re + pr;
+    const float si = up ? pi - im : im + pi;
+    const int e2 = 2 * (l & (h - 1)) * (32 / h);  // W64^e = W128^(2e)
+    const float c = ctab[e2 & 127], sn = ctab[(e2 + 96) & 127];
+    const float wi = inverse ? sn : -sn;
+    re = up ? sr * c - si * wi : sr;
+    im = up ? sr * wi + si * c : si;
+  }
+}
+__device__ __forceinline__ int rev6(int l) { return (int)(__builtin_bitreverse32((uint32_t)l) >> 26); }
+
 template <int KF>
 __device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryIn& qin, int nh, int kgroup, int hkv) {
   // waves 0..3 own query heads 0..3; further waves only join the barriers
@@ -289,43 +310,28 @@ __device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryI
       y1 = up ? p1 - y1 : y1 + p1;
     }
   } else if (a.rotation == KVQ_ROT_SRFT) {
-    // y = R q with R the packed unitary DFT times diag(s): lane l forms X_l =
-    // sum_n u_n e^(-2 pi i l n / 128), u = s * q, which gives channels 2l, 2l + 1
-    // (lane 0: X_0 and X_64)
-    if (own) {
-      sm.qf[j][2 * l] = (qin.sg & 0x80u) ? -x0 : x0;
-      sm.qf[j][2 * l + 1] = (qin.sg & 0x8000u) ? -x1 : x1;
-    }
+    // y = R q with R the packed unitary DFT times diag(s): the 64-point FFT of
+    // z_n = u_2n + i u_2n+1 (u = s * q) across the wave, then X_l = E + W128^l O from
+    // Z_l and conj Z_(64-l); lane l keeps channels 2l, 2l + 1 (lane 0: X_0 and X_64)
     if (t < 128) sm.ctab[t] = a.cos128[t];
     __syncthreads();
-    if (own) {
-      float re = 0.0f, im = 0.0f;
+    if (own) {  // whole waves
+      float re = (qin.sg & 0x80u) ? -x0 : x0, im = (qin.sg & 0x8000u) ? -x1 : x1;
+      wave_fft64(re, im, l, sm.ctab, false);
+      const int ka = rev6(l), kb = rev6((64 - l) & 63);
+      const float a_re = __shfl(re, ka), a_im = __shfl(im, ka);  // Z_l
+      const float b_re = __shfl(re, kb), b_im = -__shfl(im, kb);  // conj Z_(64-l)
+      const float e_re = 0.5f * (a_re + b_re), e_im = 0.5f * (a_im + b_im);
+      const float o_re = 0.5f * (a_im - b_im), o_im = -0.5f * (a_re - b_re);
+      const float c = sm.ctab[l], sn = sm.ctab[(l + 96) & 127];  // W128^l = (c, -sn)
+      y0 = (e_re + (o_re * c + o_im * sn)) * 0.125f;
+      y1 = (e_im + (o_im * c - o_re * sn)) * 0.125f;
       if (l == 0) {
-        for (int n = 0; n < D; n += 2) {
-          re += sm.qf[j][n] + sm.qf[j][n + 1];
-          im += sm.qf[j][n] - sm.qf[j][n + 1];
-        }
         const float c0 = bits_to_f32(KVQ_INV_SQRT_D_BITS);
-        y0 = re * c0;
-        y1 = im * c0;
-      } else {
-        // four independent partial sums (n mod 4) keep the fma chains short
-        float pr[4] = {0.0f, 0.0f, 0.0f, 0.0f}, pi[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int n0 = 0; n0 < D; n0 += 4) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int n = n0 + u, ix = (l * n) & 127;
-            pr[u] = fmaf(sm.qf[j][n], sm.ctab[ix], pr[u]);
-            pi[u] = fmaf(sm.qf[j][n], sm.ctab[(ix + 96) & 127], pi[u]);  // sin = cos(. - pi/2)
-          }
-        }
-        re = (pr[0] + pr[1]) + (pr[2] + pr[3]);
-        im = (pi[0] + pi[1]) + (pi[2] + pi[3]);
-        y0 = re * 0.125f;
-        y1 = -im * 0.125f;
+        y0 = (a_re + a_im) * c0;  // X_0
+        y1 = (a_re - a_im) * c0;  // X_64
       }
     }
-    __syncthreads();
   } else if (a.rotation == KVQ_ROT_DENSE) {
     if (own) {
       sm.qf[j][2 * l] = x0;
@@ -572,27 +578,26 @@ __device__ void combine_row(const DecodeArgs& a, int row, float* zsw, const floa
     r0 *= a.signs[c] < 0 ? -cn : cn;
     r1 *= a.signs[c + 1] < 0 ? -cn : cn;
   } else if (a.rotation == KVQ_ROT_SRFT) {
-    // R^T o: o_n = s_n (c0 (z_0 + (-1)^n z_1) + sum_{m=1..63} (z_2m cos - z_2m+1 sin)(2 pi m n / 128) / 8)
-    zsw[c] = o0;
-    zsw[c + 1] = o1;
-    __builtin_amdgcn_wave_barrier();
-    lds_wait();
+    // R^T o = s * IDFT128(V), V the Hermitian spectrum V_0 = o_0 c0, V_64 = o_1 c0,
+    // V_k = (o_2k + i o_2k+1) / 16, V_(128-k) = conj V_k.  Its even and odd samples are
+    // z_n = x_2n + i x_2n+1 = IDFT64(G)_n with G_k = (V_k + conj V_(64-k)) + i W128^(-k)
+    // (V_k - conj V_(64-k)); lane l forms G_l, the wave runs the inverse FFT, and lane l
+    // takes z_l from lane rev6(l).  (zsw is not needed: everything stays in registers.)
+    (void)zsw;
     const float c0 = bits_to_f32(KVQ_INV_SQRT_D_BITS);
-    // four independent partial sums (m mod 4; the m = 0 slot holds the DC and Nyquist terms)
-    float a0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, a1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int m0 = 0; m0 < 64; m0 += 4) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int m = m0 + u;
-        if (m == 0) continue;
-        const int i0 = (m * c) & 127, i1 = (m * (c + 1)) & 127;
-        a0[u] = fmaf(zsw[2 * m], ctab[i0], fmaf(-zsw[2 * m + 1], ctab[(i0 + 96) & 127], a0[u]));
-        a1[u] = fmaf(zsw[2 * m], ctab[i1], fmaf(-zsw[2 * m + 1], ctab[(i1 + 96) & 127], a1[u]));
-      }
+    const float vr = l == 0 ? o0 * c0 : o0 * 0.0625f, vi = l == 0 ? 0.0f : o1 * 0.0625f;
+    float qr = __shfl(vr, (64 - l) & 63), qi = __shfl(vi, (64 - l) & 63);  // V_(64-l)
+    if (l == 0) {
+      qr = o1 * c0;  // V_64
+      qi = 0.0f;
     }
-    const float acc0 = (a0[0] + a0[1]) + (a0[2] + a0[3]), acc1 = (a1[0] + a1[1]) + (a1[2] + a1[3]);
-    r0 = fmaf(c0, zsw[0] + zsw[1], 0.125f * acc0);   // n = c is even
-    r1 = fmaf(c0, zsw[0] - zsw[1], 0.125f * acc1);   // n = c + 1 is odd
+    const float pr = vr + qr, pi = vi - qi;  // V + conj Q
+    const float dr = vr - qr, di = vi + qi;  // V - conj Q
+    const float cw = ctab[l], sw = ctab[(l + 96) & 127];  // W128^(-l) = (cw, sw)
+    float gr = pr - (dr * sw + di * cw), gi = pi + (dr * cw - di * sw);
+    wave_fft64(gr, gi, l, ctab, true);
+    r0 = __shfl(gr, rev6(l));
+    r1 = __shfl(gi, rev6(l));
     if (a.signs[c] < 0) r0 = -r0;
     if (a.signs[c + 1] < 0) r1 = -r1;
   } else if (a.rotation == KVQ_ROT_DENSE) {
