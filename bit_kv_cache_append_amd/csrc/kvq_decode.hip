@@ -197,6 +197,48 @@ __device__ __forceinline__ float sum_same_head(float v) {
   v += __shfl_xor(v, 32);
   return v;
 }
+// v of lane l ^ M: DPP moves for masks inside a row of 16 (quad permutes; (l ^ 3) then a
+// half-row mirror (l ^ 7) is l ^ 4; (l ^ 7) then a row mirror (l ^ 15) is l ^ 8), a
+// shuffle through the LDS crossbar otherwise
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  if constexpr (M == 1) return dpp_f<0xB1>(v);
+  else if constexpr (M == 2) return dpp_f<0x4E>(v);
+  else if constexpr (M == 4) return dpp_f<0x141>(dpp_f<0x1B>(v));
+  else if constexpr (M == 8) return dpp_f<0x140>(dpp_f<0x141>(v));
+  else return __shfl_xor(v, M);
+}
+// one Walsh-Hadamard stage across lanes on two values per lane: the lower lane of each
+// pair keeps own + partner, the upper partner - own
+template <int M>
+__device__ __forceinline__ void wht_stage(float& y0, float& y1, int l) {
+  const float p0 = lane_xor<M>(y0), p1 = lane_xor<M>(y1);
+  const bool up = (l & M) != 0;
+  y0 = up ? p0 - y0 : y0 + p0;
+  y1 = up ? p1 - y1 : y1 + p1;
+}
+__device__ __forceinline__ void wht_lanes(float& y0, float& y1, int l) {  // h = 2, 4, ..., 64 (masks 1..32)
+  wht_stage<1>(y0, y1, l);
+  wht_stage<2>(y0, y1, l);
+  wht_stage<4>(y0, y1, l);
+  wht_stage<8>(y0, y1, l);
+  wht_stage<16>(y0, y1, l);
+  wht_stage<32>(y0, y1, l);
+}
+// one radix-2 stage of the wave FFT below (span H)
+template <int H>
+__device__ __forceinline__ void fft_stage(float& re, float& im, int l, const float* ctab, bool inverse) {
+  const float pr = lane_xor<H>(re), pi = lane_xor<H>(im);
+  const bool up = (l & H) != 0;
+  const float sr = up ? pr - re : re + pr;
+  const float si = up ? pi - im : im + pi;
+  const int e2 = 2 * (l & (H - 1)) * (32 / H);  // W64^e = W128^(2e)
+  const float c = ctab[e2 & 127], sn = ctab[(e2 + 96) & 127];
+  const float wi = inverse ? sn : -sn;
+  re = up ? sr * c - si * wi : sr;
+  im = up ? sr * wi + si * c : si;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
@@ -265,18 +307,12 @@ __device__ __forceinline__ QueryIn query_loads(const DecodeArgs& a, int b, int h
 // holds point rev6(p).  Forward: W64 = e^(-2 pi i / 64); inverse (unnormalised): e^(+...).
 // ctab: cos(2 pi k / 128), k = 0..127 (sin x = cos(x - pi/2): index + 96).
 __device__ __forceinline__ void wave_fft64(float& re, float& im, int l, const float* ctab, bool inverse) {
-#pragma unroll
-  for (int h = 32; h >= 1; h >>= 1) {
-    const float pr = __shfl_xor(re, h), pi = __shfl_xor(im, h);
-    const bool up = (l & h) != 0;
-    const float sr = up ? pr - re : re + pr;
-    const float si = up ? pi - im : im + pi;
-    const int e2 = 2 * (l & (h - 1)) * (32 / h);  // W64^e = W128^(2e)
-    const float c = ctab[e2 & 127], sn = ctab[(e2 + 96) & 127];
-    const float wi = inverse ? sn : -sn;
-    re = up ? sr * c - si * wi : sr;
-    im = up ? sr * wi + si * c : si;
-  }
+  fft_stage<32>(re, im, l, ctab, inverse);
+  fft_stage<16>(re, im, l, ctab, inverse);
+  fft_stage<8>(re, im, l, ctab, inverse);
+  fft_stage<4>(re, im, l, ctab, inverse);
+  fft_stage<2>(re, im, l, ctab, inverse);
+  fft_stage<1>(re, im, l, ctab, inverse);
 }
 __device__ __forceinline__ int rev6(int l) { return (int)(__builtin_bitreverse32((uint32_t)l) >> 26); }
 
@@ -303,12 +339,7 @@ __device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryI
     x1 = (qin.sg & 0x8000u) ? -x1 : x1;
     y0 = x0 + x1;
     y1 = x0 - x1;
-    for (int msk = 1; msk < 64; msk <<= 1) {
-      const float p0 = __shfl_xor(y0, msk), p1 = __shfl_xor(y1, msk);
-      const bool up = (l & msk) != 0;
-      y0 = up ? p0 - y0 : y0 + p0;
-      y1 = up ? p1 - y1 : y1 + p1;
-    }
+    wht_lanes(y0, y1, l);
   } else if (a.rotation == KVQ_ROT_SRFT) {
     // y = R q with R the packed unitary DFT times diag(s): the 64-point FFT of
     // z_n = u_2n + i u_2n+1 (u = s * q) across the wave, then X_l = E + W128^l O from
@@ -568,12 +599,7 @@ __device__ void combine_row(const DecodeArgs& a, int row, float* zsw, const floa
     // R^T o = diag(s) H o / sqrt(128): the butterflies over this head's 64 lanes
     r0 = o0 + o1;
     r1 = o0 - o1;
-    for (int msk = 1; msk < 64; msk <<= 1) {
-      const float q0 = __shfl_xor(r0, msk), q1 = __shfl_xor(r1, msk);
-      const bool up = (l & msk) != 0;
-      r0 = up ? q0 - r0 : r0 + q0;
-      r1 = up ? q1 - r1 : r1 + q1;
-    }
+    wht_lanes(r0, r1, l);
     const float cn = bits_to_f32(KVQ_INV_SQRT_D_BITS);
     r0 *= a.signs[c] < 0 ? -cn : cn;
     r1 *= a.signs[c + 1] < 0 ? -cn : cn;
