@@ -183,20 +183,6 @@ __device__ __forceinline__ h2 e4m3x2_to_h2(uint32_t b0, uint32_t b1) {
 }
 
 // ------------------------------------------------------------------ reductions
-__device__ __forceinline__ float max_same_head(float v) {  // over lanes with equal (lane & 3)
-  v = fmaxf(v, __shfl_xor(v, 4));
-  v = fmaxf(v, __shfl_xor(v, 8));
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
-}
-__device__ __forceinline__ float sum_same_head(float v) {
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
-}
 // v of lane l ^ M: DPP moves for masks inside a row of 16 (quad permutes; (l ^ 3) then a
 // half-row mirror (l ^ 7) is l ^ 4; (l ^ 7) then a row mirror (l ^ 15) is l ^ 8), a
 // shuffle through the LDS crossbar otherwise
@@ -239,13 +225,35 @@ __device__ __forceinline__ void fft_stage(float& re, float& im, int l, const flo
   im = up ? sr * wi + si * c : si;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-  for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+__device__ __forceinline__ float max_same_head(float v) {  // over lanes with equal (lane & 3)
+  v = fmaxf(v, lane_xor<4>(v));
+  v = fmaxf(v, lane_xor<8>(v));
+  v = fmaxf(v, lane_xor<16>(v));
+  v = fmaxf(v, lane_xor<32>(v));
   return v;
 }
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+__device__ __forceinline__ float sum_same_head(float v) {
+  v += lane_xor<4>(v);
+  v += lane_xor<8>(v);
+  v += lane_xor<16>(v);
+  v += lane_xor<32>(v);
   return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, lane_xor<1>(v));
+  v = fmaxf(v, lane_xor<2>(v));
+  v = fmaxf(v, lane_xor<4>(v));
+  v = fmaxf(v, lane_xor<8>(v));
+  v = fmaxf(v, lane_xor<16>(v));
+  return fmaxf(v, lane_xor<32>(v));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += lane_xor<1>(v);
+  v += lane_xor<2>(v);
+  v += lane_xor<4>(v);
+  v += lane_xor<8>(v);
+  v += lane_xor<16>(v);
+  return v + lane_xor<32>(v);
 }
 template <int H>
 __device__ __forceinline__ float quad_bcast(float v) {
@@ -432,13 +440,13 @@ __device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryI
   }
   // per-group sums of the 16-bit codes (groups of 16 channels = 8 lanes, 32 = 16 lanes)
   float gs = (float)(q0 + q1);
-  gs += __shfl_xor(gs, 1);
-  gs += __shfl_xor(gs, 2);
-  gs += __shfl_xor(gs, 4);
+  gs += lane_xor<1>(gs);
+  gs += lane_xor<2>(gs);
+  gs += lane_xor<4>(gs);
   if (kgroup == 16) {
     if (own && (l & 7) == 0) sm.qsum[j][l >> 3] = gs;
   } else {
-    gs += __shfl_xor(gs, 8);
+    gs += lane_xor<8>(gs);
     if (kgroup == 128) {
       gs += __shfl_xor(gs, 16);
       gs += __shfl_xor(gs, 32);
@@ -499,7 +507,7 @@ __device__ void write_record(const DecodeArgs& a, DecodeSmem& sm, int b, int hq0
     // ||q|| * scale from the prologue's q * scale * log2(e)
     const float q0 = sm.qo[hh][c], q1 = sm.qo[hh][c + 1];
     float sq = q0 * q0 + q1 * q1;
-    for (int off = 32; off > 0; off >>= 1) sq += __shfl_xor(sq, off);
+    sq = wave_sum(sq);
     qn = sqrtf(sq) / LOG2E;
   }
   if (l == 0) {
