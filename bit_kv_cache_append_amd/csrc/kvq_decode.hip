@@ -186,13 +186,32 @@ __device__ __forceinline__ h2 e4m3x2_to_h2(uint32_t b0, uint32_t b1) {
 // v of lane l ^ M: DPP moves for masks inside a row of 16 (quad permutes; (l ^ 3) then a
 // half-row mirror (l ^ 7) is l ^ 4; (l ^ 7) then a row mirror (l ^ 15) is l ^ 8), a
 // shuffle through the LDS crossbar otherwise
+// {v of lane l, v of lane l ^ M} in every lane, M = 16 or 32 (the gfx950 row and
+// half-wave swaps: the first result holds the lower rows, the second the upper ones)
+template <int M>
+__device__ __forceinline__ void lane_pair(float v, float& lo, float& hi) {
+  const int vi = __float_as_int(v);
+  if constexpr (M == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(vi, vi, false, false);
+    lo = __int_as_float(p[0]);
+    hi = __int_as_float(p[1]);
+  } else {
+    const auto p = __builtin_amdgcn_permlane32_swap(vi, vi, false, false);
+    lo = __int_as_float(p[0]);
+    hi = __int_as_float(p[1]);
+  }
+}
 template <int M>
 __device__ __forceinline__ float lane_xor(float v) {
   if constexpr (M == 1) return dpp_f<0xB1>(v);
   else if constexpr (M == 2) return dpp_f<0x4E>(v);
   else if constexpr (M == 4) return dpp_f<0x141>(dpp_f<0x1B>(v));
   else if constexpr (M == 8) return dpp_f<0x140>(dpp_f<0x141>(v));
-  else return __shfl_xor(v, M);
+  else {
+    float lo, hi;
+    lane_pair<M>(v, lo, hi);
+    return (__lane_id() & M) ? lo : hi;
+  }
 }
 // one Walsh-Hadamard stage across lanes on two values per lane: the lower lane of each
 // pair keeps own + partner, the upper partner - own
@@ -225,35 +244,42 @@ __device__ __forceinline__ void fft_stage(float& re, float& im, int l, const flo
   im = up ? sr * wi + si * c : si;
 }
 
+// max / sum with lane l ^ M for M = 16, 32: both lanes of a pair form the same value
+template <int M>
+__device__ __forceinline__ float max_with(float v) {
+  float lo, hi;
+  lane_pair<M>(v, lo, hi);
+  return fmaxf(lo, hi);
+}
+template <int M>
+__device__ __forceinline__ float sum_with(float v) {
+  float lo, hi;
+  lane_pair<M>(v, lo, hi);
+  return lo + hi;
+}
 __device__ __forceinline__ float max_same_head(float v) {  // over lanes with equal (lane & 3)
   v = fmaxf(v, lane_xor<4>(v));
   v = fmaxf(v, lane_xor<8>(v));
-  v = fmaxf(v, lane_xor<16>(v));
-  v = fmaxf(v, lane_xor<32>(v));
-  return v;
+  return max_with<32>(max_with<16>(v));
 }
 __device__ __forceinline__ float sum_same_head(float v) {
   v += lane_xor<4>(v);
   v += lane_xor<8>(v);
-  v += lane_xor<16>(v);
-  v += lane_xor<32>(v);
-  return v;
+  return sum_with<32>(sum_with<16>(v));
 }
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, lane_xor<1>(v));
   v = fmaxf(v, lane_xor<2>(v));
   v = fmaxf(v, lane_xor<4>(v));
   v = fmaxf(v, lane_xor<8>(v));
-  v = fmaxf(v, lane_xor<16>(v));
-  return fmaxf(v, lane_xor<32>(v));
+  return max_with<32>(max_with<16>(v));
 }
 __device__ __forceinline__ float wave_sum(float v) {
   v += lane_xor<1>(v);
   v += lane_xor<2>(v);
   v += lane_xor<4>(v);
   v += lane_xor<8>(v);
-  v += lane_xor<16>(v);
-  return v + lane_xor<32>(v);
+  return sum_with<32>(sum_with<16>(v));
 }
 template <int H>
 __device__ __forceinline__ float quad_bcast(float v) {
@@ -448,8 +474,7 @@ __device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryI
   } else {
     gs += lane_xor<8>(gs);
     if (kgroup == 128) {
-      gs += __shfl_xor(gs, 16);
-      gs += __shfl_xor(gs, 32);
+      gs = sum_with<32>(sum_with<16>(gs));
     }
     if (own && (l & 15) == 0) sm.qsum[j][l >> 4] = gs;
   }
@@ -781,9 +806,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float max_same_head_fast(float v) {
   v = fmaxf(v, dpp_f<0x124>(v));  // row_ror:4
   v = fmaxf(v, dpp_f<0x128>(v));  // row_ror:8
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  return max_with<32>(max_with<16>(v));
 }
 
 // MODE 0: codes only.  MODE 1: blocks of the full-precision window recomputed
