@@ -49,6 +49,9 @@ CASES = {
     "fp4-search": (synth.config(5, B=2, T=1024), [1024, 701]),
     "int4-srft": (synth.config(2, B=2, T=640, rotation="srft"), [640, 300]),
     "int4-g16": (synth.config(2, B=2, T=640, k_group=16, v_group=16), [640, 129]),
+    # two groups of four query heads per kv head, and a partial group of two
+    "int4-gqa8-two-groups": (synth.config(2, B=2, Hq=16, Hkv=2, T=640), [640, 513]),
+    "int8k-int4v-gqa2": (synth.config(3, B=1, Hq=4, Hkv=2, T=512), [450]),
 }
 
 
