@@ -73,7 +73,7 @@ def test_block_mass_and_selection_match_oracle(name):
     for b in range(c["B"]):
         nb = (seq[b] + 63) // 64
         assert not got[b, :, nb:].any()
-    for tau in (0.5, 0.9, 0.995, 1.0):
+    for tau in (0.0, 0.5, 0.9, 0.995, 1.0, 2.0):
         fl = kvq.select_blocks(p, mass, seq, tau)
         torch.cuda.synchronize()
         want = adaptive.select_blocks(got, np.array(seq), tau, c["Hkv"])

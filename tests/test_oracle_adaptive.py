@@ -106,3 +106,17 @@ def test_dense_fallback_replaces_rows_over_eps():
     assert redo.tolist() == [[False, True, False]]
     assert o[0, 1].tolist() == [7.0, 7.0] and o[0, 0].tolist() == [1.0, 1.0]
     assert c.tolist() == [[0.1, 0.0, 0.2]]
+
+
+def test_top_blocks_tau_zero_and_above_one():
+    # tau_cov = 0: the shortest prefix reaching 0 is one block, the largest mass (lowest
+    # index among equal masses); tau_cov > 1: coverage is never reached, every block is kept
+    rng = np.random.default_rng(31)
+    for n in (1, 2, 7, 33):
+        m = rng.random(n).astype(np.float32)
+        m = (m / m.sum()).astype(np.float32)
+        assert adaptive.top_blocks(m, n, 0.0) == [int(np.argmax(m))]
+        assert sorted(adaptive.top_blocks(m, n, 2.0)) == list(range(n))
+    tie = np.array([0.25, 0.25, 0.5, 0.5], np.float32)[::-1].copy()  # masses 0.5, 0.5, 0.25, 0.25
+    assert adaptive.top_blocks(tie, 4, 0.0) == [0]
+    assert adaptive.top_blocks(tie, 4, 0.75) == [0, 1]
