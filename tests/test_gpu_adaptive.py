@@ -73,11 +73,14 @@ def test_block_mass_and_selection_match_oracle(name):
     for b in range(c["B"]):
         nb = (seq[b] + 63) // 64
         assert not got[b, :, nb:].any()
-    for tau in (0.0, 0.5, 0.9, 0.995, 1.0, 2.0):
+    for tau in (0.0, 0.5, 0.9, 0.995, 1.0):
         fl = kvq.select_blocks(p, mass, seq, tau)
         torch.cuda.synchronize()
         want = adaptive.select_blocks(got, np.array(seq), tau, c["Hkv"])
         assert np.array_equal(fl.cpu().numpy(), want), f"{name}: selection differs at tau_cov {tau}"
+    with pytest.raises(kvq.KvqError) as e:  # coverage is a fraction: the call rejects 2
+        kvq.select_blocks(p, mass, seq, 2.0)
+    assert e.value.status == -1
     # union with given flags, in place
     base = np.zeros((c["B"], c["Hkv"], c["T"] // 64), np.uint8)
     base[:, :, 1] = 1
