@@ -1274,33 +1274,41 @@ __device__ __forceinline__ void fast_process(const AppendArgs& a, FastSmem& sm, 
   }
 }
 
+// Two units per workgroup (the K and the V tile of one position range): both
+// units' input rows are loaded first, so twice the bytes are in flight per thread.
 template <int KF, int KG, int VF, int VG, bool BF16, bool SRFT = false>
 __global__ __launch_bounds__(NT) void append_fast_kernel(AppendArgs a, int ntiles) {
   static_assert(VF == KVQ_INT4 || VF == KVQ_FP4, "V codes of the fast path are nibbles");
   __shared__ FastSmem sm;
   const int t = threadIdx.x;
-  const FastUnit U = fast_unit(a, blockIdx.x, ntiles);
-  if (U.lo >= U.hi) return;  // uniform over the workgroup
-  uint32_t w[16];
-  fast_load(U.src, w);
+  const int nunits = ntiles * a.H * 2 * a.B;
+  const int u0 = 2 * (int)blockIdx.x, u1 = min(u0 + 1, nunits - 1);
+  const FastUnit U0 = fast_unit(a, u0, ntiles), U1 = fast_unit(a, u1, ntiles);
+  const bool run0 = U0.lo < U0.hi, run1 = u1 != u0 && U1.lo < U1.hi;  // uniform over the workgroup
+  if (!run0 && !run1) return;
+  uint32_t w0[16], w1[16];
+  fast_load(U0.src, w0);  // rows of an empty unit still lie inside the input (row 0 of its stream)
+  fast_load(U1.src, w1);
+  __builtin_amdgcn_sched_barrier(0);
   // sign masks: bit 15 / bit 31 of pair k of quarter q set where the sign is negative
   if ((SRFT || a.rotation == KVQ_ROT_SIGN_FWHT) && t < 64) {
     const int qq = t >> 4, k = t & 15;
     const uint16_t sp = *reinterpret_cast<const uint16_t*>(a.signs + 32 * qq + 2 * k);
     sm.smask[qq][k] = ((uint32_t)(sp & 0x80u) << 8) | ((uint32_t)(sp & 0x8000u) << 16);
   }
+  SrftRegSmem* ssp = nullptr;
   if constexpr (SRFT) {
     __shared__ SrftRegSmem ss;
     if (t < 65) {
       ss.twr[t] = a.tw_re[t];
       ss.twi[t] = a.tw_im[t];
     }
-    __syncthreads();
-    fast_process<KF, KG, VF, VG, BF16, true>(a, sm, &ss, U, w);
-  } else {
-    __syncthreads();
-    fast_process<KF, KG, VF, VG, BF16, false>(a, sm, nullptr, U, w);
+    ssp = &ss;
   }
+  __syncthreads();
+  if (run0) fast_process<KF, KG, VF, VG, BF16, SRFT>(a, sm, ssp, U0, w0);
+  __syncthreads();  // the shared staging areas are reused by the second unit
+  if (run1) fast_process<KF, KG, VF, VG, BF16, SRFT>(a, sm, ssp, U1, w1);
 }
 
 // ================================================================ dense rotation on matrix cores
@@ -1576,7 +1584,7 @@ hipError_t launch_append(const AppendArgs& a, int grid_x, hipStream_t s) {
   dim3 grid(grid_x, a.H, 2 * a.B);  // K and V of every sequence in one launch
   const bool rescale = a.lam_k != nullptr || a.lam_v != nullptr;  // the generic kernel applies it
   if (a.rotation == KVQ_ROT_SRFT && !rescale) {  // SRFT in registers for the common pairs
-    const dim3 fgrid(grid_x * a.H * 2 * a.B);
+    const dim3 fgrid((grid_x * a.H * 2 * a.B + 1) / 2);  // two units per workgroup
 #define KVQ_FAST_SRFT(KF, KG, VF, VG)                                                  \
     if (a.k_fmt == KF && (KF == KVQ_FP4 || a.k_group == KG) && a.v_fmt == VF &&          \
         (VF == KVQ_FP4 || a.v_group == VG)) {                                            \
@@ -1595,7 +1603,7 @@ hipError_t launch_append(const AppendArgs& a, int grid_x, hipStream_t s) {
 #undef KVQ_FAST_SRFT
   }
   if ((a.rotation == KVQ_ROT_NONE || a.rotation == KVQ_ROT_SIGN_FWHT) && !rescale) {
-    const dim3 fgrid(grid_x * a.H * 2 * a.B);
+    const dim3 fgrid((grid_x * a.H * 2 * a.B + 1) / 2);  // two units per workgroup
 #define KVQ_FAST(KF, KG, VF, VG)                                                       \
     if (a.k_fmt == KF && a.k_group == KG && a.v_fmt == VF && a.v_group == VG) {         \
       if (a.in_bf16)                                                                    \
