@@ -417,7 +417,7 @@ def adaptive_ladder(args, c, p, caches, q, seq, ws, out, cert, bnd, flg, batch_t
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one MI355X; --gpus {args.gpus} is not supported (this build runs on one GPU).",
+        print(f"bench.py measures one MI355X; --gpus {args.gpus} is not supported (the library runs on one GPU).",
               file=sys.stderr)
         sys.exit(2)
     if args.workload != 2:
