@@ -3,7 +3,7 @@
 Every computation runs in the HIP kernels of libkvq.so; this module turns torch
 tensors into device pointers and the current HIP stream, calls the C entry
 points of the same names (kvq_append, kvq_error_bound, kvq_decode_attn,
-kvq_decode_attn_dense, kvq_calibrate_clip, kvq_block_mass, kvq_select_blocks,
+kvq_decode_attn_dense, kvq_decode_attn_noalloc, kvq_calibrate_clip, kvq_block_mass, kvq_select_blocks,
 kvq_dense_fallback, kvq_calibrate_lambda, kvq_buffer_bytes, kvq_decode_workspace_bytes, kvq_decode_splits) and raises KvqError on a non-zero status.  There is
 no fallback: if the library is not built, importing the functions raises.
 """
@@ -78,6 +78,8 @@ def lib():
         L.kvq_error_bound.argtypes = [P(Params), P(CacheStruct), vp, P(i32), ctypes.c_float, vp, vp, vp]
         L.kvq_decode_attn.restype = i32
         L.kvq_decode_attn.argtypes = [P(Params), P(CacheStruct), vp, P(i32), vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.kvq_decode_attn_noalloc.restype = i32
+        L.kvq_decode_attn_noalloc.argtypes = [P(Params), P(CacheStruct), vp, P(i32), vp, vp, vp, vp]
         L.kvq_decode_attn_dense.restype = i32
         L.kvq_decode_attn_dense.argtypes = [P(Params), vp, vp, vp, P(i32), vp, vp, ctypes.c_size_t, vp]
         L.kvq_block_mass.restype = i32
@@ -223,6 +225,20 @@ def decode_attn(p, cache, q, seq_len, flags=None, certificate=False, ws=None, ou
     _check(lib().kvq_decode_attn(ctypes.byref(p), ctypes.byref(cs), _ptr(q), _i32(seq_len), _ptr(flags), _ptr(out),
                                  _ptr(cert) if certificate else None, _ptr(ws), ws.numel() * ws.element_size(),
                                  stream if stream is not None else _stream()))
+    return (out, cert) if certificate else out
+
+
+def decode_attn_noalloc(p, cache, q, seq_len, flags=None, certificate=False, out=None, cert=None, stream=None):
+    """kvq_decode_attn_noalloc: kvq_decode_attn on the library's fixed per-device workspace."""
+    import torch
+    if out is None:
+        out = torch.empty((p.batch, p.n_q_heads, 128), dtype=torch.float32, device=q.device)
+    if certificate and cert is None:
+        cert = torch.empty((p.batch, p.n_q_heads), dtype=torch.float32, device=q.device)
+    cs = cache.struct()
+    _check(lib().kvq_decode_attn_noalloc(ctypes.byref(p), ctypes.byref(cs), _ptr(q), _i32(seq_len), _ptr(flags),
+                                         _ptr(out), _ptr(cert) if certificate else None,
+                                         stream if stream is not None else _stream()))
     return (out, cert) if certificate else out
 
 

@@ -364,24 +364,36 @@ kvq_status kvq_error_bound(const kvq_params* p, const kvq_cache* c, const void* 
   return KVQ_OK;
 }
 
+// ws == nullptr with noalloc: the library's fixed per-device workspace (no allocation)
 static kvq_status decode_common(const kvq_params* p, const kvq_cache* c, const void* q, const int32_t* seq_len_host,
                                 const uint8_t* flags, float* out, float* cert, void* ws, size_t ws_bytes,
-                                void* stream, bool dense, const void* kd, const void* vd) {
+                                void* stream, bool dense, const void* kd, const void* vd, bool noalloc = false) {
   kvq_status st = check_params(p);
   if (st) return st;
   if (!q || !out) return fail(KVQ_ERR_INVALID_ARG, "q/out are NULL");
   DecodeArgs a;
   memset(&a, 0, sizeof(a));
   if ((st = check_seq(p, seq_len_host, a.seq))) return st;
-  const size_t need = kvq_decode_workspace_bytes(p);
-  if (!ws || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
-  if (((uintptr_t)ws & 255u) != 0) return fail(KVQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   int max_chunks = 0;
   for (int b = 0; b < p->batch; ++b) {
     const int ch = (a.seq.v[b] + TILE - 1) / TILE;
     if (ch > max_chunks) max_chunks = ch;
   }
   const int n_splits = choose_splits(p, max_chunks > 0 ? max_chunks : 1, dense);
+  if (noalloc) {
+    const size_t nctr = ctr_bytes(p);
+    const size_t nrec = (size_t)p->batch * p->n_q_heads * n_splits * PART_FLOATS * sizeof(float);
+    if (nctr > SCRATCH_CTR_BYTES)
+      return fail(KVQ_ERR_WORKSPACE, "the fixed workspace holds %zu bytes of split counters; this call needs %zu",
+                  SCRATCH_CTR_BYTES, nctr);
+    if (nrec > SCRATCH_BYTES - SCRATCH_CTR_BYTES)
+      return fail(KVQ_ERR_WORKSPACE, "the fixed workspace holds %zu bytes of split records; this call needs %zu",
+                  SCRATCH_BYTES - SCRATCH_CTR_BYTES, nrec);
+  } else {
+    const size_t need = kvq_decode_workspace_bytes(p);
+    if (!ws || ws_bytes < need) return fail(KVQ_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, ws_bytes);
+    if (((uintptr_t)ws & 255u) != 0) return fail(KVQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
   a.q = (const uint16_t*)q;
   if (dense) {
     if (!kd || !vd || !aligned16(kd) || !aligned16(vd))
@@ -411,8 +423,17 @@ static kvq_status decode_common(const kvq_params* p, const kvq_cache* c, const v
     a.signs = c->signs;
     a.rot = c->rot_f16;
   }
-  a.ctr = (int*)ws;
-  a.part = (float*)((char*)ws + ctr_bytes(p));
+  hipStream_t s = (hipStream_t)stream;
+  if (noalloc) {
+    void* base = nullptr;
+    hipError_t e = decode_scratch(&base, s);
+    if (e != hipSuccess) return hip_fail(e, "fixed decode workspace");
+    a.ctr = (int*)base;
+    a.part = (float*)((char*)base + SCRATCH_CTR_BYTES);
+  } else {
+    a.ctr = (int*)ws;
+    a.part = (float*)((char*)ws + ctr_bytes(p));
+  }
   a.out = out;
   a.cert = dense ? nullptr : cert;
   a.B = p->batch;
@@ -430,7 +451,6 @@ static kvq_status decode_common(const kvq_params* p, const kvq_cache* c, const v
   if (a.chunks_per_split < 1) a.chunks_per_split = 1;
   a.scale = softmax_scale(p);
   if (a.rotation == KVQ_ROT_SRFT) srft_cos_table(a.cos128);
-  hipStream_t s = (hipStream_t)stream;
   hipError_t e = launch_decode(a, p->k_fmt, p->v_fmt, dense, s);
   if (e == hipErrorNotSupported) return fail(KVQ_ERR_UNSUPPORTED, "format combination not supported by decode");
   if (e != hipSuccess) return hip_fail(e, "decode launch");
@@ -523,6 +543,13 @@ kvq_status kvq_decode_attn(const kvq_params* p, const kvq_cache* c, const void* 
                            size_t workspace_bytes, void* stream) {
   return decode_common(p, c, q, seq_len_host, block_flags, out, certificate, workspace, workspace_bytes, stream, false,
                        nullptr, nullptr);
+}
+
+kvq_status kvq_decode_attn_noalloc(const kvq_params* p, const kvq_cache* c, const void* q,
+                                   const int32_t* seq_len_host, const uint8_t* block_flags, float* out,
+                                   float* certificate, void* stream) {
+  return decode_common(p, c, q, seq_len_host, block_flags, out, certificate, nullptr, 0, stream, false, nullptr,
+                       nullptr, true);
 }
 
 kvq_status kvq_decode_attn_dense(const kvq_params* p, const void* k, const void* v, const void* q,

@@ -34,6 +34,8 @@
 // counter, on records written and read with agent-coherent accesses.  The fp16
 // baseline uses a separate combine launch for the same merge.
 
+#include <mutex>
+
 #include "kvq_common.h"
 
 namespace kvq {
@@ -1430,7 +1432,45 @@ __global__ __launch_bounds__(NT, 2) void decode_dense_split(DecodeArgs a) {
   write_record<false, 4, false>(a, sm, b, hq0, nh, split);
 }
 
+// ------------------------------------------------------------------ allocation-free workspace
+// A fixed device array that serves as the decode workspace of kvq_decode_attn_noalloc:
+// arrival counters in its first SCRATCH_CTR_BYTES (only ever written as counters, so
+// every completed call leaves all of them zero, whatever the shapes of the calls),
+// split records after them.  Every device holds its own copy, at its own address.
+static __device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
+
+__global__ __launch_bounds__(256) void zero_words(uint32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
 }  // namespace
+
+// Device address of this device's scratch array (the array's name is only a host-side
+// stand-in).  Looked up once per device, with that device current; the first lookup also
+// clears the counter region with a fill kernel on the caller's stream (no memset: the
+// call may be under graph capture).
+hipError_t decode_scratch(void** ptr, hipStream_t s) {
+  static std::mutex mu;
+  static void* addr[MAX_DEVICES] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    hipLaunchKernelGGL(zero_words, dim3(16), dim3(256), 0, s, static_cast<uint32_t*>(p),
+                       (int)(SCRATCH_CTR_BYTES / sizeof(uint32_t)));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs& a, int k_fmt, int v_fmt, bool dense, hipStream_t s) {
   const int HG = (a.G + 3) / 4;

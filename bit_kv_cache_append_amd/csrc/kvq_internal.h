@@ -110,6 +110,11 @@ constexpr int MAX_SELECT_BLOCKS = 4096;  // selection sorts one head's blocks in
 // [8+D..8+2D) oo: original-basis accumulator of exactly recomputed blocks.
 constexpr int PART_FLOATS = 8 + 2 * D;
 constexpr int MAX_SPLITS = 128;
+// The allocation-free decode's fixed workspace: 8 MiB per device, counters in the first
+// 64 KiB (16384 of them), records in the rest.
+constexpr size_t SCRATCH_BYTES = size_t(8) << 20;
+constexpr size_t SCRATCH_CTR_BYTES = size_t(64) << 10;
+constexpr int MAX_DEVICES = 64;
 
 struct DecodeArgs {
   const uint16_t* q;  // [B][Hq][128]
@@ -147,6 +152,7 @@ hipError_t launch_window_copy(const AppendArgs& a, hipStream_t s);
 hipError_t launch_calibrate(const CalibArgs& a, hipStream_t s);
 hipError_t launch_bound(const BoundArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int k_fmt, int v_fmt, bool dense, hipStream_t s);
+hipError_t decode_scratch(void** ptr, hipStream_t s);
 hipError_t launch_block_mass(const AdaptArgs& a, hipStream_t s);
 hipError_t launch_select(const AdaptArgs& a, hipStream_t s);
 hipError_t launch_fallback(const AdaptArgs& a, hipStream_t s);

@@ -32,7 +32,9 @@
  *
  * Conventions for every call:
  *  - Ownership: the caller allocates and frees every buffer; the library never
- *    allocates device or host memory and keeps no state between calls.
+ *    allocates device or host memory.  It keeps no state between calls, except
+ *    for kvq_decode_attn_noalloc: a fixed device array per device (part of the
+ *    library's code object) and its looked-up address.
  *    Pointers named *_host are host memory, all others device memory.
  *  - Asynchrony: work is enqueued on `stream` (0 = the null stream); results are
  *    valid once the stream has synchronised.  Calls that share buffers must be
@@ -266,6 +268,26 @@ kvq_status kvq_error_bound(const kvq_params* p, const kvq_cache* cache, const vo
 kvq_status kvq_decode_attn(const kvq_params* p, const kvq_cache* cache, const void* q,
                            const int32_t* seq_len_host, const uint8_t* block_flags, float* out,
                            float* certificate, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvq_decode_attn without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation and the same q/out/certificate/flags
+ * contract as kvq_decode_attn, with the split counters and records kept in a fixed
+ * device array of the library (8 MiB per device: 64 KiB of counters, the rest for
+ * records), which each device holds until the process ends.  It calls no
+ * hipMalloc/hipFree.  The first call on a device looks the array's address up (with
+ * that device current) and clears its counters with a fill kernel on `stream`.
+ * A call needing more than the array holds (B * Hkv * ceil(G/4) * 4 bytes of
+ * counters above 64 KiB, or B * Hq * splits * 1056 bytes of records above
+ * 8 MiB - 64 KiB; splits as kvq_decode_splits reports) returns KVQ_ERR_WORKSPACE
+ * and enqueues nothing.  All calls on one device share the array: calls that
+ * overlap in time on one device (different streams, no ordering) race and give
+ * wrong results; order them (one stream or events).
+ */
+kvq_status kvq_decode_attn_noalloc(const kvq_params* p, const kvq_cache* cache, const void* q,
+                                   const int32_t* seq_len_host, const uint8_t* block_flags, float* out,
+                                   float* certificate, void* stream);
 
 /*
  * Adaptive precision ("Runtime-Certified Bounded-Error Quantized Attention",

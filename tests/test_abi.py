@@ -122,3 +122,25 @@ def test_adaptive_entry_points_validate_without_gpu():
     # the dense fallback reads the originals: it needs keep_fp16_copy
     st = L.kvq_dense_fallback(ctypes.byref(p), ctypes.byref(cs), fake, seq, ctypes.c_float(0.1), fake, fake, None)
     assert st == -1 and b"keep_fp16_copy" in L.kvq_last_error()
+
+
+def test_noalloc_decode_rejects_oversize_without_gpu():
+    # kvq_decode_attn_noalloc keeps its counters and records in a fixed 8 MiB array per
+    # device; calls that need more are refused on the host before anything is enqueued
+    L = kvq.lib()
+    fake = 1 << 20  # never dereferenced: validation fails first
+    cs = kvq.CacheStruct(k_codes=fake, k_meta=fake, v_codes=fake, v_meta=fake, signs=fake)
+    # 256 x 64 query rows, one split each: 256 * 64 * 1056 bytes of records > 8 MiB - 64 KiB
+    p = kvq.make_params(256, 64, 64, 64)
+    seq = (ctypes.c_int32 * 256)(*([64] * 256))
+    st = L.kvq_decode_attn_noalloc(ctypes.byref(p), ctypes.byref(cs), fake, seq, None, fake, None, None)
+    assert st == -3 and b"split records" in L.kvq_last_error()
+    # 256 sequences x 128 kv heads: 128 KiB of arrival counters > 64 KiB
+    p = kvq.make_params(256, 256, 128, 64)
+    st = L.kvq_decode_attn_noalloc(ctypes.byref(p), ctypes.byref(cs), fake, seq, None, fake, None, None)
+    assert st == -3 and b"split counters" in L.kvq_last_error()
+    # other argument errors are reported as for kvq_decode_attn
+    p = kvq.make_params(2, 8, 2, 256)
+    two = (ctypes.c_int32 * 2)(10, 10)
+    assert L.kvq_decode_attn_noalloc(ctypes.byref(p), ctypes.byref(cs), None, two, None, fake, None, None) == -1
+
