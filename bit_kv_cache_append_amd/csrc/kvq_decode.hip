@@ -683,7 +683,10 @@ __device__ void combine_row(const DecodeArgs& a, int row, float* zsw, const floa
   *reinterpret_cast<float2*>(out + c) = make_float2(r0, r1);
   if (CERT && a.cert && l == 0) {
     const float dstar = rec_ld<COH>(rec0 + 5) * ek;
-    a.cert[row] = 2.0f * (1.0f - expf(-2.0f * dstar)) * vn + E * inv;
+    // key term: total-variation distance under logit moves of at most dstar is at most
+    // tanh(dstar / 2), times twice the largest value norm; value term: mass-weighted
+    // reconstruction errors of the blocks read from codes
+    a.cert[row] = 2.0f * tanhf(0.5f * dstar) * vn + E * inv;
   }
 }
 

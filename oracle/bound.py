@@ -24,11 +24,20 @@ Block bound for kv head h, with the largest query norm of its GQA group:
 
 Certificate for query head hq after a pass in which flagged blocks were exact:
     Delta*  = ||q_hq|| * sigma * max_{b unflagged} ek_b
-    E       = 2 (1 - exp(-2 Delta*)) max_b vn_b + sum_{b unflagged} P_b ev_b
-with P_b the block's softmax mass in that pass.  Why it holds: with every logit
-perturbed by at most Delta*, each softmax weight changes by a factor in
-[exp(-2 Delta*), exp(2 Delta*)], so the total-variation distance is at most
-1 - exp(-2 Delta*); o - o_hat = sum (p - p_hat) v + sum p_hat (v - v_hat).
+    E       = 2 tanh(Delta* / 2) max_b vn_b + sum_{b unflagged} P_b ev_b
+with P_b the block's softmax mass in that pass.  Why it holds:
+o - o_hat = sum_i (p_i - p_hat_i) v_i + sum_i p_hat_i (v_i - v_hat_i).  The second
+sum is at most sum_b P_b ev_b (flagged blocks use exact values).  In the first,
+||.|| <= sum_i |p_i - p_hat_i| ||v_i|| <= 2 TV(p, p_hat) max ||v||, and with every
+logit moved by some delta_i, |delta_i| <= Delta* (flagged keys exact: delta = 0), the
+total-variation distance is at most tanh(Delta* / 2): for any token set A,
+p_hat(A) is largest when delta = +Delta* on A and -Delta* elsewhere, which gives
+p_hat(A) - p(A) = x a / (1 + (a - 1) x) - x with x = p(A), a = exp(2 Delta*),
+whose maximum over x (at x = 1 / (1 + sqrt a)) is (sqrt a - 1) / (sqrt a + 1) =
+tanh(Delta* / 2).  Both steps are attained (two tokens with p(A) = 1 / (1 + e^Delta*),
+logits moved by +-Delta*, values +-max||v|| along one direction, value errors
+along the same direction), so the certificate is the smallest bound these tracked
+quantities allow.
 """
 
 import numpy as np
@@ -97,5 +106,5 @@ def certificate(desc, q_bits, dtype, seq_len, flags, mass, softmax_scale=None):
             dstar = np.linalg.norm(q[b, hq]) * sigma * ekmax
             vnmax = desc[b, h, :nb, 2].max() if nb else 0.0
             val = np.sum(mass[b, hq, :nb][unf] * desc[b, h, :nb, 1][unf])
-            E[b, hq] = 2.0 * (1.0 - np.exp(-2.0 * dstar)) * vnmax + val
+            E[b, hq] = 2.0 * np.tanh(0.5 * dstar) * vnmax + val
     return E

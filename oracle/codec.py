@@ -38,9 +38,10 @@ fp4 E2M1 with an E4M3 scale per 16, absmax or searched
     Mode "offsets" is the search as the page states it: the candidates are the
     E4M3 bit patterns c0 + f of the absmax scale c0 = E4M3(t), for the integer
     offsets f = -2, ..., 6 in that order (the page's reinterpret-add-reinterpret),
-    keeping only non-negative finite patterns 0x00..0x7E.  Readings: the page
-    prints no range; [-2, 6] covers the ~1.5x larger scales it finds optimal
-    for many blocks (absmax mapped to 4 instead of 6) plus two smaller ones.
+    keeping only non-negative finite patterns 0x00..0x7E.  The range is the
+    page's own example (f in [-2, 6]); it covers the ~1.5x larger scales the page
+    finds optimal for many blocks (absmax mapped to 4 instead of 6) plus two
+    smaller ones.
 
 Layout of the cache buffers (bytes; little-endian; B batch, H kv heads,
 Tmax positions, a multiple of 64):
@@ -172,7 +173,14 @@ def dequant_asym2(codes, scales, offsets):
 
 
 def _fp4_block_error(yb, codes, S):
-    """err = fl32(seqsum_{j<8} fl32(d_j^2) + seqsum_{8<=j<16} fl32(d_j^2)), d = fl32(y - e*S)."""
+    """err = fl32(seqsum_{j<8} fl32(d_j^2) + seqsum_{8<=j<16} fl32(d_j^2)), d = fl32(y - e*S).
+
+    The page defines the error as the sum of squared residuals over the block, not an
+    order of summation; the reading taken is two sequential fp32 partial sums (elements
+    0..7 and 8..15) added at the end, which halves the dependent-add chain per
+    candidate in a write kernel.  The order decides the choice on near ties, so it is
+    part of the bit-exact contract (pinned by tests/golden/fp4_sum_order.txt).
+    """
     e = nx.e2m1_value(codes)
     prod = nx.f32(e * np.asarray(S, np.float64)[..., None])  # exact: <= 6 significant bits
     d = nx.f32(yb - prod)

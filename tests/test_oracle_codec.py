@@ -372,3 +372,23 @@ def test_lambda_helps_groups_with_an_outlier_channel():
     e_plain = np.mean((codec.decode_k(plain, 0, 0, 0, 512) - y)[:, normal] ** 2)
     e_lam = np.mean((codec.decode_k(scaled, 0, 0, 0, 512) - y)[:, normal] ** 2)
     assert e_lam < 0.05 * e_plain, (e_lam, e_plain)
+
+
+def test_fp4_sum_order_fixture():
+    # "Search Your Block Floating Point Scales!", Methodology, ScaleSearch: smallest squared
+    # error wins.  On these blocks (built by tests/golden/make_fp4_sum_order.py, which does not
+    # use the oracle) the halves order and the sequential order pick different scales; the
+    # oracle must pick the halves order's scale.
+    rows = list(_rows("fp4_sum_order.txt"))
+    assert len(rows) >= 4
+    n = 0
+    for blk, codes in zip(rows[0::2], rows[1::2]):
+        assert blk[0] == "block" and codes[0] == "halves_code"
+        y = np.zeros((1, 128), np.float32)
+        y[0, :16] = np.array([int(b, 16) for b in blk[1:17]], np.uint32).view(np.float32)
+        _, sc = codec.quantize_fp4(y, "search9")
+        want, other = int(codes[1], 16), int(codes[3], 16)
+        assert want != other
+        assert int(sc[0, 0]) == want, (hex(int(sc[0, 0])), hex(want), hex(other))
+        n += 1
+    assert n >= 2

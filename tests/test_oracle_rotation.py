@@ -172,3 +172,18 @@ def test_twiddles_are_the_rounded_fp64_values():
         ang = 2 * np.pi * k / 128
         assert wr[k] == np.float32(np.cos(ang)) and wi[k] == np.float32(-np.sin(ang))
         assert abs(float(wr[k]) - np.cos(ang)) <= abs(np.spacing(np.float32(wr[k]))) / 2
+
+
+def test_srft_pass_order_golden():
+    # hand-derived bits ("When Quantization Is Free", Methodology sections 1-2): the
+    # Stockham passes add points 32 apart first; the other order changes the last bits
+    x = np.zeros(128, np.float16)
+    outs = {}
+    for row in _rows("srft_pass_order.txt"):
+        if row[0] == "in":
+            x.view(np.uint16)[int(row[1])] = int(row[2], 16)
+        else:
+            outs[int(row[1])] = int(row[2], 16)
+    y = rot.srft_f32(x.astype(np.float32)[None], np.ones(128))[0]
+    for idx, bits in outs.items():
+        assert int(y[idx].view(np.uint32)) == bits, (idx, hex(int(y[idx].view(np.uint32))), hex(bits))
