@@ -82,6 +82,10 @@ kvq_status check_cache(const kvq_params* p, const kvq_cache* c, bool need_desc) 
   } else if (need_desc) {
     return fail(KVQ_ERR_INVALID_ARG, "this call needs keep_fp16_copy");
   }
+  // The descriptors are residual norms in the rotated basis; they bound original-basis
+  // errors only for an orthogonal rotation, and the fp16-rounded dense matrix is not one.
+  if (p->keep_fp16_copy && p->rotation == KVQ_ROT_DENSE)
+    return fail(KVQ_ERR_UNSUPPORTED, "keep_fp16_copy (certified descriptors) is not supported with the dense rotation");
   if (p->keep_fp16_copy && (c->lambda_k || c->lambda_v))
     return fail(KVQ_ERR_UNSUPPORTED, "per-channel rescale factors are not supported with keep_fp16_copy");
   if (p->sink_blocks + p->recent_blocks > 0 &&

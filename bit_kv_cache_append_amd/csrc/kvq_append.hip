@@ -1564,20 +1564,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3))) void
 }
 
 // resident workgroups of the persistent dense kernel on the current device
+// Resident workgroups of the persistent dense int2 kernel on the current device (asked
+// on every call: no state is kept between calls).
 static int dense_grid_limit(bool bf16) {
-  static int cached[2][64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  int& c = cached[bf16 ? 1 : 0][dev];
-  if (c == 0) {
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    hipError_t e = bf16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, append_dense_int2_kernel<true>, NT, 0)
-                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, append_dense_int2_kernel<false>, NT, 0);
-    if (e != hipSuccess || per_cu <= 0) per_cu = 1;
-    c = cus * per_cu;
-  }
-  return c;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  hipError_t e = bf16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, append_dense_int2_kernel<true>, NT, 0)
+                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, append_dense_int2_kernel<false>, NT, 0);
+  if (e != hipSuccess || per_cu <= 0) per_cu = 1;
+  return cus * per_cu;
 }
 
 hipError_t launch_append(const AppendArgs& a, int grid_x, hipStream_t s) {

@@ -144,3 +144,15 @@ def test_noalloc_decode_rejects_oversize_without_gpu():
     two = (ctypes.c_int32 * 2)(10, 10)
     assert L.kvq_decode_attn_noalloc(ctypes.byref(p), ctypes.byref(cs), None, two, None, fake, None, None) == -1
 
+
+def test_certified_cache_with_dense_rotation_rejected_without_gpu():
+    # the block descriptors are rotated-basis residual norms: they bound original-basis errors
+    # only for an orthogonal rotation, and the fp16-rounded dense matrix is not orthogonal
+    L = kvq.lib()
+    p = kvq.make_params(2, 8, 2, 256, "int2", "int2", rotation="dense", keep_fp16_copy=True)
+    fake = 1 << 20  # never dereferenced: validation fails first
+    cs = kvq.CacheStruct(k_codes=fake, k_meta=fake, v_codes=fake, v_meta=fake, blk_desc=fake, k_orig=fake,
+                         v_orig=fake, rot_f16=fake)
+    starts = (ctypes.c_int32 * 2)(0, 0)
+    st = L.kvq_append(ctypes.byref(p), ctypes.byref(cs), fake, fake, starts, 4, None)
+    assert st == -2 and b"dense" in L.kvq_last_error()
