@@ -15,16 +15,17 @@ Four caches (and four copies of the prefill input) are used in rotation: the
 decode of step i reads the cache appended in step i-2, so between two uses of a
 cache at least 3 x 144 MiB of other data streams through the 256 MB Infinity
 Cache and every timed call reads its inputs from HBM.  Each kernel sequence is
-also timed on its own (back-to-back calls over the rotating buffers, HIP events
-around the batch on the stream the calls are launched on), and once more with a
-1 GiB read flush and events around every single call (that figure includes the
-event and launch overhead of one isolated call).
+also timed on its own: batches of back-to-back calls over the rotating buffers,
+HIP events around each batch on the stream the calls are launched on, the median
+of the batch means (decode: 8 batches of 16 calls); and once more as 50 single
+calls, each after a 1 GiB read flush (median; includes one launch).
 
-value = decode effective KV GB/s = packed K/V bytes (codes + scales) / mean
-decode call time (split kernel + combine kernel).  The same-shape fp16 decode
-(kvq_decode_attn_dense) is timed the same way for the int4-vs-fp16 comparison;
-append throughput is reported in Mvec/s.  The CPU oracle is timed on a bounded
-sample as a reported baseline.
+value = decode effective KV GB/s = packed K/V bytes (codes + scales) / median
+decode call time (one launch: the splits are merged by their last workgroup).
+The same-shape fp16 decode (kvq_decode_attn_dense) is timed the same way for the
+int4-vs-fp16 comparison; append throughput is reported in Mvec/s.  The CPU oracle
+is timed as a reported baseline: one process on 4 sequences, and one process per
+available core (at most 16) over all 16 sequences.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
 """
@@ -82,6 +83,15 @@ def parse():
     return args
 
 
+def median_of_batches(batch_time, fn, per, n_batches):
+    """(median, min) over n_batches of the mean ms per call of per back-to-back calls of fn(i)
+    (HIP events around each batch, on the stream the calls are launched on)."""
+    vals = []
+    for k in range(n_batches):
+        vals.append(batch_time(lambda i, k=k: fn(k * per + i), per))
+    return float(np.median(vals)), float(np.min(vals))
+
+
 def attention_window_tokens(T, n_sink, n_recent):
     """Tokens of a T-token sequence in its first n_sink and last n_recent 64-token blocks."""
     nb = (T + 63) // 64
@@ -105,37 +115,109 @@ def kernel_traffic(roofline_kernel_src):
     return rec.get("hbm_bytes_per_call")
 
 
-def cpu_baseline(c, sample_b):
-    """Time the oracle on sample_b sequences of the same workload (reported baseline only)."""
-    from threadpoolctl import threadpool_limits
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_seq_setup(c, b):
+    """Inputs of sequence b and an oracle cache holding its context before the prefill."""
     import synth
+    from oracle import codec
+    cs = dict(c, B=1)
+    T, P, H = c["T"], c["prefill"], c["Hkv"]
+    k = np.stack([synth.kv_slice(c, 0, b, h, 0, T) for h in range(H)])[None]
+    v = np.stack([synth.kv_slice(c, 1, b, h, 0, T) for h in range(H)])[None]
+    s = synth.signs(c)
+    oc = codec.Cache(1, H, T, cs["k_fmt"], cs["v_fmt"], cs["k_group"], cs["v_group"])
+    codec.append(oc, k[:, :, :T - P], v[:, :, :T - P], np.zeros(1, int), "f16", cs["rotation"], s,
+                 scale_mode=cs["scale_mode"])
+    q = synth.queries(c)[b:b + 1]
+    return k, v, s, oc, q
+
+
+def _oracle_seq_run(c, k, v, s, oc, q):
+    """Times (append of the prefill, decode over the whole context) of one sequence."""
     from oracle import attention, codec
     T, P = c["T"], c["prefill"]
-    H = c["Hkv"]
+    t0 = time.perf_counter()
+    codec.append(oc, k[:, :, T - P:], v[:, :, T - P:], np.full(1, T - P), "f16", c["rotation"], s,
+                 scale_mode=c["scale_mode"])
+    t1 = time.perf_counter()
+    attention.decode_attention(oc, q, "f16", np.full(1, T), c["rotation"], s)
+    t2 = time.perf_counter()
+    return t1 - t0, t2 - t1
+
+
+def _oracle_worker(c, seqs, barrier, out):
+    """One process of the N-process baseline: set its sequences up, wait for the others, then
+    run the prefill appends of all of them and, after a second barrier, their decodes."""
+    os.environ["OMP_NUM_THREADS"] = "1"
+    from threadpoolctl import threadpool_limits
     with threadpool_limits(1):
-        cs = synth.config(2, B=sample_b, rotation=c["rotation"])
-        k = synth.kv_all(cs, 0, 0, T)
-        v = synth.kv_all(cs, 1, 0, T)
-        s = synth.signs(cs)
-        oc = codec.Cache(sample_b, H, T, cs["k_fmt"], cs["v_fmt"], cs["k_group"], cs["v_group"])
-        codec.append(oc, k[:, :, :T - P], v[:, :, :T - P], np.zeros(sample_b, int), "f16", cs["rotation"], s,
-                     scale_mode=cs["scale_mode"])
-        t0 = time.perf_counter()
-        codec.append(oc, k[:, :, T - P:], v[:, :, T - P:], np.full(sample_b, T - P), "f16", cs["rotation"], s,
-                     scale_mode=cs["scale_mode"])
-        t_app = time.perf_counter() - t0
-        q = synth.queries(cs)
-        t0 = time.perf_counter()
-        attention.decode_attention(oc, q, "f16", np.full(sample_b, T), cs["rotation"], s)
-        t_dec = time.perf_counter() - t0
-    kv_bytes = sample_b * H * T * 144
-    vecs = sample_b * H * P * 2
+        st = [_oracle_seq_setup(c, b) for b in seqs]
+        from oracle import attention, codec
+        T, P = c["T"], c["prefill"]
+        barrier.wait()
+        ta0 = time.time()
+        for k, v, s, oc, q in st:
+            codec.append(oc, k[:, :, T - P:], v[:, :, T - P:], np.full(1, T - P), "f16", c["rotation"], s,
+                         scale_mode=c["scale_mode"])
+        ta1 = time.time()
+        barrier.wait()
+        td0 = time.time()
+        for k, v, s, oc, q in st:
+            attention.decode_attention(oc, q, "f16", np.full(1, T), c["rotation"], s)
+        td1 = time.time()
+    out.put((ta0, ta1, td0, td1))
+
+
+def cpu_baseline(c, sample_b):
+    """The oracle timed on the host cores (a reported baseline, not the target).
+
+    One process (one BLAS thread) on sample_b sequences; then N processes (one BLAS thread
+    each, N = the cores this process may use, at most 16) over all B sequences, released
+    together by a barrier after their set-up, the append and the decode timed separately."""
+    import multiprocessing as mp
+    from threadpoolctl import threadpool_limits
+    T, P, H, B = c["T"], c["prefill"], c["Hkv"], c["B"]
+    bytes_per_seq = H * T * 144
+    with threadpool_limits(1):
+        app1 = dec1 = 0.0
+        for b in range(sample_b):
+            st = _oracle_seq_setup(c, b)
+            ta, td = _oracle_seq_run(c, *st)
+            app1 += ta
+            dec1 += td
+    cores = len(os.sched_getaffinity(0))
+    nproc = max(1, min(16, cores, B))
+    ctx = mp.get_context("spawn")  # the parent has initialised the GPU: no fork
+    barrier = ctx.Barrier(nproc)
+    out = ctx.Queue()
+    procs = [ctx.Process(target=_oracle_worker, args=(c, list(range(r, B, nproc)), barrier, out)) for r in range(nproc)]
+    for pr in procs:
+        pr.start()
+    res = [out.get(timeout=600) for _ in procs]
+    for pr in procs:
+        pr.join(timeout=60)
+    app_n = max(r[1] for r in res) - min(r[0] for r in res)
+    dec_n = max(r[3] for r in res) - min(r[2] for r in res)
+    vecs_seq = H * P * 2
     return {
-        "value": round(kv_bytes / t_dec / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": (f"{sample_b} of {c['B']} sequences: decode over {T} tokens (all {c['Hq']} q heads) took "
-                   f"{t_dec:.2f} s; the {P}-token prefill append of those sequences ({vecs} vectors) took "
-                   f"{t_app:.2f} s"),
-        "append_mvec_s": round(vecs / t_app / 1e6, 4),
+        "value": round(bytes_per_seq * B / dec_n / 1e9, 4), "unit": "GB/s", "cores": nproc, "kind": "oracle",
+        "sample": (f"all {B} sequences in {nproc} processes (one BLAS thread each, released together): decode over "
+                   f"{T} tokens of every sequence (all {c['Hq']} q heads) in {dec_n:.2f} s, the {P}-token prefill "
+                   f"append ({vecs_seq * B} vectors) in {app_n:.2f} s; one process on {sample_b} sequences: decode "
+                   f"{dec1:.2f} s, append {app1:.2f} s"),
+        "append_mvec_s": round(vecs_seq * B / app_n / 1e6, 4),
+        "single_process": {"value": round(bytes_per_seq * sample_b / dec1 / 1e9, 4),
+                           "append_mvec_s": round(vecs_seq * sample_b / app1 / 1e6, 4), "sequences": sample_b},
+        "host": {"cpus_available": cores, "cpu_model": _cpu_model()},
     }
 
 
@@ -166,13 +248,16 @@ def bench_workload(cfg_id, args):
     def progress(msg):
         print(f"[bench w{cfg_id}] {msg}", file=sys.stderr, flush=True)
 
-    def draw(tensor):
+    # certified workload: planted tokens (x10 in K and V alike), one in pieces 0-2 and two in
+    # piece 3 of every (sequence, kv head); each piece fills two of the eight 4096-token
+    # spans of the context, so every stream holds 10 planted tokens in 512 blocks (~2%)
+    plant_pos = [torch.randint(0, P, (1 if i < nrot - 1 else 2, B, H), generator=g, device=dev) for i in range(nrot)]
+
+    def draw(tensor, piece):
         shape = (B, H, P, 128)
         if c["data"] == "certified":
             x = torch.randn(shape, generator=g, device=dev) * (c["k_sigma"] if tensor == 0 else c["v_sigma"])
-            # one planted token (x10) in each of two seeded blocks per (b, head) of the piece
-            for _ in range(2):
-                t = torch.randint(0, P, (B, H), generator=g, device=dev)
+            for t in plant_pos[piece]:
                 idx = t[..., None, None].expand(B, H, 1, 128)
                 x.scatter_(2, idx, x.gather(2, idx) * c["plant_factor"])
             return x.half().view(torch.int16)
@@ -202,8 +287,8 @@ def bench_workload(cfg_id, args):
                                     ratio=c["clip_ratio"])
         for cc in caches:
             cc.clip_k, cc.clip_v = tk, tv
-    kin = [draw(0) for _ in range(nrot)]
-    vin = [draw(1) for _ in range(nrot)]
+    kin = [draw(0, i) for i in range(nrot)]
+    vin = [draw(1, i) for i in range(nrot)]
     for cc in caches:
         for t0 in range(0, T, P):
             kvq.append(p, cc, kin[(t0 // P) % nrot], vin[(t0 // P) % nrot], [t0] * B)
@@ -250,9 +335,9 @@ def bench_workload(cfg_id, args):
     step_ms = batch_time(lambda i: (do_append(i), do_decode(i + 2)), args.steps)
     progress(f"{args.steps} steps timed")
     batch_time(do_decode, nrot)
-    dec_ms = batch_time(do_decode, n_each)
+    dec_ms, dec_min = median_of_batches(batch_time, do_decode, 16, 4)
     batch_time(do_append, nrot)
-    app_ms = batch_time(do_append, n_each)
+    app_ms, _ = median_of_batches(batch_time, do_append, 8, 8)
     # the fp16/bf16 same-shape baseline: the certified workload's own originals, else fresh tensors
     if c["keep"]:
         dense = [(caches[i].bufs["k_orig"], caches[i].bufs["v_orig"]) for i in range(2)]
@@ -268,8 +353,8 @@ def bench_workload(cfg_id, args):
     dws = kvq.workspace(p)
     dout = torch.empty_like(out)
     batch_time(lambda i: kvq.decode_attn_dense(p, dense[i % 2][0], dense[i % 2][1], q, seq, ws=dws, out=dout), 2)
-    f16_ms = batch_time(lambda i: kvq.decode_attn_dense(p, dense[i % 2][0], dense[i % 2][1], q, seq, ws=dws,
-                                                        out=dout), n_each)
+    f16_ms, _ = median_of_batches(batch_time, lambda i: kvq.decode_attn_dense(p, dense[i % 2][0], dense[i % 2][1], q,
+                                                                              seq, ws=dws, out=dout), 8, 8)
     progress("batches timed")
     sizes = kvq.buffer_bytes(p)
     packed = sizes["k_codes"] + sizes["k_meta"] + sizes["v_codes"] + sizes["v_meta"]
@@ -322,7 +407,10 @@ def bench_workload(cfg_id, args):
                      "kernel": "decode_split (splits merged by their last workgroup)" + (" + bound_kernel" if c["keep"] else ""),
                      "bytes_per_call": packed + io},
         "decode_us": round(dec_s * 1e6, 2),
-        "decode_grid": [kvq.decode_splits(p, seq), H * ((Hq // H + 3) // 4), B],
+        "decode_us_min_batch": round(dec_min * 1e3, 2),
+        "decode_timing": "median over 4 batches of the mean of 16 back-to-back calls",
+        "decode_grid_workgroups": kvq.decode_splits(p, seq) * B * H * ((Hq // H + 3) // 4),
+        "decode_splits": kvq.decode_splits(p, seq),
         "fp16_decode_us": round(f16_s * 1e6, 2),
         "fp16_decode_pct_hbm_peak": round(100 * dense_bytes / f16_s / 1e9 / HBM_PEAK_GBS, 2),
         "speedup_vs_fp16": round(f16_s / dec_s, 3),
@@ -508,24 +596,25 @@ def main():
     # each kernel sequence on its own over the rotating buffers
     n_each = max(args.steps, 4 * NROT)
     batch_time(do_decode, NROT)
-    dec_ms = batch_time(do_decode, n_each)
+    dec_ms, dec_min = median_of_batches(batch_time, do_decode, 16, 8)
     batch_time(do_append, NROT)
-    app_ms = batch_time(do_append, n_each)
+    app_ms, _ = median_of_batches(batch_time, do_append, 8, 8)
     batch_time(do_dense, 2)
-    f16_ms = batch_time(do_dense, n_each)
+    f16_ms, _ = median_of_batches(batch_time, do_dense, 8, 8)
     progress("per-kernel batches timed")
     # isolated calls: 1 GiB read flush, events around each call
+    # isolated calls: 10 warm-ups, then the median of 50, each after a 1 GiB read flush
     iso = []
-    for i in range(args.warmup + args.steps):
+    for i in range(60):
         torch.sum(flush_buf, dim=0, out=sink)
         e0, e1 = ev(), ev()
         e0.record()
         do_decode(i)
         e1.record()
-        if i >= args.warmup:
+        if i >= 10:
             iso.append((e0, e1))
     torch.cuda.synchronize()
-    iso_ms = float(np.mean([a.elapsed_time(b) for a, b in iso]))
+    iso_ms = float(np.median([a.elapsed_time(b) for a, b in iso]))
     # int4 vs fp16 outputs on the same query (quantization effect, informational)
     do_decode(0)
     do_dense(0)
@@ -565,7 +654,11 @@ def main():
         "decode_us": round(dec_s * 1e6, 2),
         "decode_pct_hbm_peak": round(100 * dec_gbs / HBM_PEAK_GBS, 2),
         "decode_isolated_call_us": round(iso_ms * 1e3, 2),
-        "decode_grid": [n_splits, H * ((Hq // H + 3) // 4), B],
+        "decode_isolated_timing": "median of 50 single calls, each after a 1 GiB read flush (includes one launch)",
+        "decode_us_min_batch": round(dec_min * 1e3, 2),
+        "decode_timing": "median over 8 batches of the mean of 16 back-to-back calls over 4 rotating caches",
+        "decode_grid_workgroups": n_splits * B * H * ((Hq // H + 3) // 4),
+        "decode_splits": n_splits,
         "fp16_decode_us": round(f16_s * 1e6, 2),
         "fp16_decode_gbs": round(f16_bytes / f16_s / 1e9, 1),
         "fp16_decode_pct_hbm_peak": round(100 * f16_bytes / f16_s / 1e9 / HBM_PEAK_GBS, 2),
@@ -587,7 +680,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(c, sample_b=8)
+        result["cpu_baseline"] = cpu_baseline(c, sample_b=4)
     print(json.dumps(result))
 
 

@@ -139,6 +139,11 @@ int choose_splits(const kvq_params* p, int max_chunks, bool dense = false) {
   return (int)s;
 }
 
+int units_of(const kvq_params* p) {
+  const int G = p->n_q_heads / p->n_kv_heads;
+  return p->batch * p->n_kv_heads * ((G + 3) / 4);
+}
+
 int max_splits_for(const kvq_params* p) {
   const int a = choose_splits(p, p->max_ctx / TILE, false), b = choose_splits(p, p->max_ctx / TILE, true);
   return a > b ? a : b;
@@ -196,11 +201,10 @@ int32_t kvq_decode_splits(const kvq_params* p, const int32_t* seq_len_host) {
   return choose_splits(p, max_chunks > 0 ? max_chunks : 1);
 }
 
-// workspace: [arrival counters, one int32 per (sequence, kv head, group of 4 query heads),
-// padded to 256 bytes][split records]
+// workspace: [arrival counters, one int32 per unit (sequence, kv head, group of 4 query
+// heads), padded to 256 bytes][split records]
 static size_t ctr_bytes(const kvq_params* p) {
-  const int G = p->n_q_heads / p->n_kv_heads;
-  const size_t n = (size_t)p->batch * p->n_kv_heads * ((G + 3) / 4);
+  const size_t n = (size_t)units_of(p);
   return (n * sizeof(int32_t) + 255) & ~(size_t)255;
 }
 
@@ -438,6 +442,7 @@ static kvq_status decode_common(const kvq_params* p, const kvq_cache* c, const v
     a.ctr = (int*)ws;
     a.part = (float*)((char*)ws + ctr_bytes(p));
   }
+  a.U = units_of(p);
   a.out = out;
   a.cert = dense ? nullptr : cert;
   a.B = p->batch;

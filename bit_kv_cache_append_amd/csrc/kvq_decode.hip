@@ -294,49 +294,54 @@ __device__ __forceinline__ uint32_t quad_bcast_u(uint32_t v) {
 
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Per-wave partial results merged in LDS at the end of a split kernel.
+template <int NW>
+struct MergeArea {
+  float o[NW][4][D];   // rotated-basis accumulator by wave, head, channel
+  float oo[NW][4][D];  // original-basis accumulator of exactly recomputed chunks
+  float m[NW][4], l[NW][4], e[NW][4];
+  float ek[NW], vn[NW];
+};
+
+constexpr int MAX_VG = 8;  // V scale groups per token (groups of 16 and FP4 blocks)
+
 struct __align__(16) DecodeSmem {
-  float qf[4][D];          // query (fp32), rotated in place
-  float qr[4][D];          // dense rotation output
-  float ctab[128];         // cos(2 pi k / 128) for the SRFT rotation
-  float qo[4][D];          // original query * scale * log2e (certified recompute)
-  uint32_t qh[4][32];      // high int8 halves: dword 4n + c = MFMA operand of chain c, step n
-  uint32_t ql[4][32];      // low int8 halves, same order
-  uint32_t qf4[4][32][4];  // FP4 keys: per head and 4-channel step, fp16 query high then low parts
-  float qs[4];             // per-head dequantization of the 16-bit query
-  float qsum[4][8];        // per head, per group (of 16, 32 or 128 channels): sum of 16-bit query codes
-  uint16_t vmeta[NWS][8][16][4];  // per wave: V metadata by (element, slice, r)
-  float pb[NWS][TILE][4];    // per wave: probabilities by token (certified recompute)
-  float mrg_m[NWS][4], mrg_l[NWS][4], mrg_e[NWS][4];
-  float mrg_ek[NWS], mrg_vn[NWS];
-  float mrg_o[NWS][4][D];    // per wave, head, channel
-  float mrg_oo[NWS][4][D];
-  int next;                  // next chunk (offset from the split's first) to claim
-  int last;                  // this workgroup is the last of its stream to finish
+  float ctab[128];                   // cos(2 pi k / 128) for the SRFT rotation
+  float qo[4][D];                    // original query * scale * log2e, per head (exact recompute)
+  uint32_t qh[4][32];                // high int8 halves: dword 4n + c = MFMA operand of chain c, step n
+  uint32_t ql[4][32];                // low int8 halves, same order
+  uint32_t qf4[4][32][4];            // FP4 keys: per head and 4-channel step, fp16 query high then low parts
+  float qs[4];                       // per head: dequantization of the 16-bit query
+  float qsum[4][8];                  // per head and key group: sum of the 16-bit query codes
+  uint16_t vmeta[NWS][8][16][4];     // per wave: V metadata by (element, slice, r)
+  float zt[NWS][4][4];               // INT2 values: per wave, head, group: sum of p * offset
+  union {
+    struct {
+      float pb[NWS][TILE][4];                 // per wave: probabilities by token (exact recompute)
+      uint4 pw[NWS][MAX_VG][16][4];           // per wave: PV weights by (V group, step, head): 4 hi + 4 lo fp16
+    } loop;
+    struct {
+      float qf[NWS][D];                       // per wave: prologue scratch (dense rotation)
+      float qr[NWS][D];
+    } pro;
+    MergeArea<NWS> mrg;
+    float zsw[NWS][D];                        // per wave: merge scratch (dense inverse rotation)
+  } u;
+  int next;                          // next chunk (offset from the split's first) to claim
+  int last;                          // this workgroup is the last of its unit's to finish
+};
+
+// The fp16/bf16 baseline's shared memory, padded so that at most two of its workgroups
+// share a CU (160 KiB of LDS): with more of them resident at once the streams of V rows
+// compete for the CU's memory pipeline and the kernel runs at half the speed.
+struct __align__(16) DenseSmem {
+  float qo[4][D];
+  float pb[4][TILE][4];
+  MergeArea<4> mrg;
+  uint8_t pad[56 * 1024];
 };
 
 // ------------------------------------------------------------------ prologue
-// Rotate the 4 query heads of this workgroup (wave j holds head j, lane l its
-// channels 2l and 2l+1), prescale, quantize to 16 bits, and publish the int8
-// halves in MFMA operand order.  The Walsh-Hadamard butterflies run in the
-// order h = 1, 2, ..., 64 with the in-lane pair first and lane exchanges after.
-// The loads of the query and sign bits, issued before the first chunk's loads
-// (unconditionally, from valid addresses, so the count in flight is static).
-struct QueryIn {
-  uint16_t q0, q1;  // channels 2l, 2l+1 of head j (the wave index)
-  uint16_t sg;      // sign bytes of those channels
-};
-__device__ __forceinline__ QueryIn query_loads(const DecodeArgs& a, int b, int hq0, int nh) {
-  const int t = threadIdx.x, j = t >> 6, l = t & 63;
-  const uint16_t* qp = a.q + ((size_t)b * a.Hq + hq0 + (j < nh ? j : 0)) * D;
-  const int8_t* sp = (a.rotation == KVQ_ROT_SIGN_FWHT || a.rotation == KVQ_ROT_SRFT) ? a.signs
-                                                                                   : reinterpret_cast<const int8_t*>(a.q);
-  QueryIn r;
-  r.q0 = qp[2 * l];
-  r.q1 = qp[2 * l + 1];
-  r.sg = *reinterpret_cast<const uint16_t*>(sp + 2 * l);
-  return r;
-}
-
 // 64-point complex FFT across the lanes of a wave (lane l holds point l), radix 2,
 // decimation in frequency: stage h pairs lanes l and l ^ h, the lower takes a + b, the
 // upper (a - b) W64^((l mod h) 32 / h).  The result is in bit-reversed order: lane p
@@ -352,27 +357,45 @@ __device__ __forceinline__ void wave_fft64(float& re, float& im, int l, const fl
 }
 __device__ __forceinline__ int rev6(int l) { return (int)(__builtin_bitreverse32((uint32_t)l) >> 26); }
 
+// Rotate one query head (the whole wave: lane l holds channels 2l and 2l+1), prescale by
+// softmax_scale * log2(e), and publish it as head h: the original (scaled) query
+// for exact recompute, and the key operands: a 16-bit quantization split into int8 halves
+// in MFMA operand order plus per-group code sums (integer keys), or two fp16 parts (FP4
+// keys).  Wave-local: the caller holds the workgroup barrier that publishes the results.
+// The Walsh-Hadamard butterflies run in the order h = 1, 2, ..., 64 with the in-lane pair
+// first and lane exchanges after.
+// The loads of one head's query and sign bits, issued before the first chunk's loads.
+struct QueryIn {
+  uint32_t q01;  // channels 2l, 2l+1 (bits)
+  uint16_t sg;   // sign bytes of those channels
+};
+__device__ __forceinline__ QueryIn query_loads(const DecodeArgs& a, int b, int hq) {
+  const int l = threadIdx.x & 63;
+  QueryIn r;
+  r.q01 = *reinterpret_cast<const uint32_t*>(a.q + ((size_t)b * a.Hq + hq) * D + 2 * l);
+  r.sg = a.signs != nullptr ? *reinterpret_cast<const uint16_t*>(a.signs + 2 * l) : (uint16_t)0;
+  return r;
+}
+
 template <int KF>
-__device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryIn& qin, int nh, int kgroup, int hkv) {
-  // waves 0..3 own query heads 0..3; further waves only join the barriers
-  const int t = threadIdx.x, l = t & 63;
-  const bool own = (t >> 6) < 4;
-  const int j = (t >> 6) & 3;
+__device__ void query_head(const DecodeArgs& a, DecodeSmem& sm, const QueryIn& qin, int wv, int h, bool live,
+                           int kgroup, int hkv) {
+  const int l = threadIdx.x & 63;
   const bool bf16 = a.in_bf16 != 0;
   float x0 = 0.0f, x1 = 0.0f;
-  if (own && j < nh) {
-    x0 = widen(qin.q0, bf16);
-    x1 = widen(qin.q1, bf16);
+  if (live) {
+    x0 = widen((uint16_t)(qin.q01 & 0xFFFF), bf16);
+    x1 = widen((uint16_t)(qin.q01 >> 16), bf16);
   }
   const float pre = a.scale * LOG2E;
-  if (own) {
-    sm.qo[j][2 * l] = x0 * pre;
-    sm.qo[j][2 * l + 1] = x1 * pre;
-  }
+  sm.qo[h][2 * l] = x0 * pre;
+  sm.qo[h][2 * l + 1] = x1 * pre;
   float y0 = x0, y1 = x1;
-  if (a.rotation == KVQ_ROT_SIGN_FWHT) {
+  if (a.rotation == KVQ_ROT_SIGN_FWHT || a.rotation == KVQ_ROT_SRFT) {
     x0 = (qin.sg & 0x80u) ? -x0 : x0;
     x1 = (qin.sg & 0x8000u) ? -x1 : x1;
+  }
+  if (a.rotation == KVQ_ROT_SIGN_FWHT) {
     y0 = x0 + x1;
     y1 = x0 - x1;
     wht_lanes(y0, y1, l);
@@ -380,42 +403,40 @@ __device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryI
     // y = R q with R the packed unitary DFT times diag(s): the 64-point FFT of
     // z_n = u_2n + i u_2n+1 (u = s * q) across the wave, then X_l = E + W128^l O from
     // Z_l and conj Z_(64-l); lane l keeps channels 2l, 2l + 1 (lane 0: X_0 and X_64)
-    if (t < 128) sm.ctab[t] = a.cos128[t];
-    __syncthreads();
-    if (own) {  // whole waves
-      float re = (qin.sg & 0x80u) ? -x0 : x0, im = (qin.sg & 0x8000u) ? -x1 : x1;
-      wave_fft64(re, im, l, sm.ctab, false);
-      const int ka = rev6(l), kb = rev6((64 - l) & 63);
-      const float a_re = __shfl(re, ka), a_im = __shfl(im, ka);  // Z_l
-      const float b_re = __shfl(re, kb), b_im = -__shfl(im, kb);  // conj Z_(64-l)
-      const float e_re = 0.5f * (a_re + b_re), e_im = 0.5f * (a_im + b_im);
-      const float o_re = 0.5f * (a_im - b_im), o_im = -0.5f * (a_re - b_re);
-      const float c = sm.ctab[l], sn = sm.ctab[(l + 96) & 127];  // W128^l = (c, -sn)
-      y0 = (e_re + (o_re * c + o_im * sn)) * 0.125f;
-      y1 = (e_im + (o_im * c - o_re * sn)) * 0.125f;
-      if (l == 0) {
-        const float c0 = bits_to_f32(KVQ_INV_SQRT_D_BITS);
-        y0 = (a_re + a_im) * c0;  // X_0
-        y1 = (a_re - a_im) * c0;  // X_64
-      }
+    float re = x0, im = x1;
+    wave_fft64(re, im, l, sm.ctab, false);
+    const int ka = rev6(l), kb = rev6((64 - l) & 63);
+    const float a_re = __shfl(re, ka), a_im = __shfl(im, ka);   // Z_l
+    const float b_re = __shfl(re, kb), b_im = -__shfl(im, kb);  // conj Z_(64-l)
+    const float e_re = 0.5f * (a_re + b_re), e_im = 0.5f * (a_im + b_im);
+    const float o_re = 0.5f * (a_im - b_im), o_im = -0.5f * (a_re - b_re);
+    const float c = sm.ctab[l], sn = sm.ctab[(l + 96) & 127];  // W128^l = (c, -sn)
+    y0 = (e_re + (o_re * c + o_im * sn)) * 0.125f;
+    y1 = (e_im + (o_im * c - o_re * sn)) * 0.125f;
+    if (l == 0) {
+      const float c0 = bits_to_f32(KVQ_INV_SQRT_D_BITS);
+      y0 = (a_re + a_im) * c0;  // X_0
+      y1 = (a_re - a_im) * c0;  // X_64
     }
   } else if (a.rotation == KVQ_ROT_DENSE) {
-    if (own) {
-      sm.qf[j][2 * l] = x0;
-      sm.qf[j][2 * l + 1] = x1;
+    float* qf = sm.u.pro.qf[wv];
+    float* qr = sm.u.pro.qr[wv];
+    qf[2 * l] = x0;
+    qf[2 * l + 1] = x1;
+    __builtin_amdgcn_wave_barrier();
+    lds_wait();
+    for (int rr = 0; rr < 2; ++rr) {
+      const int row = l + 64 * rr;
+      const uint16_t* rp = a.rot + (size_t)row * D;
+      float acc = 0.0f;
+      for (int k = 0; k < D; ++k) acc = fmaf(f16_bits_to_f32(rp[k]), qf[k], acc);
+      qr[row] = acc;
     }
-    __syncthreads();
-    if (own)
-      for (int rr = 0; rr < 2; ++rr) {
-        const int row = l + 64 * rr;
-        const uint16_t* rp = a.rot + (size_t)row * D;
-        float acc = 0.0f;
-        for (int k = 0; k < D; ++k) acc = fmaf(f16_bits_to_f32(rp[k]), sm.qf[j][k], acc);
-        sm.qr[j][row] = acc;
-      }
-    __syncthreads();
-    y0 = sm.qr[j][2 * l];
-    y1 = sm.qr[j][2 * l + 1];
+    __builtin_amdgcn_wave_barrier();
+    lds_wait();
+    y0 = qr[2 * l];
+    y1 = qr[2 * l + 1];
+    __builtin_amdgcn_wave_barrier();  // the scratch is reused by the next head
   }
   if (a.lam_k != nullptr) {  // keys were stored times lambda_k: q . y = (q / lambda) . (lambda y)
     y0 = y0 / a.lam_k[(size_t)hkv * D + 2 * l];
@@ -424,7 +445,7 @@ __device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryI
   const float norm = a.rotation == KVQ_ROT_SIGN_FWHT ? bits_to_f32(KVQ_INV_SQRT_D_BITS) : 1.0f;
   y0 = y0 * norm * pre;
   y1 = y1 * norm * pre;
-  float mx = wave_max(fmaxf(fabsf(y0), fabsf(y1)));
+  const float mx = wave_max(fmaxf(fabsf(y0), fabsf(y1)));
   if constexpr (KF == KVQ_FP4) {
     // FP4 keys: the query as two fp16 parts (high + residual) after an exact
     // power-of-two scaling to |y| < 2^14; products with E2M1 codes are exact
@@ -432,28 +453,25 @@ __device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryI
     frexpf(mx, &ex);  // mx = f 2^ex, f in [0.5, 1)
     const float qs = mx > 0.0f ? ldexpf(1.0f, ex - 14) : 1.0f;
     const float inv = mx > 0.0f ? ldexpf(1.0f, 14 - ex) : 1.0f;
-    uint16_t* qp = reinterpret_cast<uint16_t*>(&sm.qf4[j][0][0]);
+    uint16_t* qq = reinterpret_cast<uint16_t*>(&sm.qf4[h][0][0]);
     const float ys[2] = {y0 * inv, y1 * inv};
-    if (own)
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int c = 2 * l + e, n = c >> 2, mm = c & 3;
-        const _Float16 hh = (_Float16)ys[e];
-        const _Float16 ll = (_Float16)(ys[e] - (float)hh);
-        qp[n * 8 + mm] = __builtin_bit_cast(uint16_t, hh);
-        qp[n * 8 + 4 + mm] = __builtin_bit_cast(uint16_t, ll);
-      }
-    if (own && l == 0) sm.qs[j] = qs;
-    __syncthreads();
+    for (int e = 0; e < 2; ++e) {
+      const int c = 2 * l + e, n = c >> 2, mm = c & 3;
+      const _Float16 hh = (_Float16)ys[e];
+      const _Float16 ll = (_Float16)(ys[e] - (float)hh);
+      qq[n * 8 + mm] = __builtin_bit_cast(uint16_t, hh);
+      qq[n * 8 + 4 + mm] = __builtin_bit_cast(uint16_t, ll);
+    }
+    if (l == 0) sm.qs[h] = qs;
     return;
   }
   const float qs = mx > 0.0f ? mx / 32000.0f : 1.0f;
   const int q0 = (int)rintf(y0 / qs), q1 = (int)rintf(y1 / qs);
   // scatter int8 halves into MFMA operand order
-  uint8_t* hb = reinterpret_cast<uint8_t*>(&sm.qh[j][0]);
-  uint8_t* lb = reinterpret_cast<uint8_t*>(&sm.ql[j][0]);
+  uint8_t* hb = reinterpret_cast<uint8_t*>(&sm.qh[h][0]);
+  uint8_t* lb = reinterpret_cast<uint8_t*>(&sm.ql[h][0]);
   const int qv[2] = {q0, q1};
-  if (own)
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int c = 2 * l + e;
@@ -472,16 +490,13 @@ __device__ void query_prologue(const DecodeArgs& a, DecodeSmem& sm, const QueryI
   gs += lane_xor<2>(gs);
   gs += lane_xor<4>(gs);
   if (kgroup == 16) {
-    if (own && (l & 7) == 0) sm.qsum[j][l >> 3] = gs;
+    if ((l & 7) == 0) sm.qsum[h][l >> 3] = gs;
   } else {
     gs += lane_xor<8>(gs);
-    if (kgroup == 128) {
-      gs = sum_with<32>(sum_with<16>(gs));
-    }
-    if (own && (l & 15) == 0) sm.qsum[j][l >> 4] = gs;
+    if (kgroup == 128) gs = sum_with<32>(sum_with<16>(gs));
+    if ((l & 15) == 0) sm.qsum[h][l >> 4] = gs;
   }
-  if (own && l == 0) sm.qs[j] = qs;
-  __syncthreads();
+  if (l == 0) sm.qs[h] = qs;
 }
 
 // ------------------------------------------------------------------ coherent record access
@@ -500,28 +515,31 @@ __device__ __forceinline__ float rec_ld(const float* p) {
 }
 
 // ------------------------------------------------------------------ split record
-// Merges the NW waves of this workgroup (in LDS, log-sum-exp weights) and writes
-// the record of (sequence, query head, split) for the combine kernel.
+// Merges waves [w0, w0 + nw) of this workgroup (log-sum-exp weights) and writes head hh's
+// record of (sequence b, query head hq0 + hh, split) for the merge; qo: the unit's
+// scaled original query (certificate: ||q|| * scale).  Called by 64 threads per head
+// (l = lane); heads at or beyond nh are skipped.
 template <bool CERT, int NW, bool COH>
-__device__ void write_record(const DecodeArgs& a, DecodeSmem& sm, int b, int hq0, int nh, int split) {
-  const int t = threadIdx.x, hh = t >> 6, l = t & 63, c = 2 * l;
+__device__ void write_record(const DecodeArgs& a, const MergeArea<NW>& mg, const float (*qo)[D], int w0, int nw,
+                             int b, int hq0, int nh, int split, int hh, int l) {
+  const int c = 2 * l;
   if (hh >= nh) return;
   float M = NEG_INF;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.mrg_m[w][hh]);
-  float wgt[NW];
-#pragma unroll
-  for (int w = 0; w < NW; ++w) wgt[w] = (M == NEG_INF) ? 0.0f : exp2f(sm.mrg_m[w][hh] - M);
+  for (int w = w0; w < w0 + nw; ++w) M = fmaxf(M, mg.m[w][hh]);
   float* rec = a.part + (((size_t)b * a.Hq + hq0 + hh) * a.n_splits + split) * PART_FLOATS;
-  float o0 = 0.0f, o1 = 0.0f, p0 = 0.0f, p1 = 0.0f;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    o0 += wgt[w] * sm.mrg_o[w][hh][c];
-    o1 += wgt[w] * sm.mrg_o[w][hh][c + 1];
+  float o0 = 0.0f, o1 = 0.0f, p0 = 0.0f, p1 = 0.0f, L = 0.0f, E = 0.0f, ek = 0.0f, vn = 0.0f;
+  for (int w = w0; w < w0 + nw; ++w) {
+    const float wgt = (M == NEG_INF) ? 0.0f : exp2f(mg.m[w][hh] - M);
+    o0 += wgt * mg.o[w][hh][c];
+    o1 += wgt * mg.o[w][hh][c + 1];
     if constexpr (CERT) {
-      p0 += wgt[w] * sm.mrg_oo[w][hh][c];
-      p1 += wgt[w] * sm.mrg_oo[w][hh][c + 1];
+      p0 += wgt * mg.oo[w][hh][c];
+      p1 += wgt * mg.oo[w][hh][c + 1];
     }
+    L += wgt * mg.l[w][hh];
+    E += wgt * mg.e[w][hh];
+    ek = fmaxf(ek, mg.ek[w]);
+    vn = fmaxf(vn, mg.vn[w]);
   }
   rec_st<COH>(rec + 8 + c, o0);
   rec_st<COH>(rec + 8 + c + 1, o1);
@@ -532,20 +550,12 @@ __device__ void write_record(const DecodeArgs& a, DecodeSmem& sm, int b, int hq0
   float qn = 0.0f;
   if constexpr (CERT) {
     // ||q|| * scale from the prologue's q * scale * log2(e)
-    const float q0 = sm.qo[hh][c], q1 = sm.qo[hh][c + 1];
+    const float q0 = qo[hh][c], q1 = qo[hh][c + 1];
     float sq = q0 * q0 + q1 * q1;
     sq = wave_sum(sq);
     qn = sqrtf(sq) / LOG2E;
   }
   if (l == 0) {
-    float L = 0.0f, E = 0.0f, ek = 0.0f, vn = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      L += wgt[w] * sm.mrg_l[w][hh];
-      E += wgt[w] * sm.mrg_e[w][hh];
-      ek = fmaxf(ek, sm.mrg_ek[w]);
-      vn = fmaxf(vn, sm.mrg_vn[w]);
-    }
     const float hdr[6] = {M, L, E, ek, vn, qn};
 #pragma unroll
     for (int i = 0; i < 6; ++i) rec_st<COH>(rec + i, hdr[i]);
@@ -817,47 +827,64 @@ __device__ __forceinline__ float max_same_head_fast(float v) {
   return fmaxf(v, __shfl_xor(v, 32));
 }
 
+// V scale groups per token whose PV weights are formed on the QK side
+__host__ __device__ constexpr int v_groups(int vf, int vg) {
+  return (vf == KVQ_FP4 || vg == 16) ? 8 : (vf == KVQ_INT2 || vg == 32) ? 4 : 1;
+}
+
 // MODE 0: codes only.  MODE 1: blocks of the full-precision window recomputed
 // exactly from their originals.  MODE 2: certified cache: window blocks and blocks
 // flagged by the error bound recomputed exactly, per-block descriptors for the
 // certificate.
+//
+// Work layout.  A unit is (sequence, kv head, group of 4 query heads).  Workgroup g of
+// the 1-D grid takes split g % S of unit g / S: a range of its 64-token chunks.  Its 8
+// waves share the range out through a counter in LDS: wave w starts with the range's
+// chunk w, and every further chunk is claimed one visit ahead.  The two waves that
+// share a SIMD do not progress equally (the older one wins issue slots), so the faster
+// one simply claims more chunks.
 template <int KF, int KG, int VF, int VG, int MODE>
 __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   constexpr bool EXACT = MODE != 0;  // exact recompute of some chunks
   constexpr bool CERT = MODE == 2;   // flags and descriptors
   __shared__ DecodeSmem sm;
-  const int b = blockIdx.z;
+  {
+    // every kernel argument the start-up needs, loaded in one batch (the empty asm makes
+    // them all available at one point, so none is loaded later behind a branch)
+    const uint16_t* p0 = a.q;
+    const int8_t* p1 = a.signs;
+    const uint8_t* p2 = a.k_codes;
+    const uint8_t* p3 = a.k_meta;
+    const uint8_t* p4 = a.v_codes;
+    const uint8_t* p5 = a.v_meta;
+    int i0 = a.G, i1 = a.Hq, i2 = a.H, i3 = a.Tmax, i4 = a.nt, i5 = a.chunks_per_split, i6 = a.rotation,
+        i7 = a.seq.v[blockIdx.x / a.n_splits / ((a.G + 3) / 4) / a.H], i8 = a.n_splits;
+    asm volatile("" ::"s"(p0), "s"(p1), "s"(p2), "s"(p3), "s"(p4), "s"(p5));
+    asm volatile("" ::"s"(i0), "s"(i1), "s"(i2), "s"(i3), "s"(i4), "s"(i5), "s"(i6), "s"(i7), "s"(i8));
+  }
+  const int t = threadIdx.x, lane = t & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: the chunk walk is scalar
+  const int S = a.n_splits;
+  const int u = blockIdx.x / S, split = blockIdx.x % S;
   const int HG = (a.G + 3) >> 2;
-  const int hkv = blockIdx.y / HG, hg = blockIdx.y % HG;
+  const int b = u / (a.H * HG), hkv = (u / HG) % a.H, hg = u % HG;
   const int hq0 = hkv * a.G + hg * 4;
   const int nh = min(4, a.G - hg * 4);
-  const int split = blockIdx.x;
   const int T = a.seq.v[b];
   const int nchunks = (T + TILE - 1) / TILE;
   const int c0 = split * a.chunks_per_split;
   const int c1 = min(nchunks, c0 + a.chunks_per_split);
-  const int t = threadIdx.x, lane = t & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: the chunk walk is scalar
-  const int j = lane & 3;     // head of this lane (QK output / softmax role)
+  const int j = lane & 3;     // head of this lane (QK output / softmax role, PV operand row)
   const int s_a = lane >> 2;  // QK slice of this lane (A role)
   const int r_a = lane & 3;
   const int tok_a = tok_of<VF>(s_a, r_a);
   const size_t stream = (size_t)b * a.H + hkv;
   constexpr int CDW = VFmt<VF>::CDW;
-  // V scale element of channels 2*lane, 2*lane+1: 32-channel group, one per token, or 16-channel block
+  constexpr int NGV = v_groups(VF, VG);
+  // V scale group of channels 2*lane, 2*lane+1: 32-channel group, one per token, or 16-channel block
   const int vgrp = (VF == KVQ_FP4 || VG == 16) ? (lane >> 3) : (VG == 128) ? 0 : (lane >> 4);
   uint16_t* vml = &sm.vmeta[wv][0][0][0];
 
-  // The first chunk's loads are in flight during the query prologue.  Every
-  // prefetch is unconditional (a wave past its last chunk reloads a chunk index
-  // that is always inside the cache), so the number of loads in flight is the
-  // same on every path.
-  const QueryIn qin = query_loads(a, b, hq0, nh);
-  __builtin_amdgcn_sched_barrier(0);
-  // Chunk schedule inside the workgroup: wave w starts with chunk c0 + w; every
-  // further chunk is claimed from a counter in LDS, one claim ahead of the chunk
-  // being loaded.  The two waves sharing a SIMD do not progress equally (the
-  // older one wins issue slots), so the faster one simply claims more chunks.
   if (t == 0) sm.next = NWS;  // published by the prologue's barrier
   auto claim = [&]() -> int {
     int v = 0;
@@ -883,13 +910,24 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
       X.vn = dp[2];
     }
   };
+  // The first chunk's loads are in flight during the query prologue.  Every prefetch is
+  // unconditional (a wave past its last chunk reloads a chunk index that is always
+  // inside the cache), so the number of loads in flight is the same on every path.
+  const int hw = wv < nh ? wv : 0;  // waves 0..3 rotate query heads 0..3 (others load a valid head)
+  const QueryIn qin = query_loads(a, b, hq0 + hw);
+  __builtin_amdgcn_sched_barrier(0);
   ChunkRegs<KF, VF, vmeta_words(VF, VG)> RA, RB;
   ChunkAux<CERT> XA, XB;
   int cA = c0 + wv;
   load_chunk<KF, KG, VF, VG>(a, stream, cA < c1 ? cA : 0, lane, tok_a, RA);
   load_aux(cA < c1 ? cA : 0, XA);
   __builtin_amdgcn_sched_barrier(0);
-  query_prologue<KF>(a, sm, qin, nh, KG, hkv);
+  if (a.rotation == KVQ_ROT_SRFT) {
+    if (t < 128) sm.ctab[t] = a.cos128[t];
+    __syncthreads();
+  }
+  if (wv < 4) query_head<KF>(a, sm, qin, wv, wv, wv < nh, KG, hkv);
+  __syncthreads();
   int pB = claim();
 
   const float qs = sm.qs[j];
@@ -898,13 +936,13 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   for (int g = 0; g < 4; ++g) qsum[g] = sm.qsum[j][g];
 
   float m = NEG_INF, lsum = 0.0f, eta = 0.0f, ekmax = 0.0f, vnmax = 0.0f;
-  f4 o[2], oo[2], oz;
+  float zacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // INT2 values: sum of p * offset per group (this lane's tokens)
+  f4 o[2], oo[2];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
     o[hf] = f4{0, 0, 0, 0};
     oo[hf] = f4{0, 0, 0, 0};
   }
-  oz = f4{0, 0, 0, 0};
 
   // ---------------------------------------------------------------- one quantized chunk
   auto quant_chunk = [&](const ChunkRegs<KF, VF, vmeta_words(VF, VG)>& R, int ch, float ev_c) {
@@ -957,9 +995,9 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
              : r == 2 ? quad_bcast_u<2>(R.kmeta[w]) : quad_bcast_u<3>(R.kmeta[w]);
       };
       static_assert(NC == 4, "query operand layout: 4 chains per 16-byte LDS read");
-  #pragma unroll
+#pragma unroll
       for (int ph = 0; ph < NPH; ++ph) {
-  #pragma unroll
+#pragma unroll
         for (int c = 0; c < NC; ++c) {
           // the offset-binary correction -8 * sum(q16) of the chain's group rides in the low half
           int corr = 0;
@@ -969,35 +1007,35 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
           ah[c] = i4{0, 0, 0, 0};
           al[c] = i4{corr, corr, corr, corr};
         }
-  #pragma unroll
+#pragma unroll
         for (int n = ph * PPH; n < (ph + 1) * PPH; ++n) {
-          // the query operands stay in LDS (registers go to deeper chunk prefetch)
+          // the query operands stay in LDS (registers go to the chunk prefetch)
           const uint4 qhv = *reinterpret_cast<const uint4*>(&sm.qh[j][4 * n]);
           const uint4 qlv = *reinterpret_cast<const uint4*>(&sm.ql[j][4 * n]);
           const int qhc[4] = {(int)qhv.x, (int)qhv.y, (int)qhv.z, (int)qhv.w};
           const int qlc[4] = {(int)qlv.x, (int)qlv.y, (int)qlv.z, (int)qlv.w};
-  #pragma unroll
+#pragma unroll
           for (int c = 0; c < NC; ++c) {
             const int av = KFmt<KF>::a_op(R.krow, c * PER + n);
             ah[c] = __builtin_amdgcn_mfma_i32_4x4x4i8(av, qhc[c], ah[c], 0, 0, 0);
             al[c] = __builtin_amdgcn_mfma_i32_4x4x4i8(av, qlc[c], al[c], 0, 0, 0);
           }
         }
-  #pragma unroll
+#pragma unroll
         for (int r = 0; r < 4; ++r) {
           if constexpr (KG == 16) {
             // group 2c + ph: its fp16 scale is half ph of metadata dword c
-  #pragma unroll
+#pragma unroll
             for (int c = 0; c < NC; ++c) {
               const uint16_t sb = (uint16_t)(kscale_word(r, c) >> (16 * ph));
               l[r] += (float)(ah[c][r] * 256 + al[c][r]) * f16_bits_to_f32(sb);
             }
           } else if constexpr (NG == 1) {
             acc[0][r] = 0;
-  #pragma unroll
+#pragma unroll
             for (int c = 0; c < NC; ++c) acc[0][r] += ah[c][r] * 256 + al[c][r];
           } else {
-  #pragma unroll
+#pragma unroll
             for (int c = 0; c < NC; ++c) acc[c][r] = ah[c][r] * 256 + al[c][r];
           }
         }
@@ -1006,15 +1044,15 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
         if constexpr (NPH > 1) __builtin_amdgcn_sched_barrier(0);
       }
       // ---- group scales of tokens pi(s, r), held by lanes 4s + r (A role): quad broadcast
-  #pragma unroll
+#pragma unroll
       for (int r = 0; r < 4 && KG != 16; ++r) {
         uint32_t sw[2], zw[2] = {0u, 0u};
-  #pragma unroll
+#pragma unroll
         for (int w = 0; w < (NG == 1 ? 1 : 2); ++w) {
           sw[w] = kscale_word(r, w);
           if constexpr (KF == KVQ_INT2) zw[w] = kscale_word(r, 2 + w);
         }
-  #pragma unroll
+#pragma unroll
         for (int g = 0; g < NG; ++g) {
           const uint16_t sb = (uint16_t)(sw[g >> 1] >> (16 * (g & 1)));
           float v = (float)acc[g][r] * f16_bits_to_f32(sb);
@@ -1026,6 +1064,7 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
         }
       }
     }
+    const bool tail = tok0 + TILE > T;  // the chunk holds positions at or past the sequence end
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       l[r] *= qs;
@@ -1051,12 +1090,55 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
       o[hf] *= av;
       if constexpr (EXACT) oo[hf] *= av;
     }
-    if constexpr (VF == KVQ_INT2) oz *= av;
-    // ---- PV
-    lds_wait();
-    const uint32_t P0 = as_u(h2{(_Float16)p[0], (_Float16)p[1]});
-    const uint32_t P1 = as_u(h2{(_Float16)p[2], (_Float16)p[3]});
-    const uint2* sc2 = reinterpret_cast<const uint2*>(vml) + vgrp * 16;
+    // ---- PV weights, formed here once per (token, V group): p * s in fp32 for this lane's
+    // four tokens (slice s_a, head j), split into an fp16 high part and the fp16 rounding
+    // of the remainder, so that the fp16 matrix products carry each weight to about
+    // 2^-22 of itself.  Positions past the sequence end have p = 0 and weight 0 (their
+    // metadata may be anything).
+    // (scales are never negative, so max(p s, 0) changes no weight and turns the 0 * NaN of
+    // a position past the end into 0)
+    const uint2* vmw = reinterpret_cast<const uint2*>(vml) + s_a;
+    uint2 sc[NGV];
+#pragma unroll
+    for (int g = 0; g < NGV; ++g) sc[g] = vmw[g * 16];
+#pragma unroll
+    for (int g = 0; g < NGV; ++g) {
+      const h2 s01 = as_h2(sc[g].x), s23 = as_h2(sc[g].y);
+      const float x0 = fmaxf(fmaf(p[0], (float)s01.x, 0.0f), 0.0f), x1 = fmaxf(fmaf(p[1], (float)s01.y, 0.0f), 0.0f);
+      const float x2 = fmaxf(fmaf(p[2], (float)s23.x, 0.0f), 0.0f), x3 = fmaxf(fmaf(p[3], (float)s23.y, 0.0f), 0.0f);
+      const h2 hi01 = {(_Float16)x0, (_Float16)x1}, hi23 = {(_Float16)x2, (_Float16)x3};
+      // the remainder x - hi is exact in fp32 (hi is x rounded to 11 bits)
+      const h2 lo01 = {(_Float16)fmaf((float)hi01.x, -1.0f, x0), (_Float16)fmaf((float)hi01.y, -1.0f, x1)};
+      const h2 lo23 = {(_Float16)fmaf((float)hi23.x, -1.0f, x2), (_Float16)fmaf((float)hi23.y, -1.0f, x3)};
+      sm.u.loop.pw[wv][g][s_a][j] = make_uint4(as_u(hi01), as_u(hi23), as_u(lo01), as_u(lo23));
+    }
+    if constexpr (VF == KVQ_INT2) {
+      // zero points: sum_t p_t z_(t, g) per group in fp32, added to every channel of the
+      // group at the end (z is constant over the group's channels; offsets may be negative,
+      // so positions past the end are masked by p)
+      uint2 zc[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) zc[g] = vmw[(4 + g) * 16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const h2 z01 = as_h2(zc[g].x), z23 = as_h2(zc[g].y);
+        float zs = p[0] * (float)z01.x + p[1] * (float)z01.y + p[2] * (float)z23.x + p[3] * (float)z23.y;
+        if (tail) zs = (p[0] > 0.0f ? p[0] * (float)z01.x : 0.0f) + (p[1] > 0.0f ? p[1] * (float)z01.y : 0.0f) +
+                       (p[2] > 0.0f ? p[2] * (float)z23.x : 0.0f) + (p[3] > 0.0f ? p[3] * (float)z23.y : 0.0f);
+        zacc[g] = zacc[g] * alpha + zs;
+      }
+    }
+    // ---- PV: step s takes the weights of tokens pi(s, 0..3) for this lane's head row and
+    // V group, high and low parts through two products each
+    const uint4* pwv = &sm.u.loop.pw[wv][vgrp][0][j];
+    auto pv_step = [&](int s, h4 B0, h4 B1) {
+      const uint4 w = pwv[4 * s];
+      const h4 Ah = cat(as_h2(w.x), as_h2(w.y)), Al = cat(as_h2(w.z), as_h2(w.w));
+      o[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(Ah, B0, o[0], 0, 0, 0);
+      o[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(Ah, B1, o[1], 0, 0, 0);
+      o[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(Al, B0, o[0], 0, 0, 0);
+      o[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(Al, B1, o[1], 0, 0, 0);
+    };
     if constexpr (VF == KVQ_FP4) {
       // tokens 4s..4s+3 of step s are the byte pairs 2(s&1), 2(s&1)+1 of word s/2
 #pragma unroll
@@ -1066,13 +1148,7 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
         const h2 c01 = (s & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 3) : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 1);
         const h2 c10 = (s & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 2) : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 0);
         const h2 c11 = (s & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 3) : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w1, 1.0f, 1);
-        const int src = (4 * s + j) << 2;
-        const uint32_t A0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)P0);
-        const uint32_t A1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)P1);
-        const uint2 sc = sc2[s];
-        const h4 A = cat(as_h2(A0) * as_h2(sc.x), as_h2(A1) * as_h2(sc.y));
-        o[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, cat(c00, c01), o[0], 0, 0, 0);
-        o[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, cat(c10, c11), o[1], 0, 0, 0);
+        pv_step(s, cat(c00, c01), cat(c10, c11));
       }
     } else if constexpr (VF == KVQ_INT4) {
 #pragma unroll
@@ -1081,48 +1157,17 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
         v_int4_pairs(R.vw[d], c0);
         v_int4_pairs(R.vw[CDW + d], c1);
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const int s = 2 * d + x;
-          const int src = (4 * s + j) << 2;
-          // the weight P s is formed in fp32 and rounded to fp16 once (an fp16 product would
-          // round a second time: over long diffuse contexts the worst output rows then come
-          // close to the 2e-3 bar; C2 full size: ≈2.0e-3 with it, ≈1.6e-3 without)
-          const uint32_t A0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)P0);
-          const uint32_t A1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)P1);
-          const h2 q01 = as_h2(A0), q23 = as_h2(A1);
-          const float pa[4] = {(float)q01.x, (float)q01.y, (float)q23.x, (float)q23.y};
-          const uint2 sc = sc2[s];
-          const h2 s01 = as_h2(sc.x), s23 = as_h2(sc.y);
-          const h4 A = {(_Float16)(pa[0] * (float)s01.x), (_Float16)(pa[1] * (float)s01.y),
-                        (_Float16)(pa[2] * (float)s23.x), (_Float16)(pa[3] * (float)s23.y)};
-          o[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, cat(c0[2 * x], c0[2 * x + 1]), o[0], 0, 0, 0);
-          o[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, cat(c1[2 * x], c1[2 * x + 1]), o[1], 0, 0, 0);
-        }
+        for (int x = 0; x < 2; ++x) pv_step(2 * d + x, cat(c0[2 * x], c0[2 * x + 1]), cat(c1[2 * x], c1[2 * x + 1]));
       }
-    } else {  // INT2 values: codes 0..3, value = c * s + z
-      const uint2* zc2 = reinterpret_cast<const uint2*>(vml) + (4 + vgrp) * 16;
+    } else {  // INT2 values: codes 0..3, value = c * s + z (z added at the end)
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         h2 c0[8], c1[8];
         v_int2_pairs(R.vw[w], c0);
         v_int2_pairs(R.vw[CDW + w], c1);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int s = 4 * w + kk;
-          const int src = (4 * s + j) << 2;
-          const uint32_t A0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)P0);
-          const uint32_t A1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)P1);
-          const uint2 sc = sc2[s];
-          const uint2 zc = zc2[s];
-          const h4 A = cat(as_h2(A0) * as_h2(sc.x), as_h2(A1) * as_h2(sc.y));
-          // zero points: P and z enter as separate operands, so each product p z is exact
-          // (a rounded fp16 p z would not cancel against the code term as it should)
-          const h4 Ap = cat(as_h2(A0), as_h2(A1));
-          const h4 Bz = cat(as_h2(zc.x), as_h2(zc.y));
-          o[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, cat(c0[2 * kk], c0[2 * kk + 1]), o[0], 0, 0, 0);
-          o[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(A, cat(c1[2 * kk], c1[2 * kk + 1]), o[1], 0, 0, 0);
-          oz = __builtin_amdgcn_mfma_f32_4x4x4f16(Ap, Bz, oz, 0, 0, 0);
-        }
+        for (int kk = 0; kk < 4; ++kk)
+          pv_step(4 * w + kk, cat(c0[2 * kk], c0[2 * kk + 1]), cat(c1[2 * kk], c1[2 * kk + 1]));
       }
     }
   };
@@ -1137,8 +1182,8 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   // first row of chunk ch's originals: its window slot, else the full copy
   auto orig_rows = [&](const uint16_t* full, const uint16_t* win, int ch) -> const uint16_t* {
     if (in_window(ch)) {
-      const int slot = ch < a.n_sink ? ch : a.n_sink + ch % a.n_recent;
-      return win + (stream * (size_t)(a.n_sink + a.n_recent) + slot) * TILE * D;
+      const int wslot = ch < a.n_sink ? ch : a.n_sink + ch % a.n_recent;
+      return win + (stream * (size_t)(a.n_sink + a.n_recent) + wslot) * TILE * D;
     }
     return full + (stream * a.Tmax + (size_t)ch * TILE) * D;
   };
@@ -1153,6 +1198,8 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
     // rather than one per row.
     const uint4* kp = reinterpret_cast<const uint4*>(orig_rows(a.k_orig, a.k_win, ch) + (size_t)tau * D);
     const uint32_t* vp = reinterpret_cast<const uint32_t*>(orig_rows(a.v_orig, a.v_win, ch)) + lane;
+    const float(*qo)[D] = sm.qo;
+    float(*pb)[4] = sm.u.loop.pb[wv];
     uint4 kr[8];
     uint32_t vr[2][16];
 #pragma unroll
@@ -1168,14 +1215,14 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
         for (int k = 0; k < 16; ++k) vr[0][k] = vp[(size_t)k * (D / 2)];
         __builtin_amdgcn_sched_barrier(0);
       }
-      const uint4 u = kr[i & 7];
-      const uint32_t ws[4] = {u.x, u.y, u.z, u.w};
+      const uint4 uq = kr[i & 7];
+      const uint32_t ws[4] = {uq.x, uq.y, uq.z, uq.w};
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int c = 8 * i + 2 * jj;
         const float k0 = widen((uint16_t)(ws[jj] & 0xFFFF), bf16), k1 = widen((uint16_t)(ws[jj] >> 16), bf16);
 #pragma unroll
-        for (int hh = 0; hh < 4; ++hh) lh[hh] = fmaf(sm.qo[hh][c + 1], k1, fmaf(sm.qo[hh][c], k0, lh[hh]));
+        for (int hh = 0; hh < 4; ++hh) lh[hh] = fmaf(qo[hh][c + 1], k1, fmaf(qo[hh][c], k0, lh[hh]));
       }
     }
     float cm[4];
@@ -1194,7 +1241,7 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
     for (int hh = 0; hh < 4; ++hh) {
       const float ph = (mh[hh] == NEG_INF || !live) ? 0.0f : fast_exp2(lh[hh] - mh[hh]);
       sums[hh] = wave_sum(ph);
-      sm.pb[wv][tau][hh] = ph;
+      pb[tau][hh] = ph;
     }
     const float mysum = (j == 0) ? sums[0] : (j == 1) ? sums[1] : (j == 2) ? sums[2] : sums[3];
     lsum = lsum * alpha + (lane < 4 ? mysum : 0.0f);
@@ -1205,7 +1252,10 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
       o[hf] *= av;
       oo[hf] *= av;
     }
-    if constexpr (VF == KVQ_INT2) oz *= av;
+    if constexpr (VF == KVQ_INT2) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) zacc[g] *= alpha;
+    }
     lds_wait();
     // value rows in batches of 16, the next batch in flight while one is accumulated
 #pragma unroll
@@ -1218,7 +1268,7 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
       for (int k = 0; k < 16; ++k) {
         const uint32_t vv = vr[bt & 1][k];
         const float v0 = widen((uint16_t)(vv & 0xFFFF), bf16), v1 = widen((uint16_t)(vv >> 16), bf16);
-        const float4 pp = *reinterpret_cast<const float4*>(&sm.pb[wv][16 * bt + k][0]);
+        const float4 pp = *reinterpret_cast<const float4*>(&pb[16 * bt + k][0]);
         oo[0] += f4{pp.x, pp.y, pp.z, pp.w} * v0;
         oo[1] += f4{pp.x, pp.y, pp.z, pp.w} * v1;
       }
@@ -1247,12 +1297,11 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
       quant_chunk(R, ch, ev_c);
     }
   };
-  // Every iteration issues the same claims and loads (a load past the stream's
-  // last chunk reloads the current, valid chunk), so the number of memory
-  // operations in flight at the loop head is the same on entry and on every
-  // iteration; the wave leaves as soon as a claimed index is past the end.
-  // (claims only grow, so once one is past the end the next is too: the loop
-  // leaves at its head, its single exit.)
+  // Every iteration issues the same claims and loads (a load past the range's last chunk
+  // reloads the current, valid chunk), so the number of memory operations in flight at
+  // the loop head is the same on entry and on every iteration; the wave leaves as soon
+  // as a claimed index is past the end.  (Claims only grow, so once one is past the end
+  // the next is too: the loop leaves at its head, its single exit.)
   while (cA < c1) {
     const int cB = c0 + __builtin_amdgcn_readfirstlane(pB);
     const int pC = claim();
@@ -1277,46 +1326,57 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   // ---------------- per-wave totals, then merge the waves in LDS
   const float lt = sum_same_head(lsum);
   const float et = CERT ? sum_same_head(eta) : 0.0f;
+  if constexpr (VF == KVQ_INT2) {
+    float ztl[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) ztl[g] = sum_same_head(zacc[g]);
+    if (lane < 4)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) sm.zt[wv][lane][g] = ztl[g];
+    __builtin_amdgcn_wave_barrier();
+    lds_wait();
+  }
+  __syncthreads();  // every wave has left its loop: the merge area aliases the loop buffers
+  MergeArea<NWS>& mg = sm.u.mrg;
   if (lane < 4) {
-    sm.mrg_m[wv][lane] = m;
-    sm.mrg_l[wv][lane] = lt;
-    sm.mrg_e[wv][lane] = et;
+    mg.m[wv][lane] = m;
+    mg.l[wv][lane] = lt;
+    mg.e[wv][lane] = et;
   }
   if (lane == 0) {
-    sm.mrg_ek[wv] = ekmax;
-    sm.mrg_vn[wv] = vnmax;
+    mg.ek[wv] = ekmax;
+    mg.vn[wv] = vnmax;
   }
 #pragma unroll
   for (int hh = 0; hh < 4; ++hh) {
     float zb = 0.0f;
-    if constexpr (VF == KVQ_INT2) zb = oz[hh];
-    sm.mrg_o[wv][hh][2 * lane] = o[0][hh] + zb;
-    sm.mrg_o[wv][hh][2 * lane + 1] = o[1][hh] + zb;
+    if constexpr (VF == KVQ_INT2) zb = sm.zt[wv][hh][vgrp];
+    mg.o[wv][hh][2 * lane] = o[0][hh] + zb;
+    mg.o[wv][hh][2 * lane + 1] = o[1][hh] + zb;
     if constexpr (EXACT) {
-      sm.mrg_oo[wv][hh][2 * lane] = oo[0][hh];
-      sm.mrg_oo[wv][hh][2 * lane + 1] = oo[1][hh];
+      mg.oo[wv][hh][2 * lane] = oo[0][hh];
+      mg.oo[wv][hh][2 * lane + 1] = oo[1][hh];
     }
   }
   __syncthreads();
-  write_record<EXACT, NWS, true>(a, sm, b, hq0, nh, split);
+  if (wv < 4) write_record<EXACT, NWS, true>(a, mg, sm.qo, 0, NWS, b, hq0, nh, split, wv, lane);
 
-  // ---------------- the last workgroup of the stream to finish merges its splits
+  // ---------------- the last workgroup of the unit to finish merges its splits
   // The records are agent-coherent atomic stores; every thread waits for its own
   // stores to complete before the barrier, so they are performed before the
   // arrival is counted.  The last arrival reads every split's record with
   // agent-coherent loads.  (No cache write-back or invalidate is needed: only
   // the records cross workgroups, and they never sit in a non-coherent cache.)
-  const int sidx = blockIdx.z * gridDim.y + blockIdx.y;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (t == 0) {
-    const int prev = __hip_atomic_fetch_add(a.ctr + sidx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm.last = prev == a.n_splits - 1;
+    const int prev = __hip_atomic_fetch_add(a.ctr + u, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.last = prev == S - 1;
   }
   __syncthreads();
   if (sm.last) {
-    if (wv < nh) combine_row<EXACT, true>(a, b * a.Hq + hq0 + wv, &sm.qf[wv][0], sm.ctab);
-    if (t == 0) __hip_atomic_store(a.ctr + sidx, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (wv < nh) combine_row<EXACT, true>(a, b * a.Hq + hq0 + wv, sm.u.zsw[wv], sm.ctab);
+    if (t == 0) __hip_atomic_store(a.ctr + u, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -1325,7 +1385,7 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
 // QK^T: 4x4x4 fp16 MFMA (lane 4s+r loads token 4s+r); PV: each lane owns channels
 // 2l, 2l+1 and accumulates p * v with the probabilities broadcast through LDS.
 __global__ __launch_bounds__(NT, 2) void decode_dense_split(DecodeArgs a) {
-  __shared__ DecodeSmem sm;
+  __shared__ DenseSmem sm;
   const int b = blockIdx.z;
   const int HG = (a.G + 3) >> 2;
   const int hkv = blockIdx.y / HG, hg = blockIdx.y % HG;
@@ -1418,21 +1478,21 @@ __global__ __launch_bounds__(NT, 2) void decode_dense_split(DecodeArgs a) {
   }
   const float lt = sum_same_head(lsum);
   if (lane < 4) {
-    sm.mrg_m[wv][lane] = m;
-    sm.mrg_l[wv][lane] = lt;
-    sm.mrg_e[wv][lane] = 0.0f;
+    sm.mrg.m[wv][lane] = m;
+    sm.mrg.l[wv][lane] = lt;
+    sm.mrg.e[wv][lane] = 0.0f;
   }
   if (lane == 0) {
-    sm.mrg_ek[wv] = 0.0f;
-    sm.mrg_vn[wv] = 0.0f;
+    sm.mrg.ek[wv] = 0.0f;
+    sm.mrg.vn[wv] = 0.0f;
   }
 #pragma unroll
   for (int hh = 0; hh < 4; ++hh) {
-    sm.mrg_o[wv][hh][2 * lane] = o[0][hh];
-    sm.mrg_o[wv][hh][2 * lane + 1] = o[1][hh];
+    sm.mrg.o[wv][hh][2 * lane] = o[0][hh];
+    sm.mrg.o[wv][hh][2 * lane + 1] = o[1][hh];
   }
   __syncthreads();
-  write_record<false, 4, false>(a, sm, b, hq0, nh, split);
+  write_record<false, 4, false>(a, sm.mrg, sm.qo, 0, 4, b, hq0, nh, split, wv, lane);
 }
 
 // ------------------------------------------------------------------ allocation-free workspace
@@ -1477,10 +1537,10 @@ hipError_t decode_scratch(void** ptr, hipStream_t s) {
 
 hipError_t launch_decode(const DecodeArgs& a, int k_fmt, int v_fmt, bool dense, hipStream_t s) {
   const int HG = (a.G + 3) / 4;
-  dim3 grid(a.n_splits, a.H * HG, a.B);
   const dim3 cgrid((a.B * a.Hq + 3) / 4);
   if (dense) {
-    hipLaunchKernelGGL(decode_dense_split, grid, dim3(NT), 0, s, a);
+    const dim3 dgrid(a.n_splits, a.H * HG, a.B);
+    hipLaunchKernelGGL(decode_dense_split, dgrid, dim3(NT), 0, s, a);
     hipLaunchKernelGGL(combine_kernel<false>, cgrid, dim3(NT), 0, s, a);
     return hipGetLastError();
   }
@@ -1490,6 +1550,8 @@ hipError_t launch_decode(const DecodeArgs& a, int k_fmt, int v_fmt, bool dense, 
   // those caches take the certified variant, whose flag and descriptor loads then
   // read a stand-in address and are ignored.)
   const int mode = a.desc != nullptr ? 2 : (a.k_win != nullptr ? (k_fmt == KVQ_INT8 ? 2 : 1) : 0);
+  // one workgroup per (unit, split), the splits of a unit consecutive
+  const dim3 grid(a.U * a.n_splits);
 #define KVQ_LAUNCH(KF, KG, VF, VG)                                                            \
   if (k_fmt == KF && a.k_group == KG && v_fmt == VF && a.v_group == VG) {                     \
     if (mode == 2) {                                                                          \

@@ -133,12 +133,13 @@ struct DecodeArgs {
   const int8_t* signs;
   const uint16_t* rot;
   float* part;              // [B][Hq][n_splits][PART_FLOATS]
-  int* ctr;                 // [B][Hkv * head groups] split arrival counters, zero between calls
+  int* ctr;                 // [U] split arrival counters per unit, zero between calls
   float* out;               // [B][Hq][128]
   float* cert;              // [B][Hq] or null
   int32_t B, Hq, H, G, Tmax, nt;
   int32_t in_bf16, rotation, k_group, v_group;
   int32_t n_splits, chunks_per_split;
+  int32_t U;  // units (sequence, kv head, group of 4 query heads)
   int32_t n_sink, n_recent;  // window blocks (0, 0 = none)
   float scale;  // softmax scale
   float cos128[128];  // fl32(cos(2 pi k / 128)): the SRFT matrix entries

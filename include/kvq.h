@@ -202,10 +202,10 @@ kvq_status kvq_buffer_bytes(const kvq_params* p, size_t* out_bytes);
 
 /* Workspace bytes kvq_decode_attn / kvq_decode_attn_dense need for these params
  * (depends on batch, heads and max_ctx only).  Host only; 0 on invalid params.
- * The workspace holds one arrival counter per (sequence, kv head, group of 4
- * query heads), through which the last split workgroup of a sequence learns that
- * it is last and merges the others' results, and one partial-result record per
- * (sequence, query head, context split).  It must be zero-filled before its
+ * The workspace holds one arrival counter per unit (sequence, kv head, group of 4
+ * query heads), through which the last of the unit's workgroups learns that it is
+ * last and merges the others' results, and one partial-result record per (sequence,
+ * query head, split).  It must be zero-filled before its
  * first use; every call leaves the counters zero again (the records' contents
  * do not matter), so one workspace serves call after call.  Calls that share a
  * workspace must not overlap (order them on one stream).  The split workgroups
@@ -214,8 +214,9 @@ kvq_status kvq_buffer_bytes(const kvq_params* p, size_t* out_bytes);
 size_t kvq_decode_workspace_bytes(const kvq_params* p);
 
 /* Number of context splits kvq_decode_attn uses for these params and sequence
- * lengths (the split kernel's grid is splits x (Hkv * ceil(Hq/Hkv / 4)) x B
- * workgroups).  Host only, informational; 0 on invalid input. */
+ * lengths: each unit (sequence, kv head, group of 4 query heads) is served by that many
+ * workgroups, each taking a range of its 64-token chunks.  Host only, informational; 0 on
+ * invalid input. */
 int32_t kvq_decode_splits(const kvq_params* p, const int32_t* seq_len_host);
 
 /*
