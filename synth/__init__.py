@@ -113,6 +113,12 @@ def _haar(r):
     return qm * np.sign(np.diag(rm))[None, :]
 
 
+def anisotropic_basis(c, tensor, h):
+    """The orthogonal basis U (fp64 [128, 128]) of the anisotropic law of (tensor, kv head):
+    vectors are U diag(i^-1/2) z with z ~ N(0, 1)."""
+    return _haar(_rng(c["cfg"], ST_U, tensor, h))
+
+
 def planted(c, b, h):
     """For the certified workload: [(block, token offset)] of planted outlier tokens."""
     nblk = c["T"] // 64
@@ -136,7 +142,7 @@ def _chunk_values(c, tensor, b, h, chunk):
         sig = c["k_sigma"] if tensor == 0 else c["v_sigma"]
         return r.standard_normal((CHUNK, D), dtype=np.float32) * np.float32(sig)
     if kind == "anisotropic":
-        u = _haar(_rng(c["cfg"], ST_U, tensor, h))
+        u = anisotropic_basis(c, tensor, h)
         z = r.standard_normal((CHUNK, D))
         lam = 1.0 / np.sqrt(np.arange(1, D + 1, dtype=np.float64))
         return (z * lam[None, :]) @ u.T
@@ -166,6 +172,13 @@ def kv_slice(c, tensor, b, h, t0, n):
     return to_bits(out, c["dtype"])
 
 
+def one_blas_thread():
+    """Pool-worker initialiser: one BLAS thread per worker process (many workers each
+    running a full-width BLAS thread pool oversubscribe the host many times over)."""
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+
+
 def kv_all(c, tensor, t0, n, workers=1, start_method="fork"):
     """[B, Hkv, n, 128] uint16 for tokens [t0, t0+n) of every stream.
 
@@ -178,7 +191,7 @@ def kv_all(c, tensor, t0, n, workers=1, start_method="fork"):
     if workers > 1 and len(jobs) > 1:
         import multiprocessing as mp
         ctx = mp.get_context(start_method)
-        with ctx.Pool(min(workers, len(jobs))) as pool:
+        with ctx.Pool(min(workers, len(jobs)), initializer=one_blas_thread) as pool:
             res = pool.starmap(kv_slice, [(c, tensor, b, h, t0, n) for b, h in jobs])
         for (b, h), r in zip(jobs, res):
             out[b, h] = r
@@ -199,7 +212,7 @@ def calibration(c, tensor, h):
     n = c.get("calib_tokens", 4096)
     st_r = _rng(c["cfg"], ST_CALIB, tensor, h)
     if c["data"] == "anisotropic":
-        u = _haar(_rng(c["cfg"], ST_U, tensor, h))
+        u = anisotropic_basis(c, tensor, h)
         z = st_r.standard_normal((n, D))
         lam = 1.0 / np.sqrt(np.arange(1, D + 1, dtype=np.float64))
         return to_bits((z * lam[None, :]) @ u.T, c["dtype"])
