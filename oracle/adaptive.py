@@ -27,17 +27,32 @@ Readings taken here (the page gives no formulas):
   is a deterministic function of those masses.
 * Promotion granularity: the decode pass recomputes a block exactly for all
   query heads that share its kv head, so the promoted set of a (sequence, kv
-  head) is the union over its query heads; promotion takes keys and values
-  together (this also covers the page's value promotion for those blocks).
-  Blocks the certified bound flags (error bound > tau) are promoted as well:
-  that is the value-error rung, with the bound as the contribution estimate.
-* The per-head fallback is triggered by the certificate: a query head whose
-  certificate after the promoted pass exceeds eps is recomputed with dense
-  attention over the originals, which returns the dense result exactly.  (The
-  page's trigger is a ranking-consistency check between quantized and
-  full-precision block scores, for which it prints no criterion; the
-  certificate bounds the same failure - quantization noise distorting the
-  attention distribution - with a proof.)
+  head) is the union over its query heads.  Promotion flags are a byte per
+  block: bit 0 = keys and values from the originals (top-K* blocks, and the
+  blocks the certified bound flags), bit 1 alone = values from the originals,
+  keys still quantized (rung 2).
+* Rung 2, value promotion: a block's estimated contribution to the value error
+  is its estimated mass times its value reconstruction error, P_b * ev_b (the
+  block's term of the certificate's value sum).  A block not already promoted
+  takes its values from the originals when that product, for any query head of
+  its kv head, exceeds a threshold tau_v.  The product is taken in fp32 from the
+  fp32 masses and descriptors, so the choice is a deterministic function of them.
+* Ranking-consistency check: for a query head, the blocks it promoted (its own
+  top-K*, in selection order = the ranking by quantized-key mass) are scored
+  again from the fp16 originals: the block's log-sum-exp of sigma q . k_t over
+  its tokens (the log of its unnormalised attention mass; the ranking ignores
+  the common normaliser).  A pair of promoted blocks is inverted when the block
+  ranked lower by the quantized keys scores more than a margin delta >= 0 above
+  the block ranked higher.  The head fails the check, and is recomputed with
+  dense attention over the originals (rung 3), when its number of inverted pairs
+  exceeds r >= 0.  The page prints no criterion: delta = 0, r = 0 is its strict
+  reading (any disagreement in order); delta and r are the caller's.
+* Rung 3 is also triggered by the certificate: a query head whose certificate
+  after the promoted pass exceeds eps falls back as well (an addition to the
+  page's trigger; the certificate bounds the same failure, quantization noise
+  distorting the attention distribution, with a proof).
+* Rung 4 (the whole layer densely) is every head falling back; it is not a
+  separate step here.
 """
 
 import numpy as np
@@ -108,11 +123,90 @@ def select_blocks(mass_f32, seq_len, tau_cov, n_kv_heads, flags_in=None):
     return out
 
 
-def dense_fallback(out, certificate, eps, dense_out):
-    """Rows whose certificate exceeds eps take the dense result (and certificate 0)."""
+def promote_values(mass_f32, ev_f32, seq_len, tau_v, n_kv_heads, flags):
+    """Rung 2 (reading above): flags uint8 [B, Hkv, nblk] with 2 set on the blocks
+    without bit 0 whose fp32 product mass * ev exceeds tau_v for some query head of
+    the kv head.  mass_f32 [B, Hq, nblk], ev_f32 [B, Hkv, nblk]."""
+    B, Hq, nblk = mass_f32.shape
+    G = Hq // n_kv_heads
+    out = np.array(flags, np.uint8, copy=True)
+    tau = np.float32(tau_v)
+    for b in range(B):
+        nb = (int(seq_len[b]) + TILE - 1) // TILE
+        for hq in range(Hq):
+            h = hq // G
+            for j in range(nb):
+                if out[b, h, j] & 1:
+                    continue
+                if np.float32(mass_f32[b, hq, j]) * np.float32(ev_f32[b, h, j]) > tau:
+                    out[b, h, j] |= 2
+    return out
+
+
+def block_scores_fp16(k_orig_bits, q_bits, dtype, seq_len, softmax_scale=None):
+    """Block scores from the originals (fp64): s[b, hq, j] = log sum_{t in block j}
+    exp(sigma q . k_t) over the positions below seq_len (original basis, no
+    rotation); -inf for blocks past the sequence.  k_orig_bits [B, Hkv, Tmax, 128]."""
+    B, Hq, _ = q_bits.shape
+    H, Tmax = k_orig_bits.shape[1], k_orig_bits.shape[2]
+    G = Hq // H
+    sigma = 1.0 / np.sqrt(D) if not softmax_scale else float(softmax_scale)
+    q = nx.widen_input(q_bits, dtype).astype(np.float64)
+    out = np.full((B, Hq, Tmax // TILE), -np.inf)
+    for b in range(B):
+        T = int(seq_len[b])
+        if T <= 0:
+            continue
+        for h in range(H):
+            k = nx.widen_input(k_orig_bits[b, h, :T], dtype).astype(np.float64)
+            for hq in range(h * G, (h + 1) * G):
+                lg = (k @ q[b, hq]) * sigma
+                for j in range((T + TILE - 1) // TILE):
+                    x = lg[j * TILE:min(T, (j + 1) * TILE)]
+                    mx = x.max()
+                    out[b, hq, j] = mx + np.log(np.sum(np.exp(x - mx)))
+    return out
+
+
+def inverted_pairs(order, score, margin):
+    """Pairs (i, j), i before j in order, with score[order[j]] > score[order[i]] + margin."""
+    n = 0
+    for a in range(len(order)):
+        for c in range(a + 1, len(order)):
+            if score[order[c]] > score[order[a]] + margin:
+                n += 1
+    return n
+
+
+def ranking_inversions(mass_f32, score16, seq_len, tau_cov, margin, window=0.0):
+    """Inverted pairs among each query head's promoted blocks (reading above).
+
+    Returns (lo, hi), int64 [B, Hq]: the count with the margin raised, and lowered,
+    by window (window = 0: lo == hi, the count itself).  A computation of the
+    scores that is accurate to window/2 counts a number in [lo, hi].
+    """
+    B, Hq, _ = mass_f32.shape
+    lo = np.zeros((B, Hq), np.int64)
+    hi = np.zeros((B, Hq), np.int64)
+    for b in range(B):
+        nb = (int(seq_len[b]) + TILE - 1) // TILE
+        if nb == 0:
+            continue
+        for hq in range(Hq):
+            order = top_blocks(mass_f32[b, hq], nb, tau_cov)
+            lo[b, hq] = inverted_pairs(order, score16[b, hq], margin + window)
+            hi[b, hq] = inverted_pairs(order, score16[b, hq], margin - window)
+    return lo, hi
+
+
+def dense_fallback(out, certificate, eps, dense_out, fail=None):
+    """Rows whose certificate exceeds eps, or that failed the ranking check (fail
+    [B, Hq] nonzero), take the dense result (and certificate 0)."""
     out = np.array(out, np.float64, copy=True)
     cert = np.array(certificate, np.float64, copy=True)
     redo = cert > eps
+    if fail is not None:
+        redo = redo | (np.asarray(fail) != 0)
     out[redo] = dense_out[redo]
     cert[redo] = 0.0
     return out, cert, redo

@@ -19,7 +19,10 @@ for the newest query token.  The plain definition is evaluated directly:
 * for blocks flagged for exact recompute (64 tokens each), the fp16 originals
   are used instead, in the original basis, for both the logits and the values
   ("Runtime-Certified ...", Methodology sections 1 and 3: fetch the fp16 data
-  and compute exact dense attention for what the bound does not cover);
+  and compute exact dense attention for what the bound does not cover); a
+  block whose flag has bit 0 clear and bit 1 set takes only its values from the
+  originals, its logits from the quantized keys (the same page, section 3,
+  rung 2: value promotion);
 * with a full-precision window, the first n_sink and the last n_recent 64-token
   blocks of the sequence are likewise taken from the full-precision originals,
   in the original basis ("OSCAR", section 2.2B: sink and recent tokens kept in
@@ -55,7 +58,7 @@ def decode_attention(cache, q_bits, dtype, seq_len, rotation, signs=None, r16=No
     """Decode attention for every (b, hq) (or the given (b, hq) rows).
 
     q_bits: uint16 [B, Hq, 128] (fp16/bf16 bit patterns); seq_len: [B];
-    flags: uint8 [B, Hkv, nblk] or None.
+    flags: uint8 [B, Hkv, nblk] or None (bit 0: exact block; bit 1 alone: exact values).
     window: (n_sink, n_recent) blocks kept at full precision, or None; then
     originals = (k_bits, v_bits), uint16 [B, Hkv, >= T, 128], the appended inputs.
     Returns (out fp64 [B, Hq, 128], block_mass fp64 [B, Hq, nblk]); rows that
@@ -81,15 +84,20 @@ def decode_attention(cache, q_bits, dtype, seq_len, rotation, signs=None, r16=No
             continue
         kh = decode_k(cache, b, h, 0, T)
         vh = decode_v(cache, b, h, 0, T)
-        exact = np.zeros(T, dtype=bool)
+        exact = np.zeros(T, dtype=bool)   # keys and values from the originals
+        exact_v = np.zeros(T, dtype=bool)  # values from the originals
         if flags is not None:
             for blk in range((T + TILE - 1) // TILE):
-                if flags[b, h, blk]:
-                    exact[blk * TILE:min(T, (blk + 1) * TILE)] = True
+                sl = slice(blk * TILE, min(T, (blk + 1) * TILE))
+                if flags[b, h, blk] & 1:
+                    exact[sl] = True
+                elif flags[b, h, blk] & 2:
+                    exact_v[sl] = True
         if window is not None:
             for blk in np.nonzero(window_blocks(T, *window))[0]:
                 exact[blk * TILE:min(T, (blk + 1) * TILE)] = True
-        if exact.any():
+        exact_v |= exact
+        if exact_v.any():
             # the originals: the kept copy, or the inputs (identical where both exist)
             src_k, src_v = (cache.k_orig, cache.v_orig) if originals is None else originals
             ko = nx.widen_input(src_k[b, h, :T], dtype).astype(np.float64)
@@ -102,10 +110,10 @@ def decode_attention(cache, q_bits, dtype, seq_len, rotation, signs=None, r16=No
             m = np.max(logits)
             w = np.exp(logits - m)
             p = w / np.sum(w)
-            o_rot = p[~exact] @ vh[~exact]
+            o_rot = p[~exact_v] @ vh[~exact_v]
             o = R.T @ o_rot
-            if exact.any():
-                o = o + p[exact] @ vo[exact]
+            if exact_v.any():
+                o = o + p[exact_v] @ vo[exact_v]
             out[b, hq] = o
             for blk in range((T + TILE - 1) // TILE):
                 mass[b, hq, blk] = np.sum(p[blk * TILE:min(T, (blk + 1) * TILE)])

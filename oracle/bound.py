@@ -23,9 +23,12 @@ Block bound for kv head h, with the largest query norm of its GQA group:
     bound_b = Delta_b + ev_b;  block flagged for exact recompute iff bound_b > tau.
 
 Certificate for query head hq after a pass in which flagged blocks were exact:
-    Delta*  = ||q_hq|| * sigma * max_{b unflagged} ek_b
-    E       = 2 tanh(Delta* / 2) max_b vn_b + sum_{b unflagged} P_b ev_b
-with P_b the block's softmax mass in that pass.  Why it holds:
+    Delta*  = ||q_hq|| * sigma * max_{b: keys quantized} ek_b
+    E       = 2 tanh(Delta* / 2) max_b vn_b + sum_{b: values quantized} P_b ev_b
+with P_b the block's softmax mass in that pass.  A flag with bit 0 makes a
+block's keys and values exact; bit 1 alone makes only its values exact (value
+promotion), so such a block still counts in Delta* but not in the value sum.
+Why it holds:
 o - o_hat = sum_i (p_i - p_hat_i) v_i + sum_i p_hat_i (v_i - v_hat_i).  The second
 sum is at most sum_b P_b ev_b (flagged blocks use exact values).  In the first,
 ||.|| <= sum_i |p_i - p_hat_i| ||v_i|| <= 2 TV(p, p_hat) max ||v||, and with every
@@ -101,10 +104,12 @@ def certificate(desc, q_bits, dtype, seq_len, flags, mass, softmax_scale=None):
         nb = (int(seq_len[b]) + TILE - 1) // TILE
         for hq in range(Hq):
             h = hq // G
-            unf = flags[b, h, :nb] == 0 if flags is not None else np.ones(nb, bool)
-            ekmax = desc[b, h, :nb, 0][unf].max() if unf.any() else 0.0
+            f = flags[b, h, :nb] if flags is not None else np.zeros(nb, np.uint8)
+            kq = (f & 1) == 0        # keys quantized
+            vq = (f & 3) == 0        # values quantized
+            ekmax = desc[b, h, :nb, 0][kq].max() if kq.any() else 0.0
             dstar = np.linalg.norm(q[b, hq]) * sigma * ekmax
             vnmax = desc[b, h, :nb, 2].max() if nb else 0.0
-            val = np.sum(mass[b, hq, :nb][unf] * desc[b, h, :nb, 1][unf])
+            val = np.sum(mass[b, hq, :nb][vq] * desc[b, h, :nb, 1][vq])
             E[b, hq] = 2.0 * np.tanh(0.5 * dstar) * vnmax + val
     return E

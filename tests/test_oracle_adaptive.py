@@ -5,7 +5,11 @@ The block mass is pinned by closed forms (identical keys give each block its
 share of the tokens; two key values give the two-level softmax), by the sum over
 blocks and by zeros past the sequence; the top-K* choice by brute force over all
 subsets of small block sets with exactly representable masses; the union over a
-kv head's query heads and the fallback by hand-made cases.
+kv head's query heads and the fallback by hand-made cases.  Rung 2 (value
+promotion) and the ranking-consistency check are pinned by hand cases with
+exactly representable products and scores, the inverted-pair count by the
+discordant pairs of scipy's Kendall tau, and the fp16 block scores by a closed
+form (constant keys per block) and by scipy's logsumexp.
 """
 import itertools
 
@@ -120,3 +124,122 @@ def test_top_blocks_tau_zero_and_above_one():
     tie = np.array([0.25, 0.25, 0.5, 0.5], np.float32)[::-1].copy()  # masses 0.5, 0.5, 0.25, 0.25
     assert adaptive.top_blocks(tie, 4, 0.0) == [0]
     assert adaptive.top_blocks(tie, 4, 0.75) == [0, 1]
+
+
+# ---------------------------------------------------------------- rung 2 and the ranking check
+def test_promote_values_hand_case():
+    # kv head 0 has query heads 0, 1; kv head 1 has query heads 2, 3.  Products mass * ev
+    # (fp32, exact here: powers of two): block 0 of kv head 0 reaches 0.25 through query
+    # head 1 only, block 1 is already exact (bit 0) and stays 1, block 2 equals tau_v (not
+    # above it), block 3 lies past the sequence.
+    mass = np.zeros((1, 4, 4), np.float32)
+    mass[0, 0] = [0.125, 0.5, 0.25, 0.5]
+    mass[0, 1] = [0.5, 0.5, 0.25, 0.5]
+    mass[0, 2] = [0.0, 0.25, 0.0, 0.0]
+    mass[0, 3] = [0.0, 0.0, 0.0, 0.0]
+    ev = np.zeros((1, 2, 4), np.float32)
+    ev[0, 0] = [0.5, 1.0, 0.5, 1.0]
+    ev[0, 1] = [1.0, 1.0, 1.0, 1.0]
+    fl = np.zeros((1, 2, 4), np.uint8)
+    fl[0, 0, 1] = 1
+    got = adaptive.promote_values(mass, ev, np.array([192]), 0.125, 2, fl)
+    assert got[0].tolist() == [[2, 1, 0, 0], [0, 2, 0, 0]]
+    assert fl[0].tolist() == [[0, 1, 0, 0], [0, 0, 0, 0]]  # the input is not modified
+    # threshold above every product: nothing added
+    assert np.array_equal(adaptive.promote_values(mass, ev, np.array([192]), 0.5, 2, fl), fl)
+
+
+def test_inverted_pairs_hand_cases():
+    s = np.array([0.0, 1.0, 0.5])
+    assert adaptive.inverted_pairs([0, 1, 2], s, 0.0) == 2   # (0,1) and (0,2)
+    assert adaptive.inverted_pairs([0, 1, 2], s, 0.6) == 1   # only (0,1) by more than 0.6
+    assert adaptive.inverted_pairs([1, 2, 0], s, 0.0) == 0   # already in decreasing order
+    assert adaptive.inverted_pairs([2, 0, 1], s, 0.0) == 2   # (2,1) and (0,1)
+    assert adaptive.inverted_pairs([], s, 0.0) == 0
+    assert adaptive.inverted_pairs([1], s, 0.0) == 0
+    # equal scores are never inverted, at any margin >= 0
+    assert adaptive.inverted_pairs([0, 1], np.array([0.5, 0.5]), 0.0) == 0
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_inverted_pairs_is_the_discordant_count_of_kendalls_tau(seed):
+    # with distinct scores and margin 0 the inverted pairs are the discordant pairs between
+    # the order and the scores ranked decreasingly: D = (1 - tau) / 2 * n (n - 1) / 2
+    from scipy.stats import kendalltau
+    rng = np.random.default_rng(70 + seed)
+    n = int(rng.integers(5, 40))
+    order = list(rng.permutation(n))
+    score = rng.standard_normal(n)
+    pos = np.empty(n)
+    pos[order] = np.arange(n)
+    tau = kendalltau(pos, -score).statistic
+    want = round((1.0 - tau) / 2.0 * n * (n - 1) / 2.0)
+    assert adaptive.inverted_pairs(order, score, 0.0) == want
+
+
+def test_block_scores_fp16_closed_form():
+    # block j holds the key c_j e_0 on all its tokens and q = a e_0: its score is
+    # log(n_j) + sigma a c_j with n_j its token count (the last block is partial)
+    T, Tmax = 200, 256
+    c = np.array([1.0, -2.0, 0.5, 3.0])
+    k = np.zeros((1, 1, Tmax, 128))
+    for j in range(4):
+        k[0, 0, 64 * j:64 * (j + 1), 0] = c[j]
+    q = np.zeros((1, 2, 128))
+    q[0, 0, 0], q[0, 1, 0] = 2.0, -0.25
+    s = adaptive.block_scores_fp16(synth.to_bits(k, "f16"), synth.to_bits(q, "f16"), "f16", np.array([T]))
+    n = np.array([64, 64, 64, 8])
+    for hq, a in enumerate((2.0, -0.25)):
+        want = np.log(n) + a * c / np.sqrt(128)
+        assert np.allclose(s[0, hq], want, rtol=0, atol=1e-13)
+    s0 = adaptive.block_scores_fp16(synth.to_bits(k, "f16"), synth.to_bits(q, "f16"), "f16", np.array([64]))
+    assert np.isneginf(s0[0, :, 1:]).all() and np.isfinite(s0[0, :, 0]).all()
+
+
+def test_block_scores_fp16_matches_scipy_logsumexp():
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(71)
+    kb = synth.to_bits(rng.standard_normal((2, 2, 192, 128)), "bf16")
+    qb = synth.to_bits(rng.standard_normal((2, 4, 128)), "bf16")
+    seq = np.array([192, 100])
+    s = adaptive.block_scores_fp16(kb, qb, "bf16", seq, softmax_scale=0.3)
+    k = nx.widen_input(kb, "bf16").astype(np.float64)
+    q = nx.widen_input(qb, "bf16").astype(np.float64)
+    for b in range(2):
+        for hq in range(4):
+            lg = 0.3 * k[b, hq // 2, :seq[b]] @ q[b, hq]
+            for j in range((seq[b] + 63) // 64):
+                assert abs(s[b, hq, j] - logsumexp(lg[64 * j:64 * (j + 1)])) < 1e-12
+
+
+def test_ranking_inversions_hand_case():
+    # one query head, four blocks; the masses rank them 2, 0, 3, 1
+    mass = np.array([[[0.25, 0.0625, 0.5, 0.1875]]], np.float32)  # order 2, 0, 3, 1
+    score = np.array([[[1.0, 9.0, 2.0, 1.5]]])
+    seq = np.array([256])
+    # tau_cov 0.9: 0.5, 0.75, 0.9375 -> K* = 3, promoted in order [2, 0, 3]
+    # pairs: (2,0): 1.0 > 2.0? no; (2,3): 1.5 > 2.0? no; (0,3): 1.5 > 1.0: yes -> 1
+    lo, hi = adaptive.ranking_inversions(mass, score, seq, 0.9, 0.0)
+    assert lo.tolist() == hi.tolist() == [[1]]
+    # margin 0.5: 1.5 > 1.0 + 0.5 is false -> 0; window 0.01 around it: lo 0, hi 1
+    lo, hi = adaptive.ranking_inversions(mass, score, seq, 0.9, 0.5)
+    assert lo.tolist() == hi.tolist() == [[0]]
+    lo, hi = adaptive.ranking_inversions(mass, score, seq, 0.9, 0.5, window=0.01)
+    assert (lo.tolist(), hi.tolist()) == ([[0]], [[1]])
+    # tau_cov 1.0 promotes block 1 as well, ranked last: it scores above all three -> 3 more
+    lo, _ = adaptive.ranking_inversions(mass, score, seq, 1.0, 0.0)
+    assert lo.tolist() == [[4]]
+    # an empty sequence has no promoted blocks
+    lo, hi = adaptive.ranking_inversions(mass, score, np.array([0]), 1.0, 0.0)
+    assert lo.tolist() == hi.tolist() == [[0]]
+
+
+def test_dense_fallback_takes_failed_heads_too():
+    out = np.ones((1, 3, 2))
+    dense = np.full((1, 3, 2), 7.0)
+    cert = np.array([[0.1, 0.5, 0.2]])
+    fail = np.array([[1, 0, 0]], np.uint8)
+    o, c, redo = adaptive.dense_fallback(out, cert, 0.3, dense, fail)
+    assert redo.tolist() == [[True, True, False]]
+    assert o[0, 0].tolist() == [7.0, 7.0] and o[0, 2].tolist() == [1.0, 1.0]
+    assert c.tolist() == [[0.0, 0.0, 0.2]]

@@ -102,6 +102,52 @@ def test_all_flagged_is_dense_attention():
         assert np.allclose(dense[b], _sdpa(qf[b], k, v, 2), rtol=1e-10, atol=1e-12)
 
 
+def test_value_only_flags_take_the_original_values():
+    # "Runtime-Certified ...", Methodology section 3, rung 2: a value-promoted block (flag 2)
+    # reads its values from the originals.  Every token carries the same value vector, so
+    # the output is that vector whatever the logits: the original with flag 2, its int4
+    # reconstruction without.
+    rng = np.random.default_rng(24)
+    T = 192
+    cache = _cache("int8", "int4", B=1, H=1, T=T, gk=128, gv=32, keep=True)
+    k = rng.standard_normal((1, 1, T, 128))
+    v = np.repeat(rng.standard_normal((1, 1, 1, 128)), T, axis=2)
+    vb = synth.to_bits(v, "f16")
+    codec.append(cache, synth.to_bits(k, "f16"), vb, np.zeros(1, int), "f16", "none")
+    q = synth.to_bits(rng.standard_normal((1, 2, 128)), "f16")
+    v16 = vb[0, 0, 0].view(np.float16).astype(np.float64)
+    out2, _ = attention.decode_attention(cache, q, "f16", np.array([T]), "none", flags=np.full((1, 1, 3), 2, np.uint8))
+    out0, _ = attention.decode_attention(cache, q, "f16", np.array([T]), "none")
+    assert np.abs(out2[0] - v16).max() <= 1e-12 * np.abs(v16).max()
+    assert np.abs(out0[0] - v16).max() > 1e-3  # int4 reconstruction error: the case tells them apart
+
+
+def test_value_only_flags_keep_the_quantized_logits():
+    # Values on the int4 grid (each 32-channel group holds +-7/8, entries k/8): their codes
+    # are exact, so a value-promoted block (flag 2) gives the same output as no promotion,
+    # while a full promotion (flag 1) also takes exact keys and gives dense attention.
+    rng = np.random.default_rng(25)
+    T = 192
+    cache = _cache("int8", "int4", B=1, H=1, T=T, gk=128, gv=32, keep=True)
+    k = rng.standard_normal((1, 1, T, 128))
+    v = rng.integers(-7, 8, size=(1, 1, T, 128)) / 8.0
+    v[..., ::32] = 7.0 / 8.0
+    kb, vb = synth.to_bits(k, "f16"), synth.to_bits(v, "f16")
+    codec.append(cache, kb, vb, np.zeros(1, int), "f16", "none")
+    assert np.array_equal(codec.decode_v(cache, 0, 0, 0, T), v[0, 0])
+    q = synth.to_bits(3.0 * rng.standard_normal((1, 2, 128)), "f16")
+    seq = np.array([T])
+    flag = lambda f: np.full((1, 1, 3), f, np.uint8)
+    out0, _ = attention.decode_attention(cache, q, "f16", seq, "none")
+    out1, _ = attention.decode_attention(cache, q, "f16", seq, "none", flags=flag(1))
+    out2, _ = attention.decode_attention(cache, q, "f16", seq, "none", flags=flag(2))
+    out3, _ = attention.decode_attention(cache, q, "f16", seq, "none", flags=flag(3))
+    dense = attention.dense_attention(cache.k_orig, cache.v_orig, q, "f16", seq)
+    assert np.allclose(out2, out0, rtol=1e-12, atol=1e-15)
+    assert np.allclose(out1, dense, rtol=1e-12, atol=1e-15) and np.array_equal(out3, out1)
+    assert np.abs(out2 - dense).max() > 1e-4  # int8 key error moves the logits
+
+
 @pytest.mark.parametrize("T,window,want", [
     (323, (1, 2), [1, 0, 0, 0, 1, 1]),   # 6 blocks, the last one partial
     (100, (1, 2), [1, 1]),               # window wider than the sequence

@@ -126,3 +126,17 @@ def test_both_terms_are_attained(delta, ev):
     E = _cert([(ek[:64].max(), ev, vn), (ek[64:].max(), ev, vn)], [0, 0], [ph[:64].sum(), ph[64:].sum()], 128)
     assert err <= E * (1 + 1e-12)
     assert E <= err * (1 + 1e-12), (E, err)
+
+
+def test_value_promoted_block_counts_in_the_key_term_only():
+    # Blocks (ek, ev, vn, mass, flag): block 1 is value-promoted (flag 2), block 2 exact
+    # (flag 1).  With ||q|| sigma = 1 the key term takes ek over the blocks whose keys are
+    # quantized, blocks 0 and 1: Delta* = max(0.5, ln 3) = ln 3, and 2 tanh(ln 3 / 2) = 1,
+    # so the key term is max vn = 4.  The value sum takes block 0 only: 0.5 * 0.25.
+    # E = 4 + 0.125.  Dropping block 1 from Delta* gives 2 tanh(0.25) 4 + 0.125 = 2.0747...;
+    # counting its value error gives 4 + 0.125 + 0.25 * 10 = 6.625.
+    rows = [(0.5, 0.25, 1.0), (math.log(3.0), 10.0, 2.0), (5.0, 10.0, 4.0)]
+    E = _cert(rows, [0, 2, 1], [0.5, 0.25, 0.25], 192)
+    assert abs(E - 4.125) <= 1e-12 * 4.125, E
+    # bit 0 takes precedence: flag 3 is a fully exact block
+    assert _cert(rows, [0, 2, 3], [0.5, 0.25, 0.25], 192) == E
