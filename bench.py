@@ -32,6 +32,7 @@ available core (at most 16) over all 16 sequences.
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -58,10 +59,13 @@ def parse():
     ap.add_argument("--window", type=str, default=None, metavar="SINK,RECENT",
                     help="workloads 3/4/5: keep the first SINK and last RECENT 64-token blocks of every "
                          "sequence at full precision")
-    ap.add_argument("--adaptive", type=str, default=None, metavar="TAU_COV,EPS",
-                    help="workload 3: also time the adaptive-precision ladder (scoring pass, top-K* promotion "
-                         "covering TAU_COV of the estimated mass, decode, dense fallback of heads whose "
-                         "certificate exceeds EPS)")
+    ap.add_argument("--adaptive", type=str, default=None, metavar="TAU_COV,EPS[,TAU_V[,MARGIN[,MAX_INV]]]",
+                    help="workload 3 with retrieval needles and queries that seek them: also time the "
+                         "adaptive-precision ladder (scoring pass, top-K* promotion covering TAU_COV of the "
+                         "estimated mass, value promotion of blocks whose mass times value error exceeds TAU_V "
+                         "(default 1e-6), ranking-consistency check with margin MARGIN (default 0) and at most "
+                         "MAX_INV inverted pairs (default 0), decode, dense fallback of the heads that fail the "
+                         "check or whose certificate exceeds EPS)")
     ap.add_argument("--rotation", default="sign_fwht", choices=("sign_fwht", "srft"),
                     help="workload 2: the rotation applied before quantization (sign + Walsh-Hadamard, or the "
                          "sign + real-packed FFT form)")
@@ -71,9 +75,11 @@ def parse():
     if args.adaptive is not None:
         if args.workload != 3:
             ap.error("--adaptive applies to workload 3 (the certified cache)")
-        args.adaptive = tuple(float(x) for x in args.adaptive.split(","))
-        if len(args.adaptive) != 2:
-            ap.error("--adaptive takes TAU_COV,EPS")
+        vals = [float(x) for x in args.adaptive.split(",")]
+        if not 2 <= len(vals) <= 5:
+            ap.error("--adaptive takes TAU_COV,EPS[,TAU_V[,MARGIN[,MAX_INV]]]")
+        vals += [1e-6, 0.0, 0.0][len(vals) - 2:]
+        args.adaptive = tuple(vals[:4]) + (int(vals[4]),)
     if args.window is not None:
         if args.workload == 2:
             ap.error("--window applies to workloads 3, 4 and 5")
@@ -240,6 +246,8 @@ def bench_workload(cfg_id, args):
     c = synth.config(cfg_id)
     if args.window is not None:
         c["sink_blocks"], c["recent_blocks"] = args.window
+    if args.adaptive is not None:
+        c["needles"] = 4
     B, Hq, H, T, P = c["B"], c["Hq"], c["Hkv"], c["T"], c["prefill"]
     nrot = 4
     g = torch.Generator(device=dev)
@@ -248,10 +256,26 @@ def bench_workload(cfg_id, args):
     def progress(msg):
         print(f"[bench w{cfg_id}] {msg}", file=sys.stderr, flush=True)
 
-    # certified workload: planted tokens (x10 in K and V alike), one in pieces 0-2 and two in
-    # piece 3 of every (sequence, kv head); each piece fills two of the eight 4096-token
-    # spans of the context, so every stream holds 10 planted tokens in 512 blocks (~2%)
-    plant_pos = [torch.randint(0, P, (1 if i < nrot - 1 else 2, B, H), generator=g, device=dev) for i in range(nrot)]
+    # The certified workload fills its context with T / P distinct pieces (the others reuse nrot
+    # pieces): planted tokens (x10 in K and V alike), two in each of the first two pieces and
+    # one in each other piece of every (sequence, kv head), so every stream holds 10 planted
+    # tokens in 512 blocks (~2%).  With needles, every stream also holds that many retrieval
+    # needles at uniform positions: needle i's key is L_i sqrt(128) / a * u for a unit
+    # direction u of the stream, L_i = top - i (top uniform in 20 +- 0.5; in one stream of
+    # eight, L_1 = L_0 - 0.005), and the queries of the stream's heads are a u + (I - u u^T) z,
+    # which gives needle i the logit L_i.
+    nfill = T // P if c["data"] == "certified" else nrot
+    plant_pos = [torch.randint(0, P, (2 if i < 10 - nfill else 1, B, H), generator=g, device=dev)
+                 for i in range(nfill)]
+    nn = int(c.get("needles", 0))
+    if nn:
+        nu = torch.randn((B, H, 128), generator=g, device=dev, dtype=torch.float64)
+        nu /= nu.norm(dim=-1, keepdim=True)
+        nlog = (c["needle_top"] + torch.rand((B, H, 1), generator=g, device=dev, dtype=torch.float64) - 0.5
+                - torch.arange(nn, device=dev, dtype=torch.float64))
+        tie = (torch.arange(B * H, device=dev) % c["needle_tie_every"] == 0).view(B, H)
+        nlog[..., 1] = torch.where(tie, nlog[..., 0] - 0.005, nlog[..., 1])
+        npos = torch.randint(0, T, (B, H, nn), generator=g, device=dev)
 
     def draw(tensor, piece):
         shape = (B, H, P, 128)
@@ -260,6 +284,12 @@ def bench_workload(cfg_id, args):
             for t in plant_pos[piece]:
                 idx = t[..., None, None].expand(B, H, 1, 128)
                 x.scatter_(2, idx, x.gather(2, idx) * c["plant_factor"])
+            if nn and tensor == 0:
+                for i in range(nn):
+                    here = (npos[..., i] // P == piece)[..., None, None]
+                    idx = (npos[..., i] % P)[..., None, None].expand(B, H, 1, 128)
+                    key = (nlog[..., i, None] * math.sqrt(128) / c["needle_q"] * nu).float()[:, :, None, :]
+                    x.scatter_(2, idx, torch.where(here, key, x.gather(2, idx)))
             return x.half().view(torch.int16)
         if c["data"] == "anisotropic":
             z = torch.randn(shape, generator=g, device=dev)
@@ -287,14 +317,17 @@ def bench_workload(cfg_id, args):
                                     ratio=c["clip_ratio"])
         for cc in caches:
             cc.clip_k, cc.clip_v = tk, tv
-    kin = [draw(0, i) for i in range(nrot)]
-    vin = [draw(1, i) for i in range(nrot)]
+    kin = [draw(0, i) for i in range(nfill)]
+    vin = [draw(1, i) for i in range(nfill)]
     for cc in caches:
         for t0 in range(0, T, P):
-            kvq.append(p, cc, kin[(t0 // P) % nrot], vin[(t0 // P) % nrot], [t0] * B)
+            kvq.append(p, cc, kin[(t0 // P) % nfill], vin[(t0 // P) % nfill], [t0] * B)
     torch.cuda.synchronize()
     progress("caches filled")
     q = torch.randn((B, Hq, 128), generator=g, device=dev)
+    if nn:
+        uq = nu.float().repeat_interleave(Hq // H, dim=1)
+        q = c["needle_q"] * uq + q - (q * uq).sum(-1, keepdim=True) * uq
     q = (q.bfloat16() if c["dtype"] == "bf16" else q.half()).view(torch.int16)
     seq = [T] * B
     ws = kvq.workspace(p)
@@ -325,7 +358,14 @@ def bench_workload(cfg_id, args):
             kvq.decode_attn(p, cc, q, seq, ws=ws, out=out)
 
     def do_append(i):
-        kvq.append(p, caches[i % nrot], kin[i % nrot], vin[i % nrot], [T - P] * B)
+        # a 4096-token prefill: the reused pieces go to the last span; the distinct pieces of
+        # the certified workload go back to their own spans (among the last nrot), so the
+        # cache's contents, planted tokens and needles included, stay as filled
+        if nfill == nrot:
+            kvq.append(p, caches[i % nrot], kin[i % nrot], vin[i % nrot], [T - P] * B)
+        else:
+            piece = nfill - nrot + i % nrot
+            kvq.append(p, caches[i % nrot], kin[piece], vin[piece], [piece * P] * B)
 
     n_each = max(args.steps, 4 * nrot)
     for i in range(args.warmup):
@@ -401,7 +441,8 @@ def bench_workload(cfg_id, args):
         "data": f"synthetic, drawn on the GPU from a seeded generator ({c['data']}){extra}",
         "config": {"workload": c["name"], "B": B, "Hq": Hq, "Hkv": H, "head_dim": 128, "context": T,
                    "prefill_tokens": P, "formats": fmt, "rotation": c["rotation"], "input": c["dtype"],
-                   **({"window_blocks": list(args.window)} if args.window is not None else {})},
+                   **({"window_blocks": list(args.window)} if args.window is not None else {}),
+                   **({"needles": nn} if nn else {})},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "decode_split (splits merged by their last workgroup)" + (" + bound_kernel" if c["keep"] else ""),
@@ -435,6 +476,10 @@ def bench_workload(cfg_id, args):
                                      "kernel": "append_fast_kernel<fp4, fp4>"}
     if args.adaptive is not None:
         result["adaptive"] = adaptive_ladder(args, c, p, caches, q, seq, ws, out, cert, bnd, flg, batch_time, n_each)
+        # the same step without the ladder: the bound and the certified decode with its flags
+        # (decode_us above), and dense fp16 attention over the originals
+        result["adaptive"]["certified_decode_us"] = result["decode_us"]
+        result["adaptive"]["fp16_decode_us"] = result["fp16_decode_us"]
         progress("adaptive ladder timed")
     if args.copy_calibration:
         src = torch.full((256 << 20,), 3, dtype=torch.uint8, device=dev)
@@ -449,11 +494,13 @@ def adaptive_ladder(args, c, p, caches, q, seq, ws, out, cert, bnd, flg, batch_t
     """Times of the adaptive-precision ladder on the certified cache, stage by stage."""
     import torch
     import bit_kv_cache_append_amd as kvq
-    tau_cov, eps = args.adaptive
+    tau_cov, eps, tau_v, margin, max_inv = args.adaptive
     B, Hq, H, T = c["B"], c["Hq"], c["Hkv"], c["T"]
     nrot = len(caches)
     mass = torch.empty((B, Hq, T // 64), dtype=torch.float32, device=q.device)
     prom = torch.empty_like(flg)
+    inv = torch.empty((B, Hq), dtype=torch.int32, device=q.device)
+    fail = torch.empty((B, Hq), dtype=torch.uint8, device=q.device)
 
     def stages(i, which):
         cc = caches[i % nrot]
@@ -463,38 +510,55 @@ def adaptive_ladder(args, c, p, caches, q, seq, ws, out, cert, bnd, flg, batch_t
             kvq.block_mass(p, cc, q, seq, mass=mass)
         if "select" in which:
             kvq.select_blocks(p, mass, seq, tau_cov, flags_in=flg, flags_out=prom)
+        if "promote" in which:
+            kvq.promote_values(p, cc, mass, seq, tau_v, prom)
+        if "rank" in which:
+            kvq.ranking_check(p, cc, q, seq, mass, tau_cov, margin, max_inv, out=(inv, fail))
         if "decode" in which:
             kvq.decode_attn(p, cc, q, seq, flags=prom, certificate=True, ws=ws, out=out, cert=cert)
         if "fallback" in which:
-            kvq.dense_fallback(p, cc, q, seq, eps, out, cert)
+            kvq.dense_fallback(p, cc, q, seq, eps, out, cert, fail=fail)
 
-    allst = ("bound", "mass", "select", "decode", "fallback")
+    allst = ("bound", "mass", "select", "promote", "rank", "decode", "fallback")
     for i in range(nrot):
         stages(i, allst)
     torch.cuda.synchronize()
     step_ms = batch_time(lambda i: stages(i, allst), n_each)
+    bound_ms = batch_time(lambda i: stages(i, ("bound",)), n_each)
     mass_ms = batch_time(lambda i: stages(i, ("mass",)), n_each)
     sel_ms = batch_time(lambda i: stages(i, ("select",)), n_each)
     stages(0, ("bound", "mass", "select"))
-    dec_ms = batch_time(lambda i: kvq.decode_attn(p, caches[0], q, seq, flags=prom, certificate=True, ws=ws, out=out,
-                                                  cert=cert), n_each)
+    p0 = prom.clone()
+    prom_ms = batch_time(lambda i: (prom.copy_(p0), stages(0, ("promote",))), n_each)
+    copy_ms = batch_time(lambda i: prom.copy_(p0), n_each)
+    rank_ms = batch_time(lambda i: stages(0, ("rank",)), n_each)
+    stages(0, ("promote",))
+    dec_ms = batch_time(lambda i: stages(0, ("decode",)), n_each)
     c0 = cert.clone()
-    fb_ms = batch_time(lambda i: (cert.copy_(c0), kvq.dense_fallback(p, caches[0], q, seq, eps, out, cert)), n_each)
+    fb_ms = batch_time(lambda i: (cert.copy_(c0), stages(0, ("fallback",))), n_each)
     torch.cuda.synchronize()
-    nprom = int(prom.sum().item())
+    pr = prom.cpu().numpy()
     nbound = int(flg.sum().item())
-    nfall = int((c0 > eps).sum().item())
+    nfail = int(fail.sum().item())
+    nfall = int(((c0 > eps) | (fail != 0)).sum().item())
     sizes = kvq.buffer_bytes(p)
     kbytes = sizes["k_codes"] + sizes["k_meta"] + B * Hq * 128 * 2 + B * Hq * (T // 64) * 4
+    invn = inv.cpu().numpy()
     return {
-        "tau_cov": tau_cov, "eps": eps,
+        "tau_cov": tau_cov, "eps": eps, "tau_v": tau_v, "ranking_margin": margin, "ranking_max_inversions": max_inv,
+        "data": f"{c['needles']} retrieval needles per (sequence, kv head), queries that seek them",
         "step_us": round(step_ms * 1e3, 2),
+        "error_bound_us": round(bound_ms * 1e3, 2),
         "block_mass_us": round(mass_ms * 1e3, 2),
         "select_us": round(sel_ms * 1e3, 2),
+        "promote_values_us": round(max(prom_ms - copy_ms, 0.0) * 1e3, 2),
+        "ranking_check_us": round(rank_ms * 1e3, 2),
         "decode_promoted_us": round(dec_ms * 1e3, 2),
         "fallback_us_incl_cert_copy": round(fb_ms * 1e3, 2),
-        "blocks_promoted": nprom, "blocks_flagged_by_bound": nbound, "blocks": int(prom.numel()),
-        "heads_fallen_back": nfall, "heads": B * Hq,
+        "blocks": int(prom.numel()), "blocks_flagged_by_bound": nbound,
+        "blocks_promoted": int(((pr & 1) != 0).sum()), "blocks_value_promoted": int(((pr & 3) == 2).sum()),
+        "heads": B * Hq, "heads_failing_ranking_check": nfail, "heads_fallen_back": nfall,
+        "inversions_max": int(invn.max()), "heads_with_inversions": int((invn > 0).sum()),
         "block_mass_roofline": {"bound": "hbm", "achieved": round(kbytes / (mass_ms / 1e3) / 1e9, 1),
                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": round(kbytes / (mass_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),

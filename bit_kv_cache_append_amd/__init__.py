@@ -4,7 +4,7 @@ Every computation runs in the HIP kernels of libkvq.so; this module turns torch
 tensors into device pointers and the current HIP stream, calls the C entry
 points of the same names (kvq_append, kvq_error_bound, kvq_decode_attn,
 kvq_decode_attn_dense, kvq_decode_attn_noalloc, kvq_calibrate_clip, kvq_block_mass, kvq_select_blocks,
-kvq_dense_fallback, kvq_calibrate_lambda, kvq_buffer_bytes, kvq_decode_workspace_bytes, kvq_decode_splits) and raises KvqError on a non-zero status.  There is
+kvq_promote_values, kvq_ranking_check, kvq_dense_fallback, kvq_calibrate_lambda, kvq_buffer_bytes, kvq_decode_workspace_bytes, kvq_decode_splits) and raises KvqError on a non-zero status.  There is
 no fallback: if the library is not built, importing the functions raises.
 """
 
@@ -86,8 +86,13 @@ def lib():
         L.kvq_block_mass.argtypes = [P(Params), P(CacheStruct), vp, P(i32), vp, vp]
         L.kvq_select_blocks.restype = i32
         L.kvq_select_blocks.argtypes = [P(Params), vp, P(i32), ctypes.c_float, vp, vp, vp]
+        L.kvq_promote_values.restype = i32
+        L.kvq_promote_values.argtypes = [P(Params), P(CacheStruct), vp, P(i32), ctypes.c_float, vp, vp]
+        L.kvq_ranking_check.restype = i32
+        L.kvq_ranking_check.argtypes = [P(Params), P(CacheStruct), vp, P(i32), vp, ctypes.c_float, ctypes.c_float,
+                                        i32, vp, vp, vp]
         L.kvq_dense_fallback.restype = i32
-        L.kvq_dense_fallback.argtypes = [P(Params), P(CacheStruct), vp, P(i32), ctypes.c_float, vp, vp, vp]
+        L.kvq_dense_fallback.argtypes = [P(Params), P(CacheStruct), vp, P(i32), ctypes.c_float, vp, vp, vp, vp]
         L.kvq_calibrate_lambda.restype = i32
         L.kvq_calibrate_lambda.argtypes = [P(Params), P(CacheStruct), vp, vp, i32, vp, vp, vp]
         L.kvq_calibrate_clip.restype = i32
@@ -275,11 +280,35 @@ def select_blocks(p, mass, seq_len, tau_cov, flags_in=None, flags_out=None, stre
     return flags_out
 
 
-def dense_fallback(p, cache, q, seq_len, eps, out, cert, stream=None):
-    """kvq_dense_fallback: rows with cert > eps recomputed densely from the originals (in place)."""
+def promote_values(p, cache, mass, seq_len, tau_v, flags, stream=None):
+    """kvq_promote_values: bit 1 on the blocks whose mass * ev exceeds tau_v (flags in place)."""
     cs = cache.struct()
-    _check(lib().kvq_dense_fallback(ctypes.byref(p), ctypes.byref(cs), _ptr(q), _i32(seq_len), float(eps), _ptr(out),
-                                    _ptr(cert), stream if stream is not None else _stream()))
+    _check(lib().kvq_promote_values(ctypes.byref(p), ctypes.byref(cs), _ptr(mass), _i32(seq_len), float(tau_v),
+                                    _ptr(flags), stream if stream is not None else _stream()))
+    return flags
+
+
+def ranking_check(p, cache, q, seq_len, mass, tau_cov, margin=0.0, max_inversions=0, out=None, stream=None):
+    """kvq_ranking_check: (inversions int32 [B, Hq], fail uint8 [B, Hq]) (out: that pair to fill)."""
+    import torch
+    if out is None:
+        inv = torch.empty((p.batch, p.n_q_heads), dtype=torch.int32, device=mass.device)
+        fl = torch.empty((p.batch, p.n_q_heads), dtype=torch.uint8, device=mass.device)
+    else:
+        inv, fl = out
+    cs = cache.struct()
+    _check(lib().kvq_ranking_check(ctypes.byref(p), ctypes.byref(cs), _ptr(q), _i32(seq_len), _ptr(mass),
+                                   float(tau_cov), float(margin), int(max_inversions), _ptr(inv), _ptr(fl),
+                                   stream if stream is not None else _stream()))
+    return inv, fl
+
+
+def dense_fallback(p, cache, q, seq_len, eps, out, cert, fail=None, stream=None):
+    """kvq_dense_fallback: rows with cert > eps, or fail set, recomputed densely from the
+    originals (in place; cert may be None when fail is given)."""
+    cs = cache.struct()
+    _check(lib().kvq_dense_fallback(ctypes.byref(p), ctypes.byref(cs), _ptr(q), _i32(seq_len), float(eps),
+                                    _ptr(fail), _ptr(out), _ptr(cert), stream if stream is not None else _stream()))
     return out, cert
 
 

@@ -429,26 +429,24 @@ __global__ __launch_bounds__(NTA) void mass_kernel(AdaptArgs a) {
   for (int j = t; j < a.nt; j += NTA) m[j] = j < nb ? expf(m[j] - lse) : 0.0f;
 }
 
-// Promotion flags.  flags_init_kernel writes the given flags (or zeros); then one
-// workgroup per (sequence, query head) sorts that head's blocks by decreasing mass
-// (equal masses: lower index first) and marks the shortest prefix whose fp32
-// running sum, taken in that order, reaches tau_cov.  The query heads of a kv head
-// mark the same flag row; they only ever store 1, so their order does not matter.
-// The running sum is one thread's sequential fp32 additions, so the choice is
-// reproducible bit for bit.
+// Promotion flags.  flags_init_kernel copies the given flags (or writes zeros); then
+// one workgroup per (sequence, query head) sets bit 0 on its top-K* blocks.  The query
+// heads of a kv head mark the same flag row; each stores the byte's initial value with
+// bit 0 set (no one changes another bit meanwhile), so their order does not matter.
 __global__ __launch_bounds__(NTA) void flags_init_kernel(AdaptArgs a) {
   const size_t n = (size_t)a.B * a.H * a.nt;
   for (size_t j = (size_t)blockIdx.x * NTA + threadIdx.x; j < n; j += (size_t)gridDim.x * NTA)
-    a.flags_out[j] = (a.flags_in != nullptr && a.flags_in[j] != 0) ? 1 : 0;
+    a.flags_out[j] = a.flags_in != nullptr ? a.flags_in[j] : 0;
 }
 
-__global__ __launch_bounds__(NTA) void select_kernel(AdaptArgs a) {
-  __shared__ unsigned long long key[MAX_SELECT_BLOCKS];
-  __shared__ int kstar;
-  const int row = blockIdx.x, b = row / a.Hq, h = (row % a.Hq) / a.G;
+// Sorts the blocks [0, nb) of row (sequence, query head) by decreasing mass (equal
+// masses: lower index first) into key[] (the mass bits above the complemented block
+// index) and returns K*, the length of the shortest prefix whose fp32 running sum
+// reaches tau_cov (nb if none does).  Called by the whole workgroup, nb >= 1; the
+// result is uniform.  The running sum is one thread's sequential fp32 additions, so
+// the choice is reproducible bit for bit.
+__device__ int sorted_top(const AdaptArgs& a, int row, int nb, unsigned long long* key, int* kstar) {
   const int t = threadIdx.x;
-  const int nb = (a.seq.v[b] + TILE - 1) / TILE;
-  if (nb == 0) return;  // uniform
   int npow = 2;
   while (npow < nb) npow <<= 1;
   const float* m = a.mass + (size_t)row * a.nt;
@@ -489,16 +487,116 @@ __global__ __launch_bounds__(NTA) void select_kernel(AdaptArgs a) {
         }
       }
     }
-    kstar = k;
+    *kstar = k;
   }
   __syncthreads();
+  return *kstar;
+}
+__device__ __forceinline__ int block_of_key(unsigned long long k) { return (int)(0xFFFFFFFFu - (uint32_t)k); }
+
+__global__ __launch_bounds__(NTA) void select_kernel(AdaptArgs a) {
+  __shared__ unsigned long long key[MAX_SELECT_BLOCKS];
+  __shared__ int kstar;
+  const int row = blockIdx.x, b = row / a.Hq, h = (row % a.Hq) / a.G;
+  const int nb = (a.seq.v[b] + TILE - 1) / TILE;
+  if (nb == 0) return;  // uniform
+  const int K = sorted_top(a, row, nb, key, &kstar);
   uint8_t* fl = a.flags_out + ((size_t)b * a.H + h) * a.nt;
-  for (int j = t; j < kstar; j += NTA) fl[0xFFFFFFFFu - (uint32_t)key[j]] = 1;
+  for (int j = threadIdx.x; j < K; j += NTA) {
+    const int blk = block_of_key(key[j]);
+    fl[blk] = (uint8_t)(fl[blk] | 1);
+  }
 }
 
-// Dense fallback of one (sequence, query head): if its certificate exceeds eps,
-// exact attention over the originals (original basis, no rotation), and the
-// certificate becomes 0.  One workgroup per row; wave w takes blocks w, w + 4, ...
+// Value promotion (rung 2): a block without bit 0 gets bit 1 when mass * ev (fp32) of
+// some query head of its kv head exceeds tau_v.  One thread per (sequence, kv head,
+// block), in place.
+__global__ __launch_bounds__(NTA) void promote_kernel(AdaptArgs a) {
+  const size_t n = (size_t)a.B * a.H * a.nt;
+  for (size_t idx = (size_t)blockIdx.x * NTA + threadIdx.x; idx < n; idx += (size_t)gridDim.x * NTA) {
+    const int jb = (int)(idx % a.nt);
+    const size_t bh = idx / a.nt;
+    const int h = (int)(bh % a.H), b = (int)(bh / a.H);
+    if (jb >= (a.seq.v[b] + TILE - 1) / TILE) continue;
+    const uint8_t f = a.flags_out[idx];
+    if (f & 1) continue;
+    const float ev = a.desc[idx * 3 + 1];
+    const float* m = a.mass + ((size_t)b * a.Hq + (size_t)h * a.G) * a.nt + jb;
+    bool up = false;
+    for (int g = 0; g < a.G; ++g) up = up || __fmul_rn(m[(size_t)g * a.nt], ev) > a.tau_v;
+    if (up) a.flags_out[idx] = (uint8_t)(f | 2);
+  }
+}
+
+// Ranking-consistency check of one (sequence, query head): its promoted blocks (the
+// top-K* of its masses, in that order) are scored from the fp16 originals, score =
+// log sum_t exp(scale q . k_t) over the block's positions (fp32), and the pairs (i, j),
+// i ranked before j, with score_j > score_i + margin are counted; the head fails when
+// the count exceeds max_inv.  Wave w scores ranks w, w + 4, ... (lane = token); the
+// pairs are counted by thread in columns j.
+__global__ __launch_bounds__(NTA) void rank_kernel(AdaptArgs a) {
+  __shared__ unsigned long long key[MAX_SELECT_BLOCKS];
+  __shared__ float sc[MAX_SELECT_BLOCKS];
+  __shared__ float qs[D];
+  __shared__ int kstar, count;
+  const int row = blockIdx.x, b = row / a.Hq, hq = row % a.Hq, h = hq / a.G;
+  const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
+  const int T = a.seq.v[b];
+  const int nb = (T + TILE - 1) / TILE;
+  if (nb == 0) {  // uniform: no promoted blocks
+    if (t == 0) {
+      a.inv[row] = 0;
+      a.fail[row] = 0;
+    }
+    return;
+  }
+  const bool bf16 = a.in_bf16 != 0;
+  if (t < D) qs[t] = widen(a.q[(size_t)row * D + t], bf16) * a.scale;
+  if (t == 0) count = 0;
+  const int K = sorted_top(a, row, nb, key, &kstar);  // (its barriers publish qs and count)
+  const size_t stream = (size_t)b * a.H + h;
+  for (int i = wv; i < K; i += NTA / 64) {
+    const int tok = block_of_key(key[i]) * TILE + lane;
+    float lg = NEG_INF_A;
+    if (tok < T) {
+      const uint4* kp = reinterpret_cast<const uint4*>(a.k_orig + (stream * a.Tmax + tok) * D);
+      uint4 kr[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) kr[e] = kp[e];
+      lg = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const uint32_t w4[4] = {kr[e].x, kr[e].y, kr[e].z, kr[e].w};
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int ch = 8 * e + 2 * x;
+          lg = fmaf(qs[ch], widen((uint16_t)(w4[x] & 0xFFFF), bf16), lg);
+          lg = fmaf(qs[ch + 1], widen((uint16_t)(w4[x] >> 16), bf16), lg);
+        }
+      }
+    }
+    const float mx = wmax(lg);  // a promoted block holds at least one position below T
+    const float se = wsum(tok < T ? expf(lg - mx) : 0.0f);
+    if (lane == 0) sc[i] = mx + logf(se);
+  }
+  __syncthreads();
+  int n = 0;
+  for (int jj = t; jj < K; jj += NTA) {
+    const float sj = sc[jj];
+    for (int i = 0; i < jj; ++i) n += sj > sc[i] + a.margin ? 1 : 0;
+  }
+  for (int o = 1; o < 64; o <<= 1) n += __shfl_xor(n, o);
+  if (lane == 0) atomicAdd(&count, n);
+  __syncthreads();
+  if (t == 0) {
+    a.inv[row] = count;
+    a.fail[row] = count > a.max_inv ? 1 : 0;
+  }
+}
+
+// Dense fallback of one (sequence, query head): if its certificate exceeds eps or it
+// failed the ranking check, exact attention over the originals (original basis, no
+// rotation), and the certificate becomes 0.  One workgroup per row; wave w takes blocks w, w + 4, ...
 // with a running max and sum, and the waves are merged at the end.
 __global__ __launch_bounds__(NTA) void fallback_kernel(AdaptArgs a) {
   __shared__ float qs[D];
@@ -506,7 +604,8 @@ __global__ __launch_bounds__(NTA) void fallback_kernel(AdaptArgs a) {
   __shared__ float wm[4], wl[4];
   __shared__ float wo[4][D];
   const int row = blockIdx.x, b = row / a.Hq, hq = row % a.Hq, h = hq / a.G;
-  if (!(a.cert[row] > a.eps)) return;  // uniform over the workgroup
+  const bool redo = (a.cert != nullptr && a.cert[row] > a.eps) || (a.fail_in != nullptr && a.fail_in[row] != 0);
+  if (!redo) return;  // uniform over the workgroup
   const int T = a.seq.v[b];
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
   const bool bf16 = a.in_bf16 != 0;
@@ -578,7 +677,7 @@ __global__ __launch_bounds__(NTA) void fallback_kernel(AdaptArgs a) {
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     *reinterpret_cast<float2*>(a.out + (size_t)row * D + 2 * lane) = make_float2(r0 * inv, r1 * inv);
-    if (lane == 0) a.cert[row] = 0.0f;
+    if (lane == 0 && a.cert != nullptr) a.cert[row] = 0.0f;
   }
 }
 
@@ -615,6 +714,17 @@ hipError_t launch_select(const AdaptArgs& a, hipStream_t s) {
 
 hipError_t launch_fallback(const AdaptArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(fallback_kernel, dim3(a.B * a.Hq), dim3(NTA), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_promote_values(const AdaptArgs& a, hipStream_t s) {
+  const size_t n = (size_t)a.B * a.H * a.nt;
+  hipLaunchKernelGGL(promote_kernel, dim3((unsigned)std::min<size_t>((n + NTA - 1) / NTA, 4096)), dim3(NTA), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ranking_check(const AdaptArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(rank_kernel, dim3(a.B * a.Hq), dim3(NTA), 0, s, a);
   return hipGetLastError();
 }
 

@@ -525,12 +525,62 @@ kvq_status kvq_select_blocks(const kvq_params* p, const float* mass, const int32
   return KVQ_OK;
 }
 
-kvq_status kvq_dense_fallback(const kvq_params* p, const kvq_cache* c, const void* q, const int32_t* seq_len_host,
-                              float eps, float* out, float* certificate, void* stream) {
+kvq_status kvq_promote_values(const kvq_params* p, const kvq_cache* c, const float* mass,
+                              const int32_t* seq_len_host, float tau_v, uint8_t* flags, void* stream) {
   kvq_status st = check_params(p);
   if (st) return st;
   if ((st = check_cache(p, c, true))) return st;
-  if (!q || !out || !certificate) return fail(KVQ_ERR_INVALID_ARG, "q/out/certificate are NULL");
+  if (!mass || !flags) return fail(KVQ_ERR_INVALID_ARG, "mass/flags are NULL");
+  if (!(tau_v >= 0.0f)) return fail(KVQ_ERR_INVALID_ARG, "tau_v must be >= 0");
+  AdaptArgs a;
+  memset(&a, 0, sizeof(a));
+  if ((st = check_seq(p, seq_len_host, a.seq))) return st;
+  adapt_common(p, a);
+  a.mass = const_cast<float*>(mass);
+  a.desc = c->blk_desc;
+  a.flags_out = flags;
+  a.tau_v = tau_v;
+  hipError_t e = launch_promote_values(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "value promotion launch");
+  return KVQ_OK;
+}
+
+kvq_status kvq_ranking_check(const kvq_params* p, const kvq_cache* c, const void* q, const int32_t* seq_len_host,
+                             const float* mass, float tau_cov, float margin, int32_t max_inversions,
+                             int32_t* inversions, uint8_t* fail_out, void* stream) {
+  kvq_status st = check_params(p);
+  if (st) return st;
+  if ((st = check_cache(p, c, true))) return st;
+  if (!q || !mass || !inversions || !fail_out) return fail(KVQ_ERR_INVALID_ARG, "q/mass/inversions/fail are NULL");
+  if (!(tau_cov >= 0.0f && tau_cov <= 1.0f)) return fail(KVQ_ERR_INVALID_ARG, "tau_cov must be in [0, 1]");
+  if (!(margin >= 0.0f) || margin == INFINITY) return fail(KVQ_ERR_INVALID_ARG, "margin must be finite and >= 0");
+  if (max_inversions < 0) return fail(KVQ_ERR_INVALID_ARG, "max_inversions must be >= 0");
+  if (p->max_ctx / TILE > MAX_SELECT_BLOCKS)
+    return fail(KVQ_ERR_UNSUPPORTED, "the ranking check supports max_ctx / 64 <= %d blocks", MAX_SELECT_BLOCKS);
+  AdaptArgs a;
+  memset(&a, 0, sizeof(a));
+  if ((st = check_seq(p, seq_len_host, a.seq))) return st;
+  adapt_common(p, a);
+  a.q = (const uint16_t*)q;
+  a.k_orig = (const uint16_t*)c->k_orig;
+  a.mass = const_cast<float*>(mass);
+  a.tau_cov = tau_cov;
+  a.margin = margin;
+  a.max_inv = max_inversions;
+  a.inv = inversions;
+  a.fail = fail_out;
+  hipError_t e = launch_ranking_check(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "ranking check launch");
+  return KVQ_OK;
+}
+
+kvq_status kvq_dense_fallback(const kvq_params* p, const kvq_cache* c, const void* q, const int32_t* seq_len_host,
+                              float eps, const uint8_t* head_fail, float* out, float* certificate, void* stream) {
+  kvq_status st = check_params(p);
+  if (st) return st;
+  if ((st = check_cache(p, c, true))) return st;
+  if (!q || !out) return fail(KVQ_ERR_INVALID_ARG, "q/out are NULL");
+  if (!certificate && !head_fail) return fail(KVQ_ERR_INVALID_ARG, "certificate and fail are both NULL");
   if (!(eps >= 0.0f)) return fail(KVQ_ERR_INVALID_ARG, "eps must be >= 0");
   AdaptArgs a;
   memset(&a, 0, sizeof(a));
@@ -541,6 +591,7 @@ kvq_status kvq_dense_fallback(const kvq_params* p, const kvq_cache* c, const voi
   a.v_orig = (const uint16_t*)c->v_orig;
   a.out = out;
   a.cert = certificate;
+  a.fail_in = head_fail;
   a.eps = eps;
   hipError_t e = launch_fallback(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "fallback launch");

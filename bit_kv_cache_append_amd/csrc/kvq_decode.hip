@@ -944,8 +944,51 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
     oo[hf] = f4{0, 0, 0, 0};
   }
 
+  // ---------------------------------------------------------------- chunks read from the originals
+  // Window blocks: the first n_sink and the last n_recent blocks of the sequence,
+  // kept at full precision in k_win/v_win ("OSCAR", section 2.2B, mixed-precision
+  // layout).  They are attended exactly, like blocks flagged by the error bound.
+  auto in_window = [&](int ch) -> bool {
+    return a.k_win != nullptr && (ch < a.n_sink || ch >= nchunks - a.n_recent);
+  };
+  // first row of chunk ch's originals: its window slot, else the full copy
+  auto orig_rows = [&](const uint16_t* full, const uint16_t* win, int ch) -> const uint16_t* {
+    if (in_window(ch)) {
+      const int wslot = ch < a.n_sink ? ch : a.n_sink + ch % a.n_recent;
+      return win + (stream * (size_t)(a.n_sink + a.n_recent) + wslot) * TILE * D;
+    }
+    return full + (stream * a.Tmax + (size_t)ch * TILE) * D;
+  };
+  // Original values of one chunk into oo: lane l holds channels 2l, 2l+1 of every token
+  // (vp = the chunk's first row + lane, in dwords), the weights of (token, head) in the
+  // wave's pb (written and waited for by the caller); vr[0] holds the first 16 rows.  The
+  // value rows go in batches of 16, the next batch in flight while one is accumulated.
+  // Rows at or past the sequence end count as zeros (their weights are 0, and whatever
+  // bits the buffer holds there must not turn 0 * x into a NaN).
+  auto pv_orig = [&](int ch, const uint32_t* vp, uint32_t(&vr)[2][16]) {
+    const bool bf16 = a.in_bf16 != 0;
+    const float(*pb)[4] = sm.u.loop.pb[wv];
+    const int nlive = T - ch * TILE;  // rows of the chunk below the sequence end (>= 1)
+#pragma unroll
+    for (int bt = 0; bt < TILE / 16; ++bt) {
+      if (bt + 1 < TILE / 16) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) vr[(bt + 1) & 1][k] = vp[(size_t)(16 * (bt + 1) + k) * (D / 2)];
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const uint32_t vv = 16 * bt + k < nlive ? vr[bt & 1][k] : 0u;
+        const float v0 = widen((uint16_t)(vv & 0xFFFF), bf16), v1 = widen((uint16_t)(vv >> 16), bf16);
+        const float4 pp = *reinterpret_cast<const float4*>(&pb[16 * bt + k][0]);
+        oo[0] += f4{pp.x, pp.y, pp.z, pp.w} * v0;
+        oo[1] += f4{pp.x, pp.y, pp.z, pp.w} * v1;
+      }
+    }
+    lds_wait();
+  };
+
   // ---------------------------------------------------------------- one quantized chunk
-  auto quant_chunk = [&](const ChunkRegs<KF, VF, vmeta_words(VF, VG)>& R, int ch, float ev_c) {
+  auto quant_chunk = [&](const ChunkRegs<KF, VF, vmeta_words(VF, VG)>& R, int ch, float ev_c, bool vexact) {
     const int tok0 = ch * TILE;
     stage_vmeta<VF, VG>(vml, lane, R.vmeta);
     float l[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1090,6 +1133,27 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
       o[hf] *= av;
       if constexpr (EXACT) oo[hf] *= av;
     }
+    if constexpr (CERT) {
+      if (vexact) {
+        // value promotion: the logits above came from the codes, the values come from the
+        // originals, accumulated like those of an exactly recomputed chunk (weights p of
+        // token tok_of(s_a, r), head j, through LDS)
+        const uint32_t* vp = reinterpret_cast<const uint32_t*>(orig_rows(a.v_orig, a.v_win, ch)) + lane;
+        uint32_t vr[2][16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) vr[0][k] = vp[(size_t)k * (D / 2)];
+        float(*pb)[4] = sm.u.loop.pb[wv];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pb[tok_of<VF>(s_a, r)][j] = p[r];
+        if constexpr (VF == KVQ_INT2) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) zacc[g] *= alpha;
+        }
+        lds_wait();
+        pv_orig(ch, vp, vr);
+        return;
+      }
+    }
     // ---- PV weights, formed here once per (token, V group): p * s in fp32 for this lane's
     // four tokens (slice s_a, head j), split into an fp16 high part and the fp16 rounding
     // of the remainder, so that the fp16 matrix products carry each weight to about
@@ -1173,20 +1237,6 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   };
 
   // ---------------------------------------------------------------- one exactly recomputed chunk
-  // Window blocks: the first n_sink and the last n_recent blocks of the sequence,
-  // kept at full precision in k_win/v_win ("OSCAR", section 2.2B, mixed-precision
-  // layout).  They are attended exactly, like blocks flagged by the error bound.
-  auto in_window = [&](int ch) -> bool {
-    return a.k_win != nullptr && (ch < a.n_sink || ch >= nchunks - a.n_recent);
-  };
-  // first row of chunk ch's originals: its window slot, else the full copy
-  auto orig_rows = [&](const uint16_t* full, const uint16_t* win, int ch) -> const uint16_t* {
-    if (in_window(ch)) {
-      const int wslot = ch < a.n_sink ? ch : a.n_sink + ch % a.n_recent;
-      return win + (stream * (size_t)(a.n_sink + a.n_recent) + wslot) * TILE * D;
-    }
-    return full + (stream * a.Tmax + (size_t)ch * TILE) * D;
-  };
   auto exact_chunk = [&](int ch) {
     const int tok0 = ch * TILE;
     const bool bf16 = a.in_bf16 != 0;
@@ -1257,23 +1307,7 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
       for (int g = 0; g < 4; ++g) zacc[g] *= alpha;
     }
     lds_wait();
-    // value rows in batches of 16, the next batch in flight while one is accumulated
-#pragma unroll
-    for (int bt = 0; bt < TILE / 16; ++bt) {
-      if (bt + 1 < TILE / 16) {
-#pragma unroll
-        for (int k = 0; k < 16; ++k) vr[(bt + 1) & 1][k] = vp[(size_t)(16 * (bt + 1) + k) * (D / 2)];
-      }
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const uint32_t vv = vr[bt & 1][k];
-        const float v0 = widen((uint16_t)(vv & 0xFFFF), bf16), v1 = widen((uint16_t)(vv >> 16), bf16);
-        const float4 pp = *reinterpret_cast<const float4*>(&pb[16 * bt + k][0]);
-        oo[0] += f4{pp.x, pp.y, pp.z, pp.w} * v0;
-        oo[1] += f4{pp.x, pp.y, pp.z, pp.w} * v1;
-      }
-    }
-    lds_wait();
+    pv_orig(ch, vp, vr);
   };
 
   // ---------------------------------------------------------------- software-pipelined walk
@@ -1281,12 +1315,14 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   // (two register sets used alternately).
   auto visit = [&](const ChunkRegs<KF, VF, vmeta_words(VF, VG)>& R, int ch, const ChunkAux<CERT>& X) {
     float ev_c = 0.0f;
-    bool fl = false;
+    bool fl = false, fv = false;  // exact keys and values; exact values only
     if constexpr (EXACT) fl = in_window(ch);
     if constexpr (CERT) {
-      fl = fl || (a.flags != nullptr && __builtin_amdgcn_readfirstlane(X.flag) != 0);
+      const uint32_t f = a.flags != nullptr ? __builtin_amdgcn_readfirstlane(X.flag) : 0u;
+      fl = fl || (f & 1u) != 0;
+      fv = !fl && (f & 2u) != 0;
       if (a.desc != nullptr) {
-        ev_c = X.ev;
+        ev_c = fv ? 0.0f : X.ev;
         vnmax = fmaxf(vnmax, X.vn);
         if (!fl) ekmax = fmaxf(ekmax, X.ek);
       }
@@ -1294,7 +1330,7 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
     if (fl) {
       if constexpr (EXACT) exact_chunk(ch);
     } else {
-      quant_chunk(R, ch, ev_c);
+      quant_chunk(R, ch, ev_c, fv);
     }
   };
   // Every iteration issues the same claims and loads (a load past the range's last chunk

@@ -93,10 +93,15 @@ struct AdaptArgs {
   const uint8_t* flags_in;   // [B][H][nt] or null
   uint8_t* flags_out;        // [B][H][nt]
   float* out;                // [B][Hq][128] (fallback)
-  float* cert;               // [B][Hq] (fallback)
+  float* cert;               // [B][Hq] (fallback; or null)
+  const float* desc;         // [B][H][nt][3] (ek, ev, vn) (value promotion)
+  int32_t* inv;              // [B][Hq] inverted pairs (ranking check)
+  uint8_t* fail;             // [B][Hq] ranking check result
+  const uint8_t* fail_in;    // [B][Hq] heads to recompute (fallback; or null)
   int32_t B, Hq, H, G, Tmax, nt;
   int32_t in_bf16, rotation, k_fmt, k_group;
-  float scale, tau_cov, eps;
+  int32_t max_inv;
+  float scale, tau_cov, eps, tau_v, margin;
   float cos128[128];  // fl32(cos(2 pi k / 128)): the SRFT matrix entries
   SeqArray seq;
 };
@@ -157,5 +162,7 @@ hipError_t decode_scratch(void** ptr, hipStream_t s);
 hipError_t launch_block_mass(const AdaptArgs& a, hipStream_t s);
 hipError_t launch_select(const AdaptArgs& a, hipStream_t s);
 hipError_t launch_fallback(const AdaptArgs& a, hipStream_t s);
+hipError_t launch_promote_values(const AdaptArgs& a, hipStream_t s);
+hipError_t launch_ranking_check(const AdaptArgs& a, hipStream_t s);
 
 }  // namespace kvq

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 3
+#define KVQ_ABI_VERSION 4
 
 typedef int32_t kvq_status;
 #define KVQ_OK 0
@@ -251,12 +251,16 @@ kvq_status kvq_error_bound(const kvq_params* p, const kvq_cache* cache, const vo
 /*
  * Decode attention of one query token per (b, hq) over positions [0, seq_len_host[b]).
  *   q: device [B][Hq][128] in_dtype.
- *   block_flags: device uint8 [B][Hkv][max_ctx/64] or NULL; a nonzero flag makes
- *     the block use k_orig/v_orig exactly (needs keep_fp16_copy).
+ *   block_flags: device uint8 [B][Hkv][max_ctx/64] or NULL (needs keep_fp16_copy):
+ *     bit 0 set makes the block use k_orig/v_orig exactly; bit 1 set with bit 0
+ *     clear keeps its logits from the codes and takes its values from v_orig
+ *     (value promotion, "Runtime-Certified Bounded-Error Quantized Attention",
+ *     Methodology section 3, rung 2); other bits are ignored.
  *   out: device fp32 [B][Hq][128], original (unrotated) basis.  Rows with
  *     seq_len 0 are written as zeros.
  *   certificate: device fp32 [B][Hq] or NULL (needs keep_fp16_copy): an upper bound
- *     on ||out - dense attention over the originals||_2 for that row.
+ *     on ||out - dense attention over the originals||_2 for that row (blocks with
+ *     quantized keys enter its key term, blocks with quantized values its value sum).
  *   workspace: device, >= kvq_decode_workspace_bytes(p) bytes, 256-byte aligned,
  *     zero-filled before its first use (see kvq_decode_workspace_bytes).
  * With a window (sink_blocks + recent_blocks > 0), blocks j < sink_blocks and
@@ -294,9 +298,12 @@ kvq_status kvq_decode_attn_noalloc(const kvq_params* p, const kvq_cache* cache, 
  * Adaptive precision ("Runtime-Certified Bounded-Error Quantized Attention",
  * Methodology section 3): a scoring pass over the quantized keys estimates each
  * block's attention mass; the blocks covering a fraction tau_cov of it are
- * promoted to exact recompute (kvq_select_blocks, then kvq_decode_attn with the
- * flags); a head whose certificate still exceeds eps is recomputed densely
- * (kvq_dense_fallback).
+ * promoted to exact recompute (kvq_select_blocks), blocks whose value error is
+ * large against their estimated mass take exact values (kvq_promote_values, the
+ * ladder's rung 2), kvq_decode_attn runs with those flags, and a head whose
+ * promoted blocks rank differently under the originals (kvq_ranking_check), or
+ * whose certificate still exceeds eps, is recomputed densely (kvq_dense_fallback,
+ * rung 3).  Flags: device uint8 [B][Hkv][max_ctx/64], bits as for kvq_decode_attn.
  *
  * kvq_block_mass: mass[b][hq][j] = sum over the tokens t of block j of
  *   softmax_t(scale * (R q) . k_hat_t), the softmax over positions [0,
@@ -308,28 +315,56 @@ kvq_status kvq_block_mass(const kvq_params* p, const kvq_cache* cache, const voi
                           const int32_t* seq_len_host, float* mass, void* stream);
 
 /*
- * kvq_select_blocks: flags_out[b][h][j] = 1 if block j is among the top-K* blocks
- * of any query head of kv head h, or flags_in[b][h][j] != 0 (flags_in may be NULL
- * or equal flags_out).  Top-K* of a query head: its blocks below seq_len sorted by
- * decreasing mass (equal masses: lower index first), K* the shortest prefix whose
- * fp32 running sum, accumulated in that order, reaches tau_cov (all blocks if it
- * never does).  mass: device fp32 [B][Hq][max_ctx/64] (from kvq_block_mass);
- * flags: device uint8 [B][Hkv][max_ctx/64]; tau_cov in [0, 1].
+ * kvq_select_blocks: flags_out[b][h][j] = flags_in[b][h][j] (0 if flags_in is NULL)
+ * with bit 0 set if block j is among the top-K* blocks of any query head of kv head
+ * h (flags_in may equal flags_out).  Top-K* of a query head: its blocks below
+ * seq_len sorted by decreasing mass (equal masses: lower index first), K* the
+ * shortest prefix whose fp32 running sum, accumulated in that order, reaches
+ * tau_cov (all blocks if it never does).  mass: device fp32 [B][Hq][max_ctx/64]
+ * (from kvq_block_mass); tau_cov in [0, 1].
  * max_ctx / 64 must not exceed 4096 (KVQ_ERR_UNSUPPORTED otherwise).
  */
 kvq_status kvq_select_blocks(const kvq_params* p, const float* mass, const int32_t* seq_len_host,
                              float tau_cov, const uint8_t* flags_in, uint8_t* flags_out, void* stream);
 
 /*
- * kvq_dense_fallback: for every (b, hq) with certificate[b][hq] > eps, out[b][hq]
- * is replaced by attention over k_orig/v_orig (positions [0, seq_len_host[b]),
- * fp32 arithmetic, original basis) and certificate[b][hq] is set to 0; other rows
- * are left unchanged.  Needs keep_fp16_copy.  out/certificate: device, as
- * written by kvq_decode_attn.  eps >= 0.
+ * kvq_promote_values (rung 2): in place, every block j below seq_len of kv head h
+ * whose flag has bit 0 clear gets bit 1 if mass[b][hq][j] * ev_j > tau_v (one fp32
+ * product) for some query head hq of h; ev_j is the block's value error descriptor
+ * (blk_desc[..][1]).  Needs keep_fp16_copy.  mass: from kvq_block_mass; tau_v >= 0.
+ */
+kvq_status kvq_promote_values(const kvq_params* p, const kvq_cache* cache, const float* mass,
+                              const int32_t* seq_len_host, float tau_v, uint8_t* flags, void* stream);
+
+/*
+ * kvq_ranking_check: for every (b, hq), its top-K* blocks (as kvq_select_blocks
+ * chooses them from mass, in that order: the ranking by the quantized keys) are
+ * scored from k_orig, score_j = log sum_t exp(scale * q . k_t) over the block's
+ * positions below seq_len (fp32, original basis); inversions[b][hq] = the number of
+ * pairs (i, j), i ranked before j, with score_j > score_i + margin, and
+ * fail[b][hq] = inversions > max_inversions.  Needs keep_fp16_copy.
+ *   q: device [B][Hq][128] in_dtype; mass: device fp32 [B][Hq][max_ctx/64];
+ *   inversions: device int32 [B][Hq]; fail: device uint8 [B][Hq].
+ *   tau_cov in [0, 1], margin >= 0, max_inversions >= 0.  max_ctx / 64 <= 4096.
+ * The page prints no criterion for a consistent ranking: margin = 0 and
+ * max_inversions = 0 (any pair out of order) is the strict reading.
+ */
+kvq_status kvq_ranking_check(const kvq_params* p, const kvq_cache* cache, const void* q,
+                             const int32_t* seq_len_host, const float* mass, float tau_cov, float margin,
+                             int32_t max_inversions, int32_t* inversions, uint8_t* fail, void* stream);
+
+/*
+ * kvq_dense_fallback: for every (b, hq) with certificate[b][hq] > eps, or with
+ * fail[b][hq] != 0, out[b][hq] is replaced by attention over k_orig/v_orig
+ * (positions [0, seq_len_host[b]), fp32 arithmetic, original basis) and
+ * certificate[b][hq] is set to 0; other rows are left unchanged.  Needs
+ * keep_fp16_copy.  out/certificate: device, as written by kvq_decode_attn;
+ * certificate may be NULL (then only fail triggers), fail may be NULL (then only
+ * the certificate), not both.  eps >= 0.
  */
 kvq_status kvq_dense_fallback(const kvq_params* p, const kvq_cache* cache, const void* q,
-                              const int32_t* seq_len_host, float eps, float* out, float* certificate,
-                              void* stream);
+                              const int32_t* seq_len_host, float eps, const uint8_t* fail, float* out,
+                              float* certificate, void* stream);
 
 /*
  * Decode attention over uncompressed K/V in the layout of k_orig/v_orig

@@ -108,18 +108,19 @@ def top_blocks(mass_f32, n_blocks, tau_cov):
 
 
 def select_blocks(mass_f32, seq_len, tau_cov, n_kv_heads, flags_in=None):
-    """Promotion flags uint8 [B, Hkv, nblk]: the union over each kv head's query
-    heads of their top-K* blocks, OR the bound's flags (if given)."""
+    """Promotion flags uint8 [B, Hkv, nblk]: the given flags (e.g. the bound's; zeros
+    if None) with bit 0 set on the union over each kv head's query heads of their
+    top-K* blocks."""
     B, Hq, nblk = mass_f32.shape
     G = Hq // n_kv_heads
-    out = np.zeros((B, n_kv_heads, nblk), np.uint8) if flags_in is None else (np.asarray(flags_in) != 0).astype(np.uint8)
+    out = np.zeros((B, n_kv_heads, nblk), np.uint8) if flags_in is None else np.array(flags_in, np.uint8, copy=True)
     for b in range(B):
         nb = (int(seq_len[b]) + TILE - 1) // TILE
         if nb == 0:
             continue
         for hq in range(Hq):
             for i in top_blocks(mass_f32[b, hq], nb, tau_cov):
-                out[b, hq // G, i] = 1
+                out[b, hq // G, i] |= 1
     return out
 
 

@@ -10,7 +10,7 @@ into Q), which the method takes as a fixed input, like the sign vector.
 
 Seeding.  Every stream is keyed by numpy SeedSequence(1234, spawn_key=(cfg,
 stream, ...)), with streams K=0, V=1, q=2, signs=3, outliers=4, R=5, U=6,
-calib=7, plant=8.  K/V streams are further keyed by (b, kv head, chunk of 4096
+calib=7, plant=8, needle=9.  K/V streams are further keyed by (b, kv head, chunk of 4096
 tokens), so any slice of any sequence can be regenerated on its own.
 
 Workloads (d = 128 throughout; stand-ins for model KV activations, since the
@@ -19,7 +19,10 @@ pages' models and datasets are not used):
   2 llama3-8b gqa    B=16 Hq=32 Hkv=8 T=8192   fp16 N(0,1), 10 (head, channel) x8;
                                                4096-token prefill append
   3 certified        B=32 Hq=32 Hkv=8 T=32768  K 0.02 N(0,1), V 0.0015 N(0,1) fp16,
-                                               10 planted blocks per (b, head)
+                                               10 planted blocks per (b, head);
+                                               with needles=n: n retrieval needles
+                                               per (b, head) and queries that seek
+                                               them (peaked attention)
   4 int2 dense       B=64 Hq=32 Hkv=8 T=32768  fp16 U diag(i^-1/2) z, U Haar per head
   5 fp4 search       B=8  Hq=32 Hkv=8 T=131072 bf16 Student-t (nu = 4)
 """
@@ -29,7 +32,7 @@ import numpy as np
 D = 128
 CHUNK = 4096
 ROOT_SEED = 1234
-ST_K, ST_V, ST_Q, ST_SIGNS, ST_OUTL, ST_R, ST_U, ST_CALIB, ST_PLANT = range(9)
+ST_K, ST_V, ST_Q, ST_SIGNS, ST_OUTL, ST_R, ST_U, ST_CALIB, ST_PLANT, ST_NEEDLE = range(10)
 
 CONFIGS = {
     1: dict(cfg=1, name="tiny-int4", B=1, Hq=1, Hkv=1, T=1024, dtype="f16",
@@ -43,7 +46,8 @@ CONFIGS = {
     3: dict(cfg=3, name="certified-int8k-int4v", B=32, Hq=32, Hkv=8, T=32768, dtype="f16",
             k_fmt="int8", v_fmt="int4", k_group=128, v_group=128, scale_mode="absmax",
             rotation="sign_fwht", keep=True, data="certified", k_sigma=0.02, v_sigma=0.0015,
-            n_plant=10, plant_factor=10.0, tau=1e-2, prefill=4096),
+            n_plant=10, plant_factor=10.0, tau=1e-2, prefill=4096,
+            needles=0, needle_q=16.0, needle_top=20.0, needle_tie_every=8),
     4: dict(cfg=4, name="int2-dense-rotation", B=64, Hq=32, Hkv=8, T=32768, dtype="f16",
             k_fmt="int2", v_fmt="int2", k_group=32, v_group=32, scale_mode="absmax",
             rotation="dense", keep=False, data="anisotropic", clip_ratio=0.9,
@@ -128,6 +132,26 @@ def planted(c, b, h):
     return list(zip(blocks.tolist(), offs.tolist()))
 
 
+def needle_plan(c, b, h):
+    """Retrieval needles of (sequence b, kv head h) in the certified workload with
+    needles=n: (u, positions, logits).  u is a seeded unit direction; needle i sits at
+    a seeded position in its own 64-token block and its key is logits[i] sqrt(128) /
+    needle_q * u, so that a query needle_q u + (I - u u^T) z of the head's group gives it
+    the logit logits[i] (softmax scale 1/sqrt(128)).  logits[i] = top - i with top
+    drawn in needle_top +- 0.5; in one stream of every needle_tie_every the second needle
+    sits 0.005 below the first (a near tie that quantization noise may invert)."""
+    r = _rng(c["cfg"], ST_NEEDLE, b, h)
+    u = r.standard_normal(D)
+    u /= np.linalg.norm(u)
+    n = int(c["needles"])
+    blocks = r.choice(c["T"] // 64, size=n, replace=False)
+    pos = blocks * 64 + r.integers(0, 64, size=n)
+    logits = c["needle_top"] + r.uniform(-0.5, 0.5) - np.arange(n, dtype=np.float64)
+    if n > 1 and (b * c["Hkv"] + h) % c["needle_tie_every"] == 0:
+        logits[1] = logits[0] - 0.005
+    return u, pos, logits
+
+
 def _chunk_values(c, tensor, b, h, chunk):
     """fp32/fp64 values [CHUNK, 128] of one 4096-token chunk of a K or V stream."""
     st = ST_K if tensor == 0 else ST_V
@@ -169,6 +193,11 @@ def kv_slice(c, tensor, b, h, t0, n):
             pos = blk * 64 + off
             if t0 <= pos < t0 + n:
                 out[pos - t0] *= c["plant_factor"]
+        if tensor == 0 and c.get("needles"):
+            u, npos, nlog = needle_plan(c, b, h)
+            for p_, l_ in zip(npos, nlog):
+                if t0 <= p_ < t0 + n:
+                    out[p_ - t0] = l_ * np.sqrt(D) / c["needle_q"] * u
     return to_bits(out, c["dtype"])
 
 
@@ -202,9 +231,21 @@ def kv_all(c, tensor, t0, n, workers=1, start_method="fork"):
 
 
 def queries(c, step=0):
-    """Query bit patterns [B, Hq, 128]: N(0,1) in the input dtype."""
+    """Query bit patterns [B, Hq, 128]: N(0,1) in the input dtype; with needles, the
+    query of a head of kv head h is needle_q u + (I - u u^T) z, z the N(0,1) draw and u
+    the needle direction of (b, h)."""
     r = _rng(c["cfg"], ST_Q, step)
-    return to_bits(r.standard_normal((c["B"], c["Hq"], D), dtype=np.float32), c["dtype"])
+    z = r.standard_normal((c["B"], c["Hq"], D), dtype=np.float32)
+    if not c.get("needles"):
+        return to_bits(z, c["dtype"])
+    q = z.astype(np.float64)
+    G = c["Hq"] // c["Hkv"]
+    for b in range(c["B"]):
+        for h in range(c["Hkv"]):
+            u = needle_plan(c, b, h)[0]
+            for hq in range(h * G, (h + 1) * G):
+                q[b, hq] = c["needle_q"] * u + q[b, hq] - (q[b, hq] @ u) * u
+    return to_bits(q, c["dtype"])
 
 
 def calibration(c, tensor, h):

@@ -22,7 +22,7 @@ def test_library_exports_every_declared_symbol():
     assert "kvq_append" in names and "kvq_decode_attn" in names and "kvq_error_bound" in names
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
-    assert L.kvq_abi_version() == 3
+    assert L.kvq_abi_version() == 4
 
 
 def test_buffer_sizes():
@@ -119,9 +119,30 @@ def test_adaptive_entry_points_validate_without_gpu():
     big = kvq.make_params(1, 8, 2, 64 * 8192)
     one = (ctypes.c_int32 * 1)(10)
     assert L.kvq_select_blocks(ctypes.byref(big), fake, one, ctypes.c_float(0.9), None, fake, None) == -2
-    # the dense fallback reads the originals: it needs keep_fp16_copy
-    st = L.kvq_dense_fallback(ctypes.byref(p), ctypes.byref(cs), fake, seq, ctypes.c_float(0.1), fake, fake, None)
+    # the dense fallback, value promotion and ranking check read the originals or the
+    # descriptors: they need keep_fp16_copy
+    st = L.kvq_dense_fallback(ctypes.byref(p), ctypes.byref(cs), fake, seq, ctypes.c_float(0.1), None, fake, fake,
+                              None)
     assert st == -1 and b"keep_fp16_copy" in L.kvq_last_error()
+    st = L.kvq_promote_values(ctypes.byref(p), ctypes.byref(cs), fake, seq, ctypes.c_float(0.1), fake, None)
+    assert st == -1 and b"keep_fp16_copy" in L.kvq_last_error()
+    st = L.kvq_ranking_check(ctypes.byref(p), ctypes.byref(cs), fake, seq, fake, ctypes.c_float(0.9),
+                             ctypes.c_float(0.0), 0, fake, fake, None)
+    assert st == -1 and b"keep_fp16_copy" in L.kvq_last_error()
+    kp = kvq.make_params(2, 8, 2, 256, k_fmt="int8", k_group=128, keep_fp16_copy=True)
+    kc = kvq.CacheStruct(k_codes=fake, k_meta=fake, v_codes=fake, v_meta=fake, signs=fake, blk_desc=fake,
+                         k_orig=fake, v_orig=fake)
+    # the fallback needs at least one trigger: a certificate or the check's fail flags
+    st = L.kvq_dense_fallback(ctypes.byref(kp), ctypes.byref(kc), fake, seq, ctypes.c_float(0.1), None, fake, None,
+                              None)
+    assert st == -1 and b"both NULL" in L.kvq_last_error()
+    for tau_cov, margin, max_inv, what in ((1.5, 0.0, 0, b"tau_cov"), (0.9, -1.0, 0, b"margin"),
+                                           (0.9, float("inf"), 0, b"margin"), (0.9, 0.0, -1, b"max_inversions")):
+        st = L.kvq_ranking_check(ctypes.byref(kp), ctypes.byref(kc), fake, seq, fake, ctypes.c_float(tau_cov),
+                                 ctypes.c_float(margin), max_inv, fake, fake, None)
+        assert st == -1 and what in L.kvq_last_error()
+    st = L.kvq_promote_values(ctypes.byref(kp), ctypes.byref(kc), fake, seq, ctypes.c_float(-1.0), fake, None)
+    assert st == -1 and b"tau_v" in L.kvq_last_error()
 
 
 def test_noalloc_decode_rejects_oversize_without_gpu():

@@ -11,7 +11,16 @@ Attention", Methodology section 3), through the C ABI:
   promotion, decode with the promoted flags and the certificate, and the dense
   fallback of the heads whose certificate exceeds eps - against the oracle's
   attention with the same flags (2e-3 per row) and dense attention for the rows
-  that fell back.
+  that fell back;
+* on the certified workload with retrieval needles (peaked attention, top-K* of a
+  few blocks): kvq_promote_values bit-identical to the oracle's rung 2 applied to
+  the library's fp32 masses and descriptors, and in agreement with the oracle's
+  fp64 masses and descriptors wherever the product is not within 2 % of tau_v;
+  decode with value-only flags against the oracle's attention and certificate;
+  kvq_ranking_check's inversion count inside the oracle's [lo, hi] (fp64 block
+  scores from the originals, pairs within 1e-3 of the margin counted as either)
+  and its fail flags where that range decides them; and the ladder with every
+  rung, fallback triggered by the check as well as the certificate.
 """
 import numpy as np
 import pytest
@@ -138,3 +147,173 @@ def test_adaptive_ladder_on_the_certified_cache(tau_cov, eps_q, must_fall_back):
     # attention (the rows that fell back are dense attention, certificate 0)
     exact = np.where(redo[..., None], dense, ref)
     assert np.all(np.linalg.norm(exact - dense, axis=-1) <= want_cert + 1e-12)
+
+
+# ---------------------------------------------------------------- retrieval needles: rungs 2 and 3
+NEEDLES = synth.config(3, B=2, T=4096, needles=4)
+WIN = 1e-3  # fp32 block scores: log-sum-exp of 64 dot products of 128 terms, |logits| <= ~25
+
+
+def _needle_state(seq):
+    c = NEEDLES
+    s, r16, p, g = _filled(c)
+    q = synth.queries(c)
+    qd = dev_bits(q)
+    mass = kvq.block_mass(p, g, qd, seq)
+    torch.cuda.synchronize()
+    return c, s, p, g, q, qd, mass
+
+
+def _ev(c, g):
+    return g.bufs["blk_desc"].view(c["B"], c["Hkv"], c["T"] // 64, 3)[..., 1].cpu().numpy()
+
+
+@pytest.mark.parametrize("tau_cov,tau_v", [(0.5, 1e-4), (0.9, 1e-6), (0.995, 0.0)])
+def test_promote_values_matches_oracle(tau_cov, tau_v):
+    seq = [4096, 3000]
+    print(f"[adaptive] promote values tau_cov={tau_cov} tau_v={tau_v}", flush=True)
+    c, s, p, g, q, qd, mass = _needle_state(seq)
+    fl = kvq.select_blocks(p, mass, seq, tau_cov)
+    torch.cuda.synchronize()
+    f0 = fl.cpu().numpy().copy()
+    kvq.promote_values(p, g, mass, seq, tau_v, fl)
+    torch.cuda.synchronize()
+    got = fl.cpu().numpy()
+    m32 = mass.cpu().numpy()
+    want = adaptive.promote_values(m32, _ev(c, g), np.array(seq), tau_v, c["Hkv"], f0)
+    assert np.array_equal(got, want)
+    nval = int(((got & 3) == 2).sum())
+    print(f"[adaptive] {int((got & 1).sum())} blocks promoted, {nval} value-promoted of {got.size}", flush=True)
+    # the oracle's own fp64 masses and descriptors choose the same blocks away from the threshold
+    oc = oracle_view_of_gpu(c, g)
+    ref_mass = adaptive.block_mass(oc, q, c["dtype"], np.array(seq), c["rotation"], s)
+    desc = bound.block_descriptors(oc, c["dtype"], c["rotation"], s)
+    G = c["Hq"] // c["Hkv"]
+    prod = (ref_mass.reshape(c["B"], c["Hkv"], G, -1) * desc[..., 1][:, :, None, :]).max(axis=2)
+    nb = np.array([(t + 63) // 64 for t in seq])
+    live = (np.arange(prod.shape[-1])[None, None, :] < nb[:, None, None]) & ((f0 & 1) == 0)
+    sure = live & (np.abs(prod - tau_v) > 0.02 * tau_v + 1e-12)
+    assert np.array_equal(((got & 2) != 0)[sure], (prod > tau_v)[sure])
+    if tau_v > 0 and tau_cov < 0.9:
+        assert nval > 0, "the case must promote some values"
+
+
+def test_value_promoted_decode_matches_oracle():
+    seq = [4096, 3000]
+    print("[adaptive] decode with value-only flags", flush=True)
+    c, s, p, g, q, qd, mass = _needle_state(seq)
+    fl = kvq.select_blocks(p, mass, seq, 0.5)
+    kvq.promote_values(p, g, mass, seq, 1e-4, fl)
+    out, cert = kvq.decode_attn(p, g, qd, seq, flags=fl, certificate=True)
+    torch.cuda.synchronize()
+    fln = fl.cpu().numpy()
+    assert ((fln & 3) == 2).any() and ((fln & 1) != 0).any()
+    oc = oracle_view_of_gpu(c, g)
+    ref, pmass = attention.decode_attention(oc, q, c["dtype"], np.array(seq), c["rotation"], s, flags=fln)
+    err = attention.row_rel_err(out.cpu().numpy(), ref)
+    print(f"[adaptive] value-only flags: max row rel err {err.max():.3e}", flush=True)
+    assert err.max() <= TOL
+    desc = bound.block_descriptors(oc, c["dtype"], c["rotation"], s)
+    E_or = bound.certificate(desc, q, c["dtype"], np.array(seq), fln, pmass)
+    E = cert.cpu().numpy()
+    assert np.all(E >= E_or * (1 - 1e-5)) and np.all(E <= E_or * (1 + 2.0 ** -7) + 1e-9)
+    # value promotion must lower the certificate against the same keys without it
+    _, cert0 = kvq.decode_attn(p, g, qd, seq, flags=torch.from_numpy(fln & 1).cuda(), certificate=True)
+    torch.cuda.synchronize()
+    assert np.all(E <= cert0.cpu().numpy() * (1 + 1e-6))
+
+
+# (with both sequences whole, the near-tie needles of sequence 1's first kv head are in range)
+@pytest.mark.parametrize("tau_cov,margin,max_inv,seq", [(0.995, 0.0, 0, [4096, 4096]), (0.995, 0.05, 0, [4096, 3000]),
+                                                        (1.0, 0.0, 3, [4096, 3000])])
+def test_ranking_check_matches_oracle(tau_cov, margin, max_inv, seq):
+    print(f"[adaptive] ranking check tau_cov={tau_cov} margin={margin} max_inv={max_inv}", flush=True)
+    c, s, p, g, q, qd, mass = _needle_state(seq)
+    inv, fail = kvq.ranking_check(p, g, qd, seq, mass, tau_cov, margin, max_inv)
+    torch.cuda.synchronize()
+    got, gfail = inv.cpu().numpy(), fail.cpu().numpy()
+    oc = oracle_view_of_gpu(c, g)
+    score = adaptive.block_scores_fp16(oc.k_orig, q, c["dtype"], np.array(seq))
+    lo, hi = adaptive.ranking_inversions(mass.cpu().numpy(), score, np.array(seq), tau_cov, margin, window=WIN)
+    print(f"[adaptive] inversions: max {got.max()}, heads with some {int((got > 0).sum())} of {got.size}, "
+          f"undecided pairs in {int((lo != hi).sum())} heads", flush=True)
+    assert np.all((lo <= got) & (got <= hi)), (got, lo, hi)
+    assert np.array_equal(gfail != 0, got > max_inv)
+    decided = (lo > max_inv) == (hi > max_inv)
+    assert np.array_equal((gfail != 0)[decided], (lo > max_inv)[decided])
+    if tau_cov == 0.995 and margin == 0.0:
+        assert (got > 0).any(), "the near ties of the needle workload invert some heads"
+        assert np.array_equal(gfail != 0, got > 0)
+
+
+def test_ranking_check_empty_and_short_sequences():
+    seq = [0, 70]
+    c, s, p, g, q, qd, mass = _needle_state(seq)
+    inv, fail = kvq.ranking_check(p, g, qd, seq, mass, 1.0, 0.0, 0)
+    torch.cuda.synchronize()
+    oc = oracle_view_of_gpu(c, g)
+    score = adaptive.block_scores_fp16(oc.k_orig, q, c["dtype"], np.array(seq))
+    lo, hi = adaptive.ranking_inversions(mass.cpu().numpy(), score, np.array(seq), 1.0, 0.0, window=WIN)
+    got = inv.cpu().numpy()
+    assert not got[0].any() and not fail.cpu().numpy()[0].any()
+    assert np.all((lo <= got) & (got <= hi))
+
+
+@pytest.mark.parametrize("tau_cov,tau_v,eps", [(0.995, 1e-6, 1e-3), (0.9, 1e-5, 0.0)])
+def test_adaptive_ladder_with_needles(tau_cov, tau_v, eps):
+    seq = [4096, 4096]
+    print(f"[adaptive] needle ladder tau_cov={tau_cov} tau_v={tau_v} eps={eps}", flush=True)
+    c, s, p, g, q, qd, mass = _needle_state(seq)
+    _, bflags = kvq.error_bound(p, g, qd, seq, c["tau"])
+    flags = kvq.select_blocks(p, mass, seq, tau_cov, flags_in=bflags)
+    kvq.promote_values(p, g, mass, seq, tau_v, flags)
+    inv, fail = kvq.ranking_check(p, g, qd, seq, mass, tau_cov, 0.0, 0)
+    out, cert = kvq.decode_attn(p, g, qd, seq, flags=flags, certificate=True)
+    torch.cuda.synchronize()
+    out0, cert0, fl0 = out.cpu().numpy().copy(), cert.cpu().numpy().copy(), fail.cpu().numpy().copy()
+    m32 = mass.cpu().numpy()
+    want = adaptive.promote_values(m32, _ev(c, g), np.array(seq), tau_v,
+                                   c["Hkv"], adaptive.select_blocks(m32, np.array(seq), tau_cov, c["Hkv"],
+                                                                    bflags.cpu().numpy()))
+    fln = flags.cpu().numpy()
+    assert np.array_equal(fln, want)
+    # peaked attention: every head's top-K* is a handful of blocks
+    kstar = max(len(adaptive.top_blocks(m32[b, hq], 64, tau_cov)) for b in range(2) for hq in range(c["Hq"]))
+    print(f"[adaptive] largest K* {kstar}; promoted {int((fln & 1).sum())}, value-only "
+          f"{int(((fln & 3) == 2).sum())}, bound {int(bflags.sum().item())} of {fln.size}; "
+          f"{int(fl0.sum())} heads fail the ranking check", flush=True)
+    assert kstar <= 6
+    oc = oracle_view_of_gpu(c, g)
+    ref, pmass = attention.decode_attention(oc, q, c["dtype"], np.array(seq), c["rotation"], s, flags=fln)
+    assert attention.row_rel_err(out0, ref).max() <= TOL
+    kvq.dense_fallback(p, g, qd, seq, eps, out, cert, fail=fail)
+    torch.cuda.synchronize()
+    out1, cert1 = out.cpu().numpy(), cert.cpu().numpy()
+    dense = attention.dense_attention(oc.k_orig, oc.v_orig, q, c["dtype"], np.array(seq))
+    want_out, want_cert, redo = adaptive.dense_fallback(out0, cert0, eps, dense, fl0)
+    assert np.array_equal(cert1, want_cert.astype(np.float32))
+    assert np.array_equal(out1[~redo], out0[~redo])
+    if redo.any():
+        assert attention.row_rel_err(out1[redo], dense[redo]).max() <= TOL
+    exact = np.where(redo[..., None], dense, ref)
+    assert np.all(np.linalg.norm(exact - dense, axis=-1) <= want_cert + 1e-12)
+
+
+def test_fallback_on_failed_heads_only():
+    # certificate NULL: only the check's fail flags trigger the recompute
+    seq = [4096, 2500]
+    c, s, p, g, q, qd, mass = _needle_state(seq)
+    out = kvq.decode_attn(p, g, qd, seq)
+    torch.cuda.synchronize()
+    out0 = out.cpu().numpy().copy()
+    fail = torch.zeros((c["B"], c["Hq"]), dtype=torch.uint8, device="cuda")
+    fail[0, 3] = 1
+    fail[1, 17] = 1
+    kvq.dense_fallback(p, g, qd, seq, 0.0, out, None, fail=fail)
+    torch.cuda.synchronize()
+    out1 = out.cpu().numpy()
+    oc = oracle_view_of_gpu(c, g)
+    dense = attention.dense_attention(oc.k_orig, oc.v_orig, q, c["dtype"], np.array(seq))
+    redo = fail.cpu().numpy() != 0
+    assert np.array_equal(out1[~redo], out0[~redo])
+    assert attention.row_rel_err(out1[redo], dense[redo]).max() <= TOL

@@ -243,3 +243,12 @@ def test_dense_fallback_takes_failed_heads_too():
     assert redo.tolist() == [[True, True, False]]
     assert o[0, 0].tolist() == [7.0, 7.0] and o[0, 2].tolist() == [1.0, 1.0]
     assert c.tolist() == [[0.0, 0.0, 0.2]]
+
+
+def test_select_blocks_keeps_value_bits_of_the_given_flags():
+    # a value-promoted block (2) that the top-K* then promotes becomes 3; others keep theirs
+    mass = np.zeros((1, 1, 3), np.float32)
+    mass[0, 0] = [1.0, 0.0, 0.0]
+    fl_in = np.array([[[2, 2, 1]]], np.uint8)
+    got = adaptive.select_blocks(mass, np.array([192]), 0.5, 1, fl_in)
+    assert got.tolist() == [[[3, 2, 1]]]
