@@ -269,8 +269,8 @@ def bench_workload(cfg_id, args):
                  for i in range(nfill)]
     nn = int(c.get("needles", 0))
     if nn:
-        nu = torch.randn((B, H, 128), generator=g, device=dev, dtype=torch.float64)
-        nu /= nu.norm(dim=-1, keepdim=True)
+        ndir = torch.randn((B, H, 128), generator=g, device=dev, dtype=torch.float64)
+        ndir /= ndir.norm(dim=-1, keepdim=True)
         nlog = (c["needle_top"] + torch.rand((B, H, 1), generator=g, device=dev, dtype=torch.float64) - 0.5
                 - torch.arange(nn, device=dev, dtype=torch.float64))
         tie = (torch.arange(B * H, device=dev) % c["needle_tie_every"] == 0).view(B, H)
@@ -288,7 +288,7 @@ def bench_workload(cfg_id, args):
                 for i in range(nn):
                     here = (npos[..., i] // P == piece)[..., None, None]
                     idx = (npos[..., i] % P)[..., None, None].expand(B, H, 1, 128)
-                    key = (nlog[..., i, None] * math.sqrt(128) / c["needle_q"] * nu).float()[:, :, None, :]
+                    key = (nlog[..., i, None] * math.sqrt(128) / c["needle_q"] * ndir).float()[:, :, None, :]
                     x.scatter_(2, idx, torch.where(here, key, x.gather(2, idx)))
             return x.half().view(torch.int16)
         if c["data"] == "anisotropic":
@@ -326,7 +326,7 @@ def bench_workload(cfg_id, args):
     progress("caches filled")
     q = torch.randn((B, Hq, 128), generator=g, device=dev)
     if nn:
-        uq = nu.float().repeat_interleave(Hq // H, dim=1)
+        uq = ndir.float().repeat_interleave(Hq // H, dim=1)
         q = c["needle_q"] * uq + q - (q * uq).sum(-1, keepdim=True) * uq
     q = (q.bfloat16() if c["dtype"] == "bf16" else q.half()).view(torch.int16)
     seq = [T] * B
@@ -517,7 +517,7 @@ def adaptive_ladder(args, c, p, caches, q, seq, ws, out, cert, bnd, flg, batch_t
         if "decode" in which:
             kvq.decode_attn(p, cc, q, seq, flags=prom, certificate=True, ws=ws, out=out, cert=cert)
         if "fallback" in which:
-            kvq.dense_fallback(p, cc, q, seq, eps, out, cert, fail=fail)
+            kvq.dense_fallback(p, cc, q, seq, eps, out, cert, fail=fail, ws=ws)
 
     allst = ("bound", "mass", "select", "promote", "rank", "decode", "fallback")
     for i in range(nrot):

@@ -92,7 +92,8 @@ def lib():
         L.kvq_ranking_check.argtypes = [P(Params), P(CacheStruct), vp, P(i32), vp, ctypes.c_float, ctypes.c_float,
                                         i32, vp, vp, vp]
         L.kvq_dense_fallback.restype = i32
-        L.kvq_dense_fallback.argtypes = [P(Params), P(CacheStruct), vp, P(i32), ctypes.c_float, vp, vp, vp, vp]
+        L.kvq_dense_fallback.argtypes = [P(Params), P(CacheStruct), vp, P(i32), ctypes.c_float, vp, vp, vp, vp,
+                                         ctypes.c_size_t, vp]
         L.kvq_calibrate_lambda.restype = i32
         L.kvq_calibrate_lambda.argtypes = [P(Params), P(CacheStruct), vp, vp, i32, vp, vp, vp]
         L.kvq_calibrate_clip.restype = i32
@@ -303,12 +304,15 @@ def ranking_check(p, cache, q, seq_len, mass, tau_cov, margin=0.0, max_inversion
     return inv, fl
 
 
-def dense_fallback(p, cache, q, seq_len, eps, out, cert, fail=None, stream=None):
+def dense_fallback(p, cache, q, seq_len, eps, out, cert, fail=None, ws=None, stream=None):
     """kvq_dense_fallback: rows with cert > eps, or fail set, recomputed densely from the
     originals (in place; cert may be None when fail is given)."""
+    if ws is None:
+        ws = workspace(p, q.device)
     cs = cache.struct()
     _check(lib().kvq_dense_fallback(ctypes.byref(p), ctypes.byref(cs), _ptr(q), _i32(seq_len), float(eps),
-                                    _ptr(fail), _ptr(out), _ptr(cert), stream if stream is not None else _stream()))
+                                    _ptr(fail), _ptr(out), _ptr(cert), _ptr(ws), ws.numel() * ws.element_size(),
+                                    stream if stream is not None else _stream()))
     return out, cert
 
 

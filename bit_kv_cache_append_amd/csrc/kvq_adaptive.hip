@@ -2,8 +2,10 @@
 // Methodology section 3: a light scoring pass estimates every block's attention
 // mass from the quantized keys, the top-K* blocks covering a fraction tau_cov of
 // it are promoted to the full-precision originals (through the decode pass's
-// exact-recompute flags), and a head whose certificate still exceeds a tolerance
-// is recomputed with dense attention over the originals.
+// exact-recompute flags), blocks whose value error is large against their mass take
+// exact values, and the ranking of each head's promoted blocks is checked against
+// the originals.  (The dense recompute of a head is the fp16 decode's split kernel,
+// restricted to the heads that need it.)
 #include <algorithm>
 
 #include "kvq_common.h"
@@ -594,93 +596,6 @@ __global__ __launch_bounds__(NTA) void rank_kernel(AdaptArgs a) {
   }
 }
 
-// Dense fallback of one (sequence, query head): if its certificate exceeds eps or it
-// failed the ranking check, exact attention over the originals (original basis, no
-// rotation), and the certificate becomes 0.  One workgroup per row; wave w takes blocks w, w + 4, ...
-// with a running max and sum, and the waves are merged at the end.
-__global__ __launch_bounds__(NTA) void fallback_kernel(AdaptArgs a) {
-  __shared__ float qs[D];
-  __shared__ float pb[4][TILE];
-  __shared__ float wm[4], wl[4];
-  __shared__ float wo[4][D];
-  const int row = blockIdx.x, b = row / a.Hq, hq = row % a.Hq, h = hq / a.G;
-  const bool redo = (a.cert != nullptr && a.cert[row] > a.eps) || (a.fail_in != nullptr && a.fail_in[row] != 0);
-  if (!redo) return;  // uniform over the workgroup
-  const int T = a.seq.v[b];
-  const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
-  const bool bf16 = a.in_bf16 != 0;
-  if (t < D) qs[t] = widen(a.q[(size_t)row * D + t], bf16) * a.scale;
-  __syncthreads();
-  const size_t stream = (size_t)b * a.H + h;
-  const int nchunks = (T + TILE - 1) / TILE;
-  float m = NEG_INF_A, l = 0.0f, o0 = 0.0f, o1 = 0.0f;
-  for (int c = wv; c < nchunks; c += 4) {
-    const int tok = c * TILE + lane;
-    const uint4* kp = reinterpret_cast<const uint4*>(a.k_orig + (stream * a.Tmax + tok) * D);
-    uint4 kr[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) kr[i] = kp[i];
-    float lg = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t w4[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int ch = 8 * i + 2 * e;
-        lg = fmaf(qs[ch], widen((uint16_t)(w4[e] & 0xFFFF), bf16), lg);
-        lg = fmaf(qs[ch + 1], widen((uint16_t)(w4[e] >> 16), bf16), lg);
-      }
-    }
-    if (tok >= T) lg = NEG_INF_A;
-    const float m_new = fmaxf(m, wmax(lg));
-    const float alpha = m == NEG_INF_A ? 0.0f : expf(m - m_new);
-    const float p = tok < T ? expf(lg - m_new) : 0.0f;
-    l = l * alpha + wsum(p);
-    o0 *= alpha;
-    o1 *= alpha;
-    m = m_new;
-    pb[wv][lane] = p;
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    const uint32_t* vp = reinterpret_cast<const uint32_t*>(a.v_orig + (stream * a.Tmax + (size_t)c * TILE) * D) + lane;
-    for (int t0 = 0; t0 < TILE; t0 += 16) {
-      uint32_t vr[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) vr[k] = vp[(size_t)(t0 + k) * (D / 2)];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float pk = pb[wv][t0 + k];
-        o0 = fmaf(pk, widen((uint16_t)(vr[k] & 0xFFFF), bf16), o0);
-        o1 = fmaf(pk, widen((uint16_t)(vr[k] >> 16), bf16), o1);
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-  if (lane == 0) {
-    wm[wv] = m;
-    wl[wv] = l;
-  }
-  wo[wv][2 * lane] = o0;
-  wo[wv][2 * lane + 1] = o1;
-  __syncthreads();
-  if (wv == 0) {
-    float M = NEG_INF_A;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w]);
-    float L = 0.0f, r0 = 0.0f, r1 = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float e = wm[w] == NEG_INF_A ? 0.0f : expf(wm[w] - M);
-      L += e * wl[w];
-      r0 += e * wo[w][2 * lane];
-      r1 += e * wo[w][2 * lane + 1];
-    }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    *reinterpret_cast<float2*>(a.out + (size_t)row * D + 2 * lane) = make_float2(r0 * inv, r1 * inv);
-    if (lane == 0 && a.cert != nullptr) a.cert[row] = 0.0f;
-  }
-}
-
 }  // namespace
 
 hipError_t launch_block_mass(const AdaptArgs& a, hipStream_t s) {
@@ -709,11 +624,6 @@ hipError_t launch_select(const AdaptArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(select_kernel, dim3(a.B * a.Hq), dim3(NTA), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_fallback(const AdaptArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(fallback_kernel, dim3(a.B * a.Hq), dim3(NTA), 0, s, a);
   return hipGetLastError();
 }
 

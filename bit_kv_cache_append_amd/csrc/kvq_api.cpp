@@ -2,6 +2,7 @@
 // Nothing here allocates memory; every launch goes onto the caller's stream.
 
 #include <math.h>
+#include <algorithm>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -144,9 +145,19 @@ int units_of(const kvq_params* p) {
   return p->batch * p->n_kv_heads * ((G + 3) / 4);
 }
 
+// The dense fallback recomputes a few rows, so it splits each of their sequences finely
+// (chunks of 8 or more 64-token blocks, at most 16 splits) to spread them over the CUs.
+int fallback_splits(int max_chunks) {
+  int s = max_chunks / 8;
+  if (s < 1) s = 1;
+  if (s > 16) s = 16;
+  return s;
+}
+
 int max_splits_for(const kvq_params* p) {
   const int a = choose_splits(p, p->max_ctx / TILE, false), b = choose_splits(p, p->max_ctx / TILE, true);
-  return a > b ? a : b;
+  const int c = p->keep_fp16_copy ? fallback_splits(p->max_ctx / TILE) : 1;
+  return std::max(a, std::max(b, c));
 }
 
 }  // namespace
@@ -575,25 +586,44 @@ kvq_status kvq_ranking_check(const kvq_params* p, const kvq_cache* c, const void
 }
 
 kvq_status kvq_dense_fallback(const kvq_params* p, const kvq_cache* c, const void* q, const int32_t* seq_len_host,
-                              float eps, const uint8_t* head_fail, float* out, float* certificate, void* stream) {
+                              float eps, const uint8_t* head_fail, float* out, float* certificate, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   kvq_status st = check_params(p);
   if (st) return st;
   if ((st = check_cache(p, c, true))) return st;
   if (!q || !out) return fail(KVQ_ERR_INVALID_ARG, "q/out are NULL");
   if (!certificate && !head_fail) return fail(KVQ_ERR_INVALID_ARG, "certificate and fail are both NULL");
   if (!(eps >= 0.0f)) return fail(KVQ_ERR_INVALID_ARG, "eps must be >= 0");
-  AdaptArgs a;
+  const size_t need = kvq_decode_workspace_bytes(p);
+  if (!workspace || workspace_bytes < need)
+    return fail(KVQ_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  if (((uintptr_t)workspace & 255u) != 0) return fail(KVQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  DecodeArgs a;
   memset(&a, 0, sizeof(a));
   if ((st = check_seq(p, seq_len_host, a.seq))) return st;
-  adapt_common(p, a);
+  int max_chunks = 0;
+  for (int b = 0; b < p->batch; ++b) max_chunks = std::max(max_chunks, (a.seq.v[b] + TILE - 1) / TILE);
   a.q = (const uint16_t*)q;
   a.k_orig = (const uint16_t*)c->k_orig;
   a.v_orig = (const uint16_t*)c->v_orig;
+  a.part = (float*)((char*)workspace + ctr_bytes(p));
   a.out = out;
-  a.cert = certificate;
-  a.fail_in = head_fail;
-  a.eps = eps;
-  hipError_t e = launch_fallback(a, (hipStream_t)stream);
+  a.fb_cert = certificate;
+  a.fb_fail = head_fail;
+  a.fb_eps = eps;
+  a.B = p->batch;
+  a.Hq = p->n_q_heads;
+  a.H = p->n_kv_heads;
+  a.G = p->n_q_heads / p->n_kv_heads;
+  a.Tmax = p->max_ctx;
+  a.nt = p->max_ctx / TILE;
+  a.in_bf16 = p->in_dtype == KVQ_BF16;
+  a.rotation = KVQ_ROT_NONE;
+  a.n_splits = fallback_splits(max_chunks > 0 ? max_chunks : 1);
+  a.chunks_per_split = std::max(1, (max_chunks + a.n_splits - 1) / a.n_splits);
+  a.U = units_of(p);
+  a.scale = softmax_scale(p);
+  hipError_t e = launch_dense_fallback(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "fallback launch");
   return KVQ_OK;
 }

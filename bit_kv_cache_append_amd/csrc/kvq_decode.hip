@@ -331,14 +331,16 @@ struct __align__(16) DecodeSmem {
   int last;                          // this workgroup is the last of its unit's to finish
 };
 
-// The fp16/bf16 baseline's shared memory, padded so that at most two of its workgroups
-// share a CU (160 KiB of LDS): with more of them resident at once the streams of V rows
-// compete for the CU's memory pipeline and the kernel runs at half the speed.
+// The fp16/bf16 decode's shared memory (the same-shape baseline and the dense fallback
+// of the adaptive ladder), padded so that at most two of its workgroups share a CU (160
+// KiB of LDS): with more of them resident at once their streams of rows compete for the
+// CU's memory pipeline.
 struct __align__(16) DenseSmem {
   float qo[4][D];
+  uint4 qhl[4][32];  // per head and 4-channel step: fp16 high parts, then fp16 low parts
   float pb[4][TILE][4];
   MergeArea<4> mrg;
-  uint8_t pad[56 * 1024];
+  uint8_t pad[52 * 1024];
 };
 
 // ------------------------------------------------------------------ prologue
@@ -700,15 +702,27 @@ __device__ void combine_row(const DecodeArgs& a, int row, float* zsw, const floa
   }
 }
 
-// The separate combine launch (fp16 baseline path): one wave per row, ordered
-// after every split workgroup by the stream.
-template <bool CERT>
+// Rows the dense fallback recomputes: certificate above eps, or failed the ranking check.
+__device__ __forceinline__ bool fallback_row(const DecodeArgs& a, size_t row) {
+  return (a.fb_cert != nullptr && a.fb_cert[row] > a.fb_eps) || (a.fb_fail != nullptr && a.fb_fail[row] != 0);
+}
+
+// The separate combine launch of the fp16/bf16 decode: one wave per row, ordered after
+// every split workgroup by the stream.  FB: the dense fallback, which writes only the
+// rows it recomputes and sets their certificate to 0.
+template <bool FB>
 __global__ __launch_bounds__(NT) void combine_kernel(DecodeArgs a) {
   __shared__ float zs[4][D];
   const int w = threadIdx.x >> 6;
   const int row = blockIdx.x * 4 + w;
   if (row >= a.B * a.Hq) return;  // whole waves; no barrier in combine_row
-  combine_row<CERT, false>(a, row, zs[w], nullptr);  // the fp16 baseline has no rotation
+  if constexpr (FB) {
+    if (!fallback_row(a, (size_t)row)) return;
+  }
+  combine_row<false, false>(a, row, zs[w], nullptr);  // no rotation on this path
+  if constexpr (FB) {
+    if (a.fb_cert != nullptr && (threadIdx.x & 63) == 0) a.fb_cert[row] = 0.0f;
+  }
 }
 
 // ------------------------------------------------------------------ split kernel
@@ -1420,6 +1434,16 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
 // Same split structure over uncompressed [Tmax][128] fp16/bf16 K and V (no rotation).
 // QK^T: 4x4x4 fp16 MFMA (lane 4s+r loads token 4s+r); PV: each lane owns channels
 // 2l, 2l+1 and accumulates p * v with the probabilities broadcast through LDS.
+// Decode over uncompressed fp16/bf16 K/V (layout of k_orig/v_orig, original basis): one
+// workgroup of 4 waves per (sequence, kv head, group of 4 query heads, split), wave w
+// taking the split's chunks w, w + 4, ...  Per chunk a wave issues all its loads at once
+// (lane t: the key row of token t; lane l: channels 2l, 2l+1 of the 64 value rows), so
+// a whole chunk is in flight per wave.  QK^T on fp16 MFMA with the query split into an
+// fp16 high part and the fp16 rounding of the remainder (two products, fp32
+// accumulation: the logits carry the fp32 query to about 2^-22), softmax in the exp2
+// domain, PV in fp32 on the vector ALUs from the probabilities in LDS.  FB: the dense
+// fallback, which skips the units none of whose rows needs recomputing.
+template <bool FB>
 __global__ __launch_bounds__(NT, 2) void decode_dense_split(DecodeArgs a) {
   __shared__ DenseSmem sm;
   const int b = blockIdx.z;
@@ -1427,6 +1451,11 @@ __global__ __launch_bounds__(NT, 2) void decode_dense_split(DecodeArgs a) {
   const int hkv = blockIdx.y / HG, hg = blockIdx.y % HG;
   const int hq0 = hkv * a.G + hg * 4;
   const int nh = min(4, a.G - hg * 4);
+  if constexpr (FB) {
+    bool any = false;
+    for (int hh = 0; hh < nh; ++hh) any = any || fallback_row(a, (size_t)b * a.Hq + hq0 + hh);
+    if (!any) return;  // uniform over the workgroup
+  }
   const int split = blockIdx.x;
   const int T = a.seq.v[b];
   const int nchunks = (T + TILE - 1) / TILE;
@@ -1444,25 +1473,35 @@ __global__ __launch_bounds__(NT, 2) void decode_dense_split(DecodeArgs a) {
       x0 = widen(qp[2 * l], bf16);
       x1 = widen(qp[2 * l + 1], bf16);
     }
-    sm.qo[hh][2 * l] = x0 * (a.scale * LOG2E);
-    sm.qo[hh][2 * l + 1] = x1 * (a.scale * LOG2E);
+    x0 *= a.scale * LOG2E;
+    x1 *= a.scale * LOG2E;
+    sm.qo[hh][2 * l] = x0;
+    sm.qo[hh][2 * l + 1] = x1;
+    // query operand of step n (channels 4n..4n+3): lane l builds half of step l / 2
+    const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+    const _Float16 r0 = (_Float16)(x0 - (float)h0), r1 = (_Float16)(x1 - (float)h1);
+    uint32_t* qw = reinterpret_cast<uint32_t*>(&sm.qhl[hh][l >> 1]);
+    qw[l & 1] = as_u(h2{h0, h1});
+    qw[2 + (l & 1)] = as_u(h2{r0, r1});
   }
   __syncthreads();
-  // query operand: fp16 of (q * scale * log2e) for head j, channels 4n..4n+3
-  h4 qop[32];
-#pragma unroll
-  for (int n = 0; n < 32; ++n)
-    qop[n] = h4{(_Float16)sm.qo[j][4 * n], (_Float16)sm.qo[j][4 * n + 1], (_Float16)sm.qo[j][4 * n + 2],
-                (_Float16)sm.qo[j][4 * n + 3]};
   float m = NEG_INF, lsum = 0.0f;
   f4 o[2] = {f4{0, 0, 0, 0}, f4{0, 0, 0, 0}};
   for (int ch = c0 + wv; ch < c1; ch += 4) {
     const int tok0 = ch * TILE;
-    f4 acc = {0, 0, 0, 0};
+    const int nlive = T - tok0;  // rows below the sequence end (>= 1)
     const uint4* kp = reinterpret_cast<const uint4*>(a.k_orig + (stream * a.Tmax + tok0 + lane) * D);
+    const uint32_t* vp = reinterpret_cast<const uint32_t*>(a.v_orig + (stream * a.Tmax + tok0) * D) + lane;
+    uint4 kr[16];
+    uint32_t vr[TILE];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) kr[i] = kp[i];
+#pragma unroll
+    for (int tt = 0; tt < TILE; ++tt) vr[tt] = vp[(size_t)tt * (D / 2)];
+    f4 acc = {0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const uint4 u = kp[i];
+      const uint4 u = kr[i];
       h4 k0, k1;
       if (bf16) {
         const uint32_t w[4] = {u.x, u.y, u.z, u.w};
@@ -1478,12 +1517,15 @@ __global__ __launch_bounds__(NT, 2) void decode_dense_split(DecodeArgs a) {
         k0 = __builtin_bit_cast(h4, make_uint2(u.x, u.y));
         k1 = __builtin_bit_cast(h4, make_uint2(u.z, u.w));
       }
-      acc = __builtin_amdgcn_mfma_f32_4x4x4f16(k0, qop[2 * i], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_4x4x4f16(k1, qop[2 * i + 1], acc, 0, 0, 0);
+      const uint4 q0 = sm.qhl[j][2 * i], q1 = sm.qhl[j][2 * i + 1];
+      acc = __builtin_amdgcn_mfma_f32_4x4x4f16(k0, __builtin_bit_cast(h4, make_uint2(q0.x, q0.y)), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_4x4x4f16(k0, __builtin_bit_cast(h4, make_uint2(q0.z, q0.w)), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_4x4x4f16(k1, __builtin_bit_cast(h4, make_uint2(q1.x, q1.y)), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_4x4x4f16(k1, __builtin_bit_cast(h4, make_uint2(q1.z, q1.w)), acc, 0, 0, 0);
     }
     float l[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) l[r] = (tok0 + 4 * (lane >> 2) + r < T) ? acc[r] : NEG_INF;
+    for (int r = 0; r < 4; ++r) l[r] = (4 * (lane >> 2) + r < nlive) ? acc[r] : NEG_INF;
     float cmax = max_same_head(fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3])));
     const float m_new = fmaxf(m, cmax);
     const float alpha = (m_new == NEG_INF) ? 1.0f : exp2f(m - m_new);
@@ -1501,10 +1543,10 @@ __global__ __launch_bounds__(NT, 2) void decode_dense_split(DecodeArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) sm.pb[wv][4 * (lane >> 2) + r][j] = p[r];
     lds_wait();
-    const uint32_t* vp = reinterpret_cast<const uint32_t*>(a.v_orig + (stream * a.Tmax + tok0) * D) + lane;
-#pragma unroll 8
+#pragma unroll
     for (int tt = 0; tt < TILE; ++tt) {
-      const uint32_t vv = vp[(size_t)tt * (D / 2)];
+      // rows at or past the sequence end count as zeros (weight 0, whatever bits they hold)
+      const uint32_t vv = tt < nlive ? vr[tt] : 0u;
       const float v0 = widen((uint16_t)(vv & 0xFFFF), bf16), v1 = widen((uint16_t)(vv >> 16), bf16);
       const float4 pp = *reinterpret_cast<const float4*>(&sm.pb[wv][tt][0]);
       o[0] += f4{pp.x, pp.y, pp.z, pp.w} * v0;
@@ -1576,7 +1618,7 @@ hipError_t launch_decode(const DecodeArgs& a, int k_fmt, int v_fmt, bool dense, 
   const dim3 cgrid((a.B * a.Hq + 3) / 4);
   if (dense) {
     const dim3 dgrid(a.n_splits, a.H * HG, a.B);
-    hipLaunchKernelGGL(decode_dense_split, dgrid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL(decode_dense_split<false>, dgrid, dim3(NT), 0, s, a);
     hipLaunchKernelGGL(combine_kernel<false>, cgrid, dim3(NT), 0, s, a);
     return hipGetLastError();
   }
@@ -1615,5 +1657,15 @@ hipError_t launch_decode(const DecodeArgs& a, int k_fmt, int v_fmt, bool dense, 
   return hipErrorNotSupported;
 }
 
+
+// The dense fallback: the fp16/bf16 decode over the cache's originals, restricted to the
+// units holding a row to recompute (the others leave at once), then the combine of those
+// rows only.
+hipError_t launch_dense_fallback(const DecodeArgs& a, hipStream_t s) {
+  const int HG = (a.G + 3) / 4;
+  hipLaunchKernelGGL(decode_dense_split<true>, dim3(a.n_splits, a.H * HG, a.B), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL(combine_kernel<true>, dim3((a.B * a.Hq + 3) / 4), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
 
 }  // namespace kvq

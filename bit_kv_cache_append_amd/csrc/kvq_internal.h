@@ -84,24 +84,20 @@ struct AdaptArgs {
   const uint16_t* q;  // [B][Hq][128]
   const uint8_t* k_codes;
   const uint8_t* k_meta;
-  const uint16_t* k_orig;  // [B][H][Tmax][128] (fallback)
-  const uint16_t* v_orig;
+  const uint16_t* k_orig;  // [B][H][Tmax][128] (ranking check)
   const int8_t* signs;
   const uint16_t* rot;
   const float* lam_k;        // [H][128] per-channel rescale of the keys, or null
   float* mass;               // [B][Hq][nt]
   const uint8_t* flags_in;   // [B][H][nt] or null
   uint8_t* flags_out;        // [B][H][nt]
-  float* out;                // [B][Hq][128] (fallback)
-  float* cert;               // [B][Hq] (fallback; or null)
   const float* desc;         // [B][H][nt][3] (ek, ev, vn) (value promotion)
   int32_t* inv;              // [B][Hq] inverted pairs (ranking check)
   uint8_t* fail;             // [B][Hq] ranking check result
-  const uint8_t* fail_in;    // [B][Hq] heads to recompute (fallback; or null)
   int32_t B, Hq, H, G, Tmax, nt;
   int32_t in_bf16, rotation, k_fmt, k_group;
   int32_t max_inv;
-  float scale, tau_cov, eps, tau_v, margin;
+  float scale, tau_cov, tau_v, margin;
   float cos128[128];  // fl32(cos(2 pi k / 128)): the SRFT matrix entries
   SeqArray seq;
 };
@@ -141,6 +137,9 @@ struct DecodeArgs {
   int* ctr;                 // [U] split arrival counters per unit, zero between calls
   float* out;               // [B][Hq][128]
   float* cert;              // [B][Hq] or null
+  float* fb_cert;           // dense fallback: rows with fb_cert > fb_eps ... (or null)
+  const uint8_t* fb_fail;   // ... or fb_fail != 0 (or null) are recomputed; the others untouched
+  float fb_eps;
   int32_t B, Hq, H, G, Tmax, nt;
   int32_t in_bf16, rotation, k_group, v_group;
   int32_t n_splits, chunks_per_split;
@@ -161,7 +160,7 @@ hipError_t launch_decode(const DecodeArgs& a, int k_fmt, int v_fmt, bool dense, 
 hipError_t decode_scratch(void** ptr, hipStream_t s);
 hipError_t launch_block_mass(const AdaptArgs& a, hipStream_t s);
 hipError_t launch_select(const AdaptArgs& a, hipStream_t s);
-hipError_t launch_fallback(const AdaptArgs& a, hipStream_t s);
+hipError_t launch_dense_fallback(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_promote_values(const AdaptArgs& a, hipStream_t s);
 hipError_t launch_ranking_check(const AdaptArgs& a, hipStream_t s);
 

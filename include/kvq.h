@@ -200,8 +200,9 @@ const char* kvq_last_error(void);
  * (0 for buffers the configuration does not use).  Host only. */
 kvq_status kvq_buffer_bytes(const kvq_params* p, size_t* out_bytes);
 
-/* Workspace bytes kvq_decode_attn / kvq_decode_attn_dense need for these params
- * (depends on batch, heads and max_ctx only).  Host only; 0 on invalid params.
+/* Workspace bytes kvq_decode_attn / kvq_decode_attn_dense / kvq_dense_fallback need
+ * for these params (depends on batch, heads, max_ctx and keep_fp16_copy only).  Host
+ * only; 0 on invalid params.
  * The workspace holds one arrival counter per unit (sequence, kv head, group of 4
  * query heads), through which the last of the unit's workgroups learns that it is
  * last and merges the others' results, and one partial-result record per (sequence,
@@ -356,20 +357,24 @@ kvq_status kvq_ranking_check(const kvq_params* p, const kvq_cache* cache, const 
 /*
  * kvq_dense_fallback: for every (b, hq) with certificate[b][hq] > eps, or with
  * fail[b][hq] != 0, out[b][hq] is replaced by attention over k_orig/v_orig
- * (positions [0, seq_len_host[b]), fp32 arithmetic, original basis) and
- * certificate[b][hq] is set to 0; other rows are left unchanged.  Needs
- * keep_fp16_copy.  out/certificate: device, as written by kvq_decode_attn;
- * certificate may be NULL (then only fail triggers), fail may be NULL (then only
- * the certificate), not both.  eps >= 0.
+ * (positions [0, seq_len_host[b]), original basis; the same arithmetic as
+ * kvq_decode_attn_dense) and certificate[b][hq] is set to 0; other rows are left
+ * unchanged.  Needs keep_fp16_copy.  out/certificate: device, as written by
+ * kvq_decode_attn; certificate may be NULL (then only fail triggers), fail may be
+ * NULL (then only the certificate), not both.  eps >= 0.  workspace: as for
+ * kvq_decode_attn (its records are overwritten; its counters are not used).
  */
 kvq_status kvq_dense_fallback(const kvq_params* p, const kvq_cache* cache, const void* q,
                               const int32_t* seq_len_host, float eps, const uint8_t* fail, float* out,
-                              float* certificate, void* stream);
+                              float* certificate, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Decode attention over uncompressed K/V in the layout of k_orig/v_orig
  * ([B][Hkv][Tmax][128] in_dtype); no rotation.  Same q/out/workspace contract as
- * kvq_decode_attn.  Only the shape fields and in_dtype of p are used.
+ * kvq_decode_attn.  Only the shape fields and in_dtype of p are used.  Logits: the
+ * fp32 query times scale (split into an fp16 high part and the fp16 rounding of the
+ * remainder) against the keys in fp16 (bf16 keys rounded to fp16), fp32 accumulation;
+ * softmax and the value sums in fp32.
  */
 kvq_status kvq_decode_attn_dense(const kvq_params* p, const void* k, const void* v, const void* q,
                                  const int32_t* seq_len_host, float* out, void* workspace,

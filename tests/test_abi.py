@@ -122,7 +122,7 @@ def test_adaptive_entry_points_validate_without_gpu():
     # the dense fallback, value promotion and ranking check read the originals or the
     # descriptors: they need keep_fp16_copy
     st = L.kvq_dense_fallback(ctypes.byref(p), ctypes.byref(cs), fake, seq, ctypes.c_float(0.1), None, fake, fake,
-                              None)
+                              fake, 1 << 30, None)
     assert st == -1 and b"keep_fp16_copy" in L.kvq_last_error()
     st = L.kvq_promote_values(ctypes.byref(p), ctypes.byref(cs), fake, seq, ctypes.c_float(0.1), fake, None)
     assert st == -1 and b"keep_fp16_copy" in L.kvq_last_error()
@@ -134,8 +134,12 @@ def test_adaptive_entry_points_validate_without_gpu():
                          k_orig=fake, v_orig=fake)
     # the fallback needs at least one trigger: a certificate or the check's fail flags
     st = L.kvq_dense_fallback(ctypes.byref(kp), ctypes.byref(kc), fake, seq, ctypes.c_float(0.1), None, fake, None,
-                              None)
+                              fake, 1 << 30, None)
     assert st == -1 and b"both NULL" in L.kvq_last_error()
+    # and a workspace of kvq_decode_workspace_bytes
+    st = L.kvq_dense_fallback(ctypes.byref(kp), ctypes.byref(kc), fake, seq, ctypes.c_float(0.1), fake, fake, fake,
+                              fake, 256, None)
+    assert st == -3 and b"workspace" in L.kvq_last_error()
     for tau_cov, margin, max_inv, what in ((1.5, 0.0, 0, b"tau_cov"), (0.9, -1.0, 0, b"margin"),
                                            (0.9, float("inf"), 0, b"margin"), (0.9, 0.0, -1, b"max_inversions")):
         st = L.kvq_ranking_check(ctypes.byref(kp), ctypes.byref(kc), fake, seq, fake, ctypes.c_float(tau_cov),
