@@ -895,6 +895,10 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   const size_t stream = (size_t)b * a.H + hkv;
   constexpr int CDW = VFmt<VF>::CDW;
   constexpr int NGV = v_groups(VF, VG);
+  // PV weights p * s in two fp16 parts (about 2^-22 of themselves) for integer values, one
+  // fp16 rounding for FP4 values: with it their worst attention rows are ~3e-4 (the bar is
+  // 2e-3), and the second pair of products cost ~7 % of their decode time
+  constexpr bool PV_LO = VF != KVQ_FP4;
   // V scale group of channels 2*lane, 2*lane+1: 32-channel group, one per token, or 16-channel block
   const int vgrp = (VF == KVQ_FP4 || VG == 16) ? (lane >> 3) : (VG == 128) ? 0 : (lane >> 4);
   uint16_t* vml = &sm.vmeta[wv][0][0][0];
@@ -1169,10 +1173,10 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
       }
     }
     // ---- PV weights, formed here once per (token, V group): p * s in fp32 for this lane's
-    // four tokens (slice s_a, head j), split into an fp16 high part and the fp16 rounding
-    // of the remainder, so that the fp16 matrix products carry each weight to about
-    // 2^-22 of itself.  Positions past the sequence end have p = 0 and weight 0 (their
-    // metadata may be anything).
+    // four tokens (slice s_a, head j), rounded to fp16 and (PV_LO) the fp16 rounding of the
+    // remainder, so that the fp16 matrix products carry each weight to about 2^-22 of
+    // itself.  Positions past the sequence end have p = 0 and weight 0 (their metadata may
+    // be anything).
     // (scales are never negative, so max(p s, 0) changes no weight and turns the 0 * NaN of
     // a position past the end into 0)
     const uint2* vmw = reinterpret_cast<const uint2*>(vml) + s_a;
@@ -1185,10 +1189,14 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
       const float x0 = fmaxf(fmaf(p[0], (float)s01.x, 0.0f), 0.0f), x1 = fmaxf(fmaf(p[1], (float)s01.y, 0.0f), 0.0f);
       const float x2 = fmaxf(fmaf(p[2], (float)s23.x, 0.0f), 0.0f), x3 = fmaxf(fmaf(p[3], (float)s23.y, 0.0f), 0.0f);
       const h2 hi01 = {(_Float16)x0, (_Float16)x1}, hi23 = {(_Float16)x2, (_Float16)x3};
-      // the remainder x - hi is exact in fp32 (hi is x rounded to 11 bits)
-      const h2 lo01 = {(_Float16)fmaf((float)hi01.x, -1.0f, x0), (_Float16)fmaf((float)hi01.y, -1.0f, x1)};
-      const h2 lo23 = {(_Float16)fmaf((float)hi23.x, -1.0f, x2), (_Float16)fmaf((float)hi23.y, -1.0f, x3)};
-      sm.u.loop.pw[wv][g][s_a][j] = make_uint4(as_u(hi01), as_u(hi23), as_u(lo01), as_u(lo23));
+      if constexpr (PV_LO) {
+        // the remainder x - hi is exact in fp32 (hi is x rounded to 11 bits)
+        const h2 lo01 = {(_Float16)fmaf((float)hi01.x, -1.0f, x0), (_Float16)fmaf((float)hi01.y, -1.0f, x1)};
+        const h2 lo23 = {(_Float16)fmaf((float)hi23.x, -1.0f, x2), (_Float16)fmaf((float)hi23.y, -1.0f, x3)};
+        sm.u.loop.pw[wv][g][s_a][j] = make_uint4(as_u(hi01), as_u(hi23), as_u(lo01), as_u(lo23));
+      } else {
+        sm.u.loop.pw[wv][g][s_a][j] = make_uint4(as_u(hi01), as_u(hi23), 0u, 0u);
+      }
     }
     if constexpr (VF == KVQ_INT2) {
       // zero points: sum_t p_t z_(t, g) per group in fp32, added to every channel of the
@@ -1211,11 +1219,14 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
     const uint4* pwv = &sm.u.loop.pw[wv][vgrp][0][j];
     auto pv_step = [&](int s, h4 B0, h4 B1) {
       const uint4 w = pwv[4 * s];
-      const h4 Ah = cat(as_h2(w.x), as_h2(w.y)), Al = cat(as_h2(w.z), as_h2(w.w));
+      const h4 Ah = cat(as_h2(w.x), as_h2(w.y));
       o[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(Ah, B0, o[0], 0, 0, 0);
       o[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(Ah, B1, o[1], 0, 0, 0);
-      o[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(Al, B0, o[0], 0, 0, 0);
-      o[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(Al, B1, o[1], 0, 0, 0);
+      if constexpr (PV_LO) {
+        const h4 Al = cat(as_h2(w.z), as_h2(w.w));
+        o[0] = __builtin_amdgcn_mfma_f32_4x4x4f16(Al, B0, o[0], 0, 0, 0);
+        o[1] = __builtin_amdgcn_mfma_f32_4x4x4f16(Al, B1, o[1], 0, 0, 0);
+      }
     };
     if constexpr (VF == KVQ_FP4) {
       // tokens 4s..4s+3 of step s are the byte pairs 2(s&1), 2(s&1)+1 of word s/2
@@ -1430,10 +1441,7 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ dense fp16 baseline
-// Same split structure over uncompressed [Tmax][128] fp16/bf16 K and V (no rotation).
-// QK^T: 4x4x4 fp16 MFMA (lane 4s+r loads token 4s+r); PV: each lane owns channels
-// 2l, 2l+1 and accumulates p * v with the probabilities broadcast through LDS.
+// ------------------------------------------------------------------ dense fp16 decode
 // Decode over uncompressed fp16/bf16 K/V (layout of k_orig/v_orig, original basis): one
 // workgroup of 4 waves per (sequence, kv head, group of 4 query heads, split), wave w
 // taking the split's chunks w, w + 4, ...  Per chunk a wave issues all its loads at once
