@@ -41,6 +41,10 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 MFMA_F32_PEAK_TFLOPS = 157.3
+# VALU issue peak without packed instructions (the build disables packed fp32): 256 CUs x
+# 4 SIMDs x 16 lanes per clock (one wave64 instruction per SIMD every 4 cycles) x 2.4 GHz,
+# in lane-instructions per second; the published 157.3 TFLOP/s counts packed fp32 FMAs
+VALU_PEAK_TLANES = 256 * 4 * 16 * 2.4e9 / 1e12
 METRIC = "decode-attn effective KV GB/s & % HBM peak (int4 vs fp16); append Mvec/s"
 NROT = 4
 
@@ -119,6 +123,27 @@ def kernel_traffic(roofline_kernel_src):
     if rec.get("kernel_source_sha256") != sha:
         return None
     return rec.get("hbm_bytes_per_call")
+
+
+def append_valu_roofline(key, app_s):
+    """VALU roofline of an append launch: the committed per-launch VALU instruction count of
+    this workload (SQ_INSTS_VALU, valid only for the kernel source it was taken on) x 64
+    lanes / the launch time measured here, against VALU_PEAK_TLANES; None without a record."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    try:
+        rec = json.load(open(os.path.join(here, "profiles", "append_valu.json")))
+        sha = hashlib.sha256(open(os.path.join(here, rec["kernel_source"]), "rb").read()).hexdigest()
+    except (OSError, ValueError, KeyError):
+        return None
+    w = rec.get("workloads", {}).get(key)
+    if rec.get("kernel_source_sha256") != sha or w is None:
+        return None
+    achieved = w["valu_wave_instr_per_launch"] * 64 / app_s / 1e12
+    return {"bound": "alu", "achieved": round(achieved, 2), "peak": round(VALU_PEAK_TLANES, 2),
+            "unit": "T VALU lane-instructions/s", "frac": round(achieved / VALU_PEAK_TLANES, 4),
+            "kernel": w["kernel"], "valu_wave_instr_per_launch": w["valu_wave_instr_per_launch"],
+            **({"note": w["note"]} if "note" in w else {})}
 
 
 def _cpu_model():
@@ -467,13 +492,12 @@ def bench_workload(cfg_id, args):
         result["append_roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_F32_PEAK_TFLOPS,
                                      "unit": "TFLOP/s", "frac": round(tf / MFMA_F32_PEAK_TFLOPS, 4),
                                      "kernel": "append_dense_int2_kernel"}
-    elif c["k_fmt"] == "fp4" and c["scale_mode"] == "search9":
-        # the scale search is VALU work: per 16-element block and candidate scale, 7 compares and
-        # selects plus the squared error per element (see the FP4 quantizer); reported against the
-        # fp32 vector issue rate of 256 CUs x 4 SIMDs x 16 lanes at 2.4 GHz
-        result["append_roofline"] = {"bound": "alu", "achieved_gbs": round(app_bytes / app_s / 1e9, 1),
-                                     "hbm_frac": round(app_bytes / app_s / 1e9 / HBM_PEAK_GBS, 4),
-                                     "kernel": "append_fast_kernel<fp4, fp4>"}
+    else:
+        # the fast append is VALU work (the exact fp32 rotation, quotients and packing; for FP4
+        # the scale search): its instruction count per launch against the VALU issue peak
+        valu = append_valu_roofline(c["name"], app_s) if args.window is None else None
+        if valu is not None:
+            result["append_roofline"] = valu
     if args.adaptive is not None:
         result["adaptive"] = adaptive_ladder(args, c, p, caches, q, seq, ws, out, cert, bnd, flg, batch_time, n_each)
         # the same step without the ladder: the bound and the certified decode with its flags
@@ -737,6 +761,9 @@ def main():
         "input_gen_s": round(t_gen, 2),
     }
     result["roofline"]["traffic"] = kernel_traffic("bit_kv_cache_append_amd/csrc/kvq_decode.hip")
+    valu = append_valu_roofline(c["name"] + ("-srft" if args.rotation == "srft" else ""), app_s)
+    if valu is not None:
+        result["append_roofline"] = valu
     if args.copy_calibration:
         src = torch.full((256 << 20,), 3, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

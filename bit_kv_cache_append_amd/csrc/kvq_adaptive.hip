@@ -449,6 +449,50 @@ __global__ __launch_bounds__(NTA) void flags_init_kernel(AdaptArgs a) {
 // the choice is reproducible bit for bit.
 __device__ int sorted_top(const AdaptArgs& a, int row, int nb, unsigned long long* key, int* kstar) {
   const int t = threadIdx.x;
+  {
+    // Peaked heads first: up to FAST extractions of the largest remaining key (each thread
+    // holds up to 16 keys of blocks t, t + 256, ...; a wave reduction, then the four waves'
+    // best through LDS), the same additions in the same order as the walk over the sorted
+    // keys below.  Heads that are still short of tau_cov after FAST blocks take the sort.
+    constexpr int FAST = 32, PER = MAX_SELECT_BLOCKS / NTA;
+    __shared__ unsigned long long wbest[NTA / 64];
+    const float* mf = a.mass + (size_t)row * a.nt;
+    unsigned long long mine[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int j = t + NTA * i;
+      mine[i] = j < nb ? (((unsigned long long)__float_as_uint(mf[j]) << 32) | (0xFFFFFFFFu - (uint32_t)j)) : 0ull;
+    }
+    float run = 0.0f;
+    int k = 0;
+    bool done = false;
+    while (!done && k < FAST && k < nb) {
+      unsigned long long best = 0ull;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) best = mine[i] > best ? mine[i] : best;
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long other = __shfl_xor(best, o);
+        best = other > best ? other : best;
+      }
+      if ((t & 63) == 0) wbest[t >> 6] = best;
+      __syncthreads();
+#pragma unroll
+      for (int w = 0; w < NTA / 64; ++w) best = wbest[w] > best ? wbest[w] : best;
+      __syncthreads();  // wbest is rewritten by the next round
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (mine[i] == best) mine[i] = 0ull;  // keys are distinct: only the owner matches
+      if (t == 0) key[k] = best;
+      run = run + __uint_as_float((uint32_t)(best >> 32));
+      ++k;
+      done = run >= a.tau_cov;
+    }
+    if (done || k == nb) {
+      if (t == 0) *kstar = k;
+      __syncthreads();
+      return *kstar;
+    }
+  }
   int npow = 2;
   while (npow < nb) npow <<= 1;
   const float* m = a.mass + (size_t)row * a.nt;
