@@ -87,8 +87,6 @@ kvq_status check_cache(const kvq_params* p, const kvq_cache* c, bool need_desc) 
   // errors only for an orthogonal rotation, and the fp16-rounded dense matrix is not one.
   if (p->keep_fp16_copy && p->rotation == KVQ_ROT_DENSE)
     return fail(KVQ_ERR_UNSUPPORTED, "keep_fp16_copy (certified descriptors) is not supported with the dense rotation");
-  if (p->keep_fp16_copy && (c->lambda_k || c->lambda_v))
-    return fail(KVQ_ERR_UNSUPPORTED, "per-channel rescale factors are not supported with keep_fp16_copy");
   if (p->sink_blocks + p->recent_blocks > 0 &&
       (!c->k_win || !c->v_win || !aligned16(c->k_win) || !aligned16(c->v_win)))
     return fail(KVQ_ERR_INVALID_ARG, "a window (sink_blocks + recent_blocks > 0) needs k_win and v_win, 16-byte aligned");

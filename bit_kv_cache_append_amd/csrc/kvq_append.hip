@@ -101,12 +101,14 @@ __device__ __forceinline__ float rne_quot(float y, float sf, float r) {
 
 // ---------------------------------------------------------------- quantizers
 // Each returns packed code dwords for the lane's 32 channels, writes metadata
-// elements (fp16 bits or E4M3 codes) and the squared-residual partial sum.
+// elements (fp16 bits or E4M3 codes) and the squared-residual partial sum (each
+// residual times il[j] when il is given: with per-channel factors lambda, il = 1 /
+// lambda takes the residual back to the unscaled basis).
 
 // symmetric int4/int8; group 16 (two per lane), 32 (in-lane) or 128 (quad).
 // meta0/meta1: the scales of channels 0..15 and 16..31 of the lane (equal unless group 16)
 __device__ __forceinline__ void quant_sym(const float y[32], int qmax, int group, int codes[32],
-                                          uint16_t& meta0, uint16_t& meta1, float& res2) {
+                                          uint16_t& meta0, uint16_t& meta1, float& res2, const float* il) {
   float a[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int j = 0; j < 32; ++j) a[j >> 4] = fmaxf(a[j >> 4], fabsf(y[j]));
@@ -137,6 +139,7 @@ __device__ __forceinline__ void quant_sym(const float y[32], int qmax, int group
     if (s != 0.0f) c = fminf(fmaxf(rne_quot(y[j], s, r[j >> 4]), -qm), qm);
     codes[j] = (int)c;
     float d = y[j] - c * s;
+    if (il) d = d * il[j];
     acc = acc + d * d;
   }
   res2 = acc;
@@ -144,7 +147,7 @@ __device__ __forceinline__ void quant_sym(const float y[32], int qmax, int group
 
 // asymmetric int2, group 32, optional clamp to [-t_c, t_c] first
 __device__ __forceinline__ void quant_asym2(const float y[32], const float* clip, int codes[32], uint16_t& ms,
-                                            uint16_t& mz, float& res2) {
+                                            uint16_t& mz, float& res2, const float* il) {
   float yc[32];
 #pragma unroll
   for (int j = 0; j < 32; ++j) {
@@ -178,6 +181,7 @@ __device__ __forceinline__ void quant_asym2(const float y[32], const float* clip
     }
     codes[j] = (int)c;
     float d = y[j] - (c * sf + zf);  // residual against the unclipped value
+    if (il) d = d * il[j];
     acc = acc + d * d;
   }
   res2 = acc;
@@ -232,7 +236,7 @@ __device__ __forceinline__ float fp4_zero_err(const float* y) {
 // multiplicative search, the bit patterns c0 - 2 .. c0 + 6 of c0 = E4M3(t) (kept inside
 // 0x00..0x7E) for the offset search, c0 alone for absmax.
 __device__ __forceinline__ void quant_fp4(const float y[32], int mode, int codes[32], uint8_t sc[2],
-                                          float& res2) {
+                                          float& res2, const float* il) {
   const float mults[9] = {0.9f, 0.925f, 0.95f, 0.975f, 1.0f, 1.025f, 1.05f, 1.075f, 1.1f};
   float acc = 0.0f;
 #pragma unroll
@@ -276,6 +280,7 @@ __device__ __forceinline__ void quant_fp4(const float y[32], int mode, int codes
       int cd = codes[16 * blk + j];
       float v = e2m1_mag(cd & 7) * S;
       float d = fabsf(yb[j]) - v;
+      if (il) d = d * il[16 * blk + j];
       acc = acc + d * d;
     }
   }
@@ -554,11 +559,25 @@ __global__ __launch_bounds__(NT) void append_kernel(AppendArgs a) {
     for (int j = 0; j < 32; ++j) y[j] = x[j];
   }
 
-  // per-channel rescale ("When Quantization Is Free", Methodology sections 2-3), fp32
+  // norm of the rotated vector (descriptor slack), before any rescale
+  float ynorm2 = 0.0f;
+  if (a.desc) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) ynorm2 = ynorm2 + y[j] * y[j];
+  }
+  // per-channel rescale ("When Quantization Is Free", Methodology sections 2-3), fp32;
+  // with descriptors the residuals are taken back to the unscaled basis (times 1 / lambda)
+  float ilam[32];
+  const float* il = nullptr;
   if (const float* lam = tensor ? a.lam_v : a.lam_k) {
     const float* lp = lam + (size_t)h * D + 32 * q;
 #pragma unroll
     for (int j = 0; j < 32; ++j) y[j] = y[j] * lp[j];
+    if (a.desc) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) ilam[j] = 1.0f / lp[j];
+      il = ilam;
+    }
   }
 
   // quantize
@@ -566,13 +585,13 @@ __global__ __launch_bounds__(NT) void append_kernel(AppendArgs a) {
   uint16_t m0 = 0, m1 = 0;  // metadata elements of this lane
   float res2 = 0.0f;
   if (fmt == KVQ_INT4 || fmt == KVQ_INT8) {
-    quant_sym(y, fmt == KVQ_INT4 ? 7 : 127, group, codes, m0, m1, res2);
+    quant_sym(y, fmt == KVQ_INT4 ? 7 : 127, group, codes, m0, m1, res2, il);
   } else if (fmt == KVQ_INT2) {
     const float* clip = tensor ? a.clip_v : a.clip_k;
-    quant_asym2(y, clip ? clip + (size_t)h * D + 32 * q : nullptr, codes, m0, m1, res2);
+    quant_asym2(y, clip ? clip + (size_t)h * D + 32 * q : nullptr, codes, m0, m1, res2, il);
   } else {
     uint8_t sc[2];
-    quant_fp4(y, a.scale_mode, codes, sc, res2);
+    quant_fp4(y, a.scale_mode, codes, sc, res2, il);
     m0 = (uint16_t)(sc[0] | (sc[1] << 8));
   }
 
@@ -585,15 +604,13 @@ __global__ __launch_bounds__(NT) void append_kernel(AppendArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) d4[i] = s4[i];
     }
-    float ynorm2 = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) ynorm2 = ynorm2 + y[j] * y[j];
     // outward-rounded norms: fp32 sum/sqrt error and the rotation's own rounding
     // (SRFT: six butterfly passes and the unpack, each a few fp32 roundings of values no
-    // larger than the vector norm, twiddles within half an ulp: far below 4e-6 relative)
-    const float slack = a.rotation == KVQ_ROT_DENSE ? 2.44140625e-4f
-                      : a.rotation == KVQ_ROT_SIGN_FWHT ? 9.5367431640625e-7f
-                      : a.rotation == KVQ_ROT_SRFT ? 4.0e-6f : 0.0f;
+    // larger than the vector norm, twiddles within half an ulp: far below 4e-6 relative);
+    // with factors, also the rounding of y * lambda (|fl(y l) - y l| / l <= |y| 2^-24)
+    const float slack = (a.rotation == KVQ_ROT_DENSE ? 2.44140625e-4f
+                         : a.rotation == KVQ_ROT_SIGN_FWHT ? 9.5367431640625e-7f
+                         : a.rotation == KVQ_ROT_SRFT ? 4.0e-6f : 0.0f) + (il ? 1.1920928955078125e-7f : 0.0f);
     float rn = sqrtf(quad_sum(res2)) * 1.0009765625f + sqrtf(quad_sum(ynorm2)) * slack;
     float vn = sqrtf(quad_sum(xnorm2)) * 1.0009765625f;
     if (!valid) {

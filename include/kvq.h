@@ -166,7 +166,9 @@ typedef struct kvq_params {
  *                                   clipping and the group scales ("When Quantization
  *                                   Is Free", Methodology sections 2 and 3; one scale per
  *                                   coordinate with per-group scales), and decode
- *                                   divides them out; not with keep_fp16_copy
+ *                                   divides them out; with keep_fp16_copy the
+ *                                   descriptors hold the residuals taken back to
+ *                                   the unscaled basis (times 1 / lambda)
  * Code, metadata, original and window buffers must be 16-byte aligned.
  */
 typedef struct kvq_cache {
