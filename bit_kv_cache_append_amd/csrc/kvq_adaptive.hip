@@ -188,6 +188,21 @@ __device__ __forceinline__ void load_keys(const uint8_t* row, const uint8_t* met
   }
 }
 
+// Max (MAX) or sum over the 16 lanes of one head (the lanes with equal lane & 3): row
+// rotations by 4 and 8 inside each row of 16 lanes (DPP), then the gfx950 row and
+// half-wave swaps, which give every lane its own value and its partner's; no round trip
+// through the LDS crossbar.
+template <bool MAX>
+__device__ __forceinline__ float head_reduce(float v) {
+  auto op = [](float x, float y) { return MAX ? fmaxf(x, y) : x + y; };
+  v = op(v, dpp_f<0x124>(v));  // row_ror:4
+  v = op(v, dpp_f<0x128>(v));  // row_ror:8
+  const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  v = op(__int_as_float(p16[0]), __int_as_float(p16[1]));
+  const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return op(__int_as_float(p32[0]), __int_as_float(p32[1]));
+}
+
 // Scoring pass: log of the softmax numerator mass of every 64-token block,
 // lse_b = log sum_{t in b} exp(scale * q_rot . k_hat_t), per query head, written into
 // mass and normalised by mass_kernel.  One workgroup per (16 blocks, kv head, group of
@@ -398,11 +413,11 @@ __global__ __launch_bounds__(NTA) void score_kernel(AdaptArgs a) {
       if (c * TILE + s4 + r >= T) sc[r] = NEG_INF_A;
       mx = fmaxf(mx, sc[r]);
     }
-    for (int o = 4; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    mx = head_reduce<true>(mx);
     float se = 0.0f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) se += sc[r] == NEG_INF_A ? 0.0f : expf(sc[r] - mx);
-    for (int o = 4; o < 64; o <<= 1) se += __shfl_xor(se, o);
+    se = head_reduce<false>(se);
     if (lane < nh) a.mass[((size_t)b * a.Hq + hq0 + lane) * a.nt + c] = mx + logf(se);
   }
 }
