@@ -14,6 +14,7 @@ namespace kvq {
 namespace {
 
 constexpr int NTA = 256;  // 4 waves
+constexpr int NTW = 512;  // the scoring pass: 8 waves
 constexpr float NEG_INF_A = -__builtin_huge_valf();
 
 __device__ __forceinline__ float wmax(float v) {
@@ -205,12 +206,14 @@ __device__ __forceinline__ float head_reduce(float v) {
 
 // Scoring pass: log of the softmax numerator mass of every 64-token block,
 // lse_b = log sum_{t in b} exp(scale * q_rot . k_hat_t), per query head, written into
-// mass and normalised by mass_kernel.  One workgroup per (16 blocks, kv head, group of
-// 4 query heads, sequence); wave w takes blocks w, w + 4, w + 8, w + 12 of its 16, the
-// key rows of the next one in flight while one is scored.  (Measured on the certified
-// workload: ≈265 µs for 1.09 GB, ≈4.1 TB/s, with the VALU nearly idle; neither two
-// blocks in flight, eight blocks per wave nor staging coalesced loads through LDS
-// changed that, so what limits it is still open.)  The products run on the matrix
+// mass and normalised by mass_kernel.  One workgroup of 8 waves per (unit, split): a
+// unit is (sequence, kv head, group of 4 query heads), a split a range of its blocks.
+// Waves 0..3 prepare the query heads once; then wave w starts with the range's block w
+// and claims further blocks through a counter in LDS, one visit ahead, the next block's
+// key rows in flight while one is scored (two register sets used alternately).  (The
+// earlier form, short-lived 4-wave workgroups of 16 blocks each, spent a quarter of
+// every wave's life on its own query prologue and ran at ~4.1 TB/s on the certified
+// shape.)  The products run on the matrix
 // cores, 4 tokens x 4 heads x 4 channels per block of the 4x4x4 MFMA (lane 4s + r: token
 // 4s + r as the key operand; head r as the query operand and output):
 //  * integer keys: the rotated query is quantized to 24 bits (qs = max|q| / 8e6) and
@@ -221,13 +224,12 @@ __device__ __forceinline__ float head_reduce(float v) {
 //    scaling, fp32 accumulation per 16-channel block.
 // Each group's sum is scaled once by the token's group scale.
 template <int KF, int KG>
-__global__ __launch_bounds__(NTA) void score_kernel(AdaptArgs a) {
+__global__ __launch_bounds__(NTW) void score_kernel(AdaptArgs a) {
   constexpr int GS = fmt_group(KF, KG);  // channels per scale
   constexpr int NG = D / GS, SPG = GS / 4;
   constexpr int KB = row_bytes(KF);
   constexpr int KM = meta_bytes(KF, GS);
-  constexpr int NBW = 4;  // blocks per wave
-  constexpr int PF = 1;   // blocks in flight ahead of the one being scored
+  constexpr int NWV = NTW / 64;
   __shared__ float qr[4][D];
   __shared__ float tmp[4][D];
   __shared__ float ctab[128];
@@ -235,36 +237,40 @@ __global__ __launch_bounds__(NTA) void score_kernel(AdaptArgs a) {
   __shared__ float qsc[4];      // per head: the query's unit (INT: qs; FP4: the power-of-two scale)
   __shared__ int qds[4][8][4];  // per head, group, digit: digit sums (INT4 offset correction)
   __shared__ float qsf[4][4];   // per head, 32-channel group: sum of the rotated query (INT2 offsets)
-  const int b = blockIdx.z;
+  __shared__ int next;          // next block (offset from the split's first) to claim
+  const int S = a.score_splits;
+  const int u = blockIdx.x / S, split = blockIdx.x % S;
   const int HG = (a.G + 3) >> 2;
-  const int hkv = blockIdx.y / HG, hg = blockIdx.y % HG;
+  const int b = u / (a.H * HG), hkv = (u / HG) % a.H, hg = u % HG;
   const int hq0 = hkv * a.G + hg * 4;
   const int nh = min(4, a.G - hg * 4);
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int T = a.seq.v[b];
   const int nchunks = (T + TILE - 1) / TILE;
-  const int cfirst = blockIdx.x * (4 * NBW);
-  if (cfirst >= nchunks) return;  // uniform over the workgroup
+  const int c0 = split * a.score_cps, c1 = min(nchunks, c0 + a.score_cps);
+  if (c0 >= c1) return;  // uniform over the workgroup
   const size_t stream = (size_t)b * a.H + hkv;
-  // the first block's keys are in flight during the query prologue
   auto key_ptrs = [&](int c, const uint8_t*& rp, const uint8_t*& mp) {
-    const int cc = min(c, nchunks - 1);  // past the last block: reload a valid one (never scored)
-    const size_t t = (size_t)cc * TILE + lane;
+    const size_t t = (size_t)c * TILE + lane;
     rp = a.k_codes + (stream * a.Tmax + t) * KB;
     mp = a.k_meta + (stream * a.Tmax + t) * KM;
   };
-  KeyRegs<KF, KG> R[PF + 1];
-#pragma unroll
-  for (int p = 0; p < PF; ++p) {
+  auto load_block = [&](int c, KeyRegs<KF, KG>& R) {
     const uint8_t *rp, *mp;
-    key_ptrs(cfirst + wv + 4 * p, rp, mp);
-    load_keys<KF, KG>(rp, mp, R[p]);
-  }
+    key_ptrs(c, rp, mp);
+    load_keys<KF, KG>(rp, mp, R);
+  };
+  // the first block's keys are in flight during the query prologue
+  KeyRegs<KF, KG> RA, RB;
+  int cA = c0 + wv;
+  load_block(cA < c1 ? cA : c0, RA);
+  __builtin_amdgcn_sched_barrier(0);
+  if (threadIdx.x == 0) next = NWV;  // published by the prologue's barrier
   if (a.rotation == KVQ_ROT_SRFT) {
     if (threadIdx.x < 128) ctab[threadIdx.x] = a.cos128[threadIdx.x];
     __syncthreads();
   }
-  // ---- prologue: wave w rotates query head w and stores its operands
+  // ---- prologue: wave w < 4 rotates query head w and stores its operands
   float y0 = 0.0f, y1 = 0.0f;
   if (wv < nh) {
     rotated_query(a, b, hq0 + wv, qr[wv], tmp[wv], ctab);
@@ -278,7 +284,7 @@ __global__ __launch_bounds__(NTA) void score_kernel(AdaptArgs a) {
       y1 = y1 / lp[2 * lane + 1];
     }
   }
-  {
+  if (wv < 4) {
     const float ys[2] = {y0, y1};
     const float mx = wmax(fmaxf(fabsf(y0), fabsf(y1)));
     if constexpr (KF == KVQ_FP4) {
@@ -334,19 +340,13 @@ __global__ __launch_bounds__(NTA) void score_kernel(AdaptArgs a) {
   __syncthreads();
   const int j = lane & 3;  // head of this lane's outputs
   const float unit = qsc[j];
-#pragma unroll
-  for (int k = 0; k < NBW; ++k) {
-    const int c = cfirst + wv + 4 * k;
-    if (c >= nchunks) break;  // uniform over the wave; no barrier follows
-    if (k + PF < NBW) {
-      const uint8_t *rp, *mp;
-      key_ptrs(c + 4 * PF, rp, mp);
-      load_keys<KF, KG>(rp, mp, R[(k + PF) % (PF + 1)]);
-    }
-    // issue the next block's loads before this block's products (otherwise the
-    // compiler gives both blocks the same registers and the loads wait for the products)
-    __builtin_amdgcn_sched_barrier(0);
-    const KeyRegs<KF, KG>& K = R[k % (PF + 1)];
+  auto claim = [&]() -> int {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&next, 1);
+    return v;
+  };
+  // ---- one block: products, group scales, the block's log-sum-exp per head
+  auto score = [&](const KeyRegs<KF, KG>& K, int c) {
     float sc[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // tokens 4s + r, head j
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -419,6 +419,27 @@ __global__ __launch_bounds__(NTA) void score_kernel(AdaptArgs a) {
     for (int r = 0; r < 4; ++r) se += sc[r] == NEG_INF_A ? 0.0f : expf(sc[r] - mx);
     se = head_reduce<false>(se);
     if (lane < nh) a.mass[((size_t)b * a.Hq + hq0 + lane) * a.nt + c] = mx + logf(se);
+  };
+  // Blocks are claimed one visit ahead and their loads issued before the current block is
+  // scored, alternating two register sets; a load past the range's end reloads the current,
+  // valid block, so every iteration issues the same loads (claims only grow: once one is
+  // past the end the next is too, and the wave leaves at the loop head).
+  int pB = claim();
+  while (cA < c1) {
+    const int cB = c0 + __builtin_amdgcn_readfirstlane(pB);
+    const int pC = claim();
+    load_block(cB < c1 ? cB : cA, RB);
+    __builtin_amdgcn_sched_barrier(0);
+    score(RA, cA);
+    int pCv = pC;
+    asm volatile("" : "+v"(pCv));
+    const int cC = c0 + __builtin_amdgcn_readfirstlane(pCv);
+    pB = claim();
+    load_block(cC < c1 ? cC : cA, RA);
+    __builtin_amdgcn_sched_barrier(0);
+    if (cB < c1) score(RB, cB);
+    asm volatile("" : "+v"(pB));
+    cA = cC;
   }
 }
 
@@ -662,10 +683,18 @@ hipError_t launch_block_mass(const AdaptArgs& a, hipStream_t s) {
   int max_chunks = 0;
   for (int b = 0; b < a.B; ++b) max_chunks = max(max_chunks, (a.seq.v[b] + TILE - 1) / TILE);
   if (max_chunks > 0) {
-    const dim3 grid((max_chunks + 15) / 16, a.H * HG, a.B);  // 16 blocks per workgroup
+    // one workgroup per (unit, split): enough splits for ~512 workgroups (two per CU),
+    // >= 32 blocks each
+    AdaptArgs b = a;
+    const int units = a.B * a.H * HG;
+    int S = (512 + units - 1) / units;
+    S = std::max(1, std::min(S, max_chunks / 32));
+    b.score_splits = S;
+    b.score_cps = (max_chunks + S - 1) / S;
+    const dim3 grid(units * S);
 #define KVQ_SCORE(KF, KG)                                                          \
     if (a.k_fmt == KF && a.k_group == KG) {                                        \
-      hipLaunchKernelGGL((score_kernel<KF, KG>), grid, dim3(NTA), 0, s, a);        \
+      hipLaunchKernelGGL((score_kernel<KF, KG>), grid, dim3(NTW), 0, s, b);        \
     } else
     KVQ_SCORE(KVQ_INT4, 16) KVQ_SCORE(KVQ_INT4, 32) KVQ_SCORE(KVQ_INT4, 128) KVQ_SCORE(KVQ_INT8, 32) KVQ_SCORE(KVQ_INT8, 128)
     KVQ_SCORE(KVQ_INT2, 32) KVQ_SCORE(KVQ_FP4, 16) { return hipErrorNotSupported; }

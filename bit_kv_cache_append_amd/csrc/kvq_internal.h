@@ -97,6 +97,7 @@ struct AdaptArgs {
   int32_t B, Hq, H, G, Tmax, nt;
   int32_t in_bf16, rotation, k_fmt, k_group;
   int32_t max_inv;
+  int32_t score_splits, score_cps;  // scoring pass: splits per unit, blocks per split
   float scale, tau_cov, tau_v, margin;
   float cos128[128];  // fl32(cos(2 pi k / 128)): the SRFT matrix entries
   SeqArray seq;
