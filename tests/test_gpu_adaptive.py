@@ -6,7 +6,8 @@ Attention", Methodology section 3), through the C ABI:
 * kvq_select_blocks bit-identical to the oracle's selection applied to the
   library's own fp32 masses (the choice is a function of those masses; the
   masses themselves are checked against the oracle above), with and without the
-  bound's flags, in place;
+  bound's flags, in place; and equal to the selection from the oracle's own fp64
+  masses for every kv head whose query heads have no near tie at their cut;
 * the whole ladder on the certified workload: bound flags, scoring pass, top-K*
   promotion, decode with the promoted flags and the certificate, and the dense
   fallback of the heads whose certificate exceeds eps - against the oracle's
@@ -49,6 +50,27 @@ def _filled(c):
     return s, r16, p, g
 
 
+def _unambiguous_heads(mass64, seq, tau, n_kv):
+    """[B, Hkv] True where every query head's top-K* cut is clear of ties and of tau_cov."""
+    B, Hq, _ = mass64.shape
+    G = Hq // n_kv
+    ok = np.ones((B, n_kv), bool)
+    for b in range(B):
+        nb = (int(seq[b]) + 63) // 64
+        if nb == 0:
+            continue
+        for hq in range(Hq):
+            m = mass64[b, hq, :nb]
+            order = sorted(range(nb), key=lambda i: (-m[i], i))
+            run = np.cumsum(m[order])
+            k = len(adaptive.top_blocks(m.astype(np.float32), nb, tau))
+            near_tau = np.any(np.abs(run - tau) < 2e-4)
+            tie = k < nb and abs(m[order[k - 1]] - m[order[k]]) <= 2e-4 * max(m[order[k - 1]], 1e-30)
+            if near_tau or tie:
+                ok[b, hq // G] = False
+    return ok
+
+
 CASES = {
     "int8k-int4v-certified": (synth.config(3, B=2, T=2048), [2048, 1500]),
     "int4-gqa-ragged": (synth.config(2, B=3, T=1088), [1088, 1000, 0]),
@@ -85,8 +107,15 @@ def test_block_mass_and_selection_match_oracle(name):
     for tau in (0.0, 0.5, 0.9, 0.995, 1.0):
         fl = kvq.select_blocks(p, mass, seq, tau)
         torch.cuda.synchronize()
+        fln = fl.cpu().numpy()
         want = adaptive.select_blocks(got, np.array(seq), tau, c["Hkv"])
-        assert np.array_equal(fl.cpu().numpy(), want), f"{name}: selection differs at tau_cov {tau}"
+        assert np.array_equal(fln, want), f"{name}: selection differs at tau_cov {tau}"
+        # independent of the library's masses: the oracle's own fp64 masses choose the same
+        # blocks for every kv head none of whose query heads has a near tie at its cut
+        # (a running sum within 2e-4 of tau_cov, or equal masses within 2e-4 across the cut)
+        sure = _unambiguous_heads(ref, np.array(seq), tau, c["Hkv"])
+        want64 = adaptive.select_blocks(ref.astype(np.float32), np.array(seq), tau, c["Hkv"])
+        assert np.array_equal(fln[sure], want64[sure]), f"{name}: selection from fp64 masses differs at {tau}"
     with pytest.raises(kvq.KvqError) as e:  # coverage is a fraction: the call rejects 2
         kvq.select_blocks(p, mass, seq, 2.0)
     assert e.value.status == -1
