@@ -1158,14 +1158,30 @@ __device__ __forceinline__ void fast_process(const AppendArgs& a, FastSmem& sm, 
     }
     srft_regs(y, q, tau, *ss);
   } else if (fwht) {
+    if constexpr (BF16) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const uint32_t ws = w[k] ^ sm.smask[q][k];
-      y[2 * k] = widen((uint16_t)(ws & 0xFFFF), BF16);
-      y[2 * k + 1] = widen((uint16_t)(ws >> 16), BF16);
+      for (int k = 0; k < 16; ++k) {
+        const uint32_t ws = w[k] ^ sm.smask[q][k];
+        y[2 * k] = widen((uint16_t)(ws & 0xFFFF), BF16);
+        y[2 * k + 1] = widen((uint16_t)(ws >> 16), BF16);
+      }
+    } else {
+      // stage h = 1 straight from the fp16 pair: fma(a, +-1, b) with fp16 operands and an
+      // fp32 result is the exactly rounded a +- b of the widened values (mixed-precision
+      // fma), so widening and the first butterfly take one instruction per element
+      float one = 1.0f;
+      asm volatile("" : "+v"(one));  // kept opaque, so that the fma is not turned into an add
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const uint32_t ws = w[k] ^ sm.smask[q][k];
+        const float u = (float)__builtin_bit_cast(_Float16, (uint16_t)(ws & 0xFFFF));
+        const float v = (float)__builtin_bit_cast(_Float16, (uint16_t)(ws >> 16));
+        y[2 * k] = __builtin_fmaf(v, one, u);
+        y[2 * k + 1] = __builtin_fmaf(v, -one, u);
+      }
     }
 #pragma unroll
-    for (int hh = 1; hh < 32; hh *= 2)
+    for (int hh = BF16 ? 1 : 2; hh < 32; hh *= 2)
 #pragma unroll
       for (int j = 0; j < 32; ++j)
         if ((j & hh) == 0) {

@@ -120,3 +120,49 @@ def test_append_rejects_out_of_range():
     with pytest.raises(kvq.KvqError):
         kvq.append(p, gcache, k, k, [c["T"] - 5, 0])
     assert not gcache.bufs["k_codes"].any()
+
+
+def _edge_bits(shape, seed):
+    """fp16 bit patterns mixing ordinary values with edge cases: subnormals, signed zeros,
+    the largest finite values, all-zero vectors and vectors of one repeated value."""
+    rng = np.random.default_rng(seed)
+    x = synth.to_f16_bits(rng.standard_normal(shape))
+    flat = x.reshape(-1, shape[-1])
+    n = flat.shape[0]
+    pick = lambda frac: rng.random(flat.shape) < frac
+    sub = pick(0.05)  # subnormals of either sign
+    flat[sub] = (rng.integers(1, 0x400, size=int(sub.sum())) | (rng.integers(0, 2, size=int(sub.sum())) << 15)).astype(np.uint16)
+    big = pick(0.002)  # +-65504
+    flat[big] = np.where(rng.random(int(big.sum())) < 0.5, 0x7BFF, 0xFBFF).astype(np.uint16)
+    nz = pick(0.02)
+    flat[nz] = 0x8000  # negative zero
+    flat[rng.choice(n, size=max(1, n // 50), replace=False)] = 0  # whole zero vectors
+    rows = rng.choice(n, size=max(1, n // 50), replace=False)
+    flat[rows] = flat[rows, :1]  # one value repeated over the vector
+    tiny = rng.choice(n, size=max(1, n // 50), replace=False)
+    flat[tiny] = (rng.integers(1, 0x400, size=(len(tiny), shape[-1]))).astype(np.uint16)  # subnormal vectors
+    return x
+
+
+@pytest.mark.parametrize("name", ["int4-g32-gqa", "int8k-int4v-cert", "int4-g16-fwht", "fp4-f16-search",
+                                  "int4-srft-f16"])
+def test_append_edge_values_bit_exact(name):
+    """fp16 edge cases (subnormals, signed zeros, +-65504, zero and constant vectors, vectors
+    of subnormals) through the fast and generic append paths: codes, metadata, originals and
+    descriptors as the oracle's."""
+    c = CASES[name]
+    print(f"[append] edge values {name}", flush=True)
+    B, H, T = c["B"], c["Hkv"], c["T"]
+    k = _edge_bits((B, H, T, 128), 11)
+    v = _edge_bits((B, H, T, 128), 12)
+    s, r16, s_dev, r_dev = setup_rotation(c)
+    p, gcache = make_gpu_cache(c, s_dev, r_dev)
+    oc = make_oracle_cache(c)
+    kvq.append(p, gcache, dev_bits(k), dev_bits(v), [0] * B)
+    torch.cuda.synchronize()
+    codec.append(oc, k, v, np.zeros(B, int), c["dtype"], c["rotation"], s, r16, None, None, c["scale_mode"])
+    assert_bytes_equal(oc, gcache, f"edge-{name}")
+    if c["keep"]:
+        want = bound.block_descriptors(oc, c["dtype"], c["rotation"], s, r16)
+        got = gcache.bufs["blk_desc"].cpu().numpy().reshape(want.shape)
+        assert np.all(got >= want) and np.all(got <= want * (1 + 2.0 ** -8) + 1e-6 * np.abs(want).max())
