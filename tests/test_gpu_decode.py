@@ -190,3 +190,66 @@ def test_split_merge_repeatable(B, T):
     worst = max(float(attention.row_rel_err(outs[i].cpu().numpy(), refs[i % 2]).max()) for i in range(100))
     print(f"[decode] merge repeatable: worst row rel err over 100 alternating calls {worst:.2e}", flush=True)
     assert worst <= TOL
+
+
+def _prefix_view(p_small, big):
+    """A cache object for the first sequences of `big`: every buffer is laid out
+    [stream][...] with stream = b * Hkv + h, so the first B' sequences are each buffer's
+    prefix, and the view's buffers are prefixes of the big cache's (no copy)."""
+    v = kvq.Cache(p_small, signs=big.signs, rot_f16=big.rot_f16)
+    for n, t in v.bufs.items():
+        if t is not None:
+            v.bufs[n] = big.bufs[n][: t.numel()]
+    return v
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_split_count_invariance(cfg):
+    """One sequence decoded alone (8 splits per unit) and as the first of 16 (2 splits):
+    the split count changes only the fp32 order of the merge, so the two outputs agree far
+    inside the bar, both meet the oracle, and the certified cache's flags and certificates
+    agree too.  The data is appended once, through the one-sequence view."""
+    T = 8192
+    c1 = synth.config(cfg, B=1, T=T)
+    c16 = synth.config(cfg, B=16, T=T)
+    print(f"[decode] split-count invariance, config {cfg}", flush=True)
+    s, r16, s_dev, r_dev = setup_rotation(c1)
+    p16, g16 = make_gpu_cache(c16, s_dev, r_dev)
+    p1 = kvq.params_from_config(c1)
+    g1 = _prefix_view(p1, g16)
+    k = synth.kv_all(c1, 0, 0, T)
+    v = synth.kv_all(c1, 1, 0, T)
+    kvq.append(p1, g1, dev_bits(k), dev_bits(v), [0])
+    seq1, seq16 = [T], [T] + [0] * 15
+    assert kvq.decode_splits(p1, seq1) == 8 and kvq.decode_splits(p16, seq16) == 2
+    q1 = synth.queries(c1)
+    q16 = np.zeros((16,) + q1.shape[1:], dtype=q1.dtype)
+    q16[0] = q1[0]
+    cert = cfg == 3
+    if cert:
+        _, f1 = kvq.error_bound(p1, g1, dev_bits(q1), seq1, c1["tau"])
+        _, f16 = kvq.error_bound(p16, g16, dev_bits(q16), seq16, c1["tau"])
+        o1, e1 = kvq.decode_attn(p1, g1, dev_bits(q1), seq1, flags=f1, certificate=True)
+        o16, e16 = kvq.decode_attn(p16, g16, dev_bits(q16), seq16, flags=f16, certificate=True)
+    else:
+        o1 = kvq.decode_attn(p1, g1, dev_bits(q1), seq1)
+        o16 = kvq.decode_attn(p16, g16, dev_bits(q16), seq16)
+    torch.cuda.synchronize()
+    a1, a16 = o1.cpu().numpy()[0], o16.cpu().numpy()[0]
+    diff = float(attention.row_rel_err(a16[None], a1[None]).max())
+    print(f"[decode] 8 vs 2 splits: max row rel difference {diff:.2e}", flush=True)
+    assert diff <= 1e-4
+    assert not o16.cpu().numpy()[1:].any(), "empty sequences give zero rows"
+    oc = oracle_view_of_gpu(c1, g1)
+    fln = None
+    if cert:
+        fln = f1.cpu().numpy()
+        assert np.array_equal(fln[0], f16.cpu().numpy()[0])
+    ref, _ = attention.decode_attention(oc, q1, c1["dtype"], np.array(seq1), c1["rotation"], s, r16, flags=fln)
+    rows = [(0, hq) for hq in range(c1["Hq"])]
+    _check_rows(o1.cpu().numpy(), ref, rows, "8 splits")
+    _check_rows(o16.cpu().numpy()[:1], ref, rows, "2 splits")
+    if cert:
+        E1, E16 = e1.cpu().numpy()[0], e16.cpu().numpy()[0]
+        assert np.allclose(E1, E16, rtol=1e-5, atol=1e-9), "certificates differ between split counts"
+        assert not e16.cpu().numpy()[1:].any()

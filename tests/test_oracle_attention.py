@@ -279,3 +279,41 @@ def test_certificate_bounds_error(certified_small, tau):
     err = np.linalg.norm(out - dense, axis=-1)
     assert np.all(err <= E)
     assert np.all(E > 0)
+
+
+def test_corrupted_codes_escape_the_stored_certificate(certified_small):
+    """What the certificate does not catch ("Runtime-Certified Bounded-Error Quantized
+    Attention", Methodology sections 1-2: the descriptors are measured when a block is
+    written).  A block's value codes and scales changed after the append leave the stored
+    descriptors, hence the flags and the certificate, as they were, while the attention
+    moves far beyond the certificate; descriptors measured again from the damaged block
+    would flag it."""
+    import copy
+    c, cache, s, q, seq, desc = certified_small
+    tau = 1e-2
+    _, fl = bound.error_bound(desc, q, "f16", seq, tau)
+    out, mass = attention.decode_attention(cache, q, "f16", seq, "sign_fwht", s, flags=fl)
+    E = bound.certificate(desc, q, "f16", seq, fl, mass)
+    G = c["Hq"] // c["Hkv"]
+    # the unflagged block of (sequence 0, kv head 0) with the most attention mass (its heads summed)
+    m0 = mass[0, :G].sum(axis=0)
+    m0 = np.where(fl[0, 0] == 0, m0, -1.0)
+    blk = int(np.argmax(m0[: seq[0] // 64]))
+    bad = copy.deepcopy(cache)
+    bad.v_codes[0, 0, blk] = 0x77  # every value code of the block's tile +7 (int4 nibbles) ...
+    bad.v_meta[0, 0, blk].view(np.uint16)[...] = 0x3C00  # ... and every value scale 1.0 (fp16)
+    _, fl2 = bound.error_bound(desc, q, "f16", seq, tau)
+    out2, mass2 = attention.decode_attention(bad, q, "f16", seq, "sign_fwht", s, flags=fl2)
+    E2 = bound.certificate(desc, q, "f16", seq, fl2, mass2)
+    assert np.array_equal(fl2, fl) and np.array_equal(E2, E), "the stored descriptors decide flags and certificate"
+    dense = attention.dense_attention(cache.k_orig, cache.v_orig, q, "f16", seq)
+    err = np.linalg.norm(out2 - dense, axis=-1)
+    assert np.all(err[0, :G] > 2 * E[0, :G]), "the damaged block's heads: error far beyond the certificate"
+    rest = np.ones(err.shape, bool)
+    rest[0, :G] = False
+    assert np.all(err[rest] <= E[rest]), "every other row keeps its bound"
+    # measured again from the damaged codes, the block's value error flags it
+    desc2 = bound.block_descriptors(bad, c["dtype"], c["rotation"], s, seq_len=seq)
+    assert desc2[0, 0, blk, 1] > 10 * desc[0, 0, blk, 1]
+    _, fl3 = bound.error_bound(desc2, q, "f16", seq, tau)
+    assert fl3[0, 0, blk] and not fl[0, 0, blk]
