@@ -4,8 +4,10 @@ Every computation runs in the HIP kernels of libkvq.so; this module turns torch
 tensors into device pointers and the current HIP stream, calls the C entry
 points of the same names (kvq_append, kvq_error_bound, kvq_decode_attn,
 kvq_decode_attn_dense, kvq_decode_attn_noalloc, kvq_calibrate_clip, kvq_block_mass, kvq_select_blocks,
-kvq_promote_values, kvq_ranking_check, kvq_dense_fallback, kvq_calibrate_lambda, kvq_buffer_bytes, kvq_decode_workspace_bytes, kvq_decode_splits) and raises KvqError on a non-zero status.  There is
-no fallback: if the library is not built, importing the functions raises.
+kvq_promote_values, kvq_ranking_check, kvq_dense_fallback, kvq_calibrate_lambda, kvq_buffer_bytes, kvq_decode_workspace_bytes, kvq_decode_splits,
+kvq_debug_status) and raises KvqError on a non-zero status.  There is no fallback: if
+the library is not built, importing the functions raises.  KVQ_LIB in the environment
+names another build of the library to load (the layout-checking libkvq_debug.so).
 """
 
 import ctypes
@@ -14,7 +16,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvq.so")
+LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(_HERE, "libkvq.so")
+DEBUG_LIB_PATH = os.path.join(_HERE, "libkvq_debug.so")
 
 F16, BF16 = 0, 1
 INT4, INT8, INT2, FP4 = 0, 1, 2, 3
@@ -66,6 +69,8 @@ def lib():
         L.kvq_status_str.restype = ctypes.c_char_p
         L.kvq_status_str.argtypes = [i32]
         L.kvq_last_error.restype = ctypes.c_char_p
+        L.kvq_debug_status.restype = i32
+        L.kvq_debug_status.argtypes = [P(ctypes.c_uint32), i32]
         L.kvq_buffer_bytes.restype = i32
         L.kvq_buffer_bytes.argtypes = [P(Params), P(ctypes.c_size_t)]
         L.kvq_decode_workspace_bytes.restype = ctypes.c_size_t
@@ -137,6 +142,15 @@ def buffer_bytes(p):
 
 def decode_workspace_bytes(p):
     return int(lib().kvq_decode_workspace_bytes(ctypes.byref(p)))
+
+
+def debug_status(clear=True):
+    """kvq_debug_status (debug library only): (code of the first failed layout check or 0,
+    its two indices, failures counted); raises KvqError(KVQ_ERR_UNSUPPORTED) on the release
+    library."""
+    out = (ctypes.c_uint32 * 4)()
+    _check(lib().kvq_debug_status(out, int(bool(clear))))
+    return tuple(int(x) for x in out)
 
 
 def decode_splits(p, seq_len):

@@ -1,6 +1,12 @@
 """Build libkvq.so (HIP, gfx950) in place.
 
-    python -m bit_kv_cache_append_amd.build
+    python -m bit_kv_cache_append_amd.build            # libkvq.so
+    python -m bit_kv_cache_append_amd.build --debug    # libkvq_debug.so (layout checks)
+    python -m bit_kv_cache_append_amd.build --all      # both
+
+The debug library is the same sources compiled with KVQ_DEBUG: its kernels check
+every index they address against the call's sizes and record failures for
+kvq_debug_status (the release library compiles the checks out).
 
 Every translation unit is compiled with hipcc for gfx950 only.  The write-side
 unit is compiled with -ffp-contract=off so that its fp32 arithmetic keeps the
@@ -16,6 +22,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libkvq.so")
+OUT_DEBUG = os.path.join(HERE, "libkvq_debug.so")
 BUILD = os.path.join(HERE, "_build")
 
 ARCH = "gfx950"
@@ -44,8 +51,8 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src, extra):
-    obj = os.path.join(BUILD, src + ".o")
+def _compile(src, extra, bdir=BUILD):
+    obj = os.path.join(bdir, src + ".o")
     cmd = [hipcc()] + COMMON + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -53,24 +60,31 @@ def _compile(src, extra):
     return obj
 
 
-def build(verbose=True):
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose=True, debug=False):
+    """Compile every translation unit and link the library; debug=True: libkvq_debug.so."""
+    bdir = os.path.join(BUILD, "debug") if debug else BUILD
+    out = OUT_DEBUG if debug else OUT
+    flags = ["-DKVQ_DEBUG"] if debug else []
+    os.makedirs(bdir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda kv: _compile(*kv), SOURCES.items()))
-    tmp = OUT + ".tmp"
+        objs = list(ex.map(lambda kv: _compile(kv[0], kv[1] + flags, bdir), SOURCES.items()))
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {OUT}")
-    return OUT
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":
     try:
-        build()
+        if "--debug" not in sys.argv:
+            build()
+        if "--debug" in sys.argv or "--all" in sys.argv:
+            build(debug=True)
     except RuntimeError as e:
         print(e, file=sys.stderr)
         sys.exit(1)

@@ -252,6 +252,7 @@ __global__ __launch_bounds__(NTW) void score_kernel(AdaptArgs a) {
   const size_t stream = (size_t)b * a.H + hkv;
   auto key_ptrs = [&](int c, const uint8_t*& rp, const uint8_t*& mp) {
     const size_t t = (size_t)c * TILE + lane;
+    KVQ_DCHECK(stream < (size_t)a.B * a.H && c >= 0 && c < a.nt, DBG_CHUNK, stream, c);
     rp = a.k_codes + (stream * a.Tmax + t) * KB;
     mp = a.k_meta + (stream * a.Tmax + t) * KM;
   };
@@ -418,6 +419,7 @@ __global__ __launch_bounds__(NTW) void score_kernel(AdaptArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) se += sc[r] == NEG_INF_A ? 0.0f : expf(sc[r] - mx);
     se = head_reduce<false>(se);
+    KVQ_DCHECK(lane >= nh || hq0 + lane < a.Hq, DBG_ROW, (size_t)b * a.Hq + hq0 + lane, c);
     if (lane < nh) a.mass[((size_t)b * a.Hq + hq0 + lane) * a.nt + c] = mx + logf(se);
   };
   // Blocks are claimed one visit ahead and their loads issued before the current block is
@@ -449,6 +451,7 @@ __global__ __launch_bounds__(NTA) void mass_kernel(AdaptArgs a) {
   __shared__ float red[NTA / 64];
   const int row = blockIdx.x, b = row / a.Hq;
   const int nb = (a.seq.v[b] + TILE - 1) / TILE;
+  KVQ_DCHECK(row < a.B * a.Hq && nb <= a.nt, DBG_ROW, row, nb);
   float* m = a.mass + (size_t)row * a.nt;
   const int t = threadIdx.x, wv = t >> 6, lane = t & 63;
   float mx = NEG_INF_A;
@@ -586,6 +589,7 @@ __global__ __launch_bounds__(NTA) void select_kernel(AdaptArgs a) {
   uint8_t* fl = a.flags_out + ((size_t)b * a.H + h) * a.nt;
   for (int j = threadIdx.x; j < K; j += NTA) {
     const int blk = block_of_key(key[j]);
+    KVQ_DCHECK(blk >= 0 && blk < nb, DBG_CHUNK, row, blk);
     fl[blk] = (uint8_t)(fl[blk] | 1);
   }
 }
@@ -639,6 +643,7 @@ __global__ __launch_bounds__(NTA) void rank_kernel(AdaptArgs a) {
   const size_t stream = (size_t)b * a.H + h;
   for (int i = wv; i < K; i += NTA / 64) {
     const int tok = block_of_key(key[i]) * TILE + lane;
+    KVQ_DCHECK(stream < (size_t)a.B * a.H && tok >= 0 && tok < nb * TILE && nb <= a.nt, DBG_CHUNK, stream, tok);
     float lg = NEG_INF_A;
     if (tok < T) {
       const uint4* kp = reinterpret_cast<const uint4*>(a.k_orig + (stream * a.Tmax + tok) * D);
@@ -725,5 +730,9 @@ hipError_t launch_ranking_check(const AdaptArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(rank_kernel, dim3(a.B * a.Hq), dim3(NTA), 0, s, a);
   return hipGetLastError();
 }
+
+#ifdef KVQ_DEBUG
+KVQ_DBG_READER(dbg_read_adaptive)
+#endif
 
 }  // namespace kvq

@@ -164,6 +164,32 @@ extern "C" {
 
 int32_t kvq_abi_version(void) { return KVQ_ABI_VERSION; }
 
+kvq_status kvq_debug_status(uint32_t* out, int32_t clear) {
+  if (!out) return fail(KVQ_ERR_INVALID_ARG, "out is NULL");
+#ifdef KVQ_DEBUG
+  // the four translation units keep their own records; the first one with a failure names it
+  hipError_t (*const readers[4])(uint32_t*, bool) = {dbg_read_append, dbg_read_decode, dbg_read_bound,
+                                                     dbg_read_adaptive};
+  out[0] = out[1] = out[2] = out[3] = 0;
+  for (auto rd : readers) {
+    uint32_t w[4];
+    const hipError_t e = rd(w, clear != 0);
+    if (e != hipSuccess) return hip_fail(e, "debug record");
+    if (out[0] == 0 && w[0] != 0) {
+      out[0] = w[0];
+      out[1] = w[1];
+      out[2] = w[2];
+    }
+    out[3] += w[3];
+  }
+  return KVQ_OK;
+#else
+  (void)clear;
+  out[0] = out[1] = out[2] = out[3] = 0;
+  return fail(KVQ_ERR_UNSUPPORTED, "layout checks exist only in the debug library (libkvq_debug.so)");
+#endif
+}
+
 const char* kvq_status_str(kvq_status s) {
   switch (s) {
     case KVQ_OK: return "KVQ_OK";

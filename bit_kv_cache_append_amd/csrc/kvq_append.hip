@@ -495,6 +495,7 @@ __global__ __launch_bounds__(NT) void append_kernel(AppendArgs a) {
   const int fmt = tensor ? a.v_fmt : a.k_fmt;
   const int group = tensor ? a.v_group : a.k_group;
   const size_t stream_idx = (size_t)b * a.H + h;
+  if (valid) KVQ_DCHECK_APPEND(a, stream_idx, pos, start);
   const uint16_t* src_base = tensor ? a.v_new : a.k_new;
   const uint16_t* src = src_base + ((stream_idx * a.n_new + (valid ? pos - start : 0)) * D + 32 * q);
 
@@ -939,6 +940,7 @@ __device__ __forceinline__ FastUnit fast_unit(const AppendArgs& a, int u, int nt
   U.pos = U.tile * TILE + tau;
   U.valid = U.pos >= U.lo && U.pos < U.hi;
   U.stream_idx = (size_t)U.b * a.H + U.h;
+  if (U.valid) KVQ_DCHECK_APPEND(a, U.stream_idx, U.pos, start);
   U.src = (U.tensor ? a.v_new : a.k_new) + ((U.stream_idx * a.n_new + (U.valid ? U.pos - start : 0)) * D + 32 * q);
   return U;
 }
@@ -1483,6 +1485,7 @@ __device__ __forceinline__ void dense_int2_store(const AppendArgs& a, const Fast
   const int kt = 32 * hf + col;
   const int pos = C.tile * TILE + kt;
   const bool valid = pos >= C.lo && pos < C.hi;
+  if (valid) KVQ_DCHECK_APPEND(a, C.stream_idx, pos, a.start.v[C.b]);
   const uint16_t sk = hf ? sbits[1] : sbits[0], zk = hf ? zbits[1] : zbits[0];
   if (tensor == 0) {
     const uint32_t give = hf ? P[0] : P[1], keep = hf ? P[1] : P[0];
@@ -1699,6 +1702,9 @@ __global__ __launch_bounds__(NT) void window_copy_kernel(AppendArgs a) {
   if (lo >= hi) return;  // uniform over the workgroup
   const int slot = j < a.n_sink ? j : a.n_sink + j % a.n_recent;
   const size_t stream = (size_t)b * a.H + h;
+  KVQ_DCHECK(slot >= 0 && slot < a.n_sink + a.n_recent && lo >= j * TILE && hi <= j * TILE + TILE, DBG_WINDOW,
+             stream, j);
+  KVQ_DCHECK(stream < (size_t)a.B * a.H && lo >= start && hi <= end && hi <= a.Tmax, DBG_POS, stream, hi);
   const uint4* src = reinterpret_cast<const uint4*>((tensor ? a.v_new : a.k_new) + (stream * a.n_new + (lo - start)) * D);
   uint4* dst = reinterpret_cast<uint4*>((tensor ? a.v_win : a.k_win) +
                                         ((stream * (a.n_sink + a.n_recent) + slot) * TILE + (lo - j * TILE)) * D);
@@ -1794,5 +1800,9 @@ hipError_t launch_calibrate(const CalibArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(calibrate_kernel, dim3(a.H), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
+
+#ifdef KVQ_DEBUG
+KVQ_DBG_READER(dbg_read_append)
+#endif
 
 }  // namespace kvq

@@ -29,6 +29,7 @@ __global__ __launch_bounds__(256) void bound_kernel(BoundArgs a) {
   const float coef = qn_s * a.scale;
   const int nb = (a.seq.v[b] + TILE - 1) / TILE;
   const size_t base = ((size_t)b * a.H + h) * a.nt;
+  KVQ_DCHECK(b < a.B && nb >= 0 && nb <= a.nt, DBG_CHUNK, (size_t)b * a.H + h, nb);
   for (int j = threadIdx.x; j < a.nt; j += blockDim.x) {
     float bd = 0.0f;
     if (j < nb) {
@@ -44,5 +45,9 @@ hipError_t launch_bound(const BoundArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(bound_kernel, dim3(a.B * a.H), dim3(256), 0, s, a);
   return hipGetLastError();
 }
+
+#ifdef KVQ_DEBUG
+KVQ_DBG_READER(dbg_read_bound)
+#endif
 
 }  // namespace kvq

@@ -528,6 +528,7 @@ __device__ void write_record(const DecodeArgs& a, const MergeArea<NW>& mg, const
   if (hh >= nh) return;
   float M = NEG_INF;
   for (int w = w0; w < w0 + nw; ++w) M = fmaxf(M, mg.m[w][hh]);
+  KVQ_DCHECK(b < a.B && hq0 + hh < a.Hq && split >= 0 && split < a.n_splits, DBG_RECORD, b * a.Hq + hq0 + hh, split);
   float* rec = a.part + (((size_t)b * a.Hq + hq0 + hh) * a.n_splits + split) * PART_FLOATS;
   float o0 = 0.0f, o1 = 0.0f, p0 = 0.0f, p1 = 0.0f, L = 0.0f, E = 0.0f, ek = 0.0f, vn = 0.0f;
   for (int w = w0; w < w0 + nw; ++w) {
@@ -572,6 +573,7 @@ template <bool CERT, bool COH>
 __device__ void combine_row(const DecodeArgs& a, int row, float* zsw, const float* ctab) {
   const int l = threadIdx.x & 63, c = 2 * l;
   const int b = row / a.Hq;
+  KVQ_DCHECK(row >= 0 && row < a.B * a.Hq, DBG_ROW, row, a.n_splits);
   float* out = a.out + (size_t)row * D;
   if (a.seq.v[b] == 0) {
     *reinterpret_cast<float2*>(out + c) = make_float2(0.0f, 0.0f);
@@ -758,6 +760,8 @@ __device__ __forceinline__ void load_chunk(const DecodeArgs& a, size_t stream, i
   constexpr int KM = meta_bytes(KF, KG);
   constexpr int CDW = VFmt<VF>::CDW;
   const int tok0 = ch * TILE;
+  KVQ_DCHECK(stream < (size_t)a.B * a.H, DBG_STREAM, stream, ch);
+  KVQ_DCHECK(ch >= 0 && ch < a.nt, DBG_CHUNK, stream, ch);
   const uint4* rp = reinterpret_cast<const uint4*>(a.k_codes + (stream * a.Tmax + tok0 + tok_a) * (KDW * 4));
 #pragma unroll
   for (int i = 0; i < KDW / 4; ++i) {
@@ -973,8 +977,10 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   auto orig_rows = [&](const uint16_t* full, const uint16_t* win, int ch) -> const uint16_t* {
     if (in_window(ch)) {
       const int wslot = ch < a.n_sink ? ch : a.n_sink + ch % a.n_recent;
+      KVQ_DCHECK(wslot >= 0 && wslot < a.n_sink + a.n_recent, DBG_WINDOW, stream, ch);
       return win + (stream * (size_t)(a.n_sink + a.n_recent) + wslot) * TILE * D;
     }
+    KVQ_DCHECK(ch >= 0 && ch < a.nt, DBG_CHUNK, stream, ch);
     return full + (stream * a.Tmax + (size_t)ch * TILE) * D;
   };
   // Original values of one chunk into oo: lane l holds channels 2l, 2l+1 of every token
@@ -1431,6 +1437,7 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (t == 0) {
+    KVQ_DCHECK(u >= 0 && u < a.U, DBG_COUNTER, u, split);
     const int prev = __hip_atomic_fetch_add(a.ctr + u, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sm.last = prev == S - 1;
   }
@@ -1498,6 +1505,8 @@ __global__ __launch_bounds__(NT, 2) void decode_dense_split(DecodeArgs a) {
   for (int ch = c0 + wv; ch < c1; ch += 4) {
     const int tok0 = ch * TILE;
     const int nlive = T - tok0;  // rows below the sequence end (>= 1)
+    KVQ_DCHECK(stream < (size_t)a.B * a.H, DBG_STREAM, stream, ch);
+    KVQ_DCHECK(ch >= 0 && ch < a.nt, DBG_CHUNK, stream, ch);
     const uint4* kp = reinterpret_cast<const uint4*>(a.k_orig + (stream * a.Tmax + tok0 + lane) * D);
     const uint32_t* vp = reinterpret_cast<const uint32_t*>(a.v_orig + (stream * a.Tmax + tok0) * D) + lane;
     uint4 kr[16];
@@ -1675,5 +1684,9 @@ hipError_t launch_dense_fallback(const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(combine_kernel<true>, dim3((a.B * a.Hq + 3) / 4), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
+
+#ifdef KVQ_DEBUG
+KVQ_DBG_READER(dbg_read_decode)
+#endif
 
 }  // namespace kvq

@@ -152,6 +152,67 @@ struct DecodeArgs {
 };
 
 
+// ----------------------------------------------------------------- debug build
+// Compiled with -DKVQ_DEBUG (libkvq_debug.so), the kernels check the layout as they address
+// memory: every stream, position, chunk, block, split record and counter index against the
+// sizes the call was validated with.  A failed check does not stop the kernel: the first one
+// in a translation unit records its code and two indices in that unit's word array, and
+// every failure is counted; kvq_debug_status reads and clears them.  The release library
+// compiles the checks out.
+enum DbgCode : uint32_t {
+  DBG_NONE = 0,
+  DBG_STREAM = 1,  // (sequence, kv head) stream index outside [0, B * Hkv)
+  DBG_CHUNK = 2,   // decode chunk / 64-token block outside [0, Tmax / 64)
+  DBG_RECORD = 3,  // split record (row, split) outside [0, B * Hq) x [0, n_splits)
+  DBG_COUNTER = 4, // split arrival counter outside [0, units)
+  DBG_WINDOW = 5,  // window slot outside [0, sink + recent) or a position outside its block
+  DBG_POS = 6,     // appended position outside [0, Tmax) or outside the input's n_new rows
+  DBG_ROW = 7,     // (sequence, query head) row outside [0, B * Hq)
+};
+#ifdef KVQ_DEBUG
+static __device__ uint32_t dbg_word[4];  // first code, its two indices, failures counted
+__device__ __noinline__ static void dbg_fail(uint32_t code, uint32_t i0, uint32_t i1) {
+  uint64_t p = (uint64_t)(uintptr_t)&dbg_word[0];
+  asm volatile("" : "+v"(p));  // a per-lane address: vector memory atomics
+  uint32_t* w = reinterpret_cast<uint32_t*>(p);
+  uint32_t expect = 0;
+  if (__hip_atomic_compare_exchange_strong(w, &expect, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT)) {
+    __hip_atomic_store(w + 1, i0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(w + 2, i1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __hip_atomic_fetch_add(w + 3, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+#define KVQ_DCHECK(cond, code, i0, i1)                                            \
+  do {                                                                           \
+    if (__builtin_expect(!(cond), 0)) kvq::dbg_fail((code), (uint32_t)(i0), (uint32_t)(i1)); \
+  } while (0)
+// the host reader of this translation unit's record (waits for the device first)
+#define KVQ_DBG_READER(name)                                                                  \
+  hipError_t name(uint32_t out[4], bool clear) {                                              \
+    hipError_t e = hipDeviceSynchronize();                                                    \
+    if (e == hipSuccess) e = hipMemcpyFromSymbol(out, HIP_SYMBOL(dbg_word), 4 * sizeof(uint32_t)); \
+    if (e == hipSuccess && clear) {                                                           \
+      const uint32_t z[4] = {0u, 0u, 0u, 0u};                                                 \
+      e = hipMemcpyToSymbol(HIP_SYMBOL(dbg_word), z, sizeof(z));                              \
+    }                                                                                         \
+    return e;                                                                                 \
+  }
+hipError_t dbg_read_append(uint32_t out[4], bool clear);
+hipError_t dbg_read_decode(uint32_t out[4], bool clear);
+hipError_t dbg_read_bound(uint32_t out[4], bool clear);
+hipError_t dbg_read_adaptive(uint32_t out[4], bool clear);
+#else
+#define KVQ_DCHECK(cond, code, i0, i1) ((void)0)
+#endif
+// a token a lane writes in an append: inside its stream, the cache and the input rows
+#define KVQ_DCHECK_APPEND(a, stream, pos, start)                                               \
+  do {                                                                                        \
+    KVQ_DCHECK((stream) < (size_t)(a).B * (a).H, DBG_STREAM, (stream), (pos));                \
+    KVQ_DCHECK((pos) >= 0 && (pos) < (a).Tmax && (pos) - (start) >= 0 && (pos) - (start) < (a).n_new, DBG_POS, \
+               (stream), (pos));                                                              \
+  } while (0)
+
 // host-side launchers (defined in the .hip files)
 hipError_t launch_append(const AppendArgs& a, int grid_x, hipStream_t s);
 hipError_t launch_window_copy(const AppendArgs& a, hipStream_t s);

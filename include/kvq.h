@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 4
+#define KVQ_ABI_VERSION 5
 
 typedef int32_t kvq_status;
 #define KVQ_OK 0
@@ -197,6 +197,19 @@ const char* kvq_status_str(kvq_status s);
 
 /* Detail of the last error on the calling thread ("" if none). */
 const char* kvq_last_error(void);
+
+/* Layout checks of the debug library (libkvq_debug.so, the same sources compiled with
+ * KVQ_DEBUG; not for production use).  Its kernels check every stream, position,
+ * chunk, block, split-record and counter index they address against the sizes the call
+ * was validated with; a failed check does not stop the kernel but is recorded per
+ * device.  This call waits for the current device, then writes out[0] = code of the
+ * first recorded failure (0 = none; the codes name the index kind: 1 stream, 2 chunk or
+ * block, 3 split record, 4 counter, 5 window slot, 6 appended position, 7 query row),
+ * out[1], out[2] = the two indices it recorded, out[3] = failures counted; clear != 0
+ * resets the record.  out: host, 4 words.  The release library returns
+ * KVQ_ERR_UNSUPPORTED without touching a device; a HIP failure returns
+ * KVQ_ERR_HIP. */
+kvq_status kvq_debug_status(uint32_t* out, int32_t clear);
 
 /* Bytes of each cache buffer for these params, written to out_bytes[KVQ_NUM_BUFS]
  * (0 for buffers the configuration does not use).  Host only. */

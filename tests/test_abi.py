@@ -22,7 +22,20 @@ def test_library_exports_every_declared_symbol():
     assert "kvq_append" in names and "kvq_decode_attn" in names and "kvq_error_bound" in names
     for n in names:
         assert hasattr(L, n), f"{n} not exported"
-    assert L.kvq_abi_version() == 4
+    assert L.kvq_abi_version() == 5
+
+
+def test_debug_library_exports_the_same_symbols():
+    """libkvq_debug.so (the layout-checking build) loads and exports every declared entry
+    point; the release library has no checks and says so without touching a device."""
+    assert os.path.exists(kvq.DEBUG_LIB_PATH), "build with python -m bit_kv_cache_append_amd.build --all"
+    D = ctypes.CDLL(kvq.DEBUG_LIB_PATH)
+    for n in _declared():
+        assert hasattr(D, n), f"{n} not exported by the debug library"
+    assert D.kvq_abi_version() == 5
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.debug_status()
+    assert e.value.status == -2  # KVQ_ERR_UNSUPPORTED
 
 
 def test_buffer_sizes():
