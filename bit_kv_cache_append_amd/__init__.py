@@ -69,8 +69,9 @@ def lib():
         L.kvq_status_str.restype = ctypes.c_char_p
         L.kvq_status_str.argtypes = [i32]
         L.kvq_last_error.restype = ctypes.c_char_p
-        L.kvq_debug_status.restype = i32
-        L.kvq_debug_status.argtypes = [P(ctypes.c_uint32), i32]
+        if hasattr(L, "kvq_debug_status"):  # (libraries of ABI version 5 and later)
+            L.kvq_debug_status.restype = i32
+            L.kvq_debug_status.argtypes = [P(ctypes.c_uint32), i32]
         L.kvq_buffer_bytes.restype = i32
         L.kvq_buffer_bytes.argtypes = [P(Params), P(ctypes.c_size_t)]
         L.kvq_decode_workspace_bytes.restype = ctypes.c_size_t
