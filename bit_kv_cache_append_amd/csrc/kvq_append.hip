@@ -749,6 +749,35 @@ __device__ __forceinline__ float quot_magic(float y, float sf, float r) {
   return __builtin_amdgcn_fmed3f(m, MAGIC + (float)(OFF - QMAX), MAGIC + (float)(OFF + QMAX));
 }
 
+// y[j] = fma(partner's y[j], s, y[j]) for j = 0..15, the partner given by a DPP quad
+// permutation: v_fmac_f32 with its first source read through DPP, one instruction per
+// value (for an fma the compiler keeps a separate DPP move).  A DPP read of a register
+// written by the VALU instruction just before it needs two wait states, hence the s_nop
+// at the head of the block; inside it each instruction writes a register the next ones
+// do not read.
+#define KVQ_FMAC_DPP16(QP)                                                                \
+  asm volatile("s_nop 1\n\t"                                                              \
+      "v_fmac_f32_dpp %0, %0, %16 " QP " row_mask:0xf bank_mask:0xf\n\t"  \
+      "v_fmac_f32_dpp %1, %1, %16 " QP " row_mask:0xf bank_mask:0xf\n\t"  \
+      "v_fmac_f32_dpp %2, %2, %16 " QP " row_mask:0xf bank_mask:0xf\n\t"  \
+      "v_fmac_f32_dpp %3, %3, %16 " QP " row_mask:0xf bank_mask:0xf\n\t"  \
+      "v_fmac_f32_dpp %4, %4, %16 " QP " row_mask:0xf bank_mask:0xf\n\t"  \
+      "v_fmac_f32_dpp %5, %5, %16 " QP " row_mask:0xf bank_mask:0xf\n\t"  \
+      "v_fmac_f32_dpp %6, %6, %16 " QP " row_mask:0xf bank_mask:0xf\n\t"  \
+      "v_fmac_f32_dpp %7, %7, %16 " QP " row_mask:0xf bank_mask:0xf\n\t"  \
+      "v_fmac_f32_dpp %8, %8, %16 " QP " row_mask:0xf bank_mask:0xf\n\t"  \
+      "v_fmac_f32_dpp %9, %9, %16 " QP " row_mask:0xf bank_mask:0xf\n\t"  \
+      "v_fmac_f32_dpp %10, %10, %16 " QP " row_mask:0xf bank_mask:0xf\n\t"  \
+      "v_fmac_f32_dpp %11, %11, %16 " QP " row_mask:0xf bank_mask:0xf\n\t"  \
+      "v_fmac_f32_dpp %12, %12, %16 " QP " row_mask:0xf bank_mask:0xf\n\t"  \
+      "v_fmac_f32_dpp %13, %13, %16 " QP " row_mask:0xf bank_mask:0xf\n\t"  \
+      "v_fmac_f32_dpp %14, %14, %16 " QP " row_mask:0xf bank_mask:0xf\n\t"  \
+      "v_fmac_f32_dpp %15, %15, %16 " QP " row_mask:0xf bank_mask:0xf\n\t"  \
+               : "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3]), "+v"(y[4]), "+v"(y[5]), "+v"(y[6]), "+v"(y[7]), "+v"(y[8]), "+v"(y[9]), "+v"(y[10]), "+v"(y[11]), "+v"(y[12]), "+v"(y[13]), "+v"(y[14]), "+v"(y[15]) \
+               : "v"(s))
+__device__ __forceinline__ void fmac_dpp16_xor1(float* y, float s) { KVQ_FMAC_DPP16("quad_perm:[1,0,3,2]"); }
+__device__ __forceinline__ void fmac_dpp16_xor2(float* y, float s) { KVQ_FMAC_DPP16("quad_perm:[2,3,0,1]"); }
+
 // gather the low bytes of 4 floats into one dword (byte i = x[i] low byte)
 __device__ __forceinline__ uint32_t low_bytes4(float x0, float x1, float x2, float x3) {
   const uint32_t a = __builtin_amdgcn_perm(__float_as_uint(x1), __float_as_uint(x0), 0x0C0C0400u);
@@ -1191,13 +1220,30 @@ __device__ __forceinline__ void fast_process(const AppendArgs& a, FastSmem& sm, 
           y[j] = u + v;
           y[j + hh] = u - v;
         }
-    // lower index: own + partner; upper index: partner - own = fma(own, -1, partner)
     const float s1 = (q & 1) ? -1.0f : 1.0f, s2 = (q & 2) ? -1.0f : 1.0f;
+    float c = bits_to_f32(KVQ_INV_SQRT_D_BITS);
+    if constexpr (KF != KVQ_FP4 && VF != KVQ_FP4) {
+      // h = 32, 64 across the quad: each lane forms own + s * partner (s = -1 in the upper
+      // lane of the pair), one fma with the partner as its DPP operand.  The lower lane gets
+      // own + partner; the upper lane gets own - partner, the negation of the butterfly's
+      // partner - own (rounding to nearest is symmetric), save that an exact cancellation
+      // gives +0 either way.  Stage 64 pairs lanes with the same sign, so it runs on the
+      // negated values alike, and the lane's two signs go into its normalising factor
+      // (multiplying by -c negates multiplying by c).  Only zeros can come out with the
+      // other sign, and an integer code does not see the sign of a zero (FP4 codes do: they
+      // take the exact form below).
+      fmac_dpp16_xor1(y, s1);
+      fmac_dpp16_xor1(y + 16, s1);
+      fmac_dpp16_xor2(y, s2);
+      fmac_dpp16_xor2(y + 16, s2);
+      c = c * (s1 * s2);
+    } else {
+      // lower index: own + partner; upper index: partner - own = fma(own, -1, partner)
 #pragma unroll
-    for (int j = 0; j < 32; ++j) y[j] = __builtin_fmaf(y[j], s1, dpp_f<KVQ_DPP_XOR1>(y[j]));
+      for (int j = 0; j < 32; ++j) y[j] = __builtin_fmaf(y[j], s1, dpp_f<KVQ_DPP_XOR1>(y[j]));
 #pragma unroll
-    for (int j = 0; j < 32; ++j) y[j] = __builtin_fmaf(y[j], s2, dpp_f<KVQ_DPP_XOR2>(y[j]));
-    const float c = bits_to_f32(KVQ_INV_SQRT_D_BITS);
+      for (int j = 0; j < 32; ++j) y[j] = __builtin_fmaf(y[j], s2, dpp_f<KVQ_DPP_XOR2>(y[j]));
+    }
 #pragma unroll
     for (int j = 0; j < 32; ++j) y[j] = y[j] * c;
   } else {
