@@ -29,13 +29,17 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) { return (float)__b
 // DPP quad permutations (within groups of 4 lanes)
 #define KVQ_DPP_XOR1 0xB1
 #define KVQ_DPP_XOR2 0x4E
+// v of another lane of the same row.  Only controls under which every lane reads a lane of
+// its own row are used (quad permutations, row mirrors, row rotations), so the fill value
+// (0) is never taken; in this form the compiler can read the value through the DPP operand
+// of the instruction that uses it (a max or an add) instead of a separate move.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
 }
 
 // Non-negative finite fp32 -> OCP E4M3FN code, round-to-nearest-even, saturating at 448.
