@@ -1053,28 +1053,46 @@ __device__ __forceinline__ void fast_quantize(const float y[32], bool want_sums,
 // same way (clamped to 0x00..0x7E, which only drops repeats).  Errors
 // use the same fp32 operations as the generic quantizer: per element
 // d = |y| - Q(|y|), squared, summed over elements 0..7 and 8..15, then added.
-__device__ __forceinline__ float fp4_err16(const float ay[16], float S) {
-  const float t0 = 0.25f * S, t1 = 0.75f * S, t2 = 1.25f * S, t3 = 1.75f * S, t4 = 2.5f * S, t5 = 3.5f * S,
-              t6 = 5.0f * S;
-  const float v1 = 0.5f * S, v2 = S, v3 = 1.5f * S, v4 = 2.0f * S, v5 = 3.0f * S, v6 = 4.0f * S, v7 = 6.0f * S;
-  float lo = 0.0f, hi = 0.0f;
+//
+// Q(x) for a scale S is S times the E2M1 value nearest to x / S, ties to the even code
+// (the definition's threshold chain).  Here the quotient is formed as in quot_magic (x
+// times rcp(S), one step with the exact residual: within |q| 2^-43 of q = x / S, while a
+// quotient that is not a midpoint m of the E2M1 grid lies at least 2^-24 m from it, since
+// m S has at most 7 significant bits; a midpoint quotient comes out exact) and rounded by
+// the gfx950 fp32 -> E2M1 conversion with scale 1, which rounds to nearest, ties to the
+// even code, and saturates at 6 (checked against the chain on every midpoint, its
+// neighbours, zeros, subnormals and values past 6); the reverse conversion gives the
+// grid value exactly.  xs: the magnitudes with infinities replaced by 1e30 and NaN by 0
+// (their codes under the chain: 7 and 0), so that no quotient is a NaN.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void e2m1_quot16(const float xs[16], float S, float u[16]) {
+  const float r = S != 0.0f ? __builtin_amdgcn_rcpf(S) : 0.0f;  // S = 0: every quotient 0
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const float x = ay[j];
-    // thresholds pass as a prefix (ties go to the even code), so the last one passed names the value
-    float q = x > t0 ? v1 : 0.0f;
-    q = x >= t1 ? v2 : q;
-    q = x > t2 ? v3 : q;
-    q = x >= t3 ? v4 : q;
-    q = x > t4 ? v5 : q;
-    q = x >= t5 ? v6 : q;
-    q = x > t6 ? v7 : q;
-    const float d = x - q;
-    const float sq = d * d;
-    if (j < 8)
-      lo = lo + sq;
-    else
-      hi = hi + sq;
+    const float t = xs[j] * r;
+    const float e = __builtin_fmaf(-t, S, xs[j]);
+    u[j] = __builtin_fmaf(e, r, t);
+  }
+}
+__device__ __forceinline__ float fp4_err16(const float* y, const float xs[16], float S) {
+  float u[16];
+  e2m1_quot16(xs, S, u);
+  float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, u[2 * k], u[2 * k + 1], 1.0f, 0);
+    const f32x2 g = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+    // |y| - grid value times S: the product is exact (at most 6 significant bits), so one
+    // fma gives the rounded difference of the definition
+    const float d0 = __builtin_fmaf(-g.x, S, fabsf(y[2 * k])), d1 = __builtin_fmaf(-g.y, S, fabsf(y[2 * k + 1]));
+    const float s0 = d0 * d0, s1 = d1 * d1;
+    if (k < 4) {
+      lo = lo + s0;
+      lo = lo + s1;
+    } else {
+      hi = hi + s0;
+      hi = hi + s1;
+    }
   }
   return lo + hi;
 }
@@ -1085,12 +1103,14 @@ __device__ __forceinline__ void fast_quantize_fp4(const float y[32], int mode, b
   uint32_t sc[2];
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
-    float ay[16];
+    const float* yb = y + 16 * blk;
+    float xs[16];
     float am = 0.0f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      ay[j] = fabsf(y[16 * blk + j]);
-      am = fmaxf(am, ay[j]);
+      const float ay = fabsf(yb[j]);
+      am = fmaxf(am, ay);
+      xs[j] = ay <= 1e30f ? ay : (ay > 1e30f ? 1e30f : 0.0f);
     }
     const float t = am / 6.0f;  // correctly rounded fp32 divide
     uint32_t best, chi;
@@ -1103,9 +1123,9 @@ __device__ __forceinline__ void fast_quantize_fp4(const float y[32], int mode, b
       chi = mode == KVQ_SCALE_SEARCH_OFFSETS ? min(c0 + 6u, 0x7Eu) : c0;
     }
     if (chi > best) {
-      float best_e = fp4_err16(ay, e4m3_value(best));
+      float best_e = fp4_err16(yb, xs, e4m3_value(best));
       for (uint32_t c = best + 1; c <= chi; ++c) {
-        const float e = fp4_err16(ay, e4m3_value(c));
+        const float e = fp4_err16(yb, xs, e4m3_value(c));
         if (e < best_e) {
           best_e = e;
           best = c;
@@ -1114,33 +1134,29 @@ __device__ __forceinline__ void fast_quantize_fp4(const float y[32], int mode, b
     }
     sc[blk] = best;
     const float S = e4m3_value(best);
-    const float t0 = 0.25f * S, t1 = 0.75f * S, t2 = 1.25f * S, t3 = 1.75f * S, t4 = 2.5f * S, t5 = 3.5f * S,
-                t6 = 5.0f * S;
-    uint32_t nib[16];
+    // codes with their signs: the quotient takes the sign bit of y, and the conversion
+    // carries it (-0 included) into bit 3; a zero scale gives code 0 for every element
+    float u[16];
+    e2m1_quot16(xs, S, u);
+    uint32_t w[2] = {0u, 0u};
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float x = ay[j];
-      uint32_t idx = x > t0 ? 1u : 0u;
-      idx = x >= t1 ? 2u : idx;
-      idx = x > t2 ? 3u : idx;
-      idx = x >= t3 ? 4u : idx;
-      idx = x > t4 ? 5u : idx;
-      idx = x >= t5 ? 6u : idx;
-      idx = x > t6 ? 7u : idx;
-      idx = S != 0.0f ? idx | ((__float_as_uint(y[16 * blk + j]) >> 31) << 3) : 0u;
-      nib[j] = idx;
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t sg0 = __float_as_uint(y[16 * blk + 2 * k]) & 0x80000000u;
+      const uint32_t sg1 = __float_as_uint(y[16 * blk + 2 * k + 1]) & 0x80000000u;
+      const float v0 = __uint_as_float(__float_as_uint(u[2 * k]) | sg0);
+      const float v1 = __uint_as_float(__float_as_uint(u[2 * k + 1]) | sg1);
+      const uint32_t c = S != 0.0f ? __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v0, v1, 1.0f, 0) & 0xFFu : 0u;
+      w[k >> 2] |= c << (8 * (k & 3));
       if (want_sums) {
-        const float d = x - e2m1_mag((int)(idx & 7u)) * S;
-        acc = acc + d * d;
+        const f32x2 g = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+        const float d0 = __builtin_fmaf(-fabsf(g.x), S, fabsf(yb[2 * k]));
+        const float d1 = __builtin_fmaf(-fabsf(g.y), S, fabsf(yb[2 * k + 1]));
+        acc = acc + d0 * d0;
+        acc = acc + d1 * d1;
       }
     }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) w |= nib[8 * k + e] << (4 * e);
-      packed[2 * blk + k] = w;
-    }
+    packed[2 * blk] = w[0];
+    packed[2 * blk + 1] = w[1];
   }
   meta = (uint16_t)(sc[0] | (sc[1] << 8));
   res2 = acc;
