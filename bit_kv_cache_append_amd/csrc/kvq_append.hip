@@ -813,6 +813,14 @@ __device__ __forceinline__ constexpr int rev4(int i) {
 // (r = 1, 3), at register 15 - i (lane 0: rev4(16 - rev4(i))).  The packed output
 // goes through one LDS row per vector back to the natural channel order.  y holds
 // the sign-flipped input on entry and the rotated vector on return.
+// NEG (integer codes): passes 0 and 1 form own + s * partner in one DPP-sourced fma, so
+// the upper lane of each pair holds the negated butterfly output (as in the Hadamard fast
+// path); the twiddle of the lower lane is W^0 = 1, so no select is needed.  After both
+// passes lane q holds its values times sigma_q = (-1)^(q0 + q1); everything after is
+// linear, the Hermitian partner taken from lane q ^ 1 carries -sigma_q and is negated, and
+// sigma_q goes into the output factor.  Only signs of zeros can differ from the exact form,
+// which integer codes do not see.
+template <bool NEG>
 __device__ __forceinline__ void srft_regs(float y[32], int q, int vec, SrftRegSmem& sm) {
   float zr[16], zi[16];
 #pragma unroll
@@ -821,6 +829,26 @@ __device__ __forceinline__ void srft_regs(float y[32], int q, int vec, SrftRegSm
     zi[i] = y[2 * i + 1];
   }
   const int q0 = q & 1, q1 = q >> 1;
+  if constexpr (NEG) {
+    fmac_dpp16_xor2(zr, q1 ? -1.0f : 1.0f);
+    fmac_dpp16_xor2(zi, q1 ? -1.0f : 1.0f);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = q1 ? 32 * q0 + 2 * i : 0;
+      const float wr = sm.twr[e], wi = sm.twi[e], vr = zr[i], vi = zi[i];
+      zr[i] = vr * wr - vi * wi;
+      zi[i] = vr * wi + vi * wr;
+    }
+    fmac_dpp16_xor1(zr, q0 ? -1.0f : 1.0f);
+    fmac_dpp16_xor1(zi, q0 ? -1.0f : 1.0f);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = q0 ? 4 * i : 0;
+      const float wr = sm.twr[e], wi = sm.twi[e], vr = zr[i], vi = zi[i];
+      zr[i] = vr * wr - vi * wi;
+      zi[i] = vr * wi + vi * wr;
+    }
+  } else {
   // passes 0 and 1: the lower element takes own + partner, the upper one
   // (partner - own) W, with W64^(jm) = W128^(2jm): 32 q0 + 2i in pass 0, 4i in pass 1
   {
@@ -847,6 +875,7 @@ __device__ __forceinline__ void srft_regs(float y[32], int q, int vec, SrftRegSm
       zr[i] = q0 ? tr : vr;
       zi[i] = q0 ? ti : vi;
     }
+  }
   }
   // passes 2..5 inside the lane: pairs (i, i + h), h = 8, 4, 2, 1
   auto bfly = [&](int ia, int ib, int e) {
@@ -888,8 +917,8 @@ __device__ __forceinline__ void srft_regs(float y[32], int q, int vec, SrftRegSm
     float pr = zr[i1], pi = zi[i1];
     const float dr = dpp_f<KVQ_DPP_XOR1>(zr[i1]), di = dpp_f<KVQ_DPP_XOR1>(zi[i1]);
     if (q1) {
-      pr = dr;
-      pi = di;
+      pr = NEG ? -dr : dr;  // (the partner lane carries the opposite sign)
+      pi = NEG ? -di : di;
     } else if (q == 0) {
       pr = zr[i0];
       pi = zi[i0];
@@ -897,7 +926,8 @@ __device__ __forceinline__ void srft_regs(float y[32], int q, int vec, SrftRegSm
     const int k = 4 * rev4(i) + r;
     float xr, xi;
     unpack(zr[i], zi[i], pr, pi, k, xr, xi);
-    float v0 = xr * 0.125f, v1 = xi * 0.125f;
+    const float sc = NEG && (q0 ^ q1) ? -0.125f : 0.125f;  // 0.125 sigma_q
+    float v0 = xr * sc, v1 = xi * sc;
     if (i == 0 && q == 0) {  // X_0 and X_64 (both from Z_0) are the two real channels
       float nr, ni;
       unpack(zr[0], zi[0], zr[0], zi[0], 64, nr, ni);
@@ -1203,7 +1233,7 @@ __device__ __forceinline__ void fast_process(const AppendArgs& a, FastSmem& sm, 
       y[2 * k] = widen((uint16_t)(ws & 0xFFFF), BF16);
       y[2 * k + 1] = widen((uint16_t)(ws >> 16), BF16);
     }
-    srft_regs(y, q, tau, *ss);
+    srft_regs<KF != KVQ_FP4 && VF != KVQ_FP4>(y, q, tau, *ss);
   } else if (fwht) {
     if constexpr (BF16) {
 #pragma unroll
