@@ -515,6 +515,25 @@ __device__ __forceinline__ float rec_ld(const float* p) {
   if constexpr (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   else return *p;
 }
+// two adjacent record words (8-byte aligned) in one access
+template <bool COH>
+__device__ __forceinline__ void rec_st2(float* p, float v0, float v1) {
+  if constexpr (COH) {
+    const uint64_t w = (uint64_t)__float_as_uint(v0) | ((uint64_t)__float_as_uint(v1) << 32);
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    *reinterpret_cast<float2*>(p) = make_float2(v0, v1);
+  }
+}
+template <bool COH>
+__device__ __forceinline__ float2 rec_ld2(const float* p) {
+  if constexpr (COH) {
+    const uint64_t w = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((uint32_t)w), __uint_as_float((uint32_t)(w >> 32)));
+  } else {
+    return *reinterpret_cast<const float2*>(p);
+  }
+}
 
 // ------------------------------------------------------------------ split record
 // Merges waves [w0, w0 + nw) of this workgroup (log-sum-exp weights) and writes head hh's
@@ -544,12 +563,8 @@ __device__ void write_record(const DecodeArgs& a, const MergeArea<NW>& mg, const
     ek = fmaxf(ek, mg.ek[w]);
     vn = fmaxf(vn, mg.vn[w]);
   }
-  rec_st<COH>(rec + 8 + c, o0);
-  rec_st<COH>(rec + 8 + c + 1, o1);
-  if constexpr (CERT) {
-    rec_st<COH>(rec + 8 + D + c, p0);
-    rec_st<COH>(rec + 8 + D + c + 1, p1);
-  }
+  rec_st2<COH>(rec + 8 + c, o0, o1);
+  if constexpr (CERT) rec_st2<COH>(rec + 8 + D + c, p0, p1);
   float qn = 0.0f;
   if constexpr (CERT) {
     // ||q|| * scale from the prologue's q * scale * log2(e)
@@ -559,9 +574,9 @@ __device__ void write_record(const DecodeArgs& a, const MergeArea<NW>& mg, const
     qn = sqrtf(sq) / LOG2E;
   }
   if (l == 0) {
-    const float hdr[6] = {M, L, E, ek, vn, qn};
-#pragma unroll
-    for (int i = 0; i < 6; ++i) rec_st<COH>(rec + i, hdr[i]);
+    rec_st2<COH>(rec, M, L);
+    rec_st2<COH>(rec + 2, E, ek);
+    rec_st2<COH>(rec + 4, vn, qn);
   }
 }
 
@@ -569,7 +584,7 @@ __device__ void write_record(const DecodeArgs& a, const MergeArea<NW>& mg, const
 // One wave per (sequence, query head): log-sum-exp merge of the split records,
 // inverse rotation back to the original basis ("OSCAR", section 2.2B), and the
 // certificate.  zsw: 128 floats of LDS private to the wave.
-template <bool CERT, bool COH>
+template <bool CERT, bool COH, int SB = 8>
 __device__ void combine_row(const DecodeArgs& a, int row, float* zsw, const float* ctab) {
   const int l = threadIdx.x & 63, c = 2 * l;
   const int b = row / a.Hq;
@@ -580,11 +595,11 @@ __device__ void combine_row(const DecodeArgs& a, int row, float* zsw, const floa
     if (CERT && a.cert && l == 0) a.cert[row] = 0.0f;
     return;
   }
-  // Records in batches of 8 splits: all loads of a batch are issued together
-  // (indices past the last split reload it and get weight 0), then merged with
-  // a running maximum.
+  // Records in batches of SB splits (2 when a unit has at most 2, else 8): all loads
+  // of a batch are issued together (indices past the last split reload it and get
+  // weight 0), then merged with a running maximum.  Adjacent record words travel in
+  // pairs (one 64-bit access each).
   const float* rec0 = a.part + (size_t)row * a.n_splits * PART_FLOATS;
-  constexpr int SB = 8;
   float M = NEG_INF, L = 0.0f, E = 0.0f, ek = 0.0f, vn = 0.0f, o0 = 0.0f, o1 = 0.0f, p0 = 0.0f, p1 = 0.0f;
   for (int s0 = 0; s0 < a.n_splits; s0 += SB) {
     float4 hd[SB];
@@ -594,10 +609,11 @@ __device__ void combine_row(const DecodeArgs& a, int row, float* zsw, const floa
     for (int i = 0; i < SB; ++i) {
       const float* rec = rec0 + (size_t)min(s0 + i, a.n_splits - 1) * PART_FLOATS;
       if constexpr (COH) {
-        hd[i] = make_float4(rec_ld<true>(rec), rec_ld<true>(rec + 1), rec_ld<true>(rec + 2), rec_ld<true>(rec + 3));
+        const float2 h01 = rec_ld2<true>(rec), h23 = rec_ld2<true>(rec + 2);
+        hd[i] = make_float4(h01.x, h01.y, h23.x, h23.y);
         vs[i] = rec_ld<true>(rec + 4);
-        ov[i] = make_float2(rec_ld<true>(rec + 8 + c), rec_ld<true>(rec + 8 + c + 1));
-        if constexpr (CERT) pv[i] = make_float2(rec_ld<true>(rec + 8 + D + c), rec_ld<true>(rec + 8 + D + c + 1));
+        ov[i] = rec_ld2<true>(rec + 8 + c);
+        if constexpr (CERT) pv[i] = rec_ld2<true>(rec + 8 + D + c);
       } else {
         hd[i] = *reinterpret_cast<const float4*>(rec);
         vs[i] = rec[4];
@@ -1443,7 +1459,12 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   }
   __syncthreads();
   if (sm.last) {
-    if (wv < nh) combine_row<EXACT, true>(a, b * a.Hq + hq0 + wv, sm.u.zsw[wv], sm.ctab);
+    if (wv < nh) {
+      if (S <= 2)
+        combine_row<EXACT, true, 2>(a, b * a.Hq + hq0 + wv, sm.u.zsw[wv], sm.ctab);
+      else
+        combine_row<EXACT, true, 8>(a, b * a.Hq + hq0 + wv, sm.u.zsw[wv], sm.ctab);
+    }
     if (t == 0) __hip_atomic_store(a.ctr + u, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
