@@ -45,6 +45,7 @@ namespace {
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
 typedef int i4 __attribute__((ext_vector_type(4)));
 
 constexpr int NT = 256;   // combine kernel, fp16 baseline split kernel
@@ -144,18 +145,23 @@ __device__ __forceinline__ void v_int4_pairs(uint32_t w, h2 out[4]) {
   out[2] = as_h2((w8 & 0x000F000Fu) ^ 0x64086408u) + k1032;                    // tokens 2, 6
   out[3] = as_h2((w8 & 0x00F000F0u) ^ 0x64806480u) * k16 + k72;                // tokens 3, 7
 }
-// int2: element k and k+8 of a 16-token dword, codes 0..3
+// int2: element k and k+8 of a 16-token dword, codes 0..3.  (w & mask) | magic is one
+// three-input bit operation (truth table 0xEA over (w, mask, magic), the index of a bit
+// being w<<2 | mask<<1 | magic), which the compiler otherwise issues as an and and an or.
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic) {
+  return __builtin_amdgcn_bitop3_b32(w, mask, magic, (unsigned char)0xEA);
+}
 __device__ __forceinline__ void v_int2_pairs(uint32_t w, h2 out[8]) {
   const uint32_t magic = 0x64006400u;
   const uint32_t w10 = w >> 10;
-  out[0] = as_h2((w & 0x00030003u) | magic) + h2{(_Float16)-1024.0f, (_Float16)-1024.0f};
-  out[1] = as_h2((w & 0x000C000Cu) | magic) * h2{(_Float16)0.25f, (_Float16)0.25f} + h2{(_Float16)-256.0f, (_Float16)-256.0f};
-  out[2] = as_h2((w & 0x00300030u) | magic) * h2{(_Float16)0.0625f, (_Float16)0.0625f} + h2{(_Float16)-64.0f, (_Float16)-64.0f};
-  out[3] = as_h2((w & 0x00C000C0u) | magic) * h2{(_Float16)0.015625f, (_Float16)0.015625f} + h2{(_Float16)-16.0f, (_Float16)-16.0f};
-  out[4] = as_h2((w & 0x03000300u) | magic) * h2{(_Float16)0.00390625f, (_Float16)0.00390625f} + h2{(_Float16)-4.0f, (_Float16)-4.0f};
-  out[5] = as_h2((w10 & 0x00030003u) | magic) + h2{(_Float16)-1024.0f, (_Float16)-1024.0f};
-  out[6] = as_h2((w10 & 0x000C000Cu) | magic) * h2{(_Float16)0.25f, (_Float16)0.25f} + h2{(_Float16)-256.0f, (_Float16)-256.0f};
-  out[7] = as_h2((w10 & 0x00300030u) | magic) * h2{(_Float16)0.0625f, (_Float16)0.0625f} + h2{(_Float16)-64.0f, (_Float16)-64.0f};
+  out[0] = as_h2(and_or(w, 0x00030003u, magic)) + h2{(_Float16)-1024.0f, (_Float16)-1024.0f};
+  out[1] = as_h2(and_or(w, 0x000C000Cu, magic)) * h2{(_Float16)0.25f, (_Float16)0.25f} + h2{(_Float16)-256.0f, (_Float16)-256.0f};
+  out[2] = as_h2(and_or(w, 0x00300030u, magic)) * h2{(_Float16)0.0625f, (_Float16)0.0625f} + h2{(_Float16)-64.0f, (_Float16)-64.0f};
+  out[3] = as_h2(and_or(w, 0x00C000C0u, magic)) * h2{(_Float16)0.015625f, (_Float16)0.015625f} + h2{(_Float16)-16.0f, (_Float16)-16.0f};
+  out[4] = as_h2(and_or(w, 0x03000300u, magic)) * h2{(_Float16)0.00390625f, (_Float16)0.00390625f} + h2{(_Float16)-4.0f, (_Float16)-4.0f};
+  out[5] = as_h2(and_or(w10, 0x00030003u, magic)) + h2{(_Float16)-1024.0f, (_Float16)-1024.0f};
+  out[6] = as_h2(and_or(w10, 0x000C000Cu, magic)) * h2{(_Float16)0.25f, (_Float16)0.25f} + h2{(_Float16)-256.0f, (_Float16)-256.0f};
+  out[7] = as_h2(and_or(w10, 0x00300030u, magic)) * h2{(_Float16)0.0625f, (_Float16)0.0625f} + h2{(_Float16)-64.0f, (_Float16)-64.0f};
 }
 
 template <int VF>
@@ -919,6 +925,8 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   // fp16 rounding for FP4 values: with it their worst attention rows are ~3e-4 (the bar is
   // 2e-3), and the second pair of products cost ~7 % of their decode time
   constexpr bool PV_LO = VF != KVQ_FP4;
+  float neg_one = -1.0f;
+  asm volatile("" : "+v"(neg_one));  // opaque: fma(hi, -1, x) is not turned into x - hi
   // V scale group of channels 2*lane, 2*lane+1: 32-channel group, one per token, or 16-channel block
   const int vgrp = (VF == KVQ_FP4 || VG == 16) ? (lane >> 3) : (VG == 128) ? 0 : (lane >> 4);
   uint16_t* vml = &sm.vmeta[wv][0][0][0];
@@ -1201,6 +1209,8 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
     // be anything).
     // (scales are never negative, so max(p s, 0) changes no weight and turns the 0 * NaN of
     // a position past the end into 0)
+    // (hi is formed by packed conversions; the remainder x - hi by one mixed-precision fma per
+    // weight that reads hi's fp16 half directly, with an opaque -1 so that it stays an fma)
     const uint2* vmw = reinterpret_cast<const uint2*>(vml) + s_a;
     uint2 sc[NGV];
 #pragma unroll
@@ -1210,11 +1220,12 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
       const h2 s01 = as_h2(sc[g].x), s23 = as_h2(sc[g].y);
       const float x0 = fmaxf(fmaf(p[0], (float)s01.x, 0.0f), 0.0f), x1 = fmaxf(fmaf(p[1], (float)s01.y, 0.0f), 0.0f);
       const float x2 = fmaxf(fmaf(p[2], (float)s23.x, 0.0f), 0.0f), x3 = fmaxf(fmaf(p[3], (float)s23.y, 0.0f), 0.0f);
-      const h2 hi01 = {(_Float16)x0, (_Float16)x1}, hi23 = {(_Float16)x2, (_Float16)x3};
+      const h2 hi01 = __builtin_convertvector(f2{x0, x1}, h2), hi23 = __builtin_convertvector(f2{x2, x3}, h2);
       if constexpr (PV_LO) {
         // the remainder x - hi is exact in fp32 (hi is x rounded to 11 bits)
-        const h2 lo01 = {(_Float16)fmaf((float)hi01.x, -1.0f, x0), (_Float16)fmaf((float)hi01.y, -1.0f, x1)};
-        const h2 lo23 = {(_Float16)fmaf((float)hi23.x, -1.0f, x2), (_Float16)fmaf((float)hi23.y, -1.0f, x3)};
+        const f2 r01 = {fmaf((float)hi01.x, neg_one, x0), fmaf((float)hi01.y, neg_one, x1)};
+        const f2 r23 = {fmaf((float)hi23.x, neg_one, x2), fmaf((float)hi23.y, neg_one, x3)};
+        const h2 lo01 = __builtin_convertvector(r01, h2), lo23 = __builtin_convertvector(r23, h2);
         sm.u.loop.pw[wv][g][s_a][j] = make_uint4(as_u(hi01), as_u(hi23), as_u(lo01), as_u(lo23));
       } else {
         sm.u.loop.pw[wv][g][s_a][j] = make_uint4(as_u(hi01), as_u(hi23), 0u, 0u);
