@@ -1143,15 +1143,16 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
           sw[w] = kscale_word(r, w);
           if constexpr (KF == KVQ_INT2) zw[w] = kscale_word(r, 2 + w);
         }
+        // each group's sum times its fp16 scale (and the int2 offset times the query's
+        // group sum) accumulated by fmas that read the fp16 halves directly
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
           const uint16_t sb = (uint16_t)(sw[g >> 1] >> (16 * (g & 1)));
-          float v = (float)acc[g][r] * f16_bits_to_f32(sb);
+          l[r] = fmaf((float)acc[g][r], f16_bits_to_f32(sb), l[r]);
           if constexpr (KF == KVQ_INT2) {
             const uint16_t zb = (uint16_t)(zw[g >> 1] >> (16 * (g & 1)));
-            v = fmaf(f16_bits_to_f32(zb), qsum[g], v);
+            l[r] = fmaf(f16_bits_to_f32(zb), qsum[g], l[r]);
           }
-          l[r] += v;
         }
       }
     }
@@ -1238,14 +1239,26 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
       uint2 zc[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) zc[g] = vmw[(4 + g) * 16];
+      // one fma per token on the fp16 offsets; the chunk holding the sequence end (rare,
+      // wave-uniform) takes the masked sums in a branch of its own (the empty asm keeps the
+      // compiler from evaluating both forms on every chunk and selecting)
+      float zs[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const h2 z01 = as_h2(zc[g].x), z23 = as_h2(zc[g].y);
-        float zs = p[0] * (float)z01.x + p[1] * (float)z01.y + p[2] * (float)z23.x + p[3] * (float)z23.y;
-        if (tail) zs = (p[0] > 0.0f ? p[0] * (float)z01.x : 0.0f) + (p[1] > 0.0f ? p[1] * (float)z01.y : 0.0f) +
-                       (p[2] > 0.0f ? p[2] * (float)z23.x : 0.0f) + (p[3] > 0.0f ? p[3] * (float)z23.y : 0.0f);
-        zacc[g] = zacc[g] * alpha + zs;
+        zs[g] = fmaf(p[3], (float)z23.y, fmaf(p[2], (float)z23.x, fmaf(p[1], (float)z01.y, p[0] * (float)z01.x)));
       }
+      if (tail) {
+        asm volatile("");
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const h2 z01 = as_h2(zc[g].x), z23 = as_h2(zc[g].y);
+          zs[g] = (p[0] > 0.0f ? p[0] * (float)z01.x : 0.0f) + (p[1] > 0.0f ? p[1] * (float)z01.y : 0.0f) +
+                  (p[2] > 0.0f ? p[2] * (float)z23.x : 0.0f) + (p[3] > 0.0f ? p[3] * (float)z23.y : 0.0f);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) zacc[g] = fmaf(zacc[g], alpha, zs[g]);
     }
     // ---- PV: step s takes the weights of tokens pi(s, 0..3) for this lane's head row and
     // V group, high and low parts through two products each
