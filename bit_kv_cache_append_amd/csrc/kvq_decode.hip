@@ -1065,11 +1065,20 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
         for (int w = 0; w < 2; ++w)
           sw[w] = r == 0 ? quad_bcast_u<0>(R.kmeta[w]) : r == 1 ? quad_bcast_u<1>(R.kmeta[w])
                 : r == 2 ? quad_bcast_u<2>(R.kmeta[w]) : quad_bcast_u<3>(R.kmeta[w]);
+        // the token's 8 E4M3 block scales, exactly, by the gfx950 fp8 -> fp32 conversion
+        // (scale 1), two per instruction; blocks 0..7 in order
+        float sf[8];
 #pragma unroll
-        for (int bk = 0; bk < 8; ++bk) {
-          const uint32_t sb = (sw[bk >> 2] >> (8 * (bk & 3))) & 0xFFu;
-          l[r] = fmaf(ab[bk][r], f16_bits_to_f32((uint16_t)(sb << 7)) * 256.0f, l[r]);
+        for (int w = 0; w < 2; ++w) {
+          const f2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw[w], 1.0f, false);
+          const f2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw[w], 1.0f, true);
+          sf[4 * w] = lo.x;
+          sf[4 * w + 1] = lo.y;
+          sf[4 * w + 2] = hi.x;
+          sf[4 * w + 3] = hi.y;
         }
+#pragma unroll
+        for (int bk = 0; bk < 8; ++bk) l[r] = fmaf(ab[bk][r], sf[bk], l[r]);
       }
     } else {
       // ---- QK^T: exact integer dot products.  Four independent accumulator
