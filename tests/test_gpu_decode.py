@@ -253,3 +253,30 @@ def test_split_count_invariance(cfg):
         E1, E16 = e1.cpu().numpy()[0], e16.cpu().numpy()[0]
         assert np.allclose(E1, E16, rtol=1e-5, atol=1e-9), "certificates differ between split counts"
         assert not e16.cpu().numpy()[1:].any()
+
+
+def test_fp4_every_scale_code():
+    """FP4 keys and values over every E4M3 scale code 0x00..0x7E (subnormal, normal, the largest,
+    448) and random E2M1 nibbles, written straight into the cache bytes: the decode reads the
+    scales through the hardware fp8 conversion (keys) and the fp16 bit form (values), the oracle
+    by the E4M3 definition; attention over the same bytes within the bar."""
+    c = synth.config(5, B=2, Hq=4, Hkv=1, T=1024, dtype="f16")
+    s, r16, s_dev, r_dev = setup_rotation(c)
+    p, gcache = make_gpu_cache(c, s_dev, r_dev)
+    oc = codec.Cache(c["B"], c["Hkv"], c["T"], "fp4", "fp4", c["k_group"], c["v_group"])
+    rng = np.random.default_rng(2024)
+    oc.k_codes[...] = rng.integers(0, 256, size=oc.k_codes.shape, dtype=np.uint8)
+    oc.v_codes[...] = rng.integers(0, 256, size=oc.v_codes.shape, dtype=np.uint8)
+    oc.k_meta[...] = (np.arange(oc.k_meta.size) % 0x7F).reshape(oc.k_meta.shape).astype(np.uint8)
+    oc.v_meta[...] = ((np.arange(oc.v_meta.size) * 5) % 0x7F).reshape(oc.v_meta.shape).astype(np.uint8)
+    assert set(np.unique(oc.k_meta)) == set(range(0x7F)) and set(np.unique(oc.v_meta)) == set(range(0x7F))
+    for name in ("k_codes", "k_meta", "v_codes", "v_meta"):
+        gcache.bufs[name].copy_(torch.from_numpy(getattr(oc, name).reshape(-1)))
+    # a small query keeps the logits moderate (keys reach 6 x 448 per channel)
+    q = synth.to_f16_bits(0.02 * rng.standard_normal((c["B"], c["Hq"], 128)))
+    seq = [1024, 777]
+    out = kvq.decode_attn(p, gcache, dev_bits(q), seq)
+    torch.cuda.synchronize()
+    ref, _ = attention.decode_attention(oc, q, "f16", np.array(seq), c["rotation"], s, r16)
+    rows = [(b, hq) for b in range(c["B"]) for hq in range(c["Hq"])]
+    _check_rows(out.cpu().numpy(), ref, rows, "fp4-every-scale-code")
