@@ -189,6 +189,15 @@ __device__ __forceinline__ void load_keys(const uint8_t* row, const uint8_t* met
   }
 }
 
+// 8-bit keys with one scale per token, for the 16 x 16 x 64 integer product: tile t of
+// the block (tokens 16t..16t+15), K half s (channels 64s..64s+63); lane l holds token
+// 16t + (l & 15), channels 64s + 16 (l >> 4) .. + 15 (the product's row-operand layout),
+// and the fp16 scales of tokens 16t + 4 (l >> 4) + 0..3 (its output rows).
+struct WideKeys {
+  i4a a[8];
+  uint2 sc[4];
+};
+
 // Max (MAX) or sum over the 16 lanes of one head (the lanes with equal lane & 3): row
 // rotations by 4 and 8 inside each row of 16 lanes (DPP), then the gfx950 row and
 // half-wave swaps, which give every lane its own value and its partner's; no round trip
@@ -237,6 +246,7 @@ __global__ __launch_bounds__(NTW) void score_kernel(AdaptArgs a) {
   __shared__ float qsc[4];      // per head: the query's unit (INT: qs; FP4: the power-of-two scale)
   __shared__ int qds[4][8][4];  // per head, group, digit: digit sums (INT4 offset correction)
   __shared__ float qsf[4][4];   // per head, 32-channel group: sum of the rotated query (INT2 offsets)
+  __shared__ int qint[4][D];    // per head and channel: the 24-bit query (8-bit keys, one scale per token)
   __shared__ int next;          // next block (offset from the split's first) to claim
   const int S = a.score_splits;
   const int u = blockIdx.x / S, split = blockIdx.x % S;
@@ -261,10 +271,31 @@ __global__ __launch_bounds__(NTW) void score_kernel(AdaptArgs a) {
     key_ptrs(c, rp, mp);
     load_keys<KF, KG>(rp, mp, R);
   };
+  // 8-bit keys with one scale per token (the certified workload's keys) take the
+  // 16 x 16 x 64 integer product: 8 per block and wave instead of 96 of the 4 x 4 x 4 one
+  constexpr bool WIDE = KF == KVQ_INT8 && GS == D;
+  auto load_wide = [&](int c, WideKeys& R) {
+    KVQ_DCHECK(stream < (size_t)a.B * a.H && c >= 0 && c < a.nt, DBG_CHUNK, stream, c);
+    const uint8_t* kb = a.k_codes + (stream * a.Tmax + (size_t)c * TILE) * KB;
+    const uint8_t* mb = a.k_meta + (stream * a.Tmax + (size_t)c * TILE) * KM;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint4 u = *reinterpret_cast<const uint4*>(kb + (size_t)(16 * t + (lane & 15)) * KB + 64 * h + 16 * (lane >> 4));
+        R.a[2 * t + h] = i4a{(int)u.x, (int)u.y, (int)u.z, (int)u.w};
+      }
+      R.sc[t] = *reinterpret_cast<const uint2*>(mb + (size_t)(16 * t + 4 * (lane >> 4)) * KM);
+    }
+  };
   // the first block's keys are in flight during the query prologue
   KeyRegs<KF, KG> RA, RB;
+  WideKeys WA, WB;
   int cA = c0 + wv;
-  load_block(cA < c1 ? cA : c0, RA);
+  if constexpr (WIDE)
+    load_wide(cA < c1 ? cA : c0, WA);
+  else
+    load_block(cA < c1 ? cA : c0, RA);
   __builtin_amdgcn_sched_barrier(0);
   if (threadIdx.x == 0) next = NWV;  // published by the prologue's barrier
   if (a.rotation == KVQ_ROT_SRFT) {
@@ -310,6 +341,7 @@ __global__ __launch_bounds__(NTW) void score_kernel(AdaptArgs a) {
       for (int e = 0; e < 2; ++e) {
         const int c = 2 * lane + e;
         const int qv = (int)rintf(ys[e] / qs);  // |qv| <= 8e6
+        if constexpr (WIDE) qint[wv][c] = qv;
         const int d0 = ((qv + 128) & 255) - 128, r1 = (qv - d0) >> 8;
         const int d1 = ((r1 + 128) & 255) - 128, d2 = (r1 - d1) >> 8;  // |d2| <= 123
         int n, m;
@@ -341,6 +373,72 @@ __global__ __launch_bounds__(NTW) void score_kernel(AdaptArgs a) {
   __syncthreads();
   const int j = lane & 3;  // head of this lane's outputs
   const float unit = qsc[j];
+  // wide products: the query operand of K half s for column l & 15 = 4 d + h is digit d
+  // (0, 1, 2; column d = 3 is zero) of head h at channels 64s + 16 (l >> 4) .. + 15, the
+  // digits split as in the prologue's 4 x 4 x 4 operands
+  i4a qb[2] = {i4a{0, 0, 0, 0}, i4a{0, 0, 0, 0}};
+  if constexpr (WIDE) {
+    const int dg = (lane & 15) >> 2;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int w4[4];
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const int qv = qint[j][64 * h + 16 * (lane >> 4) + 4 * k4 + bb];
+          const int d0 = ((qv + 128) & 255) - 128, r1 = (qv - d0) >> 8;
+          const int d1 = ((r1 + 128) & 255) - 128, d2 = (r1 - d1) >> 8;
+          const int dig = dg == 0 ? d0 : dg == 1 ? d1 : dg == 2 ? d2 : 0;
+          word |= (uint32_t)(dig & 0xFF) << (8 * bb);
+        }
+        w4[k4] = (int)word;
+      }
+      qb[h] = i4a{w4[0], w4[1], w4[2], w4[3]};
+    }
+  }
+  // one block by the wide products: lane l holds digit (l & 15) >> 2 of head l & 3 for
+  // tokens 16t + 4 (l >> 4) + i; the lanes of digit 0 gather digits 1 and 2 from the
+  // lanes 4 and 8 places on in their row of 16 (a rotation by 8 either way, and the sum
+  // of the rotations by 4 and by 12, one of which reads the zero digit-3 lane) and form
+  // the sum as the 4 x 4 x 4 path does; the other lanes take no part in the reductions
+  auto score_wide = [&](const WideKeys& K, int c) {
+    i4a acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      acc[t] = i4a{0, 0, 0, 0};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(K.a[2 * t + h], qb[h], acc[t], 0, 0, 0);
+    }
+    const bool lead = (lane & 12) == 0;  // digit 0
+    const int tok = c * TILE + 4 * (lane >> 4);
+    float mx = NEG_INF_A;
+    float sc[16];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int a0 = acc[t][i];
+        const int a1 = __builtin_amdgcn_mov_dpp(a0, 0x124, 0xF, 0xF, false) + __builtin_amdgcn_mov_dpp(a0, 0x12C, 0xF, 0xF, false);
+        const int a2 = __builtin_amdgcn_mov_dpp(a0, 0x128, 0xF, 0xF, false);
+        const float part = ((float)a2 * 65536.0f + (float)a1 * 256.0f) + (float)a0;
+        const uint32_t sw = (i < 2) ? K.sc[t].x : K.sc[t].y;
+        const float sg = f16_bits_to_f32((uint16_t)(sw >> (16 * (i & 1))));
+        float v = fmaf(part * unit, sg, 0.0f);
+        if (!lead || tok + 16 * t + i >= T) v = NEG_INF_A;
+        sc[4 * t + i] = v;
+        mx = fmaxf(mx, v);
+      }
+    }
+    mx = head_reduce<true>(mx);
+    float se = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) se += sc[k] == NEG_INF_A ? 0.0f : expf(sc[k] - mx);
+    se = head_reduce<false>(se);
+    KVQ_DCHECK(lane >= nh || hq0 + lane < a.Hq, DBG_ROW, (size_t)b * a.Hq + hq0 + lane, c);
+    if (lane < nh) a.mass[((size_t)b * a.Hq + hq0 + lane) * a.nt + c] = mx + logf(se);
+  };
   auto claim = [&]() -> int {
     int v = 0;
     if (lane == 0) v = atomicAdd(&next, 1);
@@ -427,6 +525,25 @@ __global__ __launch_bounds__(NTW) void score_kernel(AdaptArgs a) {
   // valid block, so every iteration issues the same loads (claims only grow: once one is
   // past the end the next is too, and the wave leaves at the loop head).
   int pB = claim();
+  if constexpr (WIDE) {
+    while (cA < c1) {
+      const int cB = c0 + __builtin_amdgcn_readfirstlane(pB);
+      const int pC = claim();
+      load_wide(cB < c1 ? cB : cA, WB);
+      __builtin_amdgcn_sched_barrier(0);
+      score_wide(WA, cA);
+      int pCv = pC;
+      asm volatile("" : "+v"(pCv));
+      const int cC = c0 + __builtin_amdgcn_readfirstlane(pCv);
+      pB = claim();
+      load_wide(cC < c1 ? cC : cA, WA);
+      __builtin_amdgcn_sched_barrier(0);
+      if (cB < c1) score_wide(WB, cB);
+      asm volatile("" : "+v"(pB));
+      cA = cC;
+    }
+    return;
+  }
   while (cA < c1) {
     const int cB = c0 + __builtin_amdgcn_readfirstlane(pB);
     const int pC = claim();
