@@ -346,7 +346,8 @@ struct __align__(16) DenseSmem {
   uint4 qhl[4][32];  // per head and 4-channel step: fp16 high parts, then fp16 low parts
   float pb[4][TILE][4];
   MergeArea<4> mrg;
-  uint8_t pad[52 * 1024];
+  int nlist;                // dense fallback: units in the list below
+  uint8_t pad[52 * 1024];   // (dense fallback: the list of units with a row to recompute)
 };
 
 // ------------------------------------------------------------------ prologue
@@ -1512,12 +1513,11 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
 // accumulation: the logits carry the fp32 query to about 2^-22), softmax in the exp2
 // domain, PV in fp32 on the vector ALUs from the probabilities in LDS.  FB: the dense
 // fallback, which skips the units none of whose rows needs recomputing.
+// One (sequence b, kv head and query-head group y, split) of the fp16/bf16 decode.
 template <bool FB>
-__global__ __launch_bounds__(NT, 2) void decode_dense_split(DecodeArgs a) {
-  __shared__ DenseSmem sm;
-  const int b = blockIdx.z;
+__device__ __forceinline__ void dense_unit(const DecodeArgs& a, DenseSmem& sm, int b, int y, int split) {
   const int HG = (a.G + 3) >> 2;
-  const int hkv = blockIdx.y / HG, hg = blockIdx.y % HG;
+  const int hkv = y / HG, hg = y % HG;
   const int hq0 = hkv * a.G + hg * 4;
   const int nh = min(4, a.G - hg * 4);
   if constexpr (FB) {
@@ -1525,7 +1525,6 @@ __global__ __launch_bounds__(NT, 2) void decode_dense_split(DecodeArgs a) {
     for (int hh = 0; hh < nh; ++hh) any = any || fallback_row(a, (size_t)b * a.Hq + hq0 + hh);
     if (!any) return;  // uniform over the workgroup
   }
-  const int split = blockIdx.x;
   const int T = a.seq.v[b];
   const int nchunks = (T + TILE - 1) / TILE;
   const int c0 = split * a.chunks_per_split;
@@ -1644,6 +1643,64 @@ __global__ __launch_bounds__(NT, 2) void decode_dense_split(DecodeArgs a) {
   write_record<false, 4, false>(a, sm.mrg, sm.qo, 0, 4, b, hq0, nh, split, wv, lane);
 }
 
+// The same-shape baseline: one workgroup per (split, kv head and query-head group,
+// sequence).  The dense fallback (FB): a persistent grid over the (unit, split) pairs of
+// the units with a row to recompute, listed by every workgroup in the same order from the
+// rows' certificates and check results (units are few there, and workgroups of units
+// without such a row would only be dispatched to leave); units beyond the list's room
+// take the unlisted form, each workgroup walking all pairs and skipping the idle units.
+template <bool FB>
+__global__ __launch_bounds__(NT, 2) void decode_dense_split(DecodeArgs a) {
+  __shared__ DenseSmem sm;
+  if constexpr (!FB) {
+    dense_unit<false>(a, sm, blockIdx.z, blockIdx.y, blockIdx.x);
+  } else {
+    const int HG = (a.G + 3) >> 2, S = a.n_splits;
+    const int U = a.B * a.H * HG;
+    constexpr int CAP = (int)(sizeof(sm.pad) / sizeof(int));
+    int* list = reinterpret_cast<int*>(sm.pad);
+    __shared__ int cnt[NT];
+    int nitems;
+    if (U <= CAP) {
+      // thread t takes units t, t + NT, ...: count, exclusive scan over the threads, write
+      const int t = threadIdx.x;
+      auto active = [&](int u) {
+        const int b = u / (a.H * HG), y = u % (a.H * HG);
+        const int hq0 = (y / HG) * a.G + (y % HG) * 4, nh = min(4, a.G - (y % HG) * 4);
+        bool any = false;
+        for (int hh = 0; hh < nh; ++hh) any = any || fallback_row(a, (size_t)b * a.Hq + hq0 + hh);
+        return any;
+      };
+      int mine = 0;
+      for (int u = t; u < U; u += NT) mine += active(u) ? 1 : 0;
+      cnt[t] = mine;
+      __syncthreads();
+      if (t == 0) {
+        int run = 0;
+        for (int i = 0; i < NT; ++i) {
+          const int c = cnt[i];
+          cnt[i] = run;
+          run += c;
+        }
+        sm.nlist = run;
+      }
+      __syncthreads();
+      int pos = cnt[t];
+      for (int u = t; u < U; u += NT)
+        if (active(u)) list[pos++] = u;
+      __syncthreads();
+      nitems = sm.nlist * S;
+    } else {
+      nitems = U * S;
+    }
+    for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
+      const int u = U <= CAP ? list[it / S] : it / S;
+      dense_unit<true>(a, sm, u / (a.H * HG), u % (a.H * HG), it % S);
+      __syncthreads();  // the next pair reuses the shared areas
+    }
+  }
+}
+
 // ------------------------------------------------------------------ allocation-free workspace
 // A fixed device array that serves as the decode workspace of kvq_decode_attn_noalloc:
 // arrival counters in its first SCRATCH_CTR_BYTES (only ever written as counters, so
@@ -1734,7 +1791,14 @@ hipError_t launch_decode(const DecodeArgs& a, int k_fmt, int v_fmt, bool dense, 
 // rows only.
 hipError_t launch_dense_fallback(const DecodeArgs& a, hipStream_t s) {
   const int HG = (a.G + 3) / 4;
-  hipLaunchKernelGGL(decode_dense_split<true>, dim3(a.n_splits, a.H * HG, a.B), dim3(NT), 0, s, a);
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_dense_split<true>, NT, 0) != hipSuccess || per_cu <= 0)
+    per_cu = 1;
+  const long pairs = (long)a.n_splits * a.H * HG * a.B;
+  const int grid = (int)std::min<long>(pairs, (long)cus * per_cu);
+  hipLaunchKernelGGL(decode_dense_split<true>, dim3(grid), dim3(NT), 0, s, a);
   hipLaunchKernelGGL(combine_kernel<true>, dim3((a.B * a.Hq + 3) / 4), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
