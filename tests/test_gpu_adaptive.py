@@ -346,3 +346,41 @@ def test_fallback_on_failed_heads_only():
     redo = fail.cpu().numpy() != 0
     assert np.array_equal(out1[~redo], out0[~redo])
     assert attention.row_rel_err(out1[redo], dense[redo]).max() <= TOL
+
+
+def test_fallback_many_units():
+    """More (sequence, kv head, head group) units than the fallback's shared-memory list
+    holds (216 x 64 = 13824 > 13312): every workgroup walks all the unit and split pairs and
+    skips the units without a row to recompute; the failed rows equal dense fp64 attention over
+    the originals and every other row is left as it was."""
+    B, H, T = 216, 64, 64
+    p = kvq.make_params(B, H, H, T, k_fmt="int8", v_fmt="int4", k_group=128, v_group=128, keep_fp16_copy=True)
+    g = kvq.Cache(p, signs=torch.from_numpy(synth.signs(synth.config(3)).copy()).cuda())
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(99)
+    k = torch.randn((B, H, T, 128), generator=gen, device="cuda").half().view(torch.int16)
+    v = torch.randn((B, H, T, 128), generator=gen, device="cuda").half().view(torch.int16)
+    q = torch.randn((B, H, 128), generator=gen, device="cuda").half().view(torch.int16)
+    seq = [T] * (B - 1) + [37]
+    kvq.append(p, g, k, v, [0] * B)
+    out = kvq.decode_attn(p, g, q, seq)
+    torch.cuda.synchronize()
+    out0 = out.cpu().numpy().copy()
+    fail = torch.zeros((B, H), dtype=torch.uint8, device="cuda")
+    rows = [(0, 3), (100, 17), (215, 63)]
+    for b, h in rows:
+        fail[b, h] = 1
+    kvq.dense_fallback(p, g, q, seq, 0.0, out, None, fail=fail)
+    torch.cuda.synchronize()
+    out1 = out.cpu().numpy()
+    redo = fail.cpu().numpy() != 0
+    assert np.array_equal(out1[~redo], out0[~redo])
+    kb = g.bufs["k_orig"].cpu().numpy().view(np.uint16).reshape(B, H, T, 128)
+    vb = g.bufs["v_orig"].cpu().numpy().view(np.uint16).reshape(B, H, T, 128)
+    qb = q.cpu().numpy().view(np.uint16)
+    for b, h in rows:
+        ref = attention.dense_attention(kb[b:b + 1, h:h + 1], vb[b:b + 1, h:h + 1], qb[b:b + 1, h:h + 1], "f16",
+                                        np.array([seq[b]]))
+        err = attention.row_rel_err(out1[b:b + 1, h:h + 1], ref).max()
+        print(f"[adaptive] many-units fallback row ({b}, {h}): rel err {err:.2e}", flush=True)
+        assert err <= TOL
