@@ -1658,8 +1658,9 @@ __global__ __launch_bounds__(NT, 2) void decode_dense_split(DecodeArgs a) {
     const int HG = (a.G + 3) >> 2, S = a.n_splits;
     const int U = a.B * a.H * HG;
     constexpr int CAP = (int)(sizeof(sm.pad) / sizeof(int));
+    static_assert(CAP / NT <= 64, "one 64-bit mask of active units per thread");
     int* list = reinterpret_cast<int*>(sm.pad);
-    __shared__ int cnt[NT];
+    __shared__ int cnt[NT / 64];
     int nitems;
     if (U <= CAP) {
       // thread t takes units t, t + NT, ...: count, exclusive scan over the threads, write
@@ -1671,23 +1672,26 @@ __global__ __launch_bounds__(NT, 2) void decode_dense_split(DecodeArgs a) {
         for (int hh = 0; hh < nh; ++hh) any = any || fallback_row(a, (size_t)b * a.Hq + hq0 + hh);
         return any;
       };
-      int mine = 0;
-      for (int u = t; u < U; u += NT) mine += active(u) ? 1 : 0;
-      cnt[t] = mine;
-      __syncthreads();
-      if (t == 0) {
-        int run = 0;
-        for (int i = 0; i < NT; ++i) {
-          const int c = cnt[i];
-          cnt[i] = run;
-          run += c;
-        }
-        sm.nlist = run;
+      uint64_t bits = 0;  // unit t + NT k active (k < CAP / NT = 52)
+      for (int u = t, k = 0; u < U; u += NT, ++k)
+        if (active(u)) bits |= 1ull << k;
+      const int mine = __builtin_popcountll(bits);
+      // exclusive scan of the counts: inclusive within each wave by shuffles, then the
+      // totals of the waves before
+      const int wl = t & 63, ww = t >> 6;
+      int incl = mine;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o);
+        if (wl >= o) incl += v;
       }
+      if (wl == 63) cnt[ww] = incl;
       __syncthreads();
-      int pos = cnt[t];
-      for (int u = t; u < U; u += NT)
-        if (active(u)) list[pos++] = u;
+      int base = 0;
+      for (int w = 0; w < ww; ++w) base += cnt[w];
+      if (t == NT - 1) sm.nlist = base + incl;
+      int pos = base + incl - mine;
+      for (int u = t, k = 0; u < U; u += NT, ++k)
+        if ((bits >> k) & 1ull) list[pos++] = u;
       __syncthreads();
       nitems = sm.nlist * S;
     } else {
