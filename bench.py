@@ -17,7 +17,7 @@ cache at least 3 x 144 MiB of other data streams through the 256 MB Infinity
 Cache and every timed call reads its inputs from HBM.  Each kernel sequence is
 also timed on its own: batches of back-to-back calls over the rotating buffers,
 HIP events around each batch on the stream the calls are launched on, the median
-of the batch means (decode: 8 batches of 16 calls); and once more as 50 single
+of the batch means (decode: 32 batches of 16 calls, after 64 untimed ones); and once more as 50 single
 calls, each after a 1 GiB read flush (median; includes one launch).
 
 value = decode effective KV GB/s = packed K/V bytes (codes + scales) / median
@@ -683,8 +683,8 @@ def main():
     progress(f"{args.steps} steps timed")
     # each kernel sequence on its own over the rotating buffers
     n_each = max(args.steps, 4 * NROT)
-    batch_time(do_decode, NROT)
-    dec_ms, dec_min = median_of_batches(batch_time, do_decode, 16, 8)
+    batch_time(do_decode, 16 * NROT)  # untimed: the clocks settle under this load first
+    dec_ms, dec_min = median_of_batches(batch_time, do_decode, 16, 32)
     batch_time(do_append, NROT)
     app_ms, _ = median_of_batches(batch_time, do_append, 8, 8)
     batch_time(do_dense, 2)
@@ -744,7 +744,7 @@ def main():
         "decode_isolated_call_us": round(iso_ms * 1e3, 2),
         "decode_isolated_timing": "median of 50 single calls, each after a 1 GiB read flush (includes one launch)",
         "decode_us_min_batch": round(dec_min * 1e3, 2),
-        "decode_timing": "median over 8 batches of the mean of 16 back-to-back calls over 4 rotating caches",
+        "decode_timing": "median over 32 batches of the mean of 16 back-to-back calls over 4 rotating caches",
         "decode_grid_workgroups": n_splits * B * H * ((Hq // H + 3) // 4),
         "decode_splits": n_splits,
         "fp16_decode_us": round(f16_s * 1e6, 2),
