@@ -399,8 +399,8 @@ def bench_workload(cfg_id, args):
     torch.cuda.synchronize()
     step_ms = batch_time(lambda i: (do_append(i), do_decode(i + 2)), args.steps)
     progress(f"{args.steps} steps timed")
-    batch_time(do_decode, nrot)
-    dec_ms, dec_min = median_of_batches(batch_time, do_decode, 16, 4)
+    batch_time(do_decode, 4 * nrot)  # untimed: the clocks settle under this load first
+    dec_ms, dec_min = median_of_batches(batch_time, do_decode, 16, 8)
     batch_time(do_append, nrot)
     app_ms, _ = median_of_batches(batch_time, do_append, 8, 8)
     # the fp16/bf16 same-shape baseline: the certified workload's own originals, else fresh tensors
@@ -417,7 +417,7 @@ def bench_workload(cfg_id, args):
             dense.append((kd, vd))
     dws = kvq.workspace(p)
     dout = torch.empty_like(out)
-    batch_time(lambda i: kvq.decode_attn_dense(p, dense[i % 2][0], dense[i % 2][1], q, seq, ws=dws, out=dout), 2)
+    batch_time(lambda i: kvq.decode_attn_dense(p, dense[i % 2][0], dense[i % 2][1], q, seq, ws=dws, out=dout), 8)
     f16_ms, _ = median_of_batches(batch_time, lambda i: kvq.decode_attn_dense(p, dense[i % 2][0], dense[i % 2][1], q,
                                                                               seq, ws=dws, out=dout), 8, 8)
     progress("batches timed")
@@ -474,7 +474,7 @@ def bench_workload(cfg_id, args):
                      "bytes_per_call": packed + io},
         "decode_us": round(dec_s * 1e6, 2),
         "decode_us_min_batch": round(dec_min * 1e3, 2),
-        "decode_timing": "median over 4 batches of the mean of 16 back-to-back calls",
+        "decode_timing": "median over 8 batches of the mean of 16 back-to-back calls, after untimed ones",
         "decode_grid_workgroups": kvq.decode_splits(p, seq) * B * H * ((Hq // H + 3) // 4),
         "decode_splits": kvq.decode_splits(p, seq),
         "fp16_decode_us": round(f16_s * 1e6, 2),
@@ -685,10 +685,10 @@ def main():
     n_each = max(args.steps, 4 * NROT)
     batch_time(do_decode, 16 * NROT)  # untimed: the clocks settle under this load first
     dec_ms, dec_min = median_of_batches(batch_time, do_decode, 16, 32)
-    batch_time(do_append, NROT)
-    app_ms, _ = median_of_batches(batch_time, do_append, 8, 8)
-    batch_time(do_dense, 2)
-    f16_ms, _ = median_of_batches(batch_time, do_dense, 8, 8)
+    batch_time(do_append, 4 * NROT)
+    app_ms, _ = median_of_batches(batch_time, do_append, 8, 16)
+    batch_time(do_dense, 16)  # the same-shape baseline gets the same untimed start
+    f16_ms, _ = median_of_batches(batch_time, do_dense, 8, 16)
     progress("per-kernel batches timed")
     # isolated calls: 1 GiB read flush, events around each call
     # isolated calls: 10 warm-ups, then the median of 50, each after a 1 GiB read flush
