@@ -881,7 +881,8 @@ __host__ __device__ constexpr int v_groups(int vf, int vg) {
 // Work layout.  A unit is (sequence, kv head, group of 4 query heads).  Workgroup g of
 // the 1-D grid takes split g % S of unit g / S: a range of its 64-token chunks.  Its 8
 // waves share the range out through a counter in LDS: wave w starts with the range's
-// chunk w, and every further chunk is claimed one visit ahead.  The two waves that
+// chunk w, and every further chunk is claimed after the visit before it, its loads in
+// flight while the chunk loaded before it is visited.  The two waves that
 // share a SIMD do not progress equally (the older one wins issue slots), so the faster
 // one simply claims more chunks.
 template <int KF, int KG, int VF, int VG, int MODE>
@@ -1418,25 +1419,27 @@ __global__ __launch_bounds__(NTS) void decode_split(DecodeArgs a) {
   // reloads the current, valid chunk), so the number of memory operations in flight at
   // the loop head is the same on entry and on every iteration; the wave leaves as soon
   // as a claimed index is past the end.  (Claims only grow, so once one is past the end
-  // the next is too: the loop leaves at its head, its single exit.)
+  // the next is too: the loop leaves at its head, its single exit.)  Each chunk is claimed
+  // right after the visit before it, so a wave holds at most one chunk beyond the one it
+  // visits and the waves of a workgroup end closer together; a wave issues its loads at raised
+  // priority, so that they leave before the other wave of its SIMD takes the issue slots.
   while (cA < c1) {
     const int cB = c0 + __builtin_amdgcn_readfirstlane(pB);
-    const int pC = claim();
+    __builtin_amdgcn_s_setprio(3);
     load_chunk<KF, KG, VF, VG>(a, stream, cB < c1 ? cB : cA, lane, tok_a, RB);
     load_aux(cB < c1 ? cB : cA, XB);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     visit(RA, cA, XA);
-    // read the claim only after this chunk's work (an empty asm that takes the register
-    // keeps the read, and the wait for the atomic, from being hoisted above the work)
-    int pCv = pC;
-    asm volatile("" : "+v"(pCv));
-    const int cC = c0 + __builtin_amdgcn_readfirstlane(pCv);
-    pB = claim();
+    const int pC = claim();
+    const int cC = c0 + __builtin_amdgcn_readfirstlane(pC);
+    __builtin_amdgcn_s_setprio(3);
     load_chunk<KF, KG, VF, VG>(a, stream, cC < c1 ? cC : cA, lane, tok_a, RA);
     load_aux(cC < c1 ? cC : cA, XA);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     if (cB < c1) visit(RB, cB, XB);
-    asm volatile("" : "+v"(pB));
+    pB = claim();
     cA = cC;
   }
 
