@@ -62,7 +62,7 @@ __device__ __forceinline__ h4 cat(h2 a, h2 b) { return h4{a.x, a.y, b.x, b.y}; }
 // QK slice s (lanes 4s..4s+3) covers tokens pi(s, 0..3) of the chunk.
 template <int VF>
 __device__ __forceinline__ int tok_of(int s, int r) {
-  if constexpr (VF == KVQ_INT2) return 16 * (s >> 2) + 2 * (s & 3) + ((r & 1) << 3) + (r >> 1);
+  if constexpr (VF == KVQ_INT2) return 4 * s + 2 * (r & 1) + (r >> 1);  // even, then odd codes of a byte
   if constexpr (VF == KVQ_FP4) return 4 * s + r;  // the hardware FP4 pair conversion keeps token order
   return 8 * (s >> 1) + 2 * (s & 1) + ((r & 1) << 2) + (r >> 1);
 }
@@ -70,9 +70,8 @@ __device__ __forceinline__ int tok_of(int s, int r) {
 template <int VF>
 __device__ __forceinline__ int pos_of(int tau) {
   if constexpr (VF == KVQ_INT2) {
-    const int w = tau >> 4, e = tau & 15, rem = e & 7;
-    const int s = 4 * w + (rem >> 1), r = ((e >> 3) & 1) | ((rem & 1) << 1);
-    return 4 * s + r;
+    const int e = tau & 3;
+    return 4 * (tau >> 2) + (((e >> 1) & 1) | ((e & 1) << 1));
   } else {
     const int d = tau >> 3, e = tau & 7;
     const int s = 2 * d + ((e >> 1) & 1), r = ((e >> 2) & 1) | ((e & 1) << 1);
@@ -145,23 +144,21 @@ __device__ __forceinline__ void v_int4_pairs(uint32_t w, h2 out[4]) {
   out[2] = as_h2((w8 & 0x000F000Fu) ^ 0x64086408u) + k1032;                    // tokens 2, 6
   out[3] = as_h2((w8 & 0x00F000F0u) ^ 0x64806480u) * k16 + k72;                // tokens 3, 7
 }
-// int2: element k and k+8 of a 16-token dword, codes 0..3.  (w & mask) | magic is one
-// three-input bit operation (truth table 0xEA over (w, mask, magic), the index of a bit
-// being w<<2 | mask<<1 | magic), which the compiler otherwise issues as an and and an or.
-__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic) {
-  return __builtin_amdgcn_bitop3_b32(w, mask, magic, (unsigned char)0xEA);
-}
+// int2: the 16 codes of a dword (token i in bits 2i, 2i+1), codes 0..3.  A code in the low
+// two bits of an E2M1 nibble (high bits clear) is c / 2 exactly (0, 0.5 as a subnormal, 1,
+// 1.5), so masking the even and the odd codes into nibbles and running the gfx950 pair
+// conversion with scale 2 gives the exact fp16 code, one instruction per two codes.
+// out[2b] = tokens (4b, 4b + 2), out[2b + 1] = tokens (4b + 1, 4b + 3).
 __device__ __forceinline__ void v_int2_pairs(uint32_t w, h2 out[8]) {
-  const uint32_t magic = 0x64006400u;
-  const uint32_t w10 = w >> 10;
-  out[0] = as_h2(and_or(w, 0x00030003u, magic)) + h2{(_Float16)-1024.0f, (_Float16)-1024.0f};
-  out[1] = as_h2(and_or(w, 0x000C000Cu, magic)) * h2{(_Float16)0.25f, (_Float16)0.25f} + h2{(_Float16)-256.0f, (_Float16)-256.0f};
-  out[2] = as_h2(and_or(w, 0x00300030u, magic)) * h2{(_Float16)0.0625f, (_Float16)0.0625f} + h2{(_Float16)-64.0f, (_Float16)-64.0f};
-  out[3] = as_h2(and_or(w, 0x00C000C0u, magic)) * h2{(_Float16)0.015625f, (_Float16)0.015625f} + h2{(_Float16)-16.0f, (_Float16)-16.0f};
-  out[4] = as_h2(and_or(w, 0x03000300u, magic)) * h2{(_Float16)0.00390625f, (_Float16)0.00390625f} + h2{(_Float16)-4.0f, (_Float16)-4.0f};
-  out[5] = as_h2(and_or(w10, 0x00030003u, magic)) + h2{(_Float16)-1024.0f, (_Float16)-1024.0f};
-  out[6] = as_h2(and_or(w10, 0x000C000Cu, magic)) * h2{(_Float16)0.25f, (_Float16)0.25f} + h2{(_Float16)-256.0f, (_Float16)-256.0f};
-  out[7] = as_h2(and_or(w10, 0x00300030u, magic)) * h2{(_Float16)0.0625f, (_Float16)0.0625f} + h2{(_Float16)-64.0f, (_Float16)-64.0f};
+  const uint32_t ev = w & 0x33333333u, od = (w >> 2) & 0x33333333u;
+  out[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 2.0f, 0);
+  out[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 2.0f, 0);
+  out[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 2.0f, 1);
+  out[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 2.0f, 1);
+  out[4] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 2.0f, 2);
+  out[5] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 2.0f, 2);
+  out[6] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ev, 2.0f, 3);
+  out[7] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(od, 2.0f, 3);
 }
 
 template <int VF>
@@ -835,11 +832,14 @@ __device__ __forceinline__ void stage_vmeta(uint16_t* L, int lane, const uint32_
     o.z = as_u(e4m3x2_to_h2(w1 & 0xFF, (w1 >> 8) & 0xFF));
     o.w = as_u(e4m3x2_to_h2((w1 >> 16) & 0xFF, w1 >> 24));
     *reinterpret_cast<uint4*>(L + mm * 64 + 8 * u) = o;
-  } else if constexpr (VF == KVQ_INT2) {
-    const int mm = lane >> 3, u = lane & 7;  // tokens 8u..8u+7 of element mm
-    const int base = (mm * 16 + 4 * (u >> 1)) * 4 + (u & 1);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) L[base + 2 * e] = (uint16_t)(vmeta[e >> 1] >> (16 * (e & 1)));
+  } else if constexpr (VF == KVQ_INT2) {  // tokens 8u..8u+7 of element mm: slices 2u, 2u+1
+    const int mm = lane >> 3, u = lane & 7;
+    uint4 o;
+    o.x = (vmeta[0] & 0xFFFFu) | (vmeta[1] << 16);          // tokens 0, 2
+    o.y = (vmeta[0] >> 16) | (vmeta[1] & 0xFFFF0000u);      // tokens 1, 3
+    o.z = (vmeta[2] & 0xFFFFu) | (vmeta[3] << 16);          // tokens 4, 6
+    o.w = (vmeta[2] >> 16) | (vmeta[3] & 0xFFFF0000u);      // tokens 5, 7
+    *reinterpret_cast<uint4*>(L + mm * 64 + 8 * u) = o;
   } else if constexpr (NM == 8) {  // INT4, groups of 16: tokens 8u..8u+7 of group mm, placed as below
     const int mm = lane >> 3, u = lane & 7;
     const int base = (mm * 16 + 2 * u) * 4;
