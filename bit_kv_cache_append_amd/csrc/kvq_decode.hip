@@ -66,18 +66,6 @@ __device__ __forceinline__ int tok_of(int s, int r) {
   if constexpr (VF == KVQ_FP4) return 4 * s + r;  // the hardware FP4 pair conversion keeps token order
   return 8 * (s >> 1) + 2 * (s & 1) + ((r & 1) << 2) + (r >> 1);
 }
-// inverse: token tau -> position 4s + r
-template <int VF>
-__device__ __forceinline__ int pos_of(int tau) {
-  if constexpr (VF == KVQ_INT2) {
-    const int e = tau & 3;
-    return 4 * (tau >> 2) + (((e >> 1) & 1) | ((e & 1) << 1));
-  } else {
-    const int d = tau >> 3, e = tau & 7;
-    const int s = 2 * d + ((e >> 1) & 1), r = ((e >> 2) & 1) | ((e & 1) << 1);
-    return 4 * s + r;
-  }
-}
 
 // ------------------------------------------------------------------ K formats
 template <int KF>
